@@ -1,0 +1,122 @@
+"""Seeded synthetic inputs for the NVFP4 quantize + GEMM path.
+
+This module only draws random numbers and casts them; it holds none of the
+quantization or GEMM arithmetic, so both the HIP path and the CPU oracle may
+use it.  Everything is generated on the host with numpy's PCG64
+(``numpy.random.default_rng``) in float32 and then rounded to BF16 with
+torch's round-to-nearest-even cast, so the same host bytes feed both sides.
+
+The workloads stand in for the layers the pages talk about (no datasets or
+trained weights are needed or used):
+
+* ``tiny``: a 256x256 by 256x256 FP32 product, seed 0.
+* ``fprop_3b``: one linear layer of a ~3B transformer (the model size of
+  "Full-Stack FP4 ...", section 4): X 8192x3072 (batch 4 x seq 2048), 1% of
+  columns x20 as outlier channels; W 3072x3072 with std 0.02.
+* ``mlp_up_12b``: the MLP up-projection of a 12B hybrid model ("NVFP4 Treina
+  com Precisao de 16 Bits ...", TL;DR): X 16384x5120 with 0.5% of columns x30,
+  W 20480x5120 with std 0.015.
+* ``linear_train``: a full linear training step, M=8192, K=N=4096; X N(0,1),
+  W std 0.02, dY a Student-t(3) gradient scaled by 1e-3 (heavy tailed).
+* ``attn_scores``: attention scores QK^T ("Full-Stack FP4 ...", section 2.4):
+  Q, K [4][32][4096][128], each (batch, head) slice scaled by a per-head RMS
+  drawn log-uniformly in [0.5, 4].
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+
+def to_bf16(a: np.ndarray) -> torch.Tensor:
+    """float32 numpy array -> torch.bfloat16 CPU tensor (RNE)."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """Raw BF16 bit patterns of a CPU bfloat16 tensor as numpy uint16."""
+    assert t.dtype == torch.bfloat16
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def normal(shape, seed: int, std: float = 1.0, outlier_frac: float = 0.0,
+           outlier_scale: float = 1.0) -> np.ndarray:
+    """float32 N(0, std^2) with round(outlier_frac * cols) distinct columns
+    multiplied by outlier_scale."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    if outlier_frac > 0.0:
+        cols = shape[-1]
+        k = int(round(outlier_frac * cols))
+        idx = rng.choice(cols, k, replace=False)
+        x[..., idx] *= np.float32(outlier_scale)
+    return x
+
+
+def student_t(shape, seed: int, df: float = 3.0, scale: float = 1.0) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    return (rng.standard_t(df, size=shape) * scale).astype(np.float32)
+
+
+# --- the five workloads ----------------------------------------------------
+
+def tiny(seed: int = 0):
+    """A and B, 256x256 FP32 N(0,1), drawn in that order.  B is K x N."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((256, 256)).astype(np.float32)
+    b = rng.standard_normal((256, 256)).astype(np.float32)
+    return {"A": torch.from_numpy(a), "B": torch.from_numpy(b)}
+
+
+def fprop_3b(seed: int = 1, m: int = 8192, k: int = 3072, n: int = 3072):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((m, k), dtype=np.float32)
+    idx = rng.choice(k, int(round(0.01 * k)), replace=False)
+    x[:, idx] *= np.float32(20.0)
+    w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    return {"X": to_bf16(x), "W": to_bf16(w)}
+
+
+def mlp_up_12b(seed: int = 2, m: int = 16384, k: int = 5120, n: int = 20480):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((m, k), dtype=np.float32)
+    idx = rng.choice(k, int(round(0.005 * k)), replace=False)
+    x[:, idx] *= np.float32(30.0)
+    w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.015)
+    return {"X": to_bf16(x), "W": to_bf16(w)}
+
+
+LINEAR_SR_SEED = 0x5EED0004
+LINEAR_RHT_SEED = 0x4AD40004
+
+
+def linear_train(seed: int = 3, m: int = 8192, k: int = 4096, n: int = 4096):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((m, k), dtype=np.float32)
+    w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    dy = (rng.standard_t(3.0, size=(m, n)) * 1e-3).astype(np.float32)
+    return {"X": to_bf16(x), "W": to_bf16(w), "dY": to_bf16(dy),
+            "sr_seed": LINEAR_SR_SEED, "rht_seed": LINEAR_RHT_SEED}
+
+
+def attn_scores(seed: int = 4, b: int = 4, h: int = 32, s: int = 4096, d: int = 128):
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name in ("Q", "K"):
+        t = rng.standard_normal((b, h, s, d), dtype=np.float32)
+        rms = np.exp(rng.uniform(np.log(0.5), np.log(4.0), size=(b, h, 1, 1))).astype(np.float32)
+        t *= rms
+        out[name] = to_bf16(t)
+    out["alpha"] = float(np.float32(1.0 / np.sqrt(float(d))))  # 1/sqrt(128) -> 0x3DB504F3
+    return out
+
+
+WORKLOADS = {
+    "tiny": tiny,
+    "fprop_3b": fprop_3b,
+    "mlp_up_12b": mlp_up_12b,
+    "linear_train": linear_train,
+    "attn_scores": attn_scores,
+}

@@ -1,0 +1,215 @@
+"""ctypes front end of the plain-C NVFP4 oracle (oracle/nvfp4_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
+leg of the benchmark are the only callers.  The HIP library and its Python
+binding never import this module.
+
+Arrays are numpy.  BF16 tensors are passed as their raw bit patterns in
+``numpy.uint16`` arrays (numpy has no bfloat16); FP32 as ``numpy.float32``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nvfp4_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+ALONG_COLS, ALONG_ROWS = 0, 1
+RNE, SR = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc: -O2, no FMA contraction, no fast-math."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+             "-shared", "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        build(force=not os.path.exists(_LIB))
+        L = ctypes.CDLL(_LIB)
+        i64, u32, u64, vp = ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_void_p
+        L.oracle_e2m1_decode.argtypes = [ctypes.c_int]
+        L.oracle_e2m1_decode.restype = ctypes.c_double
+        L.oracle_e2m1_encode_rne.argtypes = [ctypes.c_float]
+        L.oracle_e2m1_encode_rne.restype = ctypes.c_int
+        L.oracle_e2m1_encode_sr.argtypes = [ctypes.c_float, u32]
+        L.oracle_e2m1_encode_sr.restype = ctypes.c_int
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_int]
+        L.oracle_e4m3_decode.restype = ctypes.c_double
+        L.oracle_e4m3_encode_rne_sat.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode_rne_sat.restype = ctypes.c_int
+        L.oracle_e2m1_encode_rne_array.argtypes = [vp, i64, vp]
+        L.oracle_e4m3_encode_rne_sat_array.argtypes = [vp, i64, vp]
+        L.oracle_philox4x32_10.argtypes = [vp, vp, vp]
+        L.oracle_sr_word.argtypes = [u64, u32, u64]
+        L.oracle_sr_word.restype = u32
+        L.oracle_rht_signs.argtypes = [u64, vp]
+        L.oracle_rht16.argtypes = [vp, vp]
+        L.oracle_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i64, ctypes.c_int,
+                                      ctypes.c_int, u64, u32, ctypes.c_int, u64, vp, vp, vp]
+        L.oracle_quantize.restype = ctypes.c_int
+        L.oracle_dequantize.argtypes = [vp, vp, ctypes.c_float, i64, i64, vp]
+        L.oracle_gemm_ref.argtypes = [vp, vp, ctypes.c_float, vp, vp, ctypes.c_float, i64, i64,
+                                      i64, i64, ctypes.c_double, vp, i64, vp, vp]
+        L.oracle_gemm_ref.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> ctypes.c_void_p:
+    assert a.flags["C_CONTIGUOUS"] or a.ndim == 0
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+# --- element codecs --------------------------------------------------------
+
+def e2m1_decode(code: int) -> float:
+    return lib().oracle_e2m1_decode(int(code))
+
+
+def e2m1_encode_rne(q: float) -> int:
+    return lib().oracle_e2m1_encode_rne(float(q))
+
+
+def e2m1_encode_sr(q: float, u: int) -> int:
+    return lib().oracle_e2m1_encode_sr(float(q), int(u))
+
+
+def e4m3_decode(byte: int) -> float:
+    return lib().oracle_e4m3_decode(int(byte))
+
+
+def e4m3_encode(y: float) -> int:
+    return lib().oracle_e4m3_encode_rne_sat(float(y))
+
+
+def e2m1_encode_rne_array(q: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    out = np.empty(q.shape, dtype=np.uint8)
+    lib().oracle_e2m1_encode_rne_array(_ptr(q), q.size, _ptr(out))
+    return out
+
+
+def e4m3_encode_array(y: np.ndarray) -> np.ndarray:
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, dtype=np.uint8)
+    lib().oracle_e4m3_encode_rne_sat_array(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+# --- random numbers and the Hadamard transform -----------------------------
+
+def philox4x32_10(counter, key) -> np.ndarray:
+    c = np.asarray(counter, dtype=np.uint32).copy()
+    k = np.asarray(key, dtype=np.uint32).copy()
+    out = np.zeros(4, dtype=np.uint32)
+    lib().oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def sr_word(seed: int, stream: int, n: int) -> int:
+    return int(lib().oracle_sr_word(seed, stream, n))
+
+
+def rht_signs(seed: int) -> np.ndarray:
+    s = np.zeros(16, dtype=np.float32)
+    lib().oracle_rht_signs(seed, _ptr(s))
+    return s
+
+
+def rht16(v: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    w = np.ascontiguousarray(v, dtype=np.float32).copy()
+    s = np.ascontiguousarray(signs, dtype=np.float32)
+    assert w.shape == (16,) and s.shape == (16,)
+    lib().oracle_rht16(_ptr(w), _ptr(s))
+    return w
+
+
+# --- quantize / dequantize / GEMM -----------------------------------------
+
+@dataclass
+class QTensor:
+    """One quantized view: codes [batch][rows][cols/2], scales [batch][rows][cols/16]."""
+    codes: np.ndarray
+    scales: np.ndarray
+    tensor_scale: np.float32
+    batch: int
+    rows: int
+    cols: int
+
+
+def quantize(x: np.ndarray, dtype: int, axis: int = ALONG_COLS, rounding: int = RNE,
+             sr_seed: int = 0, sr_stream: int = 0, rht: bool = False, rht_seed: int = 0,
+             batch: int | None = None) -> QTensor:
+    """Quantize a 2-D [rows][cols] or 3-D [batch][rows][cols] array.
+
+    ``dtype`` is F32 (x float32) or BF16 (x uint16 bit patterns).  For
+    ALONG_ROWS the quantized view is the per-batch transpose of x."""
+    x = np.ascontiguousarray(x)
+    if dtype == BF16:
+        assert x.dtype == np.uint16
+    else:
+        assert x.dtype == np.float32
+    if x.ndim == 2:
+        x3 = x.reshape(1, *x.shape)
+    else:
+        x3 = x
+    b, r, c = x3.shape
+    qr, qc = (r, c) if axis == ALONG_COLS else (c, r)
+    codes = np.zeros((b, qr, qc // 2), dtype=np.uint8)
+    scales = np.zeros((b, qr, qc // 16), dtype=np.uint8)
+    st = np.zeros(1, dtype=np.float32)
+    rc = lib().oracle_quantize(_ptr(x3), dtype, b, r, c, c, r * c, axis, rounding, sr_seed,
+                               sr_stream, int(bool(rht)), rht_seed, _ptr(codes), _ptr(scales),
+                               _ptr(st))
+    if rc != 0:
+        raise ValueError(f"oracle_quantize rejected the arguments (rc={rc})")
+    return QTensor(codes, scales, np.float32(st[0]), b, qr, qc)
+
+
+def dequantize(q: QTensor) -> np.ndarray:
+    out = np.empty((q.batch, q.rows, q.cols), dtype=np.float64)
+    lib().oracle_dequantize(_ptr(q.codes), _ptr(q.scales), float(q.tensor_scale),
+                            q.batch * q.rows, q.cols, _ptr(out))
+    return out
+
+
+def gemm_ref(a: QTensor, b: QTensor, alpha: float = 1.0, batch_index: int = 0,
+             rows: np.ndarray | None = None):
+    """Reference y = alpha * sA * sB * A^ . B^T and its bound sum |.| for one batch
+    index and the selected rows of A (all rows when ``rows`` is None)."""
+    assert a.cols == b.cols
+    M, N, K = a.rows, b.rows, a.cols
+    if rows is None:
+        sel = None
+        nsel = M
+        rp = ctypes.c_void_p(0)
+    else:
+        sel = np.ascontiguousarray(rows, dtype=np.int64)
+        nsel = sel.size
+        rp = _ptr(sel)
+    y = np.empty((nsel, N), dtype=np.float64)
+    s = np.empty((nsel, N), dtype=np.float64)
+    rc = lib().oracle_gemm_ref(_ptr(a.codes), _ptr(a.scales), float(a.tensor_scale),
+                               _ptr(b.codes), _ptr(b.scales), float(b.tensor_scale), M, N, K,
+                               batch_index, float(alpha), rp, nsel, _ptr(y), _ptr(s))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_ref failed (rc={rc})")
+    return y, s
