@@ -1,0 +1,236 @@
+"""Python binding of libnvfp4.so, the gfx950 NVFP4 quantize + block-scaled
+GEMM library (C ABI in include/nvfp4.h).
+
+This layer only marshals arguments: torch provides device memory and the
+current HIP stream, every step of the computation runs in the library's
+kernels.  There is no fallback: without the built library every call raises.
+
+Low-level entry points carry the C names (``nvfp4_quantize``, ``nvfp4_gemm``,
+``nvfp4_linear_fwd_bwd``, ...) and take raw pointers and sizes exactly as the
+C ABI does; ``quantize``, ``gemm`` and ``linear_fwd_bwd`` wrap them for torch
+tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "nvfp4.h")
+
+# enums of include/nvfp4.h
+OK, EINVAL, ESHAPE, EALIGN, EUNSUPPORTED, EHIP, EWORKSPACE = range(7)
+F32, BF16 = 0, 1
+RNE, SR = 0, 1
+ALONG_COLS, ALONG_ROWS = 0, 1
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class QTensorC(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("tensor_scale", ctypes.c_void_p), ("batch", ctypes.c_int64),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class QuantOptsC(ctypes.Structure):
+    _fields_ = [("rounding", ctypes.c_int32), ("rht", ctypes.c_int32),
+                ("sr_seed", ctypes.c_uint64), ("rht_seed", ctypes.c_uint64),
+                ("sr_stream", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+class LinearCfgC(ctypes.Structure):
+    _fields_ = [("sr_seed", ctypes.c_uint64), ("rht_seed", ctypes.c_uint64),
+                ("wgrad_sr_x", ctypes.c_int32), ("dw_dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m bit_block_scaled_nvfp4_amd.build`"
+                " (this package has no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        L.nvfp4_status_string.argtypes = [i32]
+        L.nvfp4_status_string.restype = ctypes.c_char_p
+        L.nvfp4_version.restype = i32
+        L.nvfp4_quantize_workspace_size.restype = sz
+        L.nvfp4_quantize.argtypes = [vp, i32, i64, i64, i64, i64, i64, i32,
+                                     ctypes.POINTER(QuantOptsC), ctypes.POINTER(QTensorC), vp, sz, vp]
+        L.nvfp4_quantize.restype = i32
+        L.nvfp4_gemm.argtypes = [ctypes.POINTER(QTensorC), ctypes.POINTER(QTensorC), vp, i32, i64, i64,
+                                 ctypes.c_float, vp]
+        L.nvfp4_gemm.restype = i32
+        L.nvfp4_linear_workspace_size.argtypes = [i64, i64, i64]
+        L.nvfp4_linear_workspace_size.restype = sz
+        L.nvfp4_linear_fwd_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                                           ctypes.POINTER(LinearCfgC), vp, sz, vp]
+        L.nvfp4_linear_fwd_bwd.restype = i32
+        _lib = L
+    return _lib
+
+
+# --- C-named entry points (raw pointers / sizes) ---------------------------
+
+def nvfp4_status_string(status: int) -> str:
+    return lib().nvfp4_status_string(int(status)).decode()
+
+
+status_string = nvfp4_status_string
+
+
+def nvfp4_version() -> int:
+    return lib().nvfp4_version()
+
+
+def nvfp4_quantize_workspace_size() -> int:
+    return lib().nvfp4_quantize_workspace_size()
+
+
+def nvfp4_linear_workspace_size(M: int, N: int, K: int) -> int:
+    return lib().nvfp4_linear_workspace_size(M, N, K)
+
+
+def nvfp4_quantize(x_ptr, x_dtype, batch, rows, cols, ld, batch_stride, axis, opts, out, workspace,
+                   workspace_bytes, stream) -> int:
+    return lib().nvfp4_quantize(x_ptr, x_dtype, batch, rows, cols, ld, batch_stride, axis,
+                                ctypes.byref(opts) if opts is not None else None,
+                                ctypes.byref(out) if out is not None else None,
+                                workspace, workspace_bytes, stream)
+
+
+def nvfp4_gemm(a, b, c_ptr, c_dtype, ldc, batch_stride_c, alpha, stream) -> int:
+    return lib().nvfp4_gemm(ctypes.byref(a) if a is not None else None,
+                            ctypes.byref(b) if b is not None else None,
+                            c_ptr, c_dtype, ldc, batch_stride_c, ctypes.c_float(alpha), stream)
+
+
+def nvfp4_linear_fwd_bwd(x_ptr, w_ptr, dy_ptr, y_ptr, dx_ptr, dw_ptr, M, N, K, cfg, workspace,
+                         workspace_bytes, stream) -> int:
+    return lib().nvfp4_linear_fwd_bwd(x_ptr, w_ptr, dy_ptr, y_ptr, dx_ptr, dw_ptr, M, N, K,
+                                      ctypes.byref(cfg) if cfg is not None else None,
+                                      workspace, workspace_bytes, stream)
+
+
+# --- torch wrappers ----------------------------------------------------------
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise NVFP4Error(status, what)
+
+
+@dataclass
+class QTensor:
+    """A quantized view on the GPU: codes [batch][rows][cols/2] (uint8),
+    scales [batch][rows][cols/16] (uint8, E4M3FN), tensor_scale [1] (float32)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tensor_scale: torch.Tensor
+    batch: int
+    rows: int
+    cols: int
+
+    def c_struct(self) -> QTensorC:
+        return QTensorC(self.codes.data_ptr(), self.scales.data_ptr(), self.tensor_scale.data_ptr(),
+                        self.batch, self.rows, self.cols)
+
+    @staticmethod
+    def empty(batch: int, rows: int, cols: int, device) -> "QTensor":
+        n = batch * rows * cols
+        return QTensor(torch.empty(max(n // 2, 1), dtype=torch.uint8, device=device)[: n // 2]
+                       .view(batch, rows, cols // 2),
+                       torch.empty(max(n // 16, 1), dtype=torch.uint8, device=device)[: n // 16]
+                       .view(batch, rows, cols // 16),
+                       torch.empty(1, dtype=torch.float32, device=device), batch, rows, cols)
+
+
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """Zero-filled device workspace (the C ABI requires zeros before first use)."""
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def quantize(x: torch.Tensor, axis: int = ALONG_COLS, rounding: int = RNE, sr_seed: int = 0,
+             sr_stream: int = 0, rht: bool = False, rht_seed: int = 0, out: QTensor | None = None,
+             workspace: torch.Tensor | None = None) -> QTensor:
+    """Quantize a 2-D [rows][cols] or 3-D [batch][rows][cols] CUDA tensor
+    (bfloat16 or float32, last dimension contiguous)."""
+    if x.dim() == 2:
+        x3 = x.unsqueeze(0)
+    elif x.dim() == 3:
+        x3 = x
+    else:
+        raise ValueError("x must be 2-D or 3-D")
+    if x3.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("x must be bfloat16 or float32")
+    if x3.size(2) > 1 and x3.stride(2) != 1:
+        raise ValueError("the last dimension of x must be contiguous")
+    b, r, c = x3.shape
+    qr, qc = (r, c) if axis == ALONG_COLS else (c, r)
+    if out is None:
+        out = QTensor.empty(b, qr, qc, x.device)
+    if workspace is None:
+        workspace = new_workspace(nvfp4_quantize_workspace_size(), x.device)
+    opts = QuantOptsC(rounding, int(bool(rht)), sr_seed, rht_seed, sr_stream, 0)
+    q = out.c_struct()
+    st = nvfp4_quantize(x3.data_ptr(), BF16 if x3.dtype == torch.bfloat16 else F32, b, r, c,
+                        x3.stride(1) if r > 1 else c, x3.stride(0) if b > 1 else r * c, axis, opts, q,
+                        workspace.data_ptr(), workspace.numel(), _stream(x.device))
+    _check(st, "nvfp4_quantize")
+    return out
+
+
+def gemm(a: QTensor, b: QTensor, out_dtype: torch.dtype = torch.bfloat16, alpha: float = 1.0,
+         out: torch.Tensor | None = None) -> torch.Tensor:
+    """C[b] = alpha * A^[b] . B^[b]^T -> [batch][M][N] (squeezed to 2-D when batch == 1)."""
+    created = out is None
+    if created:
+        out = torch.empty(a.batch, a.rows, b.rows, dtype=out_dtype, device=a.codes.device)
+    o3 = out if out.dim() == 3 else out.unsqueeze(0)
+    ca, cb = a.c_struct(), b.c_struct()
+    st = nvfp4_gemm(ca, cb, o3.data_ptr(), BF16 if o3.dtype == torch.bfloat16 else F32,
+                    o3.stride(1) if o3.size(1) > 1 else o3.size(2),
+                    o3.stride(0) if o3.size(0) > 1 else o3.size(1) * o3.size(2), alpha,
+                    _stream(a.codes.device))
+    _check(st, "nvfp4_gemm")
+    return out[0] if created and a.batch == 1 else out
+
+
+def linear_fwd_bwd(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, sr_seed: int, rht_seed: int,
+                   wgrad_sr_x: bool = True, dw_dtype: torch.dtype = torch.bfloat16,
+                   workspace: torch.Tensor | None = None):
+    """Fprop, Dgrad and Wgrad of Y = X W^T in NVFP4; returns (Y, dX, dW)."""
+    M, K = x.shape
+    N = w.shape[0]
+    for t in (x, w, dy):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("x, w, dy must be contiguous bfloat16")
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device=x.device)
+    dw = torch.empty(N, K, dtype=dw_dtype, device=x.device)
+    need = nvfp4_linear_workspace_size(M, N, K)
+    if workspace is None:
+        workspace = new_workspace(need, x.device)
+    cfg = LinearCfgC(sr_seed, rht_seed, int(bool(wgrad_sr_x)), F32 if dw_dtype == torch.float32 else BF16)
+    st = nvfp4_linear_fwd_bwd(x.data_ptr(), w.data_ptr(), dy.data_ptr(), y.data_ptr(), dx.data_ptr(),
+                              dw.data_ptr(), M, N, K, cfg, workspace.data_ptr(), workspace.numel(),
+                              _stream(x.device))
+    _check(st, "nvfp4_linear_fwd_bwd")
+    return y, dx, dw

@@ -1,0 +1,272 @@
+// api.hip -- the C ABI declared in include/nvfp4.h: argument validation (no
+// HIP call before it passes), launch of the quantize / GEMM kernels, and the
+// linear-layer driver (Fprop, Dgrad, Wgrad: six quantizations and three
+// GEMMs on one stream, no host synchronisation).  Linear-projection training
+// with NVFP4 GEMMs is the module "Full-Stack FP4 ..." treats in sections 1
+// and 2.1; gradient tensors take stochastic rounding and the Wgrad operands
+// the Hadamard mixing of section 2.2.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/nvfp4.h"
+#include "internal.hpp"
+
+#define NVFP4_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using nvfp4::QuantCtrl;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxExtent = int64_t(1) << 40;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Validation of one quantized-view descriptor against an expected shape.
+nvfp4_status check_view(const nvfp4_qtensor *q, int64_t batch, int64_t rows, int64_t cols) {
+  if (!q) return NVFP4_EINVAL;
+  if (q->batch != batch || q->rows != rows || q->cols != cols) return NVFP4_EINVAL;
+  if (batch * rows * cols > 0 && (!q->codes || !q->scales)) return NVFP4_EINVAL;
+  if (!q->tensor_scale) return NVFP4_EINVAL;
+  if (!aligned(q->codes, 16) || !aligned(q->scales, 4) || !aligned(q->tensor_scale, 4))
+    return NVFP4_EALIGN;
+  return NVFP4_OK;
+}
+
+nvfp4_status validate_quantize(const void *x, int32_t x_dtype, int64_t batch, int64_t rows,
+                               int64_t cols, int64_t ld, int64_t batch_stride, int32_t axis,
+                               const nvfp4_quant_opts *opts, const nvfp4_qtensor *out,
+                               const void *workspace, size_t workspace_bytes) {
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (axis != NVFP4_ALONG_COLS && axis != NVFP4_ALONG_ROWS) return NVFP4_EINVAL;
+  if (opts) {
+    if (opts->rounding != NVFP4_RNE && opts->rounding != NVFP4_SR) return NVFP4_EINVAL;
+    if (opts->rht != 0 && opts->rht != 1) return NVFP4_EINVAL;
+    if (opts->reserved != 0) return NVFP4_EINVAL;
+  }
+  if (batch < 0 || rows < 0 || cols < 0) return NVFP4_ESHAPE;
+  if (batch > kMaxExtent || rows > kMaxExtent || cols > kMaxExtent) return NVFP4_ESHAPE;
+  const int64_t contraction = axis == NVFP4_ALONG_COLS ? cols : rows;
+  if (contraction % 16 != 0) return NVFP4_ESHAPE;
+  const bool empty = batch == 0 || rows == 0 || cols == 0;
+  if (!empty) {
+    if (!x) return NVFP4_EINVAL;
+    if (ld < cols) return NVFP4_ESHAPE;
+    if (batch > 1 && batch_stride < rows * ld) return NVFP4_ESHAPE;
+    if ((double)batch * (double)rows * (double)cols > 4.0e18) return NVFP4_ESHAPE;
+  }
+  const int64_t esize = x_dtype == NVFP4_F32 ? 4 : 2;
+  if (!empty && (!aligned(x, 16) || (ld * esize) % 16 != 0 || (batch > 1 && (batch_stride * esize) % 16 != 0)))
+    return NVFP4_EALIGN;
+  const int64_t qr = axis == NVFP4_ALONG_COLS ? rows : cols;
+  const int64_t qc = axis == NVFP4_ALONG_COLS ? cols : rows;
+  nvfp4_status st = check_view(out, batch, qr, qc);
+  if (st != NVFP4_OK) return st;
+  if (!workspace || workspace_bytes < sizeof(QuantCtrl)) return NVFP4_EWORKSPACE;
+  if (!aligned(workspace, 256)) return NVFP4_EALIGN;
+  return NVFP4_OK;
+}
+
+nvfp4::QuantProblem make_quant(const void *x, bool bf16, int64_t batch, int64_t rows, int64_t cols,
+                               int64_t ld, int64_t bstride, bool along_rows, const nvfp4_quant_opts *o,
+                               const nvfp4_qtensor *out, void *ws) {
+  nvfp4::QuantProblem p{};
+  p.x = x;
+  p.bf16 = bf16;
+  p.batch = batch;
+  p.rows = rows;
+  p.cols = cols;
+  p.ld = ld;
+  p.bstride = bstride;
+  p.along_rows = along_rows;
+  p.sr = o && o->rounding == NVFP4_SR;
+  p.rht = o && o->rht;
+  p.sr_seed = o ? o->sr_seed : 0;
+  p.rht_seed = o ? o->rht_seed : 0;
+  p.sr_stream = o ? o->sr_stream : 0;
+  p.codes = out->codes;
+  p.scales = out->scales;
+  p.tensor_scale = out->tensor_scale;
+  p.ctrl = static_cast<QuantCtrl *>(ws);
+  return p;
+}
+
+nvfp4_status validate_gemm(const nvfp4_qtensor *a, const nvfp4_qtensor *b, const void *c,
+                           int32_t c_dtype, int64_t ldc, int64_t batch_stride_c) {
+  if (!a || !b) return NVFP4_EINVAL;
+  if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (a->batch < 0 || a->rows < 0 || a->cols < 0 || b->rows < 0) return NVFP4_ESHAPE;
+  if (a->cols % 16 != 0) return NVFP4_ESHAPE;
+  if (a->batch != b->batch || a->cols != b->cols) return NVFP4_EINVAL;
+  if (a->rows > kMaxExtent || b->rows > kMaxExtent || a->cols > kMaxExtent) return NVFP4_ESHAPE;
+  nvfp4_status st = check_view(a, a->batch, a->rows, a->cols);
+  if (st != NVFP4_OK) return st;
+  st = check_view(b, b->batch, b->rows, b->cols);
+  if (st != NVFP4_OK) return st;
+  const int64_t M = a->rows, N = b->rows;
+  if (a->batch * M * N > 0) {
+    if (!c) return NVFP4_EINVAL;
+    if (ldc < N) return NVFP4_ESHAPE;
+    if (a->batch > 1 && batch_stride_c < M * ldc) return NVFP4_ESHAPE;
+    if (!aligned(c, c_dtype == NVFP4_F32 ? 4 : 2)) return NVFP4_EALIGN;
+    if (a->batch > 65535) return NVFP4_EUNSUPPORTED;
+  }
+  return NVFP4_OK;
+}
+
+nvfp4::GemmProblem make_gemm(const nvfp4_qtensor *a, const nvfp4_qtensor *b, void *c, int32_t c_dtype,
+                             int64_t ldc, int64_t batch_stride_c, float alpha) {
+  nvfp4::GemmProblem p{};
+  p.a_codes = a->codes;
+  p.a_scales = a->scales;
+  p.a_st = a->tensor_scale;
+  p.b_codes = b->codes;
+  p.b_scales = b->scales;
+  p.b_st = b->tensor_scale;
+  p.batch = a->batch;
+  p.M = a->rows;
+  p.N = b->rows;
+  p.K = a->cols;
+  p.c = c;
+  p.c_bf16 = c_dtype == NVFP4_BF16;
+  p.ldc = ldc;
+  p.bstride_c = batch_stride_c;
+  p.alpha = alpha;
+  return p;
+}
+
+// Linear-driver workspace: six quantized views, each followed by its tensor
+// scale and quantize control block, every region 256-byte aligned.
+struct LinearLayout {
+  size_t codes[6], scales[6], st[6], ctrl[6];
+  int64_t rows[6], cols[6];
+  size_t total;
+};
+
+LinearLayout linear_layout(int64_t M, int64_t N, int64_t K) {
+  LinearLayout L{};
+  const int64_t shapes[6][2] = {{M, K}, {N, K}, {M, N}, {K, N}, {N, M}, {K, M}};
+  size_t off = 0;
+  for (int i = 0; i < 6; ++i) {
+    L.rows[i] = shapes[i][0];
+    L.cols[i] = shapes[i][1];
+    const size_t n = (size_t)shapes[i][0] * (size_t)shapes[i][1];
+    L.codes[i] = off;
+    off = round_up(off + n / 2, 256);
+    L.scales[i] = off;
+    off = round_up(off + n / 16, 256);
+    L.st[i] = off;
+    off += 256;
+    L.ctrl[i] = off;
+    off += sizeof(QuantCtrl);
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+NVFP4_EXPORT const char *nvfp4_status_string(int32_t status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_EINVAL: return "invalid argument";
+    case NVFP4_ESHAPE: return "unsupported shape (contraction length must be a multiple of 16)";
+    case NVFP4_EALIGN: return "misaligned pointer or stride";
+    case NVFP4_EUNSUPPORTED: return "unsupported request";
+    case NVFP4_EHIP: return "HIP launch failed";
+    case NVFP4_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+NVFP4_EXPORT int32_t nvfp4_version(void) { return (1 << 16) | 0; }
+
+NVFP4_EXPORT size_t nvfp4_quantize_workspace_size(void) { return sizeof(QuantCtrl); }
+
+NVFP4_EXPORT nvfp4_status nvfp4_quantize(const void *x, int32_t x_dtype, int64_t batch, int64_t rows,
+                                         int64_t cols, int64_t ld, int64_t batch_stride, int32_t axis,
+                                         const nvfp4_quant_opts *opts, const nvfp4_qtensor *out,
+                                         void *workspace, size_t workspace_bytes, void *stream) {
+  nvfp4_status st = validate_quantize(x, x_dtype, batch, rows, cols, ld, batch_stride, axis, opts, out,
+                                      workspace, workspace_bytes);
+  if (st != NVFP4_OK) return st;
+  const nvfp4::QuantProblem p = make_quant(x, x_dtype == NVFP4_BF16, batch, rows, cols, ld, batch_stride,
+                                           axis == NVFP4_ALONG_ROWS, opts, out, workspace);
+  return nvfp4::launch_quantize(p, static_cast<hipStream_t>(stream));
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_gemm(const nvfp4_qtensor *a, const nvfp4_qtensor *b, void *c, int32_t c_dtype,
+                                     int64_t ldc, int64_t batch_stride_c, float alpha, void *stream) {
+  nvfp4_status st = validate_gemm(a, b, c, c_dtype, ldc, batch_stride_c);
+  if (st != NVFP4_OK) return st;
+  return nvfp4::launch_gemm(make_gemm(a, b, c, c_dtype, ldc, batch_stride_c, alpha),
+                            static_cast<hipStream_t>(stream));
+}
+
+NVFP4_EXPORT size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxExtent || N > kMaxExtent || K > kMaxExtent) return 0;
+  return linear_layout(M, N, K).total;
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_linear_fwd_bwd(const void *x, const void *w, const void *dy, void *y,
+                                               void *dx, void *dw, int64_t M, int64_t N, int64_t K,
+                                               const nvfp4_linear_cfg *cfg, void *workspace,
+                                               size_t workspace_bytes, void *stream) {
+  if (!cfg || !x || !w || !dy || !y || !dx || !dw) return NVFP4_EINVAL;
+  if (cfg->dw_dtype != NVFP4_F32 && cfg->dw_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0 || M % 16 || N % 16 || K % 16) return NVFP4_ESHAPE;
+  if (M > kMaxExtent || N > kMaxExtent || K > kMaxExtent) return NVFP4_ESHAPE;
+  for (const void *p : {x, w, dy, static_cast<const void *>(y), static_cast<const void *>(dx),
+                        static_cast<const void *>(dw)})
+    if (!aligned(p, 16)) return NVFP4_EALIGN;
+  const LinearLayout L = linear_layout(M, N, K);
+  if (!workspace || workspace_bytes < L.total) return NVFP4_EWORKSPACE;
+  if (!aligned(workspace, 256)) return NVFP4_EALIGN;
+
+  uint8_t *base = static_cast<uint8_t *>(workspace);
+  nvfp4_qtensor v[6];
+  for (int i = 0; i < 6; ++i) {
+    v[i].codes = base + L.codes[i];
+    v[i].scales = base + L.scales[i];
+    v[i].tensor_scale = reinterpret_cast<float *>(base + L.st[i]);
+    v[i].batch = 1;
+    v[i].rows = L.rows[i];
+    v[i].cols = L.cols[i];
+  }
+  auto ctrl = [&](int i) { return static_cast<void *>(base + L.ctrl[i]); };
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  nvfp4_quant_opts rne{};
+  nvfp4_quant_opts dy_row{NVFP4_SR, 0, cfg->sr_seed, cfg->rht_seed, 1u, 0u};
+  nvfp4_quant_opts dy_col{NVFP4_SR, 1, cfg->sr_seed, cfg->rht_seed, 2u, 0u};
+  nvfp4_quant_opts x_col{cfg->wgrad_sr_x ? NVFP4_SR : NVFP4_RNE, 1, cfg->sr_seed, cfg->rht_seed, 3u, 0u};
+
+  struct Q {
+    const void *src;
+    int64_t rows, cols;
+    bool along_rows;
+    const nvfp4_quant_opts *o;
+  } qs[6] = {{x, M, K, false, &rne},   {w, N, K, false, &rne},  {dy, M, N, false, &dy_row},
+             {w, N, K, true, &rne},    {dy, M, N, true, &dy_col}, {x, M, K, true, &x_col}};
+  const struct {
+    int a, b;
+    void *c;
+    int32_t dtype;
+    int64_t ldc;
+  } gs[3] = {{0, 1, y, NVFP4_BF16, N}, {2, 3, dx, NVFP4_BF16, K}, {4, 5, dw, cfg->dw_dtype, K}};
+
+  for (int gi = 0; gi < 3; ++gi) {
+    for (int qi : {gs[gi].a, gs[gi].b}) {
+      const Q &q = qs[qi];
+      const nvfp4::QuantProblem p =
+          make_quant(q.src, true, 1, q.rows, q.cols, q.cols, q.rows * q.cols, q.along_rows, q.o, &v[qi], ctrl(qi));
+      const nvfp4_status st = nvfp4::launch_quantize(p, s);
+      if (st != NVFP4_OK) return st;
+    }
+    const nvfp4_status st =
+        nvfp4::launch_gemm(make_gemm(&v[gs[gi].a], &v[gs[gi].b], gs[gi].c, gs[gi].dtype, gs[gi].ldc, 0, 1.0f), s);
+    if (st != NVFP4_OK) return st;
+  }
+  return NVFP4_OK;
+}

@@ -1,0 +1,195 @@
+// device_codec.hpp -- gfx950 device primitives for NVFP4: E4M3 / E2M1 codecs,
+// Philox4x32-10, the 16-point sign-randomised Hadamard butterflies and
+// wavefront reductions.
+//
+// The element and scale formats are OCP MX E2M1 and OCP FP8 E4M3FN; the
+// pages ("NVIDIA acelera o pre-treinamento de LLM: NVFP4 no Blackwell ...",
+// section "Por Que Cada Porcento E Importante") only fix a 4-bit element with
+// its own scaling scheme.  Encoders here work on IEEE-754 bit patterns so that
+// each step costs a few integer VALU ops per element.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// ---------------------------------------------------------------------------
+// BF16 pairs
+// ---------------------------------------------------------------------------
+
+// A dword holding two BF16 values (element 2j in the low half) widens exactly.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// FP32 -> BF16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// E4M3FN block scale (only non-negative codes 0x00..0x7E are produced)
+// ---------------------------------------------------------------------------
+
+// Value of a non-negative E4M3FN code.  Codes below 8 are subnormal
+// (m * 2^-9); above, the 7 code bits shifted to the FP32 exponent/mantissa
+// position plus an exponent rebias of 127 - 7 give the value directly.
+__device__ __forceinline__ float e4m3_value(uint32_t s) {
+  return (s < 8u) ? (float)s * 0x1p-9f : __uint_as_float((s + (120u << 3)) << 20);
+}
+
+// y >= 0 -> E4M3FN code, round to nearest even, saturating at 448 (0x7E).
+// Normal range: add the rounding bias below the 3 kept mantissa bits (ties to
+// even through the kept LSB); a carry out of the mantissa bumps the exponent,
+// which is the correct rounding.  Subnormal range (< 2^-6): round y * 2^9 to
+// an integer; 8 there is the code of 2^-6.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  y = fminf(y, 448.0f);
+  if (y < 0x1p-6f) return (uint32_t)__builtin_rintf(y * 512.0f);
+  uint32_t u = __float_as_uint(y);
+  return ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 element encode
+// ---------------------------------------------------------------------------
+
+// Round-to-nearest-even onto {0, .5, 1, 1.5, 2, 3, 4, 6}, saturating at 6,
+// returning the 4-bit code (sign in bit 3, kept for zero results).
+// |q| >= 1 is a normal E2M1 number: round the FP32 mantissa to 1 bit with the
+// usual bias trick and rebias the exponent (127 -> 1).  |q| < 1 is the
+// subnormal range with step 0.5: round 2|q| to an integer (0, 1 or 2).
+__device__ __forceinline__ uint32_t e2m1_rne(float q) {
+  uint32_t sign = (__float_as_uint(q) >> 28) & 8u;
+  float a = fminf(fabsf(q), 6.0f);
+  uint32_t ua = __float_as_uint(a);
+  uint32_t nrm = ((ua + 0x1FFFFFu + ((ua >> 22) & 1u)) >> 22) - 252u;
+  uint32_t sub = (uint32_t)__builtin_rintf(a * 2.0f);
+  return sign | ((a < 1.0f) ? sub : nrm);
+}
+
+// Stochastic rounding onto the same grid with a 16-bit uniform word u: the
+// magnitude rounds up iff u < 2^16 * (|q| - lo) / step.  For |q| in [1, 6)
+// lo is |q| truncated to one mantissa bit and (|q| - lo) / step is the
+// remaining 22 mantissa bits over 2^22, so the test is an integer compare.
+// For |q| < 1 the step is 0.5: t = 2|q| is exact and lo = floor(t).  At 6 the
+// truncated code is already 7 and the fraction is 0, so no special case.
+__device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t u16) {
+  uint32_t sign = (__float_as_uint(q) >> 28) & 8u;
+  float a = fminf(fabsf(q), 6.0f);
+  uint32_t ua = __float_as_uint(a);
+  uint32_t code;
+  if (a >= 1.0f) {
+    uint32_t lo = (ua >> 22) - 252u;
+    code = lo + (((u16 << 6) < (ua & 0x3FFFFFu)) ? 1u : 0u);
+  } else {
+    float t = a * 2.0f;
+    float fl = __builtin_floorf(t);
+    code = (uint32_t)fl + (((float)u16 < (t - fl) * 65536.0f) ? 1u : 0u);
+  }
+  return sign | code;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11)
+// ---------------------------------------------------------------------------
+
+struct u32x4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+    c = u32x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// The 16 signs of the random Hadamard transform as a bit mask (bit j set:
+// s_j = -1): word 0 of the block at counter (0, 0, ~0, 0) under the seed.
+__device__ __forceinline__ uint32_t rht_sign_mask(uint64_t seed) {
+  return philox4x32_10(u32x4{0u, 0u, 0xFFFFFFFFu, 0u}, (uint32_t)seed, (uint32_t)(seed >> 32)).x &
+         0xFFFFu;
+}
+
+// The eight 16-bit stochastic-rounding words of logical elements 8g..8g+7.
+__device__ __forceinline__ u32x4 sr_block(uint64_t g, uint32_t stream, uint64_t seed) {
+  return philox4x32_10(u32x4{(uint32_t)g, (uint32_t)(g >> 32), stream, 0u}, (uint32_t)seed,
+                       (uint32_t)(seed >> 32));
+}
+
+__device__ __forceinline__ uint32_t sr_word(const u32x4 &r, int j) {
+  const uint32_t w = (j >> 1) == 0 ? r.x : (j >> 1) == 1 ? r.y : (j >> 1) == 2 ? r.z : r.w;
+  return (j & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// ---------------------------------------------------------------------------
+// Random Hadamard transform on 16 values held by one lane
+// ---------------------------------------------------------------------------
+
+// v <- (1/4) H16 diag(s) v; signs flip by XOR of the sign bit (exact), the
+// butterflies run with span 1, 2, 4, 8 in that order in FP32.
+__device__ __forceinline__ void rht16(float (&v)[16], uint32_t mask) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((mask >> j) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.25f;
+}
+
+// The same transform when a 16-block is split over a lane pair (even lane:
+// elements 0..7, odd lane: 8..15).  Spans 1, 2, 4 stay inside the lane; span 8
+// pairs element j of the even lane with element j of the odd lane.
+__device__ __forceinline__ void rht16_pair(float (&v)[8], uint32_t mask, bool odd) {
+  const uint32_t m = odd ? (mask >> 8) : mask;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((m >> j) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = __shfl_xor(v[j], 1);
+    v[j] = odd ? (p - v[j]) : (v[j] + p);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = v[j] * 0.25f;
+}
+
+// ---------------------------------------------------------------------------
+// Reductions over |x| as unsigned bit patterns (NaN patterns sort above all
+// finite values, so a NaN input poisons the maximum).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f) & 0x7FFFFFFFu; }
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
+  return v;
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,175 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 quantize + block-scaled GEMM
+ * library (libnvfp4.so).
+ *
+ * What the library computes.  The pages this follows describe NVFP4 as a
+ * 4-bit floating-point format for the weights and activations that enter the
+ * GEMMs of LLM linear layers, with BF16/FP32 kept for the accumulators and a
+ * dedicated scaling scheme because the 4-bit grid is sparse
+ * ("NVIDIA acelera o pre-treinamento de LLM: NVFP4 no Blackwell em conjunto
+ * com JAX e MaxText", sections "Por Que Cada Porcento E Importante" and
+ * "Como o Treinamento Mixed-Precision Funciona com NVFP4"); Hadamard mixing
+ * and stochastic rounding appear in "Full-Stack FP4: Stable LLM Pretraining
+ * with Quantized Projections, Optimizers, and Attention", section 2.2, and
+ * NVFP4 GEMMs for linear-layer training in the same page's section 1 and in
+ * "NVFP4 Treina com Precisao de 16 Bits ...", section "Contexto e
+ * background".  The concrete encoding used here:
+ *   - element: OCP MX E2M1 (values +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}), two codes
+ *     per byte, element 2j in the low nibble of byte j;
+ *   - block scale: OCP FP8 E4M3FN, one per 16 consecutive elements along the
+ *     contraction (GEMM K) dimension;
+ *   - tensor scale: FP32 s_t = fl(amax / 2688) with 2688 = 6 * 448, a decode
+ *     factor (value = E2M1 * E4M3 * s_t).
+ * Quantize steps, in order, for each 16-element block v of the logical view:
+ *   (optional) v <- (1/4) H16 diag(s) v, FP32 butterflies in stage order 1,2,4,8;
+ *   A = max |v| over the tensor;  s_t = fl(A / 2688);  D6 = fl(6 s_t);
+ *   S = E4M3_RNE(min(fl(max|v in block| / D6), 448))  (S = 0 when s_t = 0);
+ *   e = fl(E4M3(S) * s_t);  r = e ? fl(1 / e) : 0;  q = fl(v * r);
+ *   code = E2M1 round-to-nearest-even(q) saturating at 6, or stochastic
+ *   rounding with a 16-bit word from Philox4x32-10.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named in a struct or argument as "device" are device memory of
+ *     the current HIP device; the structs themselves are host memory read
+ *     during the call only.  The caller owns every buffer.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on `stream`; it never synchronises and never allocates.
+ *   - Synchronous return codes report argument errors (checked before any HIP
+ *     call) and launch failures.  Data-dependent problems are not reported:
+ *     inputs must be finite and the tensor amax either 0 or >= 2^-100; a
+ *     non-finite input leaves a non-finite tensor scale and unspecified codes.
+ *   - Workspaces must be zero-filled before their first use.  Each call leaves
+ *     the control words it used zero again, so a workspace can be reused by
+ *     later calls on the same stream without clearing.  Calls that are in
+ *     flight at the same time need separate workspaces.  After an
+ *     NVFP4_EHIP error, zero the workspace again.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_EINVAL = 1,      /* null pointer, unknown enum value, inconsistent views */
+  NVFP4_ESHAPE = 2,      /* contraction length not a multiple of 16, negative or oversized extents */
+  NVFP4_EALIGN = 3,      /* a pointer or stride breaks the alignment stated below */
+  NVFP4_EUNSUPPORTED = 4,/* a valid request this build does not implement */
+  NVFP4_EHIP = 5,        /* the HIP runtime refused a launch */
+  NVFP4_EWORKSPACE = 6   /* workspace missing or smaller than the *_workspace_size() figure */
+} nvfp4_status;
+
+typedef enum nvfp4_dtype { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
+typedef enum nvfp4_rounding { NVFP4_RNE = 0, NVFP4_SR = 1 } nvfp4_rounding;
+/* ALONG_COLS: blocks run along the input's contiguous dimension; the
+ * quantized view has the input's shape.  ALONG_ROWS: blocks run down the
+ * input's columns; the quantized view is the per-batch transpose. */
+typedef enum nvfp4_axis { NVFP4_ALONG_COLS = 0, NVFP4_ALONG_ROWS = 1 } nvfp4_axis;
+
+/* One quantized view [batch][rows][cols], cols = contraction length (a
+ * multiple of 16).  All three arrays are dense and owned by the caller:
+ *   codes        device, batch*rows*cols/2 bytes, 16-byte aligned;
+ *   scales       device, batch*rows*cols/16 bytes (E4M3FN bit patterns,
+ *                row-major, no swizzle), 4-byte aligned;
+ *   tensor_scale device, one float: written by nvfp4_quantize, read on the
+ *                device by nvfp4_gemm (no host round trip). */
+typedef struct nvfp4_qtensor {
+  uint8_t *codes;
+  uint8_t *scales;
+  float *tensor_scale;
+  int64_t batch, rows, cols;
+} nvfp4_qtensor;
+
+/* Quantizer options.  rounding: an nvfp4_rounding.  rht: 0/1, apply the
+ * 16-point random Hadamard transform along the contraction dimension first;
+ * its +-1 diagonal is bit j of word 0 of Philox4x32-10(counter = (0, 0,
+ * 0xFFFFFFFF, 0), key = rht_seed).  Stochastic rounding of logical element n
+ * (row-major index in the quantized view) uses 16 bits of Philox4x32-10(
+ * counter = (n/8 low, n/8 high, sr_stream, 0), key = sr_seed): the low half
+ * of output word (n%8)/2 for even n, the high half for odd n; the magnitude
+ * rounds up iff word < 2^16 * (|q| - lo) / (hi - lo). */
+typedef struct nvfp4_quant_opts {
+  int32_t rounding;
+  int32_t rht;
+  uint64_t sr_seed;
+  uint64_t rht_seed;
+  uint32_t sr_stream;
+  uint32_t reserved; /* must be 0 */
+} nvfp4_quant_opts;
+
+/* Human-readable name of a status code (static storage). */
+const char *nvfp4_status_string(int32_t status);
+
+/* Library ABI version, (major << 16) | minor. */
+int32_t nvfp4_version(void);
+
+/* Bytes of workspace nvfp4_quantize needs (a small control block). */
+size_t nvfp4_quantize_workspace_size(void);
+
+/* Quantize x to NVFP4.
+ *   x            device, [batch][rows][cols] elements of x_dtype with row
+ *                stride ld >= cols and batch stride batch_stride >= rows*ld
+ *                (elements); x, ld*esize and batch_stride*esize must be
+ *                multiples of 16 bytes.
+ *   axis         ALONG_COLS: out has rows x cols, cols % 16 == 0.
+ *                ALONG_ROWS: out has cols x rows (transpose), rows % 16 == 0.
+ *   opts         host, may be NULL for RNE without transform.
+ *   out          host struct describing the destination view; its batch, rows
+ *                and cols must equal the view's shape.
+ *   workspace    device, >= nvfp4_quantize_workspace_size() bytes, zeroed
+ *                before first use, 256-byte aligned.
+ * Empty tensors (batch, rows or cols = 0) are valid: nothing is written
+ * except tensor_scale = 0. */
+nvfp4_status nvfp4_quantize(const void *x, int32_t x_dtype, int64_t batch, int64_t rows,
+                            int64_t cols, int64_t ld, int64_t batch_stride, int32_t axis,
+                            const nvfp4_quant_opts *opts, const nvfp4_qtensor *out,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Block-scaled GEMM, both operands quantized along K ("NT" form):
+ *   C[b][i][j] = alpha * sA * sB * sum_k A^[b][i][k] * B^[b][j][k]
+ * with A^ = E2M1 * E4M3 (exact), sA/sB the tensor scales read on the device.
+ * Accumulation is FP32; the epilogue multiplies by fl(fl(sA*sB)*alpha) and
+ * stores FP32, or BF16 rounded to nearest even.
+ *   a, b         host structs: a is [batch][M][K], b is [batch][N][K].
+ *   c            device, c_dtype elements, row stride ldc >= N, batch stride
+ *                batch_stride_c >= M*ldc (elements), aligned to the element.
+ * Any M, N >= 0 and K a multiple of 16 (K = 0 gives zeros). */
+nvfp4_status nvfp4_gemm(const nvfp4_qtensor *a, const nvfp4_qtensor *b, void *c, int32_t c_dtype,
+                        int64_t ldc, int64_t batch_stride_c, float alpha, void *stream);
+
+/* Linear-layer training step in NVFP4 (all operands BF16, row-major):
+ *   Fprop  Y  = X W^T  : X [M][K] and W [N][K] along K, RNE.
+ *   Dgrad  dX = dY W   : dY [M][N] along N with stochastic rounding
+ *                        (stream 1); W^T along N (transposing), RNE.
+ *   Wgrad  dW = dY^T X : dY^T and X^T along M (transposing), both after the
+ *                        random Hadamard transform (one rht_seed), stochastic
+ *                        rounding on dY^T (stream 2) and, when wgrad_sr_x is
+ *                        nonzero, on X^T (stream 3; RNE otherwise).
+ * Y [M][N] and dX [M][K] are BF16; dW [N][K] has dtype dw_dtype.
+ * M, N, K must be multiples of 16; all pointers 16-byte aligned. */
+typedef struct nvfp4_linear_cfg {
+  uint64_t sr_seed;
+  uint64_t rht_seed;
+  int32_t wgrad_sr_x;
+  int32_t dw_dtype;
+} nvfp4_linear_cfg;
+
+/* Bytes of workspace for nvfp4_linear_fwd_bwd: the six quantized views and
+ * their control blocks.  Zero it before first use. */
+size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+
+nvfp4_status nvfp4_linear_fwd_bwd(const void *x, const void *w, const void *dy, void *y,
+                                  void *dx, void *dw, int64_t M, int64_t N, int64_t K,
+                                  const nvfp4_linear_cfg *cfg, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

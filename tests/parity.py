@@ -1,0 +1,115 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C ABI
+binding and the CPU oracle on the same host bytes, and compare.
+
+Acceptance (the reading used throughout):
+  * quantized codes, block scales and tensor scale: bit-exact;
+  * FP32 GEMM output: |y - y_ref| <= 1e-5 * sum_k |a^_ik b^_jk| (scaled);
+  * BF16 GEMM output: y equals RNE_bf16(y_ref) or one of its two BF16
+    neighbours, or, where cancellation makes the FP32 accumulation error
+    larger than one BF16 ulp of a small y_ref, |y - y_ref| <= 1e-5 * Sabs +
+    ulp_bf16(y) / 2.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import bit_block_scaled_nvfp4_amd as nv
+from bit_block_scaled_nvfp4_amd import workloads as W
+from oracle import oracle as O
+
+DEV = "cuda:0"
+FP32_TOL = 1e-5
+
+
+def host_view(x: torch.Tensor):
+    """(numpy array, oracle dtype) of a CPU tensor for the oracle."""
+    if x.dtype == torch.bfloat16:
+        return W.bf16_bits(x), O.BF16
+    return x.contiguous().numpy(), O.F32
+
+
+def oracle_quant(x: torch.Tensor, axis=O.ALONG_COLS, rounding=O.RNE, sr_seed=0, sr_stream=0,
+                 rht=False, rht_seed=0) -> O.QTensor:
+    a, dt = host_view(x)
+    return O.quantize(a, dt, axis=axis, rounding=rounding, sr_seed=sr_seed, sr_stream=sr_stream,
+                      rht=rht, rht_seed=rht_seed)
+
+
+def gpu_quant(x: torch.Tensor, axis=O.ALONG_COLS, rounding=O.RNE, sr_seed=0, sr_stream=0,
+              rht=False, rht_seed=0, device=DEV) -> nv.QTensor:
+    return nv.quantize(x.to(device), axis=axis, rounding=rounding, sr_seed=sr_seed,
+                       sr_stream=sr_stream, rht=rht, rht_seed=rht_seed)
+
+
+def to_oracle_view(q: nv.QTensor) -> O.QTensor:
+    """Copy a device quantized view back into the oracle's container."""
+    torch.cuda.synchronize()
+    return O.QTensor(q.codes.cpu().numpy().reshape(q.batch, q.rows, q.cols // 2),
+                     q.scales.cpu().numpy().reshape(q.batch, q.rows, q.cols // 16),
+                     np.float32(q.tensor_scale.cpu().numpy()[0]), q.batch, q.rows, q.cols)
+
+
+def assert_quant_equal(got: O.QTensor, want: O.QTensor, what: str = "") -> None:
+    assert got.tensor_scale.view(np.uint32) == np.float32(want.tensor_scale).view(np.uint32), \
+        f"{what}: tensor scale {got.tensor_scale!r} != {want.tensor_scale!r}"
+    bad = np.nonzero(got.scales.reshape(-1) != want.scales.reshape(-1))[0]
+    assert bad.size == 0, f"{what}: {bad.size} block scales differ, first at {bad[0]}: " \
+        f"{got.scales.reshape(-1)[bad[0]]:#x} vs {want.scales.reshape(-1)[bad[0]]:#x}"
+    bad = np.nonzero(got.codes.reshape(-1) != want.codes.reshape(-1))[0]
+    assert bad.size == 0, f"{what}: {bad.size} code bytes differ, first at {bad[0]}: " \
+        f"{got.codes.reshape(-1)[bad[0]]:#x} vs {want.codes.reshape(-1)[bad[0]]:#x}"
+
+
+def bf16_rne_bits(y: np.ndarray) -> np.ndarray:
+    """Exact round-to-nearest-even of float64 values to BF16 bit patterns."""
+    y = np.asarray(y, dtype=np.float64)
+    out = np.zeros(y.shape, dtype=np.int64)
+    nz = y != 0
+    e = np.floor(np.log2(np.abs(y[nz])))
+    scale = np.exp2(e - 7)
+    r = np.round(y[nz] / scale) * scale  # half-to-even on an exact quotient
+    out[nz] = (np.float32(r).view(np.uint32) >> 16).astype(np.int64)
+    out[~nz] = (np.signbit(y[~nz]).astype(np.int64) << 15)
+    return out
+
+
+def check_gemm(y: np.ndarray, y_ref: np.ndarray, sabs: np.ndarray, bf16: bool, what: str = "") -> dict:
+    """Apply the acceptance rule; returns pass counts, raises on any failure."""
+    y = np.asarray(y)
+    if not bf16:
+        err = np.abs(y.astype(np.float64) - y_ref)
+        bad = err > FP32_TOL * sabs
+        assert not bad.any(), f"{what}: {int(bad.sum())} FP32 outputs outside 1e-5*sum|ab|; " \
+            f"worst err {err.max():.3e} (bound there {(FP32_TOL * sabs).reshape(-1)[err.argmax()]:.3e})"
+        return {"n": y.size, "fp32_ok": y.size}
+    ybits = (np.asarray(y, dtype=np.float32).view(np.uint32) >> 16).astype(np.int64)
+    rbits = bf16_rne_bits(y_ref)
+    # signed-magnitude -> monotone integer so neighbours differ by 1
+    def mono(b):
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    ulp_ok = np.abs(mono(ybits) - mono(rbits)) <= 1
+    yv = np.asarray(y, dtype=np.float64)
+    ulp_y = np.exp2(np.floor(np.log2(np.maximum(np.abs(yv), 1e-300))) - 7)
+    cancel_ok = np.abs(yv - y_ref) <= FP32_TOL * sabs + 0.5 * ulp_y
+    bad = ~(ulp_ok | cancel_ok)
+    assert not bad.any(), f"{what}: {int(bad.sum())} BF16 outputs fail both criteria"
+    return {"n": y.size, "ulp_ok": int(ulp_ok.sum()), "cancel_only": int((~ulp_ok & cancel_ok).sum())}
+
+
+def gemm_vs_oracle(qa_gpu: nv.QTensor, qb_gpu: nv.QTensor, out_dtype=torch.bfloat16, alpha=1.0,
+                   rows=None, batches=None, what: str = "") -> dict:
+    """Run the GPU GEMM on device views, compare selected rows of selected
+    batch entries with the oracle reference computed from the same codes."""
+    y = nv.gemm(qa_gpu, qb_gpu, out_dtype=out_dtype, alpha=alpha)
+    y3 = y if y.dim() == 3 else y.unsqueeze(0)
+    qa, qb = to_oracle_view(qa_gpu), to_oracle_view(qb_gpu)
+    stats = {"n": 0}
+    for bi in (range(qa.batch) if batches is None else batches):
+        sel = np.arange(qa.rows) if rows is None else np.asarray(rows)
+        y_ref, sabs = O.gemm_ref(qa, qb, alpha, int(bi), sel)
+        got = y3[bi][torch.as_tensor(sel, device=y3.device)].float().cpu().numpy()
+        s = check_gemm(got, y_ref, sabs, out_dtype == torch.bfloat16, f"{what} batch {bi}")
+        for k, v in s.items():
+            stats[k] = stats.get(k, 0) + v
+    return stats

@@ -1,0 +1,109 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, exports
+every entry point include/nvfp4.h declares, and rejects bad arguments with the
+documented status codes before making any HIP call."""
+import ctypes
+import re
+
+import pytest
+
+import bit_block_scaled_nvfp4_amd as nv
+
+FAKE = 0x10000  # aligned, non-null; never dereferenced because validation fails first
+
+
+def declared_functions():
+    text = open(nv.HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = nv.lib()
+    names = declared_functions()
+    assert {"nvfp4_quantize", "nvfp4_gemm", "nvfp4_linear_fwd_bwd"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    for s in range(7):
+        assert nv.status_string(s) and nv.status_string(s) != "unknown status"
+    assert nv.status_string(99) == "unknown status"
+    assert nv.nvfp4_version() >> 16 == 1
+    assert nv.nvfp4_quantize_workspace_size() == 256
+
+
+def _q(batch, rows, cols, codes=FAKE, scales=FAKE, st=FAKE):
+    return nv.QTensorC(codes, scales, st, batch, rows, cols)
+
+
+def _quant(**kw):
+    a = dict(x=FAKE, dt=nv.BF16, b=1, r=32, c=64, ld=64, bs=32 * 64, axis=nv.ALONG_COLS,
+             opts=nv.QuantOptsC(0, 0, 0, 0, 0, 0), out=None, ws=FAKE, wsb=256)
+    a.update(kw)
+    if a["out"] is None:
+        qr, qc = (a["r"], a["c"]) if a["axis"] == nv.ALONG_COLS else (a["c"], a["r"])
+        a["out"] = _q(a["b"], qr, qc)
+    return nv.nvfp4_quantize(a["x"], a["dt"], a["b"], a["r"], a["c"], a["ld"], a["bs"], a["axis"],
+                             a["opts"], a["out"], a["ws"], a["wsb"], None)
+
+
+def test_quantize_argument_errors():
+    assert _quant(dt=7) == nv.EINVAL
+    assert _quant(axis=2) == nv.EINVAL
+    assert _quant(opts=nv.QuantOptsC(2, 0, 0, 0, 0, 0)) == nv.EINVAL
+    assert _quant(opts=nv.QuantOptsC(0, 3, 0, 0, 0, 0)) == nv.EINVAL
+    assert _quant(opts=nv.QuantOptsC(0, 0, 0, 0, 0, 1)) == nv.EINVAL
+    assert _quant(x=0) == nv.EINVAL
+    assert _quant(c=40, ld=40, out=_q(1, 32, 40)) == nv.ESHAPE          # K % 16 != 0
+    assert _quant(axis=nv.ALONG_ROWS, r=24, out=_q(1, 64, 24)) == nv.ESHAPE
+    assert _quant(r=-1) == nv.ESHAPE
+    assert _quant(ld=32) == nv.ESHAPE                                     # ld < cols
+    assert _quant(b=2, bs=100) == nv.ESHAPE                               # batch stride too small
+    assert _quant(x=FAKE + 2) == nv.EALIGN
+    assert _quant(ld=68) == nv.EALIGN                                     # 136-byte rows
+    assert _quant(out=_q(1, 32, 48)) == nv.EINVAL                         # view shape mismatch
+    assert _quant(out=_q(1, 32, 64, codes=0)) == nv.EINVAL
+    assert _quant(out=_q(1, 32, 64, codes=FAKE + 8)) == nv.EALIGN
+    assert _quant(out=_q(1, 32, 64, scales=FAKE + 2)) == nv.EALIGN
+    assert _quant(ws=0) == nv.EWORKSPACE
+    assert _quant(wsb=255) == nv.EWORKSPACE
+    assert _quant(ws=FAKE + 64) == nv.EALIGN
+    assert nv.nvfp4_quantize(FAKE, nv.BF16, 1, 32, 64, 64, 0, 0, None, None, FAKE, 256, None) == nv.EINVAL
+
+
+def test_gemm_argument_errors():
+    a, b = _q(1, 64, 128), _q(1, 32, 128)
+    assert nv.nvfp4_gemm(None, b, FAKE, nv.F32, 32, 0, 1.0, None) == nv.EINVAL
+    assert nv.nvfp4_gemm(a, b, FAKE, 5, 32, 0, 1.0, None) == nv.EINVAL
+    assert nv.nvfp4_gemm(a, _q(1, 32, 112), FAKE, nv.F32, 32, 0, 1.0, None) == nv.EINVAL  # K mismatch
+    assert nv.nvfp4_gemm(a, _q(2, 32, 128), FAKE, nv.F32, 32, 0, 1.0, None) == nv.EINVAL  # batch mismatch
+    assert nv.nvfp4_gemm(_q(1, 64, 120), _q(1, 32, 120), FAKE, nv.F32, 32, 0, 1.0, None) == nv.ESHAPE
+    assert nv.nvfp4_gemm(a, b, 0, nv.F32, 32, 0, 1.0, None) == nv.EINVAL
+    assert nv.nvfp4_gemm(a, b, FAKE, nv.F32, 16, 0, 1.0, None) == nv.ESHAPE                # ldc < N
+    assert nv.nvfp4_gemm(a, b, FAKE + 2, nv.F32, 32, 0, 1.0, None) == nv.EALIGN
+    assert nv.nvfp4_gemm(_q(1, 64, 128, st=0), b, FAKE, nv.F32, 32, 0, 1.0, None) == nv.EINVAL
+    assert nv.nvfp4_gemm(_q(2, 64, 128), _q(2, 32, 128), FAKE, nv.F32, 32, 10, 1.0, None) == nv.ESHAPE
+    assert nv.nvfp4_gemm(_q(70000, 1, 16), _q(70000, 1, 16), FAKE, nv.F32, 1, 1, 1.0, None) == nv.EUNSUPPORTED
+
+
+def test_linear_argument_errors_and_workspace_size():
+    M, N, K = 64, 32, 48
+    need = nv.nvfp4_linear_workspace_size(M, N, K)
+    views = [(M, K), (N, K), (M, N), (K, N), (N, M), (K, M)]
+    assert need >= sum(r * c // 2 + r * c // 16 + 512 for r, c in views)
+    assert nv.nvfp4_linear_workspace_size(0, N, K) == 0
+    cfg = nv.LinearCfgC(1, 2, 1, nv.BF16)
+    f = nv.nvfp4_linear_fwd_bwd
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, None, FAKE, need, None) == nv.EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, M, N, 40, cfg, FAKE, need, None) == nv.ESHAPE
+    assert f(FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, M, N, K, cfg, FAKE, need, None) == nv.EALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, cfg, FAKE, need - 1, None) == nv.EWORKSPACE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, nv.LinearCfgC(1, 2, 1, 9), FAKE, need, None) == nv.EINVAL
+
+
+def test_missing_library_raises(monkeypatch, tmp_path):
+    monkeypatch.setattr(nv, "_lib", None)
+    monkeypatch.setattr(nv, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        nv.lib()

@@ -1,0 +1,82 @@
+"""GPU parity of the block-scaled GEMM with the FP64 oracle reference over
+the same quantized operands: FP32 outputs within 1e-5 * sum|a^ b^|, BF16
+outputs within one BF16 ulp of the exact result (cancellation rule in
+tests/parity.py).  Ragged M/N tails, K tails that are not a multiple of the
+128-element K step, batching, alpha, strided output."""
+import numpy as np
+import pytest
+import torch
+
+import bit_block_scaled_nvfp4_amd as nv
+from bit_block_scaled_nvfp4_amd import workloads as W
+from oracle import oracle as O
+
+from .parity import DEV, assert_quant_equal, gemm_vs_oracle, gpu_quant, oracle_quant, to_oracle_view
+
+pytestmark = pytest.mark.gpu
+
+
+def _pair(M, N, K, batch, seed, wide=False):
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((batch, M, K)).astype(np.float32)
+    b = rng.standard_normal((batch, N, K)).astype(np.float32) * np.float32(0.05)
+    if wide:
+        a *= (2.0 ** rng.integers(-12, 6, (batch, M, 1))).astype(np.float32)
+    return torch.from_numpy(a).to(torch.bfloat16), torch.from_numpy(b).to(torch.bfloat16)
+
+
+SHAPES = [(1, 1, 16, 1), (7, 9, 48, 1), (33, 17, 128, 2), (129, 130, 144, 1), (300, 257, 400, 1),
+          (256, 128, 1024, 3), (64, 512, 2048, 1)]
+
+
+@pytest.mark.parametrize("M,N,K,batch", SHAPES)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_gemm_shapes(M, N, K, batch, out_dtype):
+    a, b = _pair(M, N, K, batch, M * 1000 + N + K)
+    qa, qb = gpu_quant(a), gpu_quant(b)
+    assert_quant_equal(to_oracle_view(qa), oracle_quant(a), "A")
+    stats = gemm_vs_oracle(qa, qb, out_dtype=out_dtype, alpha=0.75, what=f"{M}x{N}x{K}x{batch}")
+    assert stats["n"] == M * N * batch
+
+
+def test_gemm_wide_dynamic_range_and_zero_blocks():
+    a, b = _pair(96, 80, 256, 1, 5, wide=True)
+    a[0, 3, :64] = 0
+    b[0, 7, 32:] = 0
+    qa, qb = gpu_quant(a), gpu_quant(b)
+    for dt in (torch.float32, torch.bfloat16):
+        gemm_vs_oracle(qa, qb, out_dtype=dt, what="wide")
+
+
+def test_gemm_k_zero_gives_zeros():
+    qa = nv.QTensor.empty(1, 5, 0, DEV)
+    qb = nv.QTensor.empty(1, 3, 0, DEV)
+    qa.tensor_scale.fill_(1.0)
+    qb.tensor_scale.fill_(1.0)
+    y = nv.gemm(qa, qb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert y.shape == (5, 3) and not y.any()
+
+
+def test_gemm_strided_output():
+    a, b = _pair(40, 24, 96, 2, 17)
+    qa, qb = gpu_quant(a), gpu_quant(b)
+    big = torch.full((2, 48, 40), 7.0, dtype=torch.float32, device=DEV)
+    view = big[:, :40, :24]
+    nv.gemm(qa, qb, out=view, alpha=2.0)
+    want = nv.gemm(qa, qb, out_dtype=torch.float32, alpha=2.0)
+    torch.cuda.synchronize()
+    assert torch.equal(view, want)
+    assert torch.all(big[:, :40, 24:] == 7.0) and torch.all(big[:, 40:, :] == 7.0)
+
+
+def test_gemm_tiny_fp32_workload_full():
+    """The 256x256 FP32 workload: A along K, B (K x N) along K via the
+    transposing quantizer, every output element checked."""
+    t = W.tiny()
+    qa = gpu_quant(t["A"])
+    qb = gpu_quant(t["B"], axis=O.ALONG_ROWS)
+    assert_quant_equal(to_oracle_view(qa), oracle_quant(t["A"]), "A")
+    assert_quant_equal(to_oracle_view(qb), oracle_quant(t["B"], axis=O.ALONG_ROWS), "B")
+    stats = gemm_vs_oracle(qa, qb, out_dtype=torch.float32, what="tiny")
+    assert stats["n"] == 256 * 256

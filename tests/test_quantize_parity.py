@@ -1,0 +1,113 @@
+"""GPU parity of the quantize kernels with the CPU oracle: codes, block
+scales and tensor scale bit-exact, over both layouts, both input dtypes,
+both roundings, with and without the Hadamard transform, on ragged shapes,
+strided and batched inputs and adversarial values."""
+import numpy as np
+import pytest
+import torch
+
+from bit_block_scaled_nvfp4_amd import workloads as W
+from oracle import oracle as O
+
+from .parity import assert_quant_equal, gpu_quant, oracle_quant, to_oracle_view
+
+pytestmark = pytest.mark.gpu
+
+
+def _input(shape, seed, dtype, kind="normal"):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape).astype(np.float32)
+    if kind == "wide":  # per-row magnitudes over 2^-40 .. 2^20: subnormal / zero block scales
+        x *= (2.0 ** rng.integers(-40, 20, shape[:-1] + (1,))).astype(np.float32)
+    elif kind == "ties":  # values on E2M1 midpoints relative to a power-of-two scale
+        grid = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 0.0, -0.0], np.float32)
+        x = rng.choice(grid, shape).astype(np.float32) * rng.choice([-1, 1], shape).astype(np.float32)
+    elif kind == "heavy":
+        x = (rng.standard_t(2.0, shape) * 1e-3).astype(np.float32)
+    t = torch.from_numpy(x)
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+ROW_SHAPES = [(1, 16), (3, 48), (37, 160), (129, 1024), (1000, 48), (64, 4096)]
+COL_SHAPES = [(16, 1), (32, 7), (48, 37), (160, 1000), (256, 130), (4096, 24)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rounding", [O.RNE, O.SR])
+@pytest.mark.parametrize("rht", [False, True])
+@pytest.mark.parametrize("axis", [O.ALONG_COLS, O.ALONG_ROWS])
+def test_quantize_shapes(dtype, rounding, rht, axis):
+    shapes = ROW_SHAPES if axis == O.ALONG_COLS else COL_SHAPES
+    for i, shape in enumerate(shapes):
+        x = _input(shape, 1000 + i, dtype)
+        kw = dict(axis=axis, rounding=rounding, sr_seed=0x5EED0004 + i, sr_stream=i, rht=rht,
+                  rht_seed=0x4AD40004)
+        got = to_oracle_view(gpu_quant(x, **kw))
+        assert_quant_equal(got, oracle_quant(x, **kw), f"shape {shape}")
+
+
+@pytest.mark.parametrize("kind", ["wide", "ties", "heavy"])
+@pytest.mark.parametrize("axis", [O.ALONG_COLS, O.ALONG_ROWS])
+@pytest.mark.parametrize("rounding", [O.RNE, O.SR])
+def test_quantize_adversarial(kind, axis, rounding):
+    x = _input((96, 256), 7, "bf16", kind)
+    x[5, :32] = 0.0
+    x[7, 16:48] = -0.0
+    kw = dict(axis=axis, rounding=rounding, sr_seed=123, sr_stream=4, rht=False)
+    assert_quant_equal(to_oracle_view(gpu_quant(x, **kw)), oracle_quant(x, **kw), kind)
+
+
+def test_quantize_zero_and_empty():
+    x = torch.zeros(64, 64, dtype=torch.bfloat16)
+    x[3, 5] = -0.0
+    for axis in (O.ALONG_COLS, O.ALONG_ROWS):
+        got = to_oracle_view(gpu_quant(x, axis=axis))
+        assert_quant_equal(got, oracle_quant(x, axis=axis), "zeros")
+        assert got.tensor_scale == 0
+    q = gpu_quant(torch.zeros(0, 32, dtype=torch.bfloat16))
+    torch.cuda.synchronize()
+    assert q.tensor_scale.item() == 0.0 and q.codes.numel() == 0
+
+
+def test_quantize_strided_and_batched():
+    base = _input((3, 48, 96), 21, "bf16")          # [batch][rows][cols]
+    big = torch.zeros(3, 56, 128, dtype=torch.bfloat16)
+    big[:, :48, :96] = base
+    view = big[:, :48, :96]                          # ld = 128, batch stride = 56*128
+    for axis in (O.ALONG_COLS, O.ALONG_ROWS):
+        kw = dict(axis=axis, rounding=O.SR, sr_seed=9, sr_stream=1, rht=axis == O.ALONG_ROWS,
+                  rht_seed=77)
+        got = to_oracle_view(gpu_quant(view, **kw))
+        x3 = base.contiguous()
+        want = oracle_quant(x3, **kw)
+        assert_quant_equal(got, want, f"strided axis {axis}")
+
+
+def test_quantize_deterministic_across_calls():
+    x = _input((512, 2048), 5, "bf16")
+    kw = dict(rounding=O.SR, sr_seed=1, sr_stream=2, rht=True, rht_seed=3)
+    for axis in (O.ALONG_COLS, O.ALONG_ROWS):
+        a = to_oracle_view(gpu_quant(x, axis=axis, **kw))
+        b = to_oracle_view(gpu_quant(x, axis=axis, **kw))
+        assert_quant_equal(a, b, "repeat")
+
+
+def test_workspace_reuse_across_calls():
+    """The workspace control words are restored to zero by every call, so one
+    workspace serves a sequence of calls with different maxima."""
+    import bit_block_scaled_nvfp4_amd as nv
+    ws = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), "cuda:0")
+    for i, scale in enumerate([100.0, 1.0, 1e-3, 50.0]):
+        x = (_input((64, 128), 30 + i, "f32") * scale).to(torch.bfloat16)
+        q = nv.quantize(x.to("cuda:0"), workspace=ws)
+        assert_quant_equal(to_oracle_view(q), oracle_quant(x), f"call {i}")
+    torch.cuda.synchronize()
+    assert int(ws[:16].sum().item()) == 0
+
+
+@pytest.mark.parametrize("name", ["fprop_3b"])
+def test_quantize_fprop_full_size(name):
+    t = W.fprop_3b()
+    for key in ("X", "W"):
+        got = to_oracle_view(gpu_quant(t[key]))
+        assert_quant_equal(got, oracle_quant(t[key]), key)
