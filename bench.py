@@ -1,0 +1,164 @@
+"""Benchmark of the NVFP4 quantize + block-scaled GEMM path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fprop_3b]
+
+One step is one pass of the whole path over one batch of synthetic input:
+quantize X (RNE), quantize W (RNE), GEMM Y = X^ W^^T (BF16 out), all on one
+stream with the inputs already resident in HBM.  Inputs rotate over enough
+copies to exceed twice the 256 MB Infinity Cache, so every step reads its
+operands from HBM.  Per-kernel times come from HIP events recorded on the
+stream the kernels run on; the step time from the host clock around the
+timed steps, bracketed by device synchronisation.
+
+Prints one JSON line.  `value` is the whole-step NVFP4 GEMM throughput
+(2*M*N*K per step time, TFLOP/s); `roofline` describes the dominant kernel
+(the GEMM) against the dense FP16/BF16 MFMA peak; `cpu_baseline` times the
+CPU oracle (test infrastructure) on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import bit_block_scaled_nvfp4_amd as nv
+from bit_block_scaled_nvfp4_amd import workloads as W
+
+METRIC = "NVFP4 GEMM TFLOP/s + %MFMA peak; quantize GB/s + %HBM at 8192x3072x3072"
+PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense FP16/BF16 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+CACHE_BYTES = 256 << 20    # Infinity Cache
+QUANT_BYTES_PER_ELEM = 2 + 0.5 + 1.0 / 16  # BF16 in, E2M1 codes + E4M3 scales out
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="fprop_3b", choices=["fprop_3b", "mlp_up_12b"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=1024, help="GEMM rows in the CPU-oracle sample")
+    return p.parse_args()
+
+
+def cpu_baseline(x_cpu: torch.Tensor, w_cpu: torch.Tensor, rows: int) -> dict:
+    """The oracle as it stands, single-threaded: full quantization of X and W
+    plus the FP64 reference GEMM on `rows` rows of X, extrapolated linearly in
+    rows to the full step."""
+    from oracle import oracle as O
+    M, K = x_cpu.shape
+    N = w_cpu.shape[0]
+    xb, wb = W.bf16_bits(x_cpu), W.bf16_bits(w_cpu)
+    t0 = time.perf_counter()
+    qx = O.quantize(xb, O.BF16)
+    qw = O.quantize(wb, O.BF16)
+    t_quant = time.perf_counter() - t0
+    sel = np.linspace(0, M - 1, rows).astype(np.int64)
+    t0 = time.perf_counter()
+    O.gemm_ref(qx, qw, 1.0, 0, sel)
+    t_gemm = time.perf_counter() - t0
+    t_step = t_quant + t_gemm * (M / rows)
+    return {"value": 2.0 * M * N * K / t_step / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle quantize of all of X ({M}x{K}) and W ({N}x{K}) in {t_quant:.2f} s plus "
+                      f"the FP64 reference GEMM on {rows} of {M} rows in {t_gemm:.2f} s, "
+                      f"extrapolated linearly to the full step ({t_step:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = W.WORKLOADS[args.workload]()
+    x_cpu, w_cpu = t["X"], t["W"]
+    M, K = x_cpu.shape
+    N = w_cpu.shape[0]
+    in_bytes = (M * K + N * K) * 2
+    nbuf = max(2, int(np.ceil(2 * CACHE_BYTES / in_bytes)) + 1)
+    xs = [x_cpu.to(dev) for _ in range(nbuf)]
+    ws = [w_cpu.to(dev) for _ in range(nbuf)]
+    qxs = [nv.QTensor.empty(1, M, K, dev) for _ in range(nbuf)]
+    qws = [nv.QTensor.empty(1, N, K, dev) for _ in range(nbuf)]
+    ys = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(nbuf)]
+    wsp_x = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
+    wsp_w = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
+
+    def step(i, ev=None):
+        j = i % nbuf
+        if ev is not None:
+            ev[0].record()
+        nv.quantize(xs[j], out=qxs[j], workspace=wsp_x)
+        if ev is not None:
+            ev[1].record()
+        nv.quantize(ws[j], out=qws[j], workspace=wsp_w)
+        if ev is not None:
+            ev[2].record()
+        nv.gemm(qxs[j], qws[j], out=ys[j])
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    qx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    qw_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    gemm_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    ms_per_step = wall / args.steps * 1e3
+    flops = 2.0 * M * N * K
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    qx_gbps = QUANT_BYTES_PER_ELEM * M * K / (qx_ms * 1e-3) / 1e9
+    qw_gbps = QUANT_BYTES_PER_ELEM * N * K / (qw_ms * 1e-3) / 1e9
+    q_gbps = QUANT_BYTES_PER_ELEM * (M + N) * K / ((qx_ms + qw_ms) * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "x_dtype": "bf16",
+                   "y_dtype": "bf16", "rounding": "rne", "rotating_buffers": nbuf},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_MFMA_TFLOPS, 4), "traffic": None},
+        "kernels": {
+            "gemm": {"us": round(gemm_ms * 1e3, 2), "TFLOP/s": round(gemm_tflops, 2),
+                     "frac_mfma": round(gemm_tflops / PEAK_MFMA_TFLOPS, 4)},
+            "quantize_x": {"us": round(qx_ms * 1e3, 2), "GB/s": round(qx_gbps, 1),
+                           "frac_hbm": round(qx_gbps / PEAK_HBM_GBPS, 4)},
+            "quantize_w": {"us": round(qw_ms * 1e3, 2), "GB/s": round(qw_gbps, 1),
+                           "frac_hbm": round(qw_gbps / PEAK_HBM_GBPS, 4)},
+            "quantize_x_w": {"GB/s": round(q_gbps, 1), "frac_hbm": round(q_gbps / PEAK_HBM_GBPS, 4)},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x_cpu, w_cpu, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

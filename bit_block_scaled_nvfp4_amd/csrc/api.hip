@@ -58,8 +58,12 @@ nvfp4_status validate_quantize(const void *x, int32_t x_dtype, int64_t batch, in
     if ((double)batch * (double)rows * (double)cols > 4.0e18) return NVFP4_ESHAPE;
   }
   const int64_t esize = x_dtype == NVFP4_F32 ? 4 : 2;
-  if (!empty && (!aligned(x, 16) || (ld * esize) % 16 != 0 || (batch > 1 && (batch_stride * esize) % 16 != 0)))
-    return NVFP4_EALIGN;
+  if (!empty) {
+    if (axis == NVFP4_ALONG_COLS &&
+        (!aligned(x, 16) || (ld * esize) % 16 != 0 || (batch > 1 && (batch_stride * esize) % 16 != 0)))
+      return NVFP4_EALIGN;
+    if (axis == NVFP4_ALONG_ROWS && !aligned(x, (uintptr_t)esize)) return NVFP4_EALIGN;
+  }
   const int64_t qr = axis == NVFP4_ALONG_COLS ? rows : cols;
   const int64_t qc = axis == NVFP4_ALONG_COLS ? cols : rows;
   nvfp4_status st = check_view(out, batch, qr, qc);

@@ -70,6 +70,19 @@ __device__ __forceinline__ uint32_t e2m1_rne(float q) {
   return sign | ((a < 1.0f) ? sub : nrm);
 }
 
+// Eight values -> eight RNE codes packed into a dword (element j in nibble j)
+// with gfx950's FP32 -> FP4 converter at unit scale, two values per
+// instruction.  Its results equal e2m1_rne() on every non-NaN FP32 input
+// (checked exhaustively on the hardware over all 2^32 bit patterns).
+__device__ __forceinline__ uint32_t e2m1_rne8(const float *q) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[0], q[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[6], q[7], 1.0f, 3);
+  return w;
+}
+
 // Stochastic rounding onto the same grid with a 16-bit uniform word u: the
 // magnitude rounds up iff u < 2^16 * (|q| - lo) / step.  For |q| in [1, 6)
 // lo is |q| truncated to one mantissa bit and (|q| - lo) / step is the

@@ -47,6 +47,7 @@ struct ColArgs {
   int64_t col_groups;                // ceil(C / 8)
   int64_t row_groups;                // ceil(R / 16 / kRowBlocksPerLane)
   uint64_t units;                    // batch * row_groups * col_groups
+  bool vec_ok;                       // rows and batches start on 16-byte boundaries
   uint8_t *codes, *scales;
   float *tensor_scale;
   QuantCtrl *ctrl;
@@ -166,8 +167,10 @@ __global__ __launch_bounds__(kThreads) void row_encode_kernel(RowArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) packed |= e2m1_sr(v[j] * bs.recip, sr_word(r, j)) << (4 * j);
     } else {
+      float q[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) packed |= e2m1_rne(v[j] * bs.recip) << (4 * j);
+      for (int j = 0; j < 8; ++j) q[j] = v[j] * bs.recip;
+      packed = e2m1_rne8(q);
     }
     *reinterpret_cast<uint32_t *>(a.codes + 4 * h) = packed;
     if (!odd) a.scales[h >> 1] = (uint8_t)bs.code;
@@ -195,7 +198,7 @@ template <bool kBF16>
 __device__ __forceinline__ void col_load(const ColArgs &a, int64_t b, int64_t rb, int64_t cg,
                                          ColTile<kBF16> &t) {
   const int64_t c0 = 8 * cg;
-  const bool full = c0 + 8 <= a.C;
+  const bool full = a.vec_ok && c0 + 8 <= a.C;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int64_t off = b * a.bstride + (16 * rb + j) * a.ld + c0;
@@ -301,10 +304,11 @@ __global__ __launch_bounds__(kThreads) void col_encode_kernel(ColArgs a) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) hi |= e2m1_sr(v[8 + j] * bs.recip, sr_word(r1, j)) << (4 * j);
         } else {
+          float q[16];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) lo |= e2m1_rne(v[j] * bs.recip) << (4 * j);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) hi |= e2m1_rne(v[8 + j] * bs.recip) << (4 * j);
+          for (int j = 0; j < 16; ++j) q[j] = v[j] * bs.recip;
+          lo = e2m1_rne8(q);
+          hi = e2m1_rne8(q + 8);
         }
         *reinterpret_cast<uint2 *>(a.codes + vrow * (a.R / 2) + 8 * rb) = make_uint2(lo, hi);
         a.scales[vrow * RB + rb] = (uint8_t)bs.code;
@@ -398,6 +402,11 @@ nvfp4_status launch_quantize(const QuantProblem &p, hipStream_t s) {
     a.col_groups = (p.cols + 7) / 8;
     a.row_groups = (p.rows / 16 + kRowBlocksPerLane - 1) / kRowBlocksPerLane;
     a.units = (uint64_t)(a.batch * a.row_groups * a.col_groups);
+    {
+      const int64_t esize = p.bf16 ? 2 : 4;
+      a.vec_ok = reinterpret_cast<uintptr_t>(p.x) % 16 == 0 && (p.ld * esize) % 16 == 0 &&
+                 (p.batch == 1 || (p.bstride * esize) % 16 == 0);
+    }
     a.codes = p.codes;
     a.scales = p.scales;
     a.tensor_scale = p.tensor_scale;

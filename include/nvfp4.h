@@ -114,8 +114,10 @@ size_t nvfp4_quantize_workspace_size(void);
 /* Quantize x to NVFP4.
  *   x            device, [batch][rows][cols] elements of x_dtype with row
  *                stride ld >= cols and batch stride batch_stride >= rows*ld
- *                (elements); x, ld*esize and batch_stride*esize must be
- *                multiples of 16 bytes.
+ *                (elements).  ALONG_COLS: x, ld*esize and batch_stride*esize
+ *                must be multiples of 16 bytes.  ALONG_ROWS: x must be aligned
+ *                to its element size (16-byte aligned rows take the fast
+ *                vector-load path).
  *   axis         ALONG_COLS: out has rows x cols, cols % 16 == 0.
  *                ALONG_ROWS: out has cols x rows (transpose), rows % 16 == 0.
  *   opts         host, may be NULL for RNE without transform.
