@@ -8,21 +8,33 @@
 //
 // Exactness: every E2M1 x E4M3 product has at most 6 significant bits and
 // lies in [2^-10, 2688], so it is exact in FP16 (11 bits, normal range down
-// to 2^-14).  The kernel therefore decodes codes and scales to FP16 in
-// registers and runs v_mfma_f32_32x32x16_f16 with FP32 accumulation; only the
-// FP32 accumulation order differs from exact arithmetic.  FP16 is chosen over
-// BF16 (same MFMA rate on gfx950) because the hardware FP4 -> FP16 converter
-// and a packed FP16 multiply decode two elements per instruction each.
+// to 2^-14).  The kernel decodes codes and scales to FP16 in registers and
+// runs v_mfma_f32_32x32x16_f16 with FP32 accumulation; only the FP32
+// accumulation order differs from exact arithmetic.  FP16 rather than BF16
+// (same MFMA rate on gfx950): the hardware FP4 -> FP16 converter plus one
+// packed FP16 multiply by the block scale decode two elements per
+// instruction each.  (The converter's own scale operand only honours the
+// exponent of its FP32 argument, so it runs at unit scale.)
 //
-// Tiling: 128x128 output tile per workgroup of 4 wavefronts (2 x 2, 64x64
-// each = 2 x 2 MFMA tiles of 32x32), K step 128 (8 scale blocks).  Per K step
-// the workgroup stages 64 code bytes and 8 scale bytes per row of A and B in
-// LDS; each lane then reads 32 contiguous code bytes and one scale dword per
-// fragment.  Within a K step, lane half h of a fragment covers K offsets
-// [64h, 64h + 64): MFMA step s takes K offsets 64h + 8s .. 64h + 8s + 7 from
-// half h, which is one 16-element scale block (4h + s/2) per lane.  A and B
-// use the same assignment, so every K index meets its partner exactly once.
+// Tiling: a 256x256 output tile per workgroup of 4 wavefronts in a 2 x 2
+// grid, each wavefront owning 128x128 = 4 x 4 MFMA tiles (256 accumulator
+// registers).  Decoding costs about 9 VALU instructions per 8 elements of
+// one fragment; a 128x128 wavefront tile decodes 8 fragments per 16 MFMAs,
+// about 4.4 VALU instructions per 32-cycle MFMA, which the SIMD can overlap
+// with the matrix pipe.  K advances 128 elements (8 scale blocks) per step
+// through two LDS stages (64 code bytes + 8 scale bytes per row per step);
+// loads of step k+1 are issued before step k is computed.  Within a step,
+// lane half h of a fragment covers K offsets [64h, 64h + 64): MFMA sub-step s
+// takes offsets 64h + 8s .. 64h + 8s + 7, i.e. one scale block (4h + s/2)
+// per lane.  A and B use the same assignment, so each K index meets its
+// partner once.
+//
+// Workgroups are mapped to tiles so that each XCD (blockIdx mod 8 under the
+// round-robin dispatch) works on a contiguous range of tiles, in groups of
+// kGroupM tile rows, to keep A and B panels in that XCD's L2.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "internal.hpp"
 
@@ -32,11 +44,14 @@ namespace {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128, BN = 128, BK = 128;
+constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int kThreads = 256;
-constexpr int kCodeBytes = BK / 2;         // 64 code bytes per row per K step
-constexpr int kLdsRow = kCodeBytes + 16;   // padded LDS row
+constexpr int kRowBytes = BK / 2;  // 64 code bytes per row per K step
+constexpr int kFrag = 4;           // 32-row fragments per wavefront per operand
+constexpr int kGroupM = 8;         // tile rows per L2 group
 
 struct GemmArgs {
   const uint8_t *a_codes, *a_scales;
@@ -44,26 +59,34 @@ struct GemmArgs {
   const uint8_t *b_codes, *b_scales;
   const float *b_st;
   int64_t M, N, K;
-  int tiles_n;
+  int tiles_m, tiles_n;
   void *c;
   int64_t ldc, bstride_c;
   float alpha;
-  bool c_bf16;
 };
 
-// E4M3 scale byte s -> FP16 pair (S, S).  s << 7 placed in an FP16 is
-// S * 2^-8 for every code (the E4M3 exponent field lands in the FP16 one,
-// subnormal codes land in FP16 subnormals); one packed multiply by 256 is
-// exact and restores S.
-__device__ __forceinline__ half2_t scale_pair(uint32_t s) {
-  const uint32_t bits = s * 0x00800080u;
+// LDS stage: codes [256 rows][64 B] and scales [256 rows][8 B] per operand.
+struct Stage {
+  uint8_t a[BM * kRowBytes];
+  uint8_t b[BN * kRowBytes];
+  uint2 as[BM];
+  uint2 bs[BN];
+};
+
+// Two E4M3 scale bytes (bits 0..6 and 8..14 of w) -> two FP16 scales in one
+// dword.  An E4M3 code c shifted left by 7 and read as FP16 is c's value
+// times 2^-8 (the exponent fields line up; subnormal codes become FP16
+// subnormals), so one packed multiply by 256 gives the exact values.
+__device__ __forceinline__ half2_t scale_pair2(uint32_t w) {
+  const uint32_t spread = __builtin_amdgcn_perm(0u, w, 0x0C010C00u);  // [s0, 0, s1, 0]
   const half2_t k256 = {(_Float16)256.0f, (_Float16)256.0f};
-  return __builtin_bit_cast(half2_t, bits) * k256;
+  return __builtin_bit_cast(half2_t, spread << 7) * k256;
 }
 
-// Eight E2M1 codes (one dword, element 2j in the low nibble of byte j) times
-// the block scale, as eight FP16 values in element order.
-__device__ __forceinline__ half8_t decode8(uint32_t codes, half2_t s2) {
+// Eight E2M1 codes (element 2j in the low nibble of byte j) times one FP16
+// block scale -> eight FP16 values in element order.
+__device__ __forceinline__ half8_t decode8(uint32_t codes, _Float16 s) {
+  const half2_t s2 = {s, s};
   const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s2;
   const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s2;
   const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s2;
@@ -71,66 +94,106 @@ __device__ __forceinline__ half8_t decode8(uint32_t codes, half2_t s2) {
   return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// Global -> registers for one operand tile (rows r0..r0+127, K step k0).
-struct StageRegs {
-  uint2 codes[4];
-  uint32_t scales;
+// Global -> registers for one operand's K step.  kFast: K % 128 == 0, so a
+// row's 64 code bytes are 16-byte aligned and its 8 scale bytes 8-byte
+// aligned.  Rows past the end are clamped (their products land in output
+// rows that are never stored); K blocks past the end read as zero codes with
+// zero scales, which contribute exactly 0.
+template <bool kFast>
+struct OperandLoad {
+  uint4 codes[4];  // 4 x 16 B of the 16 KB code tile
+  uint2 scales;    // threads 0..255: one row's 8 scale bytes
+  __device__ __forceinline__ void load(const uint8_t *codes_g, const uint8_t *scales_g, int64_t rows,
+                                       int64_t K, int64_t r0, int64_t k0) {
+    const int tid = threadIdx.x;
+    const int64_t kblocks = K / 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + kThreads * i;  // 16-byte chunk of the tile
+      const int row = idx >> 2, part = idx & 3;
+      const int64_t gr = min(r0 + row, rows - 1);
+      const uint8_t *p = codes_g + gr * (K / 2) + k0 / 2 + 16 * part;
+      if (kFast) {
+        codes[i] = *reinterpret_cast<const uint4 *>(p);
+      } else {
+        const int64_t kb = k0 / 16 + 2 * part;  // blocks kb, kb+1: 8 bytes each
+        const uint2 lo = kb < kblocks ? *reinterpret_cast<const uint2 *>(p) : make_uint2(0u, 0u);
+        const uint2 hi = kb + 1 < kblocks ? *reinterpret_cast<const uint2 *>(p + 8) : make_uint2(0u, 0u);
+        codes[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    }
+    const int64_t gr = min(r0 + tid, rows - 1);
+    const uint8_t *s = scales_g + gr * kblocks + k0 / 16;
+    if (kFast) {
+      scales = *reinterpret_cast<const uint2 *>(s);
+    } else {
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (k0 / 16 + i < kblocks) w[i >> 2] |= (uint32_t)s[i] << (8 * (i & 3));
+      scales = make_uint2(w[0], w[1]);
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t *lds_codes, uint2 *lds_scales) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + kThreads * i;
+      *reinterpret_cast<uint4 *>(lds_codes + idx * 16) = codes[i];
+    }
+    lds_scales[tid] = scales;
+  }
 };
 
-__device__ __forceinline__ void stage_load(const uint8_t *codes, const uint8_t *scales, int64_t rows,
-                                           int64_t K, int64_t r0, int64_t k0, StageRegs &st) {
-  const int tid = threadIdx.x;
+// Direct global -> LDS loads of one operand's K step (K % 128 == 0).  Each
+// wavefront's global_load_lds writes 64 consecutive lane slots of LDS, so the
+// LDS tile keeps the row-major [256][64 B] code and [256][8 B] scale layout
+// while no VGPRs hold the prefetched data.  Rows past the end are clamped.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void lds_load_operand(const uint8_t *codes_g, const uint8_t *scales_g,
+                                                 int64_t rows, int64_t K, int64_t r0, int64_t k0,
+                                                 uint8_t *lds_codes, uint2 *lds_scales) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t kblocks = K / 16;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int idx = tid + kThreads * i;
-    const int row = idx >> 3, chunk = idx & 7;
-    const int64_t gr = r0 + row, kb = k0 / 16 + chunk;
-    st.codes[i] = (gr < rows && kb < kblocks)
-                      ? *reinterpret_cast<const uint2 *>(codes + gr * (K / 2) + kb * 8)
-                      : make_uint2(0u, 0u);
+    const int slot = (4 * wave + i) * 64;  // first 16-byte chunk written by this wavefront
+    const int p = slot + lane;
+    const int64_t gr = min(r0 + (p >> 2), rows - 1);
+    const uint8_t *src = codes_g + gr * (K / 2) + k0 / 2 + 16 * (p & 3);
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds_codes + 16 * slot), 16, 0, 0);
   }
-  {
-    const int row = tid >> 1, half = tid & 1;
-    const int64_t gr = r0 + row;
-    uint32_t w = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t kb = k0 / 16 + 4 * half + i;
-      const uint32_t byte = (gr < rows && kb < kblocks) ? scales[gr * kblocks + kb] : 0u;
-      w |= byte << (8 * i);
-    }
-    st.scales = w;
+  for (int i = 0; i < 2; ++i) {
+    const int slot = (2 * wave + i) * 64;  // first dword written by this wavefront
+    const int p = slot + lane;
+    const int64_t gr = min(r0 + (p >> 1), rows - 1);
+    const uint8_t *src = scales_g + gr * kblocks + k0 / 16 + 4 * (p & 1);
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)(reinterpret_cast<uint8_t *>(lds_scales) + 4 * slot), 4, 0, 0);
   }
 }
 
-__device__ __forceinline__ void stage_store(const StageRegs &st, uint8_t *lds_codes, uint32_t *lds_scales) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + kThreads * i;
-    const int row = idx >> 3, chunk = idx & 7;
-    *reinterpret_cast<uint2 *>(lds_codes + row * kLdsRow + chunk * 8) = st.codes[i];
-  }
-  lds_scales[tid] = st.scales;  // row = tid / 2, dword = tid % 2
-}
-
+template <bool kFast, bool kBF16Out>
 __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t sa_codes[BM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint8_t sb_codes[BN * kLdsRow];
-  __shared__ uint32_t sa_scales[BM * 2];
-  __shared__ uint32_t sb_scales[BN * 2];
+  __shared__ Stage stage[2];
 
-  const int tile = blockIdx.x;
+  // XCD-aware tile order: consecutive workgroups go to different XCDs, so
+  // give XCD x the x-th contiguous slice of the grouped tile order.
+  const int ntiles = g.tiles_m * g.tiles_n;
+  const int bid = blockIdx.x;
+  const int per_xcd = (ntiles + 7) / 8;
+  int t = (bid % 8) * per_xcd + bid / 8;
+  if (per_xcd * 8 != ntiles) t = bid;  // uneven split: plain order keeps the mapping a bijection
+  const int group = t / (kGroupM * g.tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(g.tiles_m - first_m, kGroupM);
+  const int in_group = t - group * kGroupM * g.tiles_n;
+  const int tm = first_m + in_group % gm;
+  const int tn = in_group / gm;
+
   const int64_t batch = blockIdx.y;
-  const int64_t m0 = (int64_t)(tile / g.tiles_n) * BM;
-  const int64_t n0 = (int64_t)(tile % g.tiles_n) * BN;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, r32 = lane & 31;
@@ -140,77 +203,127 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
   const uint8_t *bc = g.b_codes + batch * g.N * (g.K / 2);
   const uint8_t *bs = g.b_scales + batch * g.N * (g.K / 16);
 
-  floatx16 acc[2][2];
+  floatx16 acc[kFrag][kFrag];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kFrag; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kFrag; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  for (int64_t k0 = 0; k0 < g.K; k0 += BK) {
-    StageRegs ra, rb;
-    stage_load(ac, as, g.M, g.K, m0, k0, ra);
-    stage_load(bc, bs, g.N, g.K, n0, k0, rb);
-    __syncthreads();
-    stage_store(ra, sa_codes, sa_scales);
-    stage_store(rb, sb_codes, sb_scales);
-    __syncthreads();
-
-    uint4 fa[2][2], fb[2][2];
-    uint32_t sca[2], scb[2];
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int ra_row = wm * 64 + f * 32 + r32;
-      const int rb_row = wn * 64 + f * 32 + r32;
-      fa[f][0] = *reinterpret_cast<const uint4 *>(sa_codes + ra_row * kLdsRow + 32 * h);
-      fa[f][1] = *reinterpret_cast<const uint4 *>(sa_codes + ra_row * kLdsRow + 32 * h + 16);
-      fb[f][0] = *reinterpret_cast<const uint4 *>(sb_codes + rb_row * kLdsRow + 32 * h);
-      fb[f][1] = *reinterpret_cast<const uint4 *>(sb_codes + rb_row * kLdsRow + 32 * h + 16);
-      sca[f] = sa_scales[ra_row * 2 + h];
-      scb[f] = sb_scales[rb_row * 2 + h];
-    }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      half8_t av[2], bv[2];
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const uint4 qa = fa[f][s >> 2], qb = fb[f][s >> 2];
-        const uint32_t ca = (s & 3) == 0 ? qa.x : (s & 3) == 1 ? qa.y : (s & 3) == 2 ? qa.z : qa.w;
-        const uint32_t cb = (s & 3) == 0 ? qb.x : (s & 3) == 1 ? qb.y : (s & 3) == 2 ? qb.z : qb.w;
-        av[f] = decode8(ca, scale_pair((sca[f] >> (8 * (s >> 1))) & 0xFFu));
-        bv[f] = decode8(cb, scale_pair((scb[f] >> (8 * (s >> 1))) & 0xFFu));
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  const int ksteps = (int)((g.K + BK - 1) / BK);
+  OperandLoad<kFast> la, lb;  // register-staged path (K % 128 != 0)
+  if (ksteps > 0) {
+    if constexpr (kFast) {
+      lds_load_operand(ac, as, g.M, g.K, m0, 0, stage[0].a, stage[0].as);
+      lds_load_operand(bc, bs, g.N, g.K, n0, 0, stage[0].b, stage[0].bs);
+    } else {
+      la.load(ac, as, g.M, g.K, m0, 0);
+      lb.load(bc, bs, g.N, g.K, n0, 0);
+      la.store(stage[0].a, stage[0].as);
+      lb.store(stage[0].b, stage[0].bs);
     }
   }
+  __syncthreads();
 
-  // Epilogue: multiply by fl(fl(sA * sB) * alpha), store with bounds checks.
-  // Accumulator v of lane l in a 32x32 tile holds row 8*(v/4) + 4*(l/32) + v%4,
-  // column l%32.
+  for (int kt = 0; kt < ksteps; ++kt) {
+    const Stage &cur = stage[kt & 1];
+    const bool more = kt + 1 < ksteps;
+    // This lane's 32 code bytes and 4 scale bytes of every fragment.
+    uint4 ca[kFrag][2], cb[kFrag][2];
+    half2_t sa[kFrag][2], sb[kFrag][2];
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f) {
+      const int ra = wm * 128 + f * 32 + r32;
+      const int rb = wn * 128 + f * 32 + r32;
+      ca[f][0] = *reinterpret_cast<const uint4 *>(cur.a + ra * kRowBytes + 32 * h);
+      ca[f][1] = *reinterpret_cast<const uint4 *>(cur.a + ra * kRowBytes + 32 * h + 16);
+      cb[f][0] = *reinterpret_cast<const uint4 *>(cur.b + rb * kRowBytes + 32 * h);
+      cb[f][1] = *reinterpret_cast<const uint4 *>(cur.b + rb * kRowBytes + 32 * h + 16);
+      const uint32_t wa = h ? cur.as[ra].y : cur.as[ra].x;
+      const uint32_t wb = h ? cur.bs[rb].y : cur.bs[rb].x;
+      sa[f][0] = scale_pair2(wa);
+      sa[f][1] = scale_pair2(wa >> 16);
+      sb[f][0] = scale_pair2(wb);
+      sb[f][1] = scale_pair2(wb >> 16);
+    }
+
+    // Issue the next step's loads only after this step's LDS reads: the
+    // compiler orders LDS reads after outstanding LDS-bound loads, so this keeps
+    // the prefetch in flight during the math below.
+    if (more) {  // issue next step's loads; they land during this step's math
+      if constexpr (kFast) {
+        Stage &nxt = stage[(kt + 1) & 1];
+        lds_load_operand(ac, as, g.M, g.K, m0, (int64_t)(kt + 1) * BK, nxt.a, nxt.as);
+        lds_load_operand(bc, bs, g.N, g.K, n0, (int64_t)(kt + 1) * BK, nxt.b, nxt.bs);
+      } else {
+        la.load(ac, as, g.M, g.K, m0, (int64_t)(kt + 1) * BK);
+        lb.load(bc, bs, g.N, g.K, n0, (int64_t)(kt + 1) * BK);
+      }
+    }
+
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      half8_t av[kFrag], bv[kFrag];
+#pragma unroll
+      for (int f = 0; f < kFrag; ++f) {
+        const uint4 qa = ca[f][s >> 2], qb = cb[f][s >> 2];
+        const uint32_t wa = (s & 3) == 0 ? qa.x : (s & 3) == 1 ? qa.y : (s & 3) == 2 ? qa.z : qa.w;
+        const uint32_t wb = (s & 3) == 0 ? qb.x : (s & 3) == 1 ? qb.y : (s & 3) == 2 ? qb.z : qb.w;
+        av[f] = decode8(wa, sa[f][s >> 2][(s >> 1) & 1]);
+        bv[f] = decode8(wb, sb[f][s >> 2][(s >> 1) & 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < kFrag; ++i)
+#pragma unroll
+        for (int j = 0; j < kFrag; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+
+    if constexpr (!kFast) {
+      if (more) {
+        Stage &nxt = stage[(kt + 1) & 1];
+        la.store(nxt.a, nxt.as);
+        lb.store(nxt.b, nxt.bs);
+      }
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: multiply by fl(fl(sA * sB) * alpha) and store.  Accumulator v
+  // of lane l in a 32x32 tile holds row 8*(v/4) + 4*(l/32) + v%4, column l%32.
+  using OutT = typename std::conditional<kBF16Out, uint16_t, float>::type;
   const float sc = (*g.a_st * *g.b_st) * g.alpha;
+  OutT *cb_ptr = static_cast<OutT *>(g.c) + batch * g.bstride_c;
+  const int64_t row0 = m0 + wm * 128 + 4 * h;
+  const int64_t col0 = n0 + wn * 128 + r32;
+  int64_t roff[16];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int v = 0; v < 16; ++v) roff[v] = (int64_t)(8 * (v >> 2) + (v & 3)) * g.ldc;
+  const bool full = m0 + BM <= g.M && n0 + BN <= g.N;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn * 64 + j * 32 + r32;
+  for (int i = 0; i < kFrag; ++i) {
+    OutT *prow = cb_ptr + (row0 + 32 * i) * g.ldc + col0;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (row < g.M && col < g.N) {
-          const float y = acc[i][j][v] * sc;
-          const int64_t off = batch * g.bstride_c + row * g.ldc + col;
-          if (g.c_bf16)
-            static_cast<uint16_t *>(g.c)[off] = (uint16_t)bf16_rne(y);
-          else
-            static_cast<float *>(g.c)[off] = y;
+    for (int j = 0; j < kFrag; ++j) {
+      const bool col_ok = full || col0 + 32 * j < g.N;
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const int64_t r = row0 + 32 * i + 8 * (v >> 2) + (v & 3);
+        const bool ok0 = col_ok && (full || r < g.M), ok1 = col_ok && (full || r + 1 < g.M);
+        if constexpr (kBF16Out) {
+          // v_cvt_pk_bf16_f32: two FP32 -> BF16, round to nearest even
+          const float2_t y2 = {acc[i][j][v] * sc, acc[i][j][v + 1] * sc};
+          const uint32_t b2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(y2, bf16x2_t));
+          if (ok0) prow[roff[v] + 32 * j] = (uint16_t)b2;
+          if (ok1) prow[roff[v + 1] + 32 * j] = (uint16_t)(b2 >> 16);
+        } else {
+          if (ok0) prow[roff[v] + 32 * j] = acc[i][j][v] * sc;
+          if (ok1) prow[roff[v + 1] + 32 * j] = acc[i][j][v + 1] * sc;
         }
       }
     }
+  }
 }
 
 }  // namespace
@@ -228,14 +341,23 @@ nvfp4_status launch_gemm(const GemmProblem &p, hipStream_t s) {
   g.N = p.N;
   g.K = p.K;
   const int64_t tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
+  if (tm * tn > 0x7FFFFFFF || p.batch > 65535) return NVFP4_EUNSUPPORTED;
+  g.tiles_m = (int)tm;
   g.tiles_n = (int)tn;
   g.c = p.c;
-  g.c_bf16 = p.c_bf16;
   g.ldc = p.ldc;
   g.bstride_c = p.bstride_c;
   g.alpha = p.alpha;
-  if (tm * tn > 0x7FFFFFFF || p.batch > 65535) return NVFP4_EUNSUPPORTED;
-  hipLaunchKernelGGL(gemm_nvfp4_kernel, dim3((unsigned)(tm * tn), (unsigned)p.batch), dim3(kThreads), 0, s, g);
+  const dim3 grid((unsigned)(tm * tn), (unsigned)p.batch);
+  const bool fast = p.K % BK == 0;
+  if (fast && p.c_bf16)
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<true, true>), grid, dim3(kThreads), 0, s, g);
+  else if (fast)
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<true, false>), grid, dim3(kThreads), 0, s, g);
+  else if (p.c_bf16)
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<false, true>), grid, dim3(kThreads), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<false, false>), grid, dim3(kThreads), 0, s, g);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 
