@@ -16,18 +16,22 @@
 // instruction each.  (The converter's own scale operand only honours the
 // exponent of its FP32 argument, so it runs at unit scale.)
 //
-// Tiling: a 256x256 output tile per workgroup of 4 wavefronts in a 2 x 2
-// grid, each wavefront owning 128x128 = 4 x 4 MFMA tiles (256 accumulator
-// registers).  Decoding costs about 9 VALU instructions per 8 elements of
-// one fragment; a 128x128 wavefront tile decodes 8 fragments per 16 MFMAs,
-// about 4.4 VALU instructions per 32-cycle MFMA, which the SIMD can overlap
-// with the matrix pipe.  K advances 128 elements (8 scale blocks) per step
-// through two LDS stages (64 code bytes + 8 scale bytes per row per step);
-// loads of step k+1 are issued before step k is computed.  Within a step,
-// lane half h of a fragment covers K offsets [64h, 64h + 64): MFMA sub-step s
-// takes offsets 64h + 8s .. 64h + 8s + 7, i.e. one scale block (4h + s/2)
-// per lane.  A and B use the same assignment, so each K index meets its
-// partner once.
+// Tiling: a 256 x (64 * kFragN) output tile per workgroup of 4 wavefronts in
+// a 2 x 2 grid, each wavefront owning 128 x (32 * kFragN) = 4 x kFragN MFMA
+// tiles.  Decoding costs about 9 VALU instructions per 8 elements of one
+// fragment; with kFragN = 4 a wavefront decodes 8 fragments per 16 MFMAs,
+// about 4.4 VALU instructions per 32-cycle MFMA, which the SIMD overlaps with
+// the matrix pipe.  The launcher picks kFragN (4, 3 or 2) so that the tile
+// count fills the GPU in whole rounds.  K advances 128 elements (8 scale
+// blocks) per step through two LDS stages (64 code bytes + 8 scale bytes per
+// row per step).  When K % 128 == 0 the next step is fetched with
+// global_load_lds straight into the idle stage (no VGPRs hold it) right after
+// the current stage has been read into registers, so the loads fly during
+// the math; otherwise loads go through registers with K-tail zeroing.
+// Within a step, lane half h of a fragment covers K offsets [64h, 64h + 64):
+// MFMA sub-step s takes offsets 64h + 8s .. 64h + 8s + 7, i.e. one scale
+// block (4h + s/2) per lane.  A and B use the same assignment, so each K
+// index meets its partner once.
 //
 // Workgroups are mapped to tiles so that each XCD (blockIdx mod 8 under the
 // round-robin dispatch) works on a contiguous range of tiles, in groups of
@@ -38,6 +42,13 @@
 
 #include "internal.hpp"
 
+#ifndef NVFP4_GEMM_INTERLEAVE
+#define NVFP4_GEMM_INTERLEAVE 0
+#endif
+#ifndef NVFP4_GEMM_SWIZZLE
+#define NVFP4_GEMM_SWIZZLE 2
+#endif
+
 namespace nvfp4 {
 namespace {
 
@@ -46,12 +57,26 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int BM = 256, BK = 128;
 constexpr int kThreads = 256;
 constexpr int kRowBytes = BK / 2;  // 64 code bytes per row per K step
-constexpr int kFrag = 4;           // 32-row fragments per wavefront per operand
+constexpr int kFragM = 4;          // 32-row A fragments per wavefront
 constexpr int kGroupM = 8;         // tile rows per L2 group
+
+// LDS placement of the 16-byte code chunk `part` (0..3) of tile row `row`.
+// Fragment reads take the same part from 32 consecutive rows; XOR-ing the
+// part with row bits spreads those reads over all LDS banks.
+__device__ __forceinline__ int chunk_slot(int row, int part) {
+#if NVFP4_GEMM_SWIZZLE == 1
+  return row * 4 + (part ^ ((row >> 1) & 3));
+#elif NVFP4_GEMM_SWIZZLE == 2
+  return row * 4 + (part ^ ((row >> 2) & 3));
+#else
+  return row * 4 + part;
+#endif
+}
 
 struct GemmArgs {
   const uint8_t *a_codes, *a_scales;
@@ -65,12 +90,13 @@ struct GemmArgs {
   float alpha;
 };
 
-// LDS stage: codes [256 rows][64 B] and scales [256 rows][8 B] per operand.
+// LDS stage: codes [rows][64 B] and scales [rows][8 B] per operand.
+template <int kBN>
 struct Stage {
   uint8_t a[BM * kRowBytes];
-  uint8_t b[BN * kRowBytes];
+  uint8_t b[kBN * kRowBytes];
   uint2 as[BM];
-  uint2 bs[BN];
+  uint2 bs[kBN];
 };
 
 // Two E4M3 scale bytes (bits 0..6 and 8..14 of w) -> two FP16 scales in one
@@ -94,97 +120,95 @@ __device__ __forceinline__ half8_t decode8(uint32_t codes, _Float16 s) {
   return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// Global -> registers for one operand's K step.  kFast: K % 128 == 0, so a
-// row's 64 code bytes are 16-byte aligned and its 8 scale bytes 8-byte
-// aligned.  Rows past the end are clamped (their products land in output
-// rows that are never stored); K blocks past the end read as zero codes with
-// zero scales, which contribute exactly 0.
-template <bool kFast>
-struct OperandLoad {
-  uint4 codes[4];  // 4 x 16 B of the 16 KB code tile
-  uint2 scales;    // threads 0..255: one row's 8 scale bytes
-  __device__ __forceinline__ void load(const uint8_t *codes_g, const uint8_t *scales_g, int64_t rows,
-                                       int64_t K, int64_t r0, int64_t k0) {
-    const int tid = threadIdx.x;
-    const int64_t kblocks = K / 16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + kThreads * i;  // 16-byte chunk of the tile
-      const int row = idx >> 2, part = idx & 3;
-      const int64_t gr = min(r0 + row, rows - 1);
-      const uint8_t *p = codes_g + gr * (K / 2) + k0 / 2 + 16 * part;
-      if (kFast) {
-        codes[i] = *reinterpret_cast<const uint4 *>(p);
-      } else {
-        const int64_t kb = k0 / 16 + 2 * part;  // blocks kb, kb+1: 8 bytes each
-        const uint2 lo = kb < kblocks ? *reinterpret_cast<const uint2 *>(p) : make_uint2(0u, 0u);
-        const uint2 hi = kb + 1 < kblocks ? *reinterpret_cast<const uint2 *>(p + 8) : make_uint2(0u, 0u);
-        codes[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
-    }
-    const int64_t gr = min(r0 + tid, rows - 1);
-    const uint8_t *s = scales_g + gr * kblocks + k0 / 16;
-    if (kFast) {
-      scales = *reinterpret_cast<const uint2 *>(s);
-    } else {
-      uint32_t w[2] = {0u, 0u};
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (k0 / 16 + i < kblocks) w[i >> 2] |= (uint32_t)s[i] << (8 * (i & 3));
-      scales = make_uint2(w[0], w[1]);
-    }
-  }
-  __device__ __forceinline__ void store(uint8_t *lds_codes, uint2 *lds_scales) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + kThreads * i;
-      *reinterpret_cast<uint4 *>(lds_codes + idx * 16) = codes[i];
-    }
-    lds_scales[tid] = scales;
-  }
-};
-
-// Direct global -> LDS loads of one operand's K step (K % 128 == 0).  Each
-// wavefront's global_load_lds writes 64 consecutive lane slots of LDS, so the
-// LDS tile keeps the row-major [256][64 B] code and [256][8 B] scale layout
-// while no VGPRs hold the prefetched data.  Rows past the end are clamped.
-typedef __attribute__((address_space(3))) void lds_void;
-
+// Direct global -> LDS loads of one operand's K step (K % 128 == 0): each
+// wavefront's global_load_lds fills 64 consecutive lane slots, which keeps
+// the row-major [rows][64 B] code and [rows][8 B] scale layout.  Rows past
+// the end are clamped; their products only reach output rows never stored.
+template <int kRows>
 __device__ __forceinline__ void lds_load_operand(const uint8_t *codes_g, const uint8_t *scales_g,
                                                  int64_t rows, int64_t K, int64_t r0, int64_t k0,
                                                  uint8_t *lds_codes, uint2 *lds_scales) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t kblocks = K / 16;
+  constexpr int kCodeLoads = kRows * 4 / kThreads;  // 16-byte chunks per lane
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int slot = (4 * wave + i) * 64;  // first 16-byte chunk written by this wavefront
-    const int p = slot + lane;
-    const int64_t gr = min(r0 + (p >> 2), rows - 1);
-    const uint8_t *src = codes_g + gr * (K / 2) + k0 / 2 + 16 * (p & 3);
+  for (int i = 0; i < kCodeLoads; ++i) {
+    const int slot = (kCodeLoads * wave + i) * 64;
+    const int p = slot + lane;  // physical chunk: row p/4, position p%4
+    const int row = p >> 2;
+    const int part = (chunk_slot(row, p & 3)) & 3;  // the XOR swizzle is its own inverse
+    const int64_t gr = min(r0 + row, rows - 1);
+    const uint8_t *src = codes_g + gr * (K / 2) + k0 / 2 + 16 * part;
     __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds_codes + 16 * slot), 16, 0, 0);
   }
+  constexpr int kScaleLoads = (kRows * 2 + kThreads - 1) / kThreads;  // dwords per lane
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int slot = (2 * wave + i) * 64;  // first dword written by this wavefront
+  for (int i = 0; i < kScaleLoads; ++i) {
+    const int slot = (kScaleLoads * wave + i) * 64;
     const int p = slot + lane;
-    const int64_t gr = min(r0 + (p >> 1), rows - 1);
-    const uint8_t *src = scales_g + gr * kblocks + k0 / 16 + 4 * (p & 1);
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)(reinterpret_cast<uint8_t *>(lds_scales) + 4 * slot), 4, 0, 0);
+    if (slot < kRows * 2) {  // wave-uniform
+      const int64_t gr = min(r0 + (p >> 1), rows - 1);
+      const uint8_t *src = scales_g + gr * kblocks + k0 / 16 + 4 * (p & 1);
+      if (p < kRows * 2)
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(reinterpret_cast<uint8_t *>(lds_scales) + 4 * slot), 4,
+                                         0, 0);
+    }
   }
 }
 
-template <bool kFast, bool kBF16Out>
+// Register-staged loads for K % 128 != 0: K blocks past the end read as zero
+// codes with zero scales, which contribute exactly 0.
+template <int kRows>
+struct StagedLoad {
+  static constexpr int kChunks = kRows * 4 / kThreads;  // 16-byte code chunks per thread
+  uint4 codes[kChunks];
+  uint2 scales;
+  __device__ __forceinline__ void load(const uint8_t *codes_g, const uint8_t *scales_g, int64_t rows,
+                                       int64_t K, int64_t r0, int64_t k0) {
+    const int tid = threadIdx.x;
+    const int64_t kblocks = K / 16;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int idx = tid + kThreads * i;
+      const int64_t gr = min(r0 + (idx >> 2), rows - 1);
+      const uint8_t *p = codes_g + gr * (K / 2) + k0 / 2 + 16 * (idx & 3);
+      const int64_t kb = k0 / 16 + 2 * (idx & 3);  // blocks kb, kb+1: 8 bytes each
+      const uint2 lo = kb < kblocks ? *reinterpret_cast<const uint2 *>(p) : make_uint2(0u, 0u);
+      const uint2 hi = kb + 1 < kblocks ? *reinterpret_cast<const uint2 *>(p + 8) : make_uint2(0u, 0u);
+      codes[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+    uint32_t w[2] = {0u, 0u};
+    if (tid < kRows) {
+      const int64_t gr = min(r0 + tid, rows - 1);
+      const uint8_t *s = scales_g + gr * kblocks + k0 / 16;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (k0 / 16 + i < kblocks) w[i >> 2] |= (uint32_t)s[i] << (8 * (i & 3));
+    }
+    scales = make_uint2(w[0], w[1]);
+  }
+  __device__ __forceinline__ void store(uint8_t *lds_codes, uint2 *lds_scales) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int idx = tid + kThreads * i;
+      *reinterpret_cast<uint4 *>(lds_codes + chunk_slot(idx >> 2, idx & 3) * 16) = codes[i];
+    }
+    if (tid < kRows) lds_scales[tid] = scales;
+  }
+};
+
+template <int kFragN, bool kFast, bool kBF16Out>
 __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
-  __shared__ Stage stage[2];
+  constexpr int kBN = 64 * kFragN;
+  __shared__ Stage<kBN> stage[2];
 
   // XCD-aware tile order: consecutive workgroups go to different XCDs, so
   // give XCD x the x-th contiguous slice of the grouped tile order.
   const int ntiles = g.tiles_m * g.tiles_n;
   const int bid = blockIdx.x;
-  const int per_xcd = (ntiles + 7) / 8;
-  int t = (bid % 8) * per_xcd + bid / 8;
-  if (per_xcd * 8 != ntiles) t = bid;  // uneven split: plain order keeps the mapping a bijection
+  const int per_xcd = ntiles / 8;
+  const int t = (ntiles % 8 == 0) ? (bid % 8) * per_xcd + bid / 8 : bid;
   const int group = t / (kGroupM * g.tiles_n);
   const int first_m = group * kGroupM;
   const int gm = min(g.tiles_m - first_m, kGroupM);
@@ -193,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
   const int tn = in_group / gm;
 
   const int64_t batch = blockIdx.y;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * kBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, r32 = lane & 31;
@@ -203,20 +227,21 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
   const uint8_t *bc = g.b_codes + batch * g.N * (g.K / 2);
   const uint8_t *bs = g.b_scales + batch * g.N * (g.K / 16);
 
-  floatx16 acc[kFrag][kFrag];
+  floatx16 acc[kFragM][kFragN];
 #pragma unroll
-  for (int i = 0; i < kFrag; ++i)
+  for (int i = 0; i < kFragM; ++i)
 #pragma unroll
-    for (int j = 0; j < kFrag; ++j)
+    for (int j = 0; j < kFragN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int ksteps = (int)((g.K + BK - 1) / BK);
-  OperandLoad<kFast> la, lb;  // register-staged path (K % 128 != 0)
+  StagedLoad<BM> la;
+  StagedLoad<kBN> lb;
   if (ksteps > 0) {
     if constexpr (kFast) {
-      lds_load_operand(ac, as, g.M, g.K, m0, 0, stage[0].a, stage[0].as);
-      lds_load_operand(bc, bs, g.N, g.K, n0, 0, stage[0].b, stage[0].bs);
+      lds_load_operand<BM>(ac, as, g.M, g.K, m0, 0, stage[0].a, stage[0].as);
+      lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, 0, stage[0].b, stage[0].bs);
     } else {
       la.load(ac, as, g.M, g.K, m0, 0);
       lb.load(bc, bs, g.N, g.K, n0, 0);
@@ -227,35 +252,38 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
   __syncthreads();
 
   for (int kt = 0; kt < ksteps; ++kt) {
-    const Stage &cur = stage[kt & 1];
+    const Stage<kBN> &cur = stage[kt & 1];
     const bool more = kt + 1 < ksteps;
     // This lane's 32 code bytes and 4 scale bytes of every fragment.
-    uint4 ca[kFrag][2], cb[kFrag][2];
-    half2_t sa[kFrag][2], sb[kFrag][2];
+    uint4 ca[kFragM][2], cb[kFragN][2];
+    half2_t sa[kFragM][2], sb[kFragN][2];
 #pragma unroll
-    for (int f = 0; f < kFrag; ++f) {
-      const int ra = wm * 128 + f * 32 + r32;
-      const int rb = wn * 128 + f * 32 + r32;
-      ca[f][0] = *reinterpret_cast<const uint4 *>(cur.a + ra * kRowBytes + 32 * h);
-      ca[f][1] = *reinterpret_cast<const uint4 *>(cur.a + ra * kRowBytes + 32 * h + 16);
-      cb[f][0] = *reinterpret_cast<const uint4 *>(cur.b + rb * kRowBytes + 32 * h);
-      cb[f][1] = *reinterpret_cast<const uint4 *>(cur.b + rb * kRowBytes + 32 * h + 16);
-      const uint32_t wa = h ? cur.as[ra].y : cur.as[ra].x;
-      const uint32_t wb = h ? cur.bs[rb].y : cur.bs[rb].x;
-      sa[f][0] = scale_pair2(wa);
-      sa[f][1] = scale_pair2(wa >> 16);
-      sb[f][0] = scale_pair2(wb);
-      sb[f][1] = scale_pair2(wb >> 16);
+    for (int f = 0; f < kFragM; ++f) {
+      const int r = wm * 128 + f * 32 + r32;
+      ca[f][0] = *reinterpret_cast<const uint4 *>(cur.a + 16 * chunk_slot(r, 2 * h));
+      ca[f][1] = *reinterpret_cast<const uint4 *>(cur.a + 16 * chunk_slot(r, 2 * h + 1));
+      const uint32_t w = h ? cur.as[r].y : cur.as[r].x;
+      sa[f][0] = scale_pair2(w);
+      sa[f][1] = scale_pair2(w >> 16);
+    }
+#pragma unroll
+    for (int f = 0; f < kFragN; ++f) {
+      const int r = wn * (32 * kFragN) + f * 32 + r32;
+      cb[f][0] = *reinterpret_cast<const uint4 *>(cur.b + 16 * chunk_slot(r, 2 * h));
+      cb[f][1] = *reinterpret_cast<const uint4 *>(cur.b + 16 * chunk_slot(r, 2 * h + 1));
+      const uint32_t w = h ? cur.bs[r].y : cur.bs[r].x;
+      sb[f][0] = scale_pair2(w);
+      sb[f][1] = scale_pair2(w >> 16);
     }
 
     // Issue the next step's loads only after this step's LDS reads: the
-    // compiler orders LDS reads after outstanding LDS-bound loads, so this keeps
-    // the prefetch in flight during the math below.
-    if (more) {  // issue next step's loads; they land during this step's math
+    // compiler orders LDS reads after outstanding LDS-bound loads, so this
+    // keeps the prefetch in flight during the math below.
+    if (more) {
       if constexpr (kFast) {
-        Stage &nxt = stage[(kt + 1) & 1];
-        lds_load_operand(ac, as, g.M, g.K, m0, (int64_t)(kt + 1) * BK, nxt.a, nxt.as);
-        lds_load_operand(bc, bs, g.N, g.K, n0, (int64_t)(kt + 1) * BK, nxt.b, nxt.bs);
+        Stage<kBN> &nxt = stage[(kt + 1) & 1];
+        lds_load_operand<BM>(ac, as, g.M, g.K, m0, (int64_t)(kt + 1) * BK, nxt.a, nxt.as);
+        lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, (int64_t)(kt + 1) * BK, nxt.b, nxt.bs);
       } else {
         la.load(ac, as, g.M, g.K, m0, (int64_t)(kt + 1) * BK);
         lb.load(bc, bs, g.N, g.K, n0, (int64_t)(kt + 1) * BK);
@@ -264,25 +292,37 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
 
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      half8_t av[kFrag], bv[kFrag];
+      half8_t av[kFragM], bv[kFragN];
 #pragma unroll
-      for (int f = 0; f < kFrag; ++f) {
-        const uint4 qa = ca[f][s >> 2], qb = cb[f][s >> 2];
-        const uint32_t wa = (s & 3) == 0 ? qa.x : (s & 3) == 1 ? qa.y : (s & 3) == 2 ? qa.z : qa.w;
-        const uint32_t wb = (s & 3) == 0 ? qb.x : (s & 3) == 1 ? qb.y : (s & 3) == 2 ? qb.z : qb.w;
-        av[f] = decode8(wa, sa[f][s >> 2][(s >> 1) & 1]);
-        bv[f] = decode8(wb, sb[f][s >> 2][(s >> 1) & 1]);
+      for (int f = 0; f < kFragM; ++f) {
+        const uint4 q = ca[f][s >> 2];
+        const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
+        av[f] = decode8(w, sa[f][s >> 2][(s >> 1) & 1]);
       }
 #pragma unroll
-      for (int i = 0; i < kFrag; ++i)
+      for (int f = 0; f < kFragN; ++f) {
+        const uint4 q = cb[f][s >> 2];
+        const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
+        bv[f] = decode8(w, sb[f][s >> 2][(s >> 1) & 1]);
+      }
 #pragma unroll
-        for (int j = 0; j < kFrag; ++j)
+      for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
+#if NVFP4_GEMM_INTERLEAVE
+    // Ask the scheduler to alternate one MFMA with a few VALU instructions.
+#pragma unroll
+    for (int i = 0; i < 8 * kFragM * kFragN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_GEMM_INTERLEAVE, 0);
+    }
+#endif
 
     if constexpr (!kFast) {
       if (more) {
-        Stage &nxt = stage[(kt + 1) & 1];
+        Stage<kBN> &nxt = stage[(kt + 1) & 1];
         la.store(nxt.a, nxt.as);
         lb.store(nxt.b, nxt.bs);
       }
@@ -296,16 +336,16 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
   const float sc = (*g.a_st * *g.b_st) * g.alpha;
   OutT *cb_ptr = static_cast<OutT *>(g.c) + batch * g.bstride_c;
   const int64_t row0 = m0 + wm * 128 + 4 * h;
-  const int64_t col0 = n0 + wn * 128 + r32;
+  const int64_t col0 = n0 + wn * (32 * kFragN) + r32;
   int64_t roff[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) roff[v] = (int64_t)(8 * (v >> 2) + (v & 3)) * g.ldc;
-  const bool full = m0 + BM <= g.M && n0 + BN <= g.N;
+  const bool full = m0 + BM <= g.M && n0 + kBN <= g.N;
 #pragma unroll
-  for (int i = 0; i < kFrag; ++i) {
+  for (int i = 0; i < kFragM; ++i) {
     OutT *prow = cb_ptr + (row0 + 32 * i) * g.ldc + col0;
 #pragma unroll
-    for (int j = 0; j < kFrag; ++j) {
+    for (int j = 0; j < kFragN; ++j) {
       const bool col_ok = full || col0 + 32 * j < g.N;
 #pragma unroll
       for (int v = 0; v < 16; v += 2) {
@@ -326,10 +366,52 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
   }
 }
 
+template <int kFragN>
+hipError_t launch_tiles(const GemmArgs &g, int64_t batch, bool fast, bool bf16, hipStream_t s) {
+  const dim3 grid((unsigned)(g.tiles_m * g.tiles_n), (unsigned)batch);
+  if (fast && bf16)
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<kFragN, true, true>), grid, dim3(kThreads), 0, s, g);
+  else if (fast)
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<kFragN, true, false>), grid, dim3(kThreads), 0, s, g);
+  else if (bf16)
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<kFragN, false, true>), grid, dim3(kThreads), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<kFragN, false, false>), grid, dim3(kThreads), 0, s, g);
+  return hipGetLastError();
+}
+
+// N-tile width: among 256, 192 and 128, the one with the least estimated
+// time, counting a partly filled last round of workgroups as a full round
+// (one workgroup per CU, 256 CUs) and costing narrower tiles by their extra
+// decode work per MFMA.
+int pick_frag_n(int64_t M, int64_t N, int64_t batch) {
+  const int64_t tm = (M + BM - 1) / BM;
+  double best = 1e300;
+  int pick = 4;
+  const int cands[3] = {4, 3, 2};
+  const double cost_per_col[3] = {1.0, 1.05, 1.15};  // relative decode overhead per output
+  for (int c = 0; c < 3; ++c) {
+    const int fn = cands[c];
+    const int64_t tn = (N + 64 * fn - 1) / (64 * fn);
+    const int64_t tiles = tm * tn * batch;
+    const int64_t rounds = (tiles + 255) / 256;
+    const double t = (double)rounds * (double)(64 * fn) * cost_per_col[c];
+    if (t < best - 1e-9) {
+      best = t;
+      pick = fn;
+    }
+  }
+#ifdef NVFP4_GEMM_FORCE_FRAG_N
+  pick = NVFP4_GEMM_FORCE_FRAG_N;
+#endif
+  return pick;
+}
+
 }  // namespace
 
 nvfp4_status launch_gemm(const GemmProblem &p, hipStream_t s) {
   if (p.batch == 0 || p.M == 0 || p.N == 0) return NVFP4_OK;
+  if (p.batch > 65535) return NVFP4_EUNSUPPORTED;
   GemmArgs g{};
   g.a_codes = p.a_codes;
   g.a_scales = p.a_scales;
@@ -340,25 +422,21 @@ nvfp4_status launch_gemm(const GemmProblem &p, hipStream_t s) {
   g.M = p.M;
   g.N = p.N;
   g.K = p.K;
-  const int64_t tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
-  if (tm * tn > 0x7FFFFFFF || p.batch > 65535) return NVFP4_EUNSUPPORTED;
-  g.tiles_m = (int)tm;
-  g.tiles_n = (int)tn;
   g.c = p.c;
   g.ldc = p.ldc;
   g.bstride_c = p.bstride_c;
   g.alpha = p.alpha;
-  const dim3 grid((unsigned)(tm * tn), (unsigned)p.batch);
+  const int fn = pick_frag_n(p.M, p.N, p.batch);
+  const int64_t tm = (p.M + BM - 1) / BM, tn = (p.N + 64 * fn - 1) / (64 * fn);
+  if (tm * tn > 0x7FFFFFFF) return NVFP4_EUNSUPPORTED;
+  g.tiles_m = (int)tm;
+  g.tiles_n = (int)tn;
   const bool fast = p.K % BK == 0;
-  if (fast && p.c_bf16)
-    hipLaunchKernelGGL((gemm_nvfp4_kernel<true, true>), grid, dim3(kThreads), 0, s, g);
-  else if (fast)
-    hipLaunchKernelGGL((gemm_nvfp4_kernel<true, false>), grid, dim3(kThreads), 0, s, g);
-  else if (p.c_bf16)
-    hipLaunchKernelGGL((gemm_nvfp4_kernel<false, true>), grid, dim3(kThreads), 0, s, g);
-  else
-    hipLaunchKernelGGL((gemm_nvfp4_kernel<false, false>), grid, dim3(kThreads), 0, s, g);
-  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+  hipError_t e;
+  if (fn == 4) e = launch_tiles<4>(g, p.batch, fast, p.c_bf16, s);
+  else if (fn == 3) e = launch_tiles<3>(g, p.batch, fast, p.c_bf16, s);
+  else e = launch_tiles<2>(g, p.batch, fast, p.c_bf16, s);
+  return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 
 }  // namespace nvfp4

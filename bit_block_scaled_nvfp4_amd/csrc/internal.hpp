@@ -9,17 +9,31 @@
 
 namespace nvfp4 {
 
-// Control words of one quantize call, at the start of its workspace.  All
-// words are zero between calls: the last workgroup of each call restores them.
+// Control words of one quantize workspace (4 KB, zero before first use).
+// Two-pass path: the amax accumulator and the encode-pass completion counter
+// are restored to zero by the last workgroup of each call.  Single-pass
+// path: counters that only grow, so nothing needs clearing.  `release`
+// counts completed single-pass calls (the current call's epoch); `arrive`
+// spreads the arrivals of one call over 8 counters, the last arrival at each
+// bumps `top`, and the last of those publishes the next epoch in `release`.
+// Per-epoch-parity amax slots are cleared one call ahead.  Every word sits
+// on its own 128-byte line so the atomics spread over memory channels.
 struct QuantCtrl {
-  uint32_t amax_bits;  // max |v| as FP32 bits, accumulated with atomicMax
-  uint32_t done;       // workgroups finished with the encode pass
-  uint32_t arrive;     // single-pass kernel: workgroups past the amax phase
-  uint32_t depart;     // single-pass kernel: workgroups finished
-  uint32_t timeout;    // single-pass kernel: a bounded wait expired
-  uint32_t pad[59];
+  uint32_t amax_bits;  // two-pass: max |v| as FP32 bits (atomicMax)
+  uint32_t done;       // two-pass: workgroups finished with the encode pass
+  uint32_t timeout;    // single-pass: nonzero if a bounded barrier wait expired
+  uint32_t pad0[29];
+  struct alignas(128) Counter {
+    unsigned long long v;
+    uint32_t pad[30];
+  } arrive[8], top, release;
+  struct alignas(128) Slot {
+    uint32_t v;
+    uint32_t pad[31];
+  } amax[2][8];
+  uint32_t pad1[160];
 };
-static_assert(sizeof(QuantCtrl) == 256, "control block is 256 bytes");
+static_assert(sizeof(QuantCtrl) == 4096, "quantize control block is 4 KB");
 
 struct QuantProblem {
   const void *x;

@@ -1,23 +1,34 @@
 // quantize.hip -- NVFP4 quantization kernels for gfx950.
 //
-// Two passes over HBM-resident input: an amax pass (per-tensor max |v| after
-// the optional random Hadamard transform, reduced per wavefront and
-// workgroup, one atomicMax per workgroup), then an encode pass that derives
-// the tensor scale, the per-16 E4M3 block scales and the E2M1 codes.
 // Quantization of the weights and activations that feed NVFP4 GEMMs is the
 // step "NVIDIA acelera o pre-treinamento de LLM ..." describes in "Como o
 // Treinamento Mixed-Precision Funciona com NVFP4"; the Hadamard mixing and
-// stochastic rounding follow "Full-Stack FP4 ...", section 2.2.
+// stochastic rounding follow "Full-Stack FP4 ...", section 2.2.  Every block
+// scale depends on the per-tensor amax, so the tensor is either read once and
+// held on chip across a grid-wide barrier, or read twice.
 //
-// Row-wise ("along cols"): one lane owns half of a 16-element block (one
-// 16-byte BF16 load); the two halves of a block sit in an even/odd lane pair
-// and meet through a lane swap for the block maximum and the last Hadamard
-// stage.  Consecutive lanes read consecutive 16-byte chunks.
+// Row-wise ("along cols", blocks along the contiguous dimension), one lane
+// owns one whole 16-element block (two 16-byte BF16 loads), so the transform,
+// the block maximum and the block scale stay in the lane.
+//  * Single pass (tensors that fit in the register files): a grid of one
+//    512-thread workgroup per CU loads every lane's blocks
+//    (up to 16 per lane for BF16, 33.5M elements on 256 CUs) into registers, reduces the amax per
+//    wavefront and workgroup, meets the rest of the grid at an epoch
+//    barrier, then encodes from registers.  HBM sees one read of the input
+//    and one write of codes and scales.
+//  * Two passes (larger tensors or when the grid cannot be co-resident): an
+//    amax kernel and an encode kernel over the same block order; the second
+//    read largely hits the 256 MB Infinity Cache for tensors that fit it.
 // Transposing ("along rows"): one lane owns 8 input columns x 16 input rows,
 // i.e. 8 complete blocks of the transposed view, so the transform and the
-// block maximum stay in registers; consecutive lanes read consecutive
-// 16-byte chunks of each row, and a lane walks 16 consecutive row blocks so
-// its 8-byte code stores for a column fill whole 128-byte lines.
+// block maximum stay in the lane; a workgroup covers 256 input rows x 128
+// columns and stages its codes in LDS so each transposed row's 128-byte code
+// line is written by one workgroup.  Two passes.
+//
+// Encode of a block: S = E4M3(fl(max|v| / fl(6 s_t))), q = fl(v * r_S) with
+// r_S = fl(1 / fl(E4M3(S) * s_t)) from a 127-entry LDS table built once per
+// workgroup, then E2M1 (hardware converter for RNE, integer compare against
+// a Philox word for stochastic rounding).
 #include <hip/hip_runtime.h>
 
 #include "device_codec.hpp"
@@ -26,154 +37,405 @@
 namespace nvfp4 {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowBlocksPerLane = 16;  // transposing kernel: 256 input rows per lane
+constexpr int kThreads = 256;           // two-pass kernels
+#ifndef NVFP4_FUSED_THREADS
+#define NVFP4_FUSED_THREADS 512
+#endif
+constexpr int kFusedThreads = NVFP4_FUSED_THREADS;  // single-pass kernel, one workgroup per CU
+constexpr int kFusedPerCU = 1;
+constexpr int kBatch = 4;               // two-pass row kernels: blocks loaded per lane before use
+constexpr uint32_t kSpinLimit = 1u << 25;  // ~2 s of polling
 
-struct RowArgs {
-  const void *x;
-  uint64_t half_blocks;  // batch * rows * cols / 8
-  uint64_t hb_per_row;   // cols / 8
-  int64_t rows, ld, bstride;
-  uint8_t *codes, *scales;
-  float *tensor_scale;
-  QuantCtrl *ctrl;
-  uint64_t sr_seed, rht_seed;
-  uint32_t sr_stream;
+#ifndef NVFP4_FUSED_COOPERATIVE
+#define NVFP4_FUSED_COOPERATIVE 0
+#endif
+#ifndef NVFP4_FUSED_DISABLE
+#define NVFP4_FUSED_DISABLE 0
+#endif
+
+template <bool kBF16>
+struct Fused {
+  // segments held per wavefront: 16 blocks per lane (BF16) at 512 threads,
+  // i.e. 33.5M elements on 256 CUs, within the register budget
+  static constexpr int kMaxBlocks = (kBF16 ? 16 : 8) * 512 / kFusedThreads;
 };
 
-struct ColArgs {
-  const void *x;
-  int64_t batch, R, C, ld, bstride;  // input [batch][R][C]; R % 16 == 0
-  int64_t col_groups;                // ceil(C / 8)
-  int64_t row_groups;                // ceil(R / 16 / kRowBlocksPerLane)
-  uint64_t units;                    // batch * row_groups * col_groups
-  bool vec_ok;                       // rows and batches start on 16-byte boundaries
-  uint8_t *codes, *scales;
-  float *tensor_scale;
-  QuantCtrl *ctrl;
-  uint64_t sr_seed, rht_seed;
-  uint32_t sr_stream;
-};
+// ---------------------------------------------------------------------------
+// Shared pieces
+// ---------------------------------------------------------------------------
 
-__device__ __forceinline__ uint32_t load_amax(const QuantCtrl *ctrl) {
-  return __hip_atomic_load(&ctrl->amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+
+// Streaming 16-byte load / 8-byte store that bypass cache allocation: the
+// input is read exactly once and the codes are not read back here.
+__device__ __forceinline__ uint4 ld_stream(const void *p) {
+  const u32x4v v = __builtin_nontemporal_load(static_cast<const u32x4v *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(void *p, uint2 v) {
+  const u32x2v t = {v.x, v.y};
+  __builtin_nontemporal_store(t, static_cast<u32x2v *>(p));
 }
 
-// Workgroup max -> one atomicMax per workgroup.
+// 16 raw input elements of one block: BF16 pairs in 8 dwords or FP32 in 16.
+template <bool kBF16>
+struct RawBlock {
+  uint32_t w[kBF16 ? 8 : 16];
+  template <bool kStream = true>
+  __device__ __forceinline__ void load(const void *x, int64_t off) {
+    const uint8_t *p = static_cast<const uint8_t *>(x) + off * (kBF16 ? 2 : 4);
+#pragma unroll
+    for (int i = 0; i < (kBF16 ? 2 : 4); ++i) {
+      const uint4 a = kStream ? ld_stream(p + 16 * i) : *reinterpret_cast<const uint4 *>(p + 16 * i);
+      w[4 * i] = a.x; w[4 * i + 1] = a.y; w[4 * i + 2] = a.z; w[4 * i + 3] = a.w;
+    }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < (kBF16 ? 8 : 16); ++i) w[i] = 0u;
+  }
+  // Hide the words from value numbering so that a later unpack is redone
+  // rather than kept alive in 16 extra registers per block.
+  __device__ __forceinline__ void opaque() {
+#pragma unroll
+    for (int i = 0; i < (kBF16 ? 8 : 16); ++i) asm volatile("" : "+v"(w[i]));
+  }
+  __device__ __forceinline__ void values(float (&v)[16]) const {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      v[j] = kBF16 ? ((j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1])) : __uint_as_float(w[j]);
+  }
+};
+
+// max |v| over 16 values as FP32 bits.
+__device__ __forceinline__ uint32_t max_abs16(const float (&v)[16]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) m = max(m, abs_bits(v[j]));
+  return m;
+}
+
+// Block scale code from the block maximum (RNE E4M3, S = 0 when s_t = 0).
+__device__ __forceinline__ uint32_t block_scale_code(uint32_t bmax_bits, float st, float d6) {
+  return (st > 0.0f) ? e4m3_encode(__uint_as_float(bmax_bits) / d6) : 0u;
+}
+
+// recip[S] = fl(1 / fl(E4M3(S) * s_t)), or 0 when that product is 0.
+__device__ __forceinline__ void build_recip_table(float *recip, float st) {
+  for (int s = threadIdx.x; s < 127; s += blockDim.x) {
+    const float e = e4m3_value((uint32_t)s) * st;
+    recip[s] = (e == 0.0f) ? 0.0f : 1.0f / e;
+  }
+}
+
+// Encode 16 values (logical element index n0 of the first) with multiplier r
+// into two dwords of codes.
+template <bool kSR>
+__device__ __forceinline__ uint2 encode16(const float (&v)[16], float r, uint64_t n0, uint32_t stream,
+                                          uint64_t seed) {
+  float q[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) q[j] = v[j] * r;
+  if (kSR) {
+    const u32x4 r0 = sr_block(n0 / 8, stream, seed);
+    const u32x4 r1 = sr_block(n0 / 8 + 1, stream, seed);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lo |= e2m1_sr(q[j], sr_word(r0, j)) << (4 * j);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) hi |= e2m1_sr(q[8 + j], sr_word(r1, j)) << (4 * j);
+    return make_uint2(lo, hi);
+  }
+  return make_uint2(e2m1_rne8(q), e2m1_rne8(q + 8));
+}
+
+// Device-scope relaxed atomics: performed at the memory-side coherence
+// point, with no cache writeback or invalidation around them.
+template <typename T>
+__device__ __forceinline__ T atomic_load_dev(const T *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void atomic_store_dev(T *p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Stall until a returning atomic has completed (its value is consumed).
+template <typename T>
+__device__ __forceinline__ void wait_for(T v) {
+  asm volatile("" ::"v"(v));
+}
+
+__device__ __forceinline__ uint32_t load_amax(const QuantCtrl *ctrl) { return atomic_load_dev(&ctrl->amax_bits); }
+
+// Workgroup max -> one atomicMax per workgroup (two-pass amax kernels).
 __device__ __forceinline__ void block_amax_commit(uint32_t m, QuantCtrl *ctrl) {
-  __shared__ uint32_t part[kThreads / 64];
+  __shared__ uint32_t part[16];
   m = wave_max_u32(m);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) part[wave] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t r = part[0];
-#pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) r = max(r, part[i]);
-    atomicMax(&ctrl->amax_bits, r);
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = max(r, part[i]);
+    __hip_atomic_fetch_max(&ctrl->amax_bits, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// The last workgroup of the encode pass restores the control words to zero.
+// The last workgroup of an encode pass restores the two-pass words to zero.
 __device__ __forceinline__ void encode_finish(QuantCtrl *ctrl, float *tensor_scale, float st) {
   __syncthreads();
   if (threadIdx.x == 0) {
     if (blockIdx.x == 0) *tensor_scale = st;
-    __threadfence();
-    const uint32_t old = atomicAdd(&ctrl->done, 1u);
+    // Every workgroup read the amax before arriving here; the last one to
+    // arrive (seen through the returned count) clears the two-pass words.
+    const uint32_t old = __hip_atomic_fetch_add(&ctrl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == gridDim.x - 1) {
-      __hip_atomic_store(&ctrl->amax_bits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&ctrl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      atomic_store_dev(&ctrl->amax_bits, 0u);
+      atomic_store_dev(&ctrl->done, 0u);
     }
   }
-}
-
-// Per-block scale selection, shared by both layouts.
-struct BlockScale {
-  uint32_t code;  // E4M3 byte
-  float recip;    // fl(1 / fl(E4M3(code) * s_t)), 0 for a zero scale
-};
-
-__device__ __forceinline__ BlockScale block_scale(float block_max, float st, float d6) {
-  BlockScale b;
-  b.code = (st > 0.0f) ? e4m3_encode(block_max / d6) : 0u;
-  const float e = e4m3_value(b.code) * st;
-  b.recip = (e == 0.0f) ? 0.0f : 1.0f / e;
-  return b;
 }
 
 // ---------------------------------------------------------------------------
 // Row-wise kernels
 // ---------------------------------------------------------------------------
 
-template <bool kBF16, bool kContig>
-__device__ __forceinline__ void row_load(const RowArgs &a, uint64_t h, float (&v)[8]) {
-  int64_t off;
-  if (kContig) {
-    off = (int64_t)(8 * h);
+struct RowArgs {
+  const void *x;
+  uint64_t nblocks;   // batch * rows * cols / 16
+  uint64_t bpr;       // blocks per row (cols / 16)
+  int64_t rows, ld, bstride;
+  uint8_t *codes, *scales;
+  float *tensor_scale;
+  QuantCtrl *ctrl;
+  uint64_t sr_seed, rht_seed;
+  uint32_t sr_stream;
+  uint32_t nseg_iters;  // single pass: segments per wavefront
+};
+
+// Element offset of block `blk` (row-major over [batch*rows][cols/16]).
+template <bool kContig>
+__device__ __forceinline__ int64_t row_block_offset(const RowArgs &a, uint64_t blk) {
+  if (kContig) return (int64_t)(16 * blk);
+  const uint64_t row = blk / a.bpr;
+  const uint64_t cb = blk - row * a.bpr;
+  const uint64_t b = row / (uint64_t)a.rows;
+  const uint64_t r = row - b * (uint64_t)a.rows;
+  return (int64_t)b * a.bstride + (int64_t)r * a.ld + (int64_t)(16 * cb);
+}
+
+// Wavefront segments: 64 consecutive blocks handled by one wavefront.  For a
+// contiguous BF16 tensor the segment (2 KB) is read with two fully coalesced
+// 16-byte loads per lane (chunks lane and 64 + lane), after which each even /
+// odd lane pair swaps one half so that even lane 2k owns block 64 seg + k and
+// odd lane 2k+1 owns block 64 seg + 32 + k.  Otherwise lane l owns block
+// 64 seg + l and loads it directly.  Returns the lane's block index.
+// kStream: non-temporal loads (data read once); the two-pass amax kernel
+// uses cached loads instead so the encode pass can re-read from the
+// Infinity Cache.
+template <bool kBF16, bool kContig, bool kStream = true>
+__device__ __forceinline__ uint64_t load_segment(const RowArgs &a, uint64_t seg, int lane, RawBlock<kBF16> &raw) {
+  if constexpr (kBF16 && kContig) {
+    const uint4 *p = static_cast<const uint4 *>(a.x);
+    const uint64_t nchunks = 2 * a.nblocks;
+    const uint64_t c0 = seg * 128 + lane, c1 = c0 + 64;
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    const uint4 x0 = c0 < nchunks ? (kStream ? ld_stream(p + c0) : p[c0]) : zero;
+    const uint4 x1 = c1 < nchunks ? (kStream ? ld_stream(p + c1) : p[c1]) : zero;
+    const bool odd = lane & 1;
+    const uint4 send = odd ? x0 : x1;
+    const uint4 recv = make_uint4(__shfl_xor(send.x, 1), __shfl_xor(send.y, 1), __shfl_xor(send.z, 1),
+                                  __shfl_xor(send.w, 1));
+    const uint4 lo = odd ? recv : x0, hi = odd ? x1 : recv;
+    raw.w[0] = lo.x; raw.w[1] = lo.y; raw.w[2] = lo.z; raw.w[3] = lo.w;
+    raw.w[4] = hi.x; raw.w[5] = hi.y; raw.w[6] = hi.z; raw.w[7] = hi.w;
+    return seg * 64 + (uint64_t)((lane & 1) * 32 + (lane >> 1));
   } else {
-    const uint64_t row = h / a.hb_per_row;
-    const uint64_t hc = h - row * a.hb_per_row;
-    const uint64_t b = row / (uint64_t)a.rows;
-    const uint64_t r = row - b * (uint64_t)a.rows;
-    off = (int64_t)b * a.bstride + (int64_t)r * a.ld + (int64_t)(8 * hc);
+    const uint64_t blk = seg * 64 + lane;
+    if (blk < a.nblocks) raw.template load<kStream>(a.x, row_block_offset<kContig>(a, blk));
+    else raw.zero();
+    return blk;
   }
-  if (kBF16) {
-    const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + off);
-    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
-  } else {
-    const float4 p = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) + off);
-    const float4 q = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) + off + 4);
-    v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w; v[4] = q.x; v[5] = q.y; v[6] = q.z; v[7] = q.w;
+}
+
+// Encode one block (values already transformed) and store codes + scale.
+template <bool kSR>
+__device__ __forceinline__ void row_store_block(const RowArgs &a, uint64_t blk, const float (&v)[16], uint32_t S,
+                                                const float *recip) {
+  const uint2 c = encode16<kSR>(v, recip[S], 16 * blk, a.sr_stream, a.sr_seed);
+  st_stream(a.codes + 8 * blk, c);
+  a.scales[blk] = (uint8_t)S;
+}
+
+template <bool kBF16, bool kRHT, bool kSR>
+__global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_kernel(RowArgs a) {
+  constexpr int kMax = Fused<kBF16>::kMaxBlocks;
+  constexpr int kWaves = kFusedThreads / 64;
+  __shared__ float recip[128];
+  __shared__ uint32_t part[kWaves];
+  __shared__ uint32_t s_epoch;
+  __shared__ float s_amax;
+  QuantCtrl *ctrl = a.ctrl;
+  const int slot = blockIdx.x & 7;
+  const int lane = threadIdx.x & 63;
+
+  // The epoch (completed single-pass calls on this workspace) cannot advance
+  // before this workgroup arrives, so reading it here is race free.
+  if (threadIdx.x == 0) s_epoch = (uint32_t)atomic_load_dev(&ctrl->release.v);
+
+  const uint64_t nwaves = (uint64_t)gridDim.x * kWaves;
+  const uint64_t gwave = (uint64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const uint32_t mask = kRHT ? rht_sign_mask(a.rht_seed) : 0u;
+
+  // Phase 1: all loads first, then the block maxima.
+  RawBlock<kBF16> raw[kMax];
+  uint64_t blk[kMax];
+  uint32_t bmax[kMax];
+#pragma unroll
+  for (int it = 0; it < kMax; ++it) {
+    if (it < (int)a.nseg_iters) blk[it] = load_segment<kBF16, true>(a, it * nwaves + gwave, lane, raw[it]);
+    else { raw[it].zero(); blk[it] = a.nblocks; }
   }
+  uint32_t m = 0;
+#pragma unroll
+  for (int it = 0; it < kMax; ++it) {
+    float v[16];
+    raw[it].values(v);
+    if (kRHT) rht16(v, mask);
+    bmax[it] = max_abs16(v);
+    m = max(m, bmax[it]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  m = wave_max_u32(m);
+  if (lane == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+
+  // Grid barrier: publish the workgroup max, arrive, wait for the epoch to
+  // complete, then read the tensor max.  All control words are device-scope
+  // atomics at the coherence point, so relaxed ordering plus explicit
+  // completion waits suffice (acquire/release would flush and invalidate the
+  // L2 on every poll).  The wait is bounded; on expiry the timeout word is
+  // set and the kernel still finishes.
+  if (threadIdx.x == 0) {
+    uint32_t wm = part[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) wm = max(wm, part[i]);
+    const uint32_t e = s_epoch;
+    if (blockIdx.x == 0) {  // slots of the next epoch: unused since the call before this one ended
+#pragma unroll
+      for (int i = 0; i < 8; ++i) atomic_store_dev(&ctrl->amax[(e + 1) & 1][i].v, 0u);
+    }
+    const uint32_t prev = __hip_atomic_fetch_max(&ctrl->amax[e & 1][slot].v, wm, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    wait_for(prev);  // the max is performed before this workgroup counts as arrived
+    // Arrive: the last workgroup of each slot bumps `top`; the last of those
+    // releases the epoch.  Slot i holds the workgroups with index = i mod 8.
+    const unsigned n_slots = min(gridDim.x, 8u);
+    const unsigned long long in_slot = gridDim.x / 8 + ((unsigned)slot < gridDim.x % 8 ? 1 : 0);
+    const unsigned long long old =
+        __hip_atomic_fetch_add(&ctrl->arrive[slot].v, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((old + 1) % in_slot == 0) {
+      const unsigned long long t =
+          __hip_atomic_fetch_add(&ctrl->top.v, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((t + 1) % n_slots == 0) atomic_store_dev(&ctrl->release.v, (unsigned long long)e + 1);
+    }
+    for (uint32_t spin = 0;; ++spin) {
+      if (atomic_load_dev(&ctrl->release.v) > e) break;
+      if (spin >= kSpinLimit) {
+        atomic_store_dev(&ctrl->timeout, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = max(am, atomic_load_dev(&ctrl->amax[e & 1][i].v));
+    s_amax = __uint_as_float(am);
+  }
+  __syncthreads();
+  const float st = s_amax / 2688.0f;
+  const float d6 = 6.0f * st;
+  build_recip_table(recip, st);
+  __syncthreads();
+
+  // Phase 2: encode from registers.
+#pragma unroll
+  for (int it = 0; it < kMax; ++it) raw[it].opaque();
+#pragma unroll
+  for (int it = 0; it < kMax; ++it) {
+    if (blk[it] < a.nblocks) {
+      const uint32_t S = block_scale_code(bmax[it], st, d6);
+      float v[16];
+      raw[it].values(v);
+      if (kRHT) rht16(v, mask);
+      row_store_block<kSR>(a, blk[it], v, S, recip);
+    }
+    // Keep blocks from being interleaved by the scheduler: hoisting every
+    // block's unpacked values at once would exceed the register budget.
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.tensor_scale = st;
 }
 
 template <bool kBF16, bool kRHT, bool kContig>
 __global__ __launch_bounds__(kThreads) void row_amax_kernel(RowArgs a) {
   const uint32_t mask = kRHT ? rht_sign_mask(a.rht_seed) : 0u;
+  const int lane = threadIdx.x & 63;
+  const uint64_t nseg = (a.nblocks + 63) / 64;
+  const uint64_t nwaves = (uint64_t)gridDim.x * (kThreads / 64);
   uint32_t m = 0;
-  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  for (uint64_t h = (uint64_t)blockIdx.x * kThreads + threadIdx.x; h < a.half_blocks; h += stride) {
-    float v[8];
-    row_load<kBF16, kContig>(a, h, v);
-    if (kRHT) rht16_pair(v, mask, (h & 1) != 0);
+  for (uint64_t s0 = (uint64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); s0 < nseg;
+       s0 += kBatch * nwaves) {
+    RawBlock<kBF16> raw[kBatch];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = max(m, abs_bits(v[j]));
+    for (int i = 0; i < kBatch; ++i) {
+      const uint64_t seg = s0 + i * nwaves;
+      if (seg < nseg) load_segment<kBF16, kContig, false>(a, seg, lane, raw[i]);
+      else raw[i].zero();
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      float v[16];
+      raw[i].values(v);
+      if (kRHT) rht16(v, mask);
+      m = max(m, max_abs16(v));
+    }
   }
   block_amax_commit(m, a.ctrl);
 }
 
 template <bool kBF16, bool kRHT, bool kSR, bool kContig>
 __global__ __launch_bounds__(kThreads) void row_encode_kernel(RowArgs a) {
+  __shared__ float recip[128];
   const uint32_t mask = kRHT ? rht_sign_mask(a.rht_seed) : 0u;
   const float amax = __uint_as_float(load_amax(a.ctrl));
   const float st = amax / 2688.0f;
   const float d6 = 6.0f * st;
-  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  for (uint64_t h = (uint64_t)blockIdx.x * kThreads + threadIdx.x; h < a.half_blocks; h += stride) {
-    const bool odd = (h & 1) != 0;
-    float v[8];
-    row_load<kBF16, kContig>(a, h, v);
-    if (kRHT) rht16_pair(v, mask, odd);
-    uint32_t m = 0;
+  build_recip_table(recip, st);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const uint64_t nseg = (a.nblocks + 63) / 64;
+  const uint64_t nwaves = (uint64_t)gridDim.x * (kThreads / 64);
+  for (uint64_t s0 = (uint64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); s0 < nseg;
+       s0 += kBatch * nwaves) {
+    RawBlock<kBF16> raw[kBatch];
+    uint64_t blk[kBatch];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = max(m, abs_bits(v[j]));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-    const BlockScale bs = block_scale(__uint_as_float(m), st, d6);
-    uint32_t packed = 0;
-    if (kSR) {
-      const u32x4 r = sr_block(h, a.sr_stream, a.sr_seed);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) packed |= e2m1_sr(v[j] * bs.recip, sr_word(r, j)) << (4 * j);
-    } else {
-      float q[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) q[j] = v[j] * bs.recip;
-      packed = e2m1_rne8(q);
+    for (int i = 0; i < kBatch; ++i) {
+      const uint64_t seg = s0 + i * nwaves;
+      if (seg < nseg) blk[i] = load_segment<kBF16, kContig>(a, seg, lane, raw[i]);
+      else { raw[i].zero(); blk[i] = a.nblocks; }
     }
-    *reinterpret_cast<uint32_t *>(a.codes + 4 * h) = packed;
-    if (!odd) a.scales[h >> 1] = (uint8_t)bs.code;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (blk[i] < a.nblocks) {
+        float v[16];
+        raw[i].values(v);
+        if (kRHT) rht16(v, mask);
+        row_store_block<kSR>(a, blk[i], v, block_scale_code(max_abs16(v), st, d6), recip);
+      }
+    }
   }
   encode_finish(a.ctrl, a.tensor_scale, st);
 }
@@ -181,6 +443,27 @@ __global__ __launch_bounds__(kThreads) void row_encode_kernel(RowArgs a) {
 // ---------------------------------------------------------------------------
 // Transposing kernels
 // ---------------------------------------------------------------------------
+
+// Workgroup tile: 256 input rows (16 row blocks) x 128 input columns (16
+// groups of 8).  Lane (cg, rb) = (tid % 16, tid / 16) owns 8 columns x 16
+// rows = 8 blocks of the transposed view.  For each input row, the 16 lanes
+// of one row block read 256 contiguous bytes.  Codes of the whole tile (128
+// transposed rows x 128 bytes) are staged in LDS and written out as whole
+// lines.
+constexpr int kColTileRB = 16;   // row blocks per tile
+constexpr int kColTileCG = 16;   // column groups per tile
+
+struct ColArgs {
+  const void *x;
+  int64_t batch, R, C, ld, bstride;  // input [batch][R][C]; R % 16 == 0
+  int64_t tiles_r, tiles_c;          // ceil(R / 256), ceil(C / 128)
+  bool vec_ok;                       // rows and batches start on 16-byte boundaries
+  uint8_t *codes, *scales;
+  float *tensor_scale;
+  QuantCtrl *ctrl;
+  uint64_t sr_seed, rht_seed;
+  uint32_t sr_stream;
+};
 
 // 16 rows x 8 columns of raw input held as BF16 pairs (4 dwords per row) or
 // FP32 (8 floats per row).  Columns at or beyond C read as zero.
@@ -231,36 +514,39 @@ __device__ __forceinline__ void col_load(const ColArgs &a, int64_t b, int64_t rb
   }
 }
 
-__device__ __forceinline__ void col_unit(const ColArgs &a, uint64_t u, int64_t &b, int64_t &rbg,
-                                         int64_t &cg) {
-  cg = (int64_t)(u % (uint64_t)a.col_groups);
-  const uint64_t t = u / (uint64_t)a.col_groups;
-  rbg = (int64_t)(t % (uint64_t)a.row_groups);
-  b = (int64_t)(t / (uint64_t)a.row_groups);
+struct ColLane {
+  int64_t b, tr, tc, rb, cg;
+  bool valid;
+};
+
+__device__ __forceinline__ ColLane col_lane(const ColArgs &a) {
+  ColLane l;
+  const int64_t bid = blockIdx.x;
+  l.tc = bid % a.tiles_c;
+  const int64_t t = bid / a.tiles_c;
+  l.tr = t % a.tiles_r;
+  l.b = t / a.tiles_r;
+  l.cg = l.tc * kColTileCG + (threadIdx.x % kColTileCG);
+  l.rb = l.tr * kColTileRB + (threadIdx.x / kColTileCG);
+  l.valid = l.rb < a.R / 16 && 8 * l.cg < a.C;
+  return l;
 }
 
 template <bool kBF16, bool kRHT>
 __global__ __launch_bounds__(kThreads) void col_amax_kernel(ColArgs a) {
   const uint32_t mask = kRHT ? rht_sign_mask(a.rht_seed) : 0u;
-  const int64_t RB = a.R / 16;
+  const ColLane l = col_lane(a);
   uint32_t m = 0;
-  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  for (uint64_t u = (uint64_t)blockIdx.x * kThreads + threadIdx.x; u < a.units; u += stride) {
-    int64_t b, rbg, cg;
-    col_unit(a, u, b, rbg, cg);
-    const int64_t rb_end = min(RB, (rbg + 1) * kRowBlocksPerLane);
-    for (int64_t rb = rbg * kRowBlocksPerLane; rb < rb_end; ++rb) {
-      ColTile<kBF16> t;
-      col_load<kBF16>(a, b, rb, cg, t);
+  if (l.valid) {
+    ColTile<kBF16> t;
+    col_load<kBF16>(a, l.b, l.rb, l.cg, t);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v[16];
+    for (int e = 0; e < 8; ++e) {
+      float v[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = t.at(j, e);
-        if (kRHT) rht16(v, mask);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) m = max(m, abs_bits(v[j]));
-      }
+      for (int j = 0; j < 16; ++j) v[j] = t.at(j, e);
+      if (kRHT) rht16(v, mask);
+      m = max(m, max_abs16(v));
     }
   }
   block_amax_commit(m, a.ctrl);
@@ -268,51 +554,49 @@ __global__ __launch_bounds__(kThreads) void col_amax_kernel(ColArgs a) {
 
 template <bool kBF16, bool kRHT, bool kSR>
 __global__ __launch_bounds__(kThreads) void col_encode_kernel(ColArgs a) {
+  __shared__ float recip[128];
+  // [tile column][row block], rows padded by one entry against bank conflicts
+  __shared__ uint2 tile_codes[kColTileCG * 8][kColTileRB + 1];
+  __shared__ uint8_t tile_scales[kColTileCG * 8][kColTileRB + 4];
   const uint32_t mask = kRHT ? rht_sign_mask(a.rht_seed) : 0u;
   const float amax = __uint_as_float(load_amax(a.ctrl));
   const float st = amax / 2688.0f;
   const float d6 = 6.0f * st;
+  build_recip_table(recip, st);
+  __syncthreads();
+  const ColLane l = col_lane(a);
+  const int cgl = threadIdx.x % kColTileCG, rbl = threadIdx.x / kColTileCG;
+  if (l.valid) {
+    ColTile<kBF16> t;
+    col_load<kBF16>(a, l.b, l.rb, l.cg, t);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t c = 8 * l.cg + e;  // row of the transposed view
+      if (c >= a.C) break;
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = t.at(j, e);
+      if (kRHT) rht16(v, mask);
+      const uint32_t S = block_scale_code(max_abs16(v), st, d6);
+      const int64_t vrow = l.b * a.C + c;  // row index in the [batch*C][R] view
+      tile_codes[cgl * 8 + e][rbl] = encode16<kSR>(v, recip[S], (uint64_t)(vrow * a.R + 16 * l.rb), a.sr_stream,
+                                                   a.sr_seed);
+      tile_scales[cgl * 8 + e][rbl] = (uint8_t)S;
+    }
+  }
+  __syncthreads();
+  // Write out: 128 transposed rows x 16 row blocks of 8 code bytes and one
+  // scale byte; consecutive threads take consecutive row blocks of a row.
   const int64_t RB = a.R / 16;
-  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  for (uint64_t u = (uint64_t)blockIdx.x * kThreads + threadIdx.x; u < a.units; u += stride) {
-    int64_t b, rbg, cg;
-    col_unit(a, u, b, rbg, cg);
-    const int64_t rb_end = min(RB, (rbg + 1) * kRowBlocksPerLane);
-    for (int64_t rb = rbg * kRowBlocksPerLane; rb < rb_end; ++rb) {
-      ColTile<kBF16> t;
-      col_load<kBF16>(a, b, rb, cg, t);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int64_t c = 8 * cg + e;  // row of the transposed view
-        if (c >= a.C) break;
-        float v[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = t.at(j, e);
-        if (kRHT) rht16(v, mask);
-        uint32_t m = 0;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) m = max(m, abs_bits(v[j]));
-        const BlockScale bs = block_scale(__uint_as_float(m), st, d6);
-        const int64_t vrow = b * a.C + c;  // row index in the [batch*C][R] view
-        uint32_t lo = 0, hi = 0;
-        if (kSR) {
-          const uint64_t g0 = (uint64_t)(vrow * a.R + 16 * rb) / 8;
-          const u32x4 r0 = sr_block(g0, a.sr_stream, a.sr_seed);
-          const u32x4 r1 = sr_block(g0 + 1, a.sr_stream, a.sr_seed);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) lo |= e2m1_sr(v[j] * bs.recip, sr_word(r0, j)) << (4 * j);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) hi |= e2m1_sr(v[8 + j] * bs.recip, sr_word(r1, j)) << (4 * j);
-        } else {
-          float q[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) q[j] = v[j] * bs.recip;
-          lo = e2m1_rne8(q);
-          hi = e2m1_rne8(q + 8);
-        }
-        *reinterpret_cast<uint2 *>(a.codes + vrow * (a.R / 2) + 8 * rb) = make_uint2(lo, hi);
-        a.scales[vrow * RB + rb] = (uint8_t)bs.code;
-      }
+  const int64_t rb_n = min((int64_t)kColTileRB, RB - l.tr * kColTileRB);
+  for (int i = threadIdx.x; i < kColTileCG * 8 * kColTileRB; i += kThreads) {
+    const int tcol = i / kColTileRB, trb = i % kColTileRB;
+    const int64_t c = l.tc * kColTileCG * 8 + tcol;
+    if (c < a.C && trb < rb_n) {
+      const int64_t vrow = l.b * a.C + c;
+      const int64_t rb = l.tr * kColTileRB + trb;
+      st_stream(a.codes + vrow * (a.R / 2) + 8 * rb, tile_codes[tcol][trb]);
+      a.scales[vrow * RB + rb] = tile_scales[tcol][trb];
     }
   }
   encode_finish(a.ctrl, a.tensor_scale, st);
@@ -322,41 +606,87 @@ __global__ __launch_bounds__(kThreads) void col_encode_kernel(ColArgs a) {
 // Launchers
 // ---------------------------------------------------------------------------
 
-int grid_for(uint64_t items) {
-  const uint64_t want = (items + kThreads - 1) / kThreads;
-  const uint64_t cap = 256ull * 8;  // 8 workgroups per CU on a 256-CU part
+int grid_for(uint64_t items, int threads, uint64_t cap) {
+  const uint64_t want = (items + threads - 1) / threads;
   return (int)(want < 1 ? 1 : (want > cap ? cap : want));
 }
 
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+// Single-pass row-wise quantize if the tensor fits the on-chip capacity of a
+// co-resident grid; returns false (nothing launched) otherwise.
+template <bool kBF16, bool kRHT, bool kSR>
+bool try_row_fused(RowArgs a, hipStream_t s, hipError_t &err) {
+  const int cus = cu_count();
+  if (cus <= 0) return false;
+  auto kernel = row_fused_kernel<kBF16, kRHT, kSR>;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kFusedThreads, 0) != hipSuccess ||
+      per_cu < kFusedPerCU)
+    return false;
+  const uint64_t grid = (uint64_t)cus * kFusedPerCU;
+  const uint64_t nwaves = grid * (kFusedThreads / 64);
+  const uint64_t nseg = (a.nblocks + 63) / 64;
+  const uint64_t iters = (nseg + nwaves - 1) / nwaves;
+  if (iters > (uint64_t)Fused<kBF16>::kMaxBlocks) return false;
+  a.nseg_iters = (uint32_t)iters;
+#if NVFP4_FUSED_COOPERATIVE
+  void *args[] = {&a};
+  err = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)grid),
+                                   dim3(kFusedThreads), args, 0, s);
+#else
+  // A plain launch: with one workgroup per CU every workgroup becomes
+  // resident once kernels already running on other streams drain, so the
+  // grid barrier completes; the bounded wait only guards against a kernel
+  // that holds CUs indefinitely.  (The cooperative-launch API gives the same
+  // guarantee up front but costs ~18 us per call on MI355X.)
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kFusedThreads), 0, s, a);
+  err = hipGetLastError();
+#endif
+  return err == hipSuccess;
+}
+
 template <bool kBF16, bool kRHT, bool kSR, bool kContig>
-hipError_t run_row(const RowArgs &a, hipStream_t s) {
-  const int g = grid_for(a.half_blocks);
+hipError_t run_row_two_pass(const RowArgs &a, hipStream_t s) {
+  const int g = grid_for((a.nblocks + 63) / 64, (kThreads / 64) * kBatch, 256ull * 4);
   hipLaunchKernelGGL((row_amax_kernel<kBF16, kRHT, kContig>), dim3(g), dim3(kThreads), 0, s, a);
   hipLaunchKernelGGL((row_encode_kernel<kBF16, kRHT, kSR, kContig>), dim3(g), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <bool kBF16, bool kRHT, bool kSR>
-hipError_t run_col(const ColArgs &a, hipStream_t s) {
-  const int g = grid_for(a.units);
-  hipLaunchKernelGGL((col_amax_kernel<kBF16, kRHT>), dim3(g), dim3(kThreads), 0, s, a);
-  hipLaunchKernelGGL((col_encode_kernel<kBF16, kRHT, kSR>), dim3(g), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+hipError_t run_row(const RowArgs &a, bool contig, hipStream_t s) {
+  if (contig) {
+    hipError_t err = hipSuccess;
+    if (!NVFP4_FUSED_DISABLE && try_row_fused<kBF16, kRHT, kSR>(a, s, err)) return hipSuccess;
+    (void)hipGetLastError();  // a refused cooperative launch falls back to two passes
+    return run_row_two_pass<kBF16, kRHT, kSR, true>(a, s);
+  }
+  return run_row_two_pass<kBF16, kRHT, kSR, false>(a, s);
+}
+
+template <bool kBF16>
+hipError_t dispatch_row(const RowArgs &a, bool rht, bool sr, bool contig, hipStream_t s) {
+  if (rht) return sr ? run_row<kBF16, true, true>(a, contig, s) : run_row<kBF16, true, false>(a, contig, s);
+  return sr ? run_row<kBF16, false, true>(a, contig, s) : run_row<kBF16, false, false>(a, contig, s);
 }
 
 template <bool kBF16, bool kRHT, bool kSR>
-hipError_t dispatch_row(const RowArgs &a, bool contig, hipStream_t s) {
-  return contig ? run_row<kBF16, kRHT, kSR, true>(a, s) : run_row<kBF16, kRHT, kSR, false>(a, s);
+hipError_t run_col(const ColArgs &a, hipStream_t s) {
+  const uint64_t g = (uint64_t)(a.batch * a.tiles_r * a.tiles_c);
+  if (g > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((col_amax_kernel<kBF16, kRHT>), dim3((unsigned)g), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((col_encode_kernel<kBF16, kRHT, kSR>), dim3((unsigned)g), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 template <bool kBF16>
-hipError_t dispatch_flags_row(const RowArgs &a, bool rht, bool sr, bool contig, hipStream_t s) {
-  if (rht) return sr ? dispatch_row<kBF16, true, true>(a, contig, s) : dispatch_row<kBF16, true, false>(a, contig, s);
-  return sr ? dispatch_row<kBF16, false, true>(a, contig, s) : dispatch_row<kBF16, false, false>(a, contig, s);
-}
-
-template <bool kBF16>
-hipError_t dispatch_flags_col(const ColArgs &a, bool rht, bool sr, hipStream_t s) {
+hipError_t dispatch_col(const ColArgs &a, bool rht, bool sr, hipStream_t s) {
   if (rht) return sr ? run_col<kBF16, true, true>(a, s) : run_col<kBF16, true, false>(a, s);
   return sr ? run_col<kBF16, false, true>(a, s) : run_col<kBF16, false, false>(a, s);
 }
@@ -376,8 +706,8 @@ nvfp4_status launch_quantize(const QuantProblem &p, hipStream_t s) {
   if (!p.along_rows) {
     RowArgs a{};
     a.x = p.x;
-    a.half_blocks = (uint64_t)(p.batch * p.rows * p.cols / 8);
-    a.hb_per_row = (uint64_t)(p.cols / 8);
+    a.nblocks = (uint64_t)(p.batch * p.rows * p.cols / 16);
+    a.bpr = (uint64_t)(p.cols / 16);
     a.rows = p.rows;
     a.ld = p.ld;
     a.bstride = p.bstride;
@@ -389,8 +719,7 @@ nvfp4_status launch_quantize(const QuantProblem &p, hipStream_t s) {
     a.rht_seed = p.rht_seed;
     a.sr_stream = p.sr_stream;
     const bool contig = (p.ld == p.cols) && (p.batch == 1 || p.bstride == p.rows * p.ld);
-    err = p.bf16 ? dispatch_flags_row<true>(a, p.rht, p.sr, contig, s)
-                 : dispatch_flags_row<false>(a, p.rht, p.sr, contig, s);
+    err = p.bf16 ? dispatch_row<true>(a, p.rht, p.sr, contig, s) : dispatch_row<false>(a, p.rht, p.sr, contig, s);
   } else {
     ColArgs a{};
     a.x = p.x;
@@ -399,14 +728,11 @@ nvfp4_status launch_quantize(const QuantProblem &p, hipStream_t s) {
     a.C = p.cols;
     a.ld = p.ld;
     a.bstride = p.bstride;
-    a.col_groups = (p.cols + 7) / 8;
-    a.row_groups = (p.rows / 16 + kRowBlocksPerLane - 1) / kRowBlocksPerLane;
-    a.units = (uint64_t)(a.batch * a.row_groups * a.col_groups);
-    {
-      const int64_t esize = p.bf16 ? 2 : 4;
-      a.vec_ok = reinterpret_cast<uintptr_t>(p.x) % 16 == 0 && (p.ld * esize) % 16 == 0 &&
-                 (p.batch == 1 || (p.bstride * esize) % 16 == 0);
-    }
+    a.tiles_r = (p.rows / 16 + kColTileRB - 1) / kColTileRB;
+    a.tiles_c = (p.cols + 8 * kColTileCG - 1) / (8 * kColTileCG);
+    const int64_t esize = p.bf16 ? 2 : 4;
+    a.vec_ok = reinterpret_cast<uintptr_t>(p.x) % 16 == 0 && (p.ld * esize) % 16 == 0 &&
+               (p.batch == 1 || (p.bstride * esize) % 16 == 0);
     a.codes = p.codes;
     a.scales = p.scales;
     a.tensor_scale = p.tensor_scale;
@@ -414,7 +740,7 @@ nvfp4_status launch_quantize(const QuantProblem &p, hipStream_t s) {
     a.sr_seed = p.sr_seed;
     a.rht_seed = p.rht_seed;
     a.sr_stream = p.sr_stream;
-    err = p.bf16 ? dispatch_flags_col<true>(a, p.rht, p.sr, s) : dispatch_flags_col<false>(a, p.rht, p.sr, s);
+    err = p.bf16 ? dispatch_col<true>(a, p.rht, p.sr, s) : dispatch_col<false>(a, p.rht, p.sr, s);
   }
   return err == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }

@@ -30,7 +30,7 @@ def test_status_strings_and_version():
         assert nv.status_string(s) and nv.status_string(s) != "unknown status"
     assert nv.status_string(99) == "unknown status"
     assert nv.nvfp4_version() >> 16 == 1
-    assert nv.nvfp4_quantize_workspace_size() == 256
+    assert nv.nvfp4_quantize_workspace_size() == 4096
 
 
 def _q(batch, rows, cols, codes=FAKE, scales=FAKE, st=FAKE):
@@ -39,7 +39,7 @@ def _q(batch, rows, cols, codes=FAKE, scales=FAKE, st=FAKE):
 
 def _quant(**kw):
     a = dict(x=FAKE, dt=nv.BF16, b=1, r=32, c=64, ld=64, bs=32 * 64, axis=nv.ALONG_COLS,
-             opts=nv.QuantOptsC(0, 0, 0, 0, 0, 0), out=None, ws=FAKE, wsb=256)
+             opts=nv.QuantOptsC(0, 0, 0, 0, 0, 0), out=None, ws=FAKE, wsb=4096)
     a.update(kw)
     if a["out"] is None:
         qr, qc = (a["r"], a["c"]) if a["axis"] == nv.ALONG_COLS else (a["c"], a["r"])
@@ -67,9 +67,9 @@ def test_quantize_argument_errors():
     assert _quant(out=_q(1, 32, 64, codes=FAKE + 8)) == nv.EALIGN
     assert _quant(out=_q(1, 32, 64, scales=FAKE + 2)) == nv.EALIGN
     assert _quant(ws=0) == nv.EWORKSPACE
-    assert _quant(wsb=255) == nv.EWORKSPACE
+    assert _quant(wsb=4095) == nv.EWORKSPACE
     assert _quant(ws=FAKE + 64) == nv.EALIGN
-    assert nv.nvfp4_quantize(FAKE, nv.BF16, 1, 32, 64, 64, 0, 0, None, None, FAKE, 256, None) == nv.EINVAL
+    assert nv.nvfp4_quantize(FAKE, nv.BF16, 1, 32, 64, 64, 0, 0, None, None, FAKE, 4096, None) == nv.EINVAL
 
 
 def test_gemm_argument_errors():
@@ -91,7 +91,7 @@ def test_linear_argument_errors_and_workspace_size():
     M, N, K = 64, 32, 48
     need = nv.nvfp4_linear_workspace_size(M, N, K)
     views = [(M, K), (N, K), (M, N), (K, N), (N, M), (K, M)]
-    assert need >= sum(r * c // 2 + r * c // 16 + 512 for r, c in views)
+    assert need >= sum(r * c // 2 + r * c // 16 + 4096 for r, c in views)
     assert nv.nvfp4_linear_workspace_size(0, N, K) == 0
     cfg = nv.LinearCfgC(1, 2, 1, nv.BF16)
     f = nv.nvfp4_linear_fwd_bwd
