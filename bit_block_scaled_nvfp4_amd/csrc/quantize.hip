@@ -11,8 +11,8 @@
 // owns one whole 16-element block (two 16-byte BF16 loads), so the transform,
 // the block maximum and the block scale stay in the lane.
 //  * Single pass (tensors that fit in the register files): a grid of one
-//    512-thread workgroup per CU loads every lane's blocks
-//    (up to 16 per lane for BF16, 33.5M elements on 256 CUs) into registers, reduces the amax per
+//    1024-thread workgroup per CU loads every lane's blocks (up to 8 per
+//    lane for BF16, 33.5M elements on 256 CUs) into registers, reduces the amax per
 //    wavefront and workgroup, meets the rest of the grid at an epoch
 //    barrier, then encodes from registers.  HBM sees one read of the input
 //    and one write of codes and scales.
@@ -39,12 +39,12 @@ namespace {
 
 constexpr int kThreads = 256;           // two-pass kernels
 #ifndef NVFP4_FUSED_THREADS
-#define NVFP4_FUSED_THREADS 512
+#define NVFP4_FUSED_THREADS 1024
 #endif
 constexpr int kFusedThreads = NVFP4_FUSED_THREADS;  // single-pass kernel, one workgroup per CU
 constexpr int kFusedPerCU = 1;
 constexpr int kBatch = 4;               // two-pass row kernels: blocks loaded per lane before use
-constexpr uint32_t kSpinLimit = 1u << 25;  // ~2 s of polling
+constexpr uint32_t kSpinLimit = 1u << 22;  // polls before a barrier wait gives up (~1 s)
 
 #ifndef NVFP4_FUSED_COOPERATIVE
 #define NVFP4_FUSED_COOPERATIVE 0
@@ -55,8 +55,8 @@ constexpr uint32_t kSpinLimit = 1u << 25;  // ~2 s of polling
 
 template <bool kBF16>
 struct Fused {
-  // segments held per wavefront: 16 blocks per lane (BF16) at 512 threads,
-  // i.e. 33.5M elements on 256 CUs, within the register budget
+  // blocks held per lane: 33.5M BF16 (16.8M FP32) elements on 256 CUs,
+  // within the register budget of the workgroup size
   static constexpr int kMaxBlocks = (kBF16 ? 16 : 8) * 512 / kFusedThreads;
 };
 
