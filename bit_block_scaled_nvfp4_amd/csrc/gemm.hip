@@ -18,20 +18,30 @@
 //
 // Tiling: a 256 x (64 * kFragN) output tile per workgroup of 4 wavefronts in
 // a 2 x 2 grid, each wavefront owning 128 x (32 * kFragN) = 4 x kFragN MFMA
-// tiles.  Decoding costs about 9 VALU instructions per 8 elements of one
-// fragment; with kFragN = 4 a wavefront decodes 8 fragments per 16 MFMAs,
-// about 4.4 VALU instructions per 32-cycle MFMA, which the SIMD overlaps with
-// the matrix pipe.  The launcher picks kFragN (4, 3 or 2) so that the tile
-// count fills the GPU in whole rounds.  K advances 128 elements (8 scale
-// blocks) per step through two LDS stages (64 code bytes + 8 scale bytes per
-// row per step).  When K % 128 == 0 the next step is fetched with
-// global_load_lds straight into the idle stage (no VGPRs hold it) right after
-// the current stage has been read into registers, so the loads fly during
-// the math; otherwise loads go through registers with K-tail zeroing.
-// Within a step, lane half h of a fragment covers K offsets [64h, 64h + 64):
-// MFMA sub-step s takes offsets 64h + 8s .. 64h + 8s + 7, i.e. one scale
-// block (4h + s/2) per lane.  A and B use the same assignment, so each K
-// index meets its partner once.
+// tiles, one wavefront per SIMD.  K advances 128 elements (8 scale blocks)
+// per step through two LDS stages (64 code bytes + 8 scale bytes per row per
+// step).  Within a step, lane half h of a fragment covers K offsets
+// [64h, 64h + 64): MFMA sub-step s takes offsets 64h + 8s .. 64h + 8s + 7,
+// i.e. one scale block (4h + s/2) per lane.  A and B use the same
+// assignment, so each K index meets its partner once.
+//
+// The decode is the VALU cost: the FP4 -> FP16 converter issues at about half
+// the rate of a plain VALU instruction, so decoding one fragment's sub-step
+// (8 elements per lane) costs about as much issue time as 1.5 MFMAs, and with
+// one wavefront per SIMD it only overlaps the matrix pipe when it sits
+// between MFMAs of other operands.  Three main loops:
+//  * K % 128 == 0, tiles 256 x 192 / 256 x 128: software pipelined.  The next
+//    sub-step is decoded while the current one's MFMAs run (grouped one MFMA
+//    to a few VALU instructions), codes are read from LDS half a step ahead,
+//    and global_load_lds fills the stage of the step after next, so global
+//    latency has a whole step and LDS latency half a step to hide.
+//  * K % 128 == 0, tiles 256 x 256: the accumulators fill the AGPR file, so
+//    a step reads its codes from LDS, issues the next step's global_load_lds
+//    (into the idle stage, no VGPRs), then decodes and multiplies.
+//  * Other K: register-staged loads with the K tail read as zero codes and
+//    scales (zero products).
+// The launcher picks the tile width so that the tile count fills the 256
+// CUs in whole rounds.
 //
 // Workgroups are mapped to tiles so that each XCD (blockIdx mod 8 under the
 // round-robin dispatch) works on a contiguous range of tiles, in groups of
@@ -43,7 +53,7 @@
 #include "internal.hpp"
 
 #ifndef NVFP4_GEMM_INTERLEAVE
-#define NVFP4_GEMM_INTERLEAVE 0
+#define NVFP4_GEMM_INTERLEAVE 5
 #endif
 #ifndef NVFP4_GEMM_SWIZZLE
 #define NVFP4_GEMM_SWIZZLE 2
@@ -64,6 +74,9 @@ constexpr int kThreads = 256;
 constexpr int kRowBytes = BK / 2;  // 64 code bytes per row per K step
 constexpr int kFragM = 4;          // 32-row A fragments per wavefront
 constexpr int kGroupM = 8;         // tile rows per L2 group
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
+// maxima (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // LDS placement of the 16-byte code chunk `part` (0..3) of tile row `row`.
 // Fragment reads take the same part from 32 consecutive rows; XOR-ing the
@@ -92,7 +105,7 @@ struct GemmArgs {
 
 // LDS stage: codes [rows][64 B] and scales [rows][8 B] per operand.
 template <int kBN>
-struct Stage {
+struct alignas(16) Stage {
   uint8_t a[BM * kRowBytes];
   uint8_t b[kBN * kRowBytes];
   uint2 as[BM];
@@ -198,10 +211,165 @@ struct StagedLoad {
   }
 };
 
+// One lane's codes for half a K step: 16 bytes (32 elements, sub-steps
+// 4*half .. 4*half + 3) of every fragment it feeds.
+template <int kFragN>
+struct HalfCodes {
+  uint4 a[kFragM], b[kFragN];
+};
+
+// One lane's block scales for a K step as FP16 pairs: [f][0] holds blocks
+// 4h and 4h + 1 of the step, [f][1] blocks 4h + 2 and 4h + 3.
+template <int kFragN>
+struct StepScales {
+  half2_t a[kFragM][2], b[kFragN][2];
+};
+
+struct LaneCoord {
+  int wm, wn, h, r32;
+};
+
+__device__ __forceinline__ uint32_t word_of(const uint4 &q, int i) {
+  return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
+}
+
+template <int kFragN, int kBN>
+__device__ __forceinline__ void read_codes(const Stage<kBN> &st, int half, const LaneCoord &c,
+                                           HalfCodes<kFragN> &r) {
+#pragma unroll
+  for (int f = 0; f < kFragM; ++f) {
+    const int row = c.wm * 128 + f * 32 + c.r32;
+    r.a[f] = *reinterpret_cast<const uint4 *>(st.a + 16 * chunk_slot(row, 2 * c.h + half));
+  }
+#pragma unroll
+  for (int f = 0; f < kFragN; ++f) {
+    const int row = c.wn * (32 * kFragN) + f * 32 + c.r32;
+    r.b[f] = *reinterpret_cast<const uint4 *>(st.b + 16 * chunk_slot(row, 2 * c.h + half));
+  }
+}
+
+template <int kFragN, int kBN>
+__device__ __forceinline__ void read_scales(const Stage<kBN> &st, const LaneCoord &c, StepScales<kFragN> &sc) {
+#pragma unroll
+  for (int f = 0; f < kFragM; ++f) {
+    const int row = c.wm * 128 + f * 32 + c.r32;
+    const uint32_t w = c.h ? st.as[row].y : st.as[row].x;
+    sc.a[f][0] = scale_pair2(w);
+    sc.a[f][1] = scale_pair2(w >> 16);
+  }
+#pragma unroll
+  for (int f = 0; f < kFragN; ++f) {
+    const int row = c.wn * (32 * kFragN) + f * 32 + c.r32;
+    const uint32_t w = c.h ? st.bs[row].y : st.bs[row].x;
+    sc.b[f][0] = scale_pair2(w);
+    sc.b[f][1] = scale_pair2(w >> 16);
+  }
+}
+
+template <int kWord>
+__device__ __forceinline__ uint32_t word_at(const uint4 &q) {
+  return kWord == 0 ? q.x : kWord == 1 ? q.y : kWord == 2 ? q.z : q.w;
+}
+
+// Operands of MFMA sub-step kS (0..7) from the half of the codes holding it.
+template <int kS, int kFragN>
+__device__ __forceinline__ void decode_substep(const HalfCodes<kFragN> &r, const StepScales<kFragN> &sc,
+                                               half8_t (&av)[kFragM], half8_t (&bv)[kFragN]) {
+#pragma unroll
+  for (int f = 0; f < kFragM; ++f) av[f] = decode8(word_at<kS & 3>(r.a[f]), sc.a[f][kS >> 2][(kS >> 1) & 1]);
+#pragma unroll
+  for (int f = 0; f < kFragN; ++f) bv[f] = decode8(word_at<kS & 3>(r.b[f]), sc.b[f][kS >> 2][(kS >> 1) & 1]);
+}
+
+template <int kFragN>
+__device__ __forceinline__ void mfma_substep(floatx16 (&acc)[kFragM][kFragN], const half8_t (&av)[kFragM],
+                                             const half8_t (&bv)[kFragN]) {
+#pragma unroll
+  for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+    for (int j = 0; j < kFragN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+}
+
+// The MFMAs of one sub-step on av/bv, while sub-step kNext is decoded from
+// (r, sc) into av/bv's successors.
+template <int kNext, int kFragN>
+__device__ __forceinline__ void mfma_and_decode(const HalfCodes<kFragN> &r, const StepScales<kFragN> &sc,
+                                                half8_t (&av)[kFragM], half8_t (&bv)[kFragN],
+                                                floatx16 (&acc)[kFragM][kFragN]) {
+  half8_t na[kFragM], nb[kFragN];
+  decode_substep<kNext, kFragN>(r, sc, na, nb);
+  mfma_substep<kFragN>(acc, av, bv);
+#if NVFP4_GEMM_INTERLEAVE
+  // One wavefront per SIMD issues in order, so VALU work only overlaps an
+  // MFMA if it sits between MFMAs: ask for kFragM * kFragN groups of one
+  // MFMA followed by a few VALU instructions.
+#pragma unroll
+  for (int i = 0; i < kFragM * kFragN; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_GEMM_INTERLEAVE, 0);
+  }
+#endif
+#pragma unroll
+  for (int f = 0; f < kFragM; ++f) av[f] = na[f];
+#pragma unroll
+  for (int f = 0; f < kFragN; ++f) bv[f] = nb[f];
+}
+
+// Operand pointers and extents of one workgroup's tile.
+struct TileSrc {
+  const uint8_t *ac, *as, *bc, *bs;
+  int64_t M, N, K, m0, n0;
+};
+
+// One K step of the pipelined main loop (K % 128 == 0).  On entry r0 holds
+// the first half of this step's codes, sc_cur its scales, and av/bv the
+// decoded operands of sub-step 0; stage `cur` holds this step and `nxt` the
+// next one, landed or in flight.  Each sub-step's MFMAs run while the next
+// sub-step is decoded.  Mid-step, one barrier makes the next step's stage
+// visible (the compiler waits for this wave's global->LDS loads before it);
+// then the next step's first half and scales are read into r0 and sc_nxt,
+// and the step after next is fetched into `cur`, whose reads every wave has
+// completed before the barrier.
+template <int kFragN, int kBN>
+__device__ __forceinline__ void pipelined_kstep(Stage<kBN> &cur, const Stage<kBN> &nxt, const TileSrc &t, int kt,
+                                                int ksteps, const LaneCoord &c, HalfCodes<kFragN> &r0,
+                                                HalfCodes<kFragN> &r1, const StepScales<kFragN> &sc_cur,
+                                                StepScales<kFragN> &sc_nxt, half8_t (&av)[kFragM],
+                                                half8_t (&bv)[kFragN], floatx16 (&acc)[kFragM][kFragN]) {
+  read_codes<kFragN>(cur, 1, c, r1);
+  mfma_and_decode<1>(r0, sc_cur, av, bv, acc);
+  mfma_and_decode<2>(r0, sc_cur, av, bv, acc);
+  mfma_and_decode<3>(r0, sc_cur, av, bv, acc);
+  mfma_and_decode<4>(r1, sc_cur, av, bv, acc);
+  // This wave's global->LDS loads of the next step must have landed before
+  // the barrier.  Stated explicitly: the compiler's own wait for them is not
+  // reliably kept when the loads were issued in the previous loop iteration.
+  // The scheduling fences pin the wait and the barrier after the MFMAs.
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  read_codes<kFragN>(nxt, 0, c, r0);  // past the last step: stale but in-bounds LDS, never used
+  read_scales<kFragN>(nxt, c, sc_nxt);
+  if (kt + 2 < ksteps) {
+    const int64_t k0 = (int64_t)(kt + 2) * BK;
+    lds_load_operand<BM>(t.ac, t.as, t.M, t.K, t.m0, k0, cur.a, cur.as);
+    lds_load_operand<kBN>(t.bc, t.bs, t.N, t.K, t.n0, k0, cur.b, cur.bs);
+  }
+  mfma_and_decode<5>(r1, sc_cur, av, bv, acc);
+  mfma_and_decode<6>(r1, sc_cur, av, bv, acc);
+  mfma_and_decode<7>(r1, sc_cur, av, bv, acc);
+  mfma_and_decode<0>(r0, sc_nxt, av, bv, acc);
+}
+
 template <int kFragN, bool kFast, bool kBF16Out>
 __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
   constexpr int kBN = 64 * kFragN;
-  __shared__ Stage<kBN> stage[2];
+  // Two stages as separate objects: the compiler can then tell a read of one
+  // from a global->LDS load in flight into the other and does not wait for it.
+  __shared__ Stage<kBN> st0, st1;
 
   // XCD-aware tile order: consecutive workgroups go to different XCDs, so
   // give XCD x the x-th contiguous slice of the grouped tile order.
@@ -236,98 +404,137 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int ksteps = (int)((g.K + BK - 1) / BK);
-  StagedLoad<BM> la;
-  StagedLoad<kBN> lb;
-  if (ksteps > 0) {
-    if constexpr (kFast) {
-      lds_load_operand<BM>(ac, as, g.M, g.K, m0, 0, stage[0].a, stage[0].as);
-      lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, 0, stage[0].b, stage[0].bs);
-    } else {
-      la.load(ac, as, g.M, g.K, m0, 0);
-      lb.load(bc, bs, g.N, g.K, n0, 0);
-      la.store(stage[0].a, stage[0].as);
-      lb.store(stage[0].b, stage[0].bs);
-    }
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < ksteps; ++kt) {
-    const Stage<kBN> &cur = stage[kt & 1];
-    const bool more = kt + 1 < ksteps;
-    // This lane's 32 code bytes and 4 scale bytes of every fragment.
-    uint4 ca[kFragM][2], cb[kFragN][2];
-    half2_t sa[kFragM][2], sb[kFragN][2];
-#pragma unroll
-    for (int f = 0; f < kFragM; ++f) {
-      const int r = wm * 128 + f * 32 + r32;
-      ca[f][0] = *reinterpret_cast<const uint4 *>(cur.a + 16 * chunk_slot(r, 2 * h));
-      ca[f][1] = *reinterpret_cast<const uint4 *>(cur.a + 16 * chunk_slot(r, 2 * h + 1));
-      const uint32_t w = h ? cur.as[r].y : cur.as[r].x;
-      sa[f][0] = scale_pair2(w);
-      sa[f][1] = scale_pair2(w >> 16);
-    }
-#pragma unroll
-    for (int f = 0; f < kFragN; ++f) {
-      const int r = wn * (32 * kFragN) + f * 32 + r32;
-      cb[f][0] = *reinterpret_cast<const uint4 *>(cur.b + 16 * chunk_slot(r, 2 * h));
-      cb[f][1] = *reinterpret_cast<const uint4 *>(cur.b + 16 * chunk_slot(r, 2 * h + 1));
-      const uint32_t w = h ? cur.bs[r].y : cur.bs[r].x;
-      sb[f][0] = scale_pair2(w);
-      sb[f][1] = scale_pair2(w >> 16);
-    }
-
-    // Issue the next step's loads only after this step's LDS reads: the
-    // compiler orders LDS reads after outstanding LDS-bound loads, so this
-    // keeps the prefetch in flight during the math below.
-    if (more) {
-      if constexpr (kFast) {
-        Stage<kBN> &nxt = stage[(kt + 1) & 1];
-        lds_load_operand<BM>(ac, as, g.M, g.K, m0, (int64_t)(kt + 1) * BK, nxt.a, nxt.as);
-        lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, (int64_t)(kt + 1) * BK, nxt.b, nxt.bs);
-      } else {
-        la.load(ac, as, g.M, g.K, m0, (int64_t)(kt + 1) * BK);
-        lb.load(bc, bs, g.N, g.K, n0, (int64_t)(kt + 1) * BK);
-      }
-    }
-
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      half8_t av[kFragM], bv[kFragN];
-#pragma unroll
-      for (int f = 0; f < kFragM; ++f) {
-        const uint4 q = ca[f][s >> 2];
-        const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
-        av[f] = decode8(w, sa[f][s >> 2][(s >> 1) & 1]);
-      }
-#pragma unroll
-      for (int f = 0; f < kFragN; ++f) {
-        const uint4 q = cb[f][s >> 2];
-        const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
-        bv[f] = decode8(w, sb[f][s >> 2][(s >> 1) & 1]);
-      }
-#pragma unroll
-      for (int i = 0; i < kFragM; ++i)
-#pragma unroll
-        for (int j = 0; j < kFragN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-    }
-#if NVFP4_GEMM_INTERLEAVE
-    // Ask the scheduler to alternate one MFMA with a few VALU instructions.
-#pragma unroll
-    for (int i = 0; i < 8 * kFragM * kFragN; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_GEMM_INTERLEAVE, 0);
-    }
-#endif
-
-    if constexpr (!kFast) {
-      if (more) {
-        Stage<kBN> &nxt = stage[(kt + 1) & 1];
-        la.store(nxt.a, nxt.as);
-        lb.store(nxt.b, nxt.bs);
+  if constexpr (kFast && kFragN <= 3) {
+    const TileSrc src{ac, as, bc, bs, g.M, g.N, g.K, m0, n0};
+    const LaneCoord c{wm, wn, h, r32};
+    if (ksteps > 0) {
+      lds_load_operand<BM>(ac, as, g.M, g.K, m0, 0, st0.a, st0.as);
+      lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, 0, st0.b, st0.bs);
+      if (ksteps > 1) {
+        lds_load_operand<BM>(ac, as, g.M, g.K, m0, BK, st1.a, st1.as);
+        lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, BK, st1.b, st1.bs);
       }
     }
     __syncthreads();
+    HalfCodes<kFragN> r0, r1;
+    StepScales<kFragN> sc0, sc1;  // scales of even / odd steps
+    half8_t av[kFragM], bv[kFragN];
+    read_codes<kFragN>(st0, 0, c, r0);
+    read_scales<kFragN>(st0, c, sc0);
+    decode_substep<0, kFragN>(r0, sc0, av, bv);
+    for (int kt = 0; kt < ksteps; kt += 2) {
+      pipelined_kstep<kFragN>(st0, st1, src, kt, ksteps, c, r0, r1, sc0, sc1, av, bv, acc);
+      if (kt + 1 < ksteps) pipelined_kstep<kFragN>(st1, st0, src, kt + 1, ksteps, c, r0, r1, sc1, sc0, av, bv, acc);
+    }
+  } else if constexpr (kFast) {
+    // 256 x 256 tiles: the accumulators take all 256 AGPRs, which leaves no
+    // room for the pipelined loop's second code and operand buffers.  A K
+    // step reads its codes from LDS, issues the global->LDS loads of the
+    // next step, then decodes and multiplies.
+    if (ksteps > 0) {
+      lds_load_operand<BM>(ac, as, g.M, g.K, m0, 0, st0.a, st0.as);
+      lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, 0, st0.b, st0.bs);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < ksteps; ++kt) {
+      const Stage<kBN> &cur = (kt & 1) ? st1 : st0;
+      Stage<kBN> &nxt = (kt & 1) ? st0 : st1;
+      uint4 ca[kFragM][2], cb[kFragN][2];
+      half2_t sa[kFragM][2], sb[kFragN][2];
+#pragma unroll
+      for (int f = 0; f < kFragM; ++f) {
+        const int r = wm * 128 + f * 32 + r32;
+        ca[f][0] = *reinterpret_cast<const uint4 *>(cur.a + 16 * chunk_slot(r, 2 * h));
+        ca[f][1] = *reinterpret_cast<const uint4 *>(cur.a + 16 * chunk_slot(r, 2 * h + 1));
+        const uint32_t w = h ? cur.as[r].y : cur.as[r].x;
+        sa[f][0] = scale_pair2(w);
+        sa[f][1] = scale_pair2(w >> 16);
+      }
+#pragma unroll
+      for (int f = 0; f < kFragN; ++f) {
+        const int r = wn * (32 * kFragN) + f * 32 + r32;
+        cb[f][0] = *reinterpret_cast<const uint4 *>(cur.b + 16 * chunk_slot(r, 2 * h));
+        cb[f][1] = *reinterpret_cast<const uint4 *>(cur.b + 16 * chunk_slot(r, 2 * h + 1));
+        const uint32_t w = h ? cur.bs[r].y : cur.bs[r].x;
+        sb[f][0] = scale_pair2(w);
+        sb[f][1] = scale_pair2(w >> 16);
+      }
+      // Issued after this step's LDS reads, so no read waits on them.
+      if (kt + 1 < ksteps) {
+        lds_load_operand<BM>(ac, as, g.M, g.K, m0, (int64_t)(kt + 1) * BK, nxt.a, nxt.as);
+        lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, (int64_t)(kt + 1) * BK, nxt.b, nxt.bs);
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        half8_t av[kFragM], bv[kFragN];
+#pragma unroll
+        for (int f = 0; f < kFragM; ++f) av[f] = decode8(word_of(ca[f][s >> 2], s & 3), sa[f][s >> 2][(s >> 1) & 1]);
+#pragma unroll
+        for (int f = 0; f < kFragN; ++f) bv[f] = decode8(word_of(cb[f][s >> 2], s & 3), sb[f][s >> 2][(s >> 1) & 1]);
+        mfma_substep<kFragN>(acc, av, bv);
+      }
+      // The next stage must have landed before the barrier.  The scheduling
+      // fences keep the wait below this step's math (hoisted, it would wait
+      // for the loads just issued) and the MFMAs above the barrier.
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+    }
+  } else {
+    StagedLoad<BM> la;
+    StagedLoad<kBN> lb;
+    if (ksteps > 0) {
+      la.load(ac, as, g.M, g.K, m0, 0);
+      lb.load(bc, bs, g.N, g.K, n0, 0);
+      la.store(st0.a, st0.as);
+      lb.store(st0.b, st0.bs);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < ksteps; ++kt) {
+      const Stage<kBN> &cur = (kt & 1) ? st1 : st0;
+      Stage<kBN> &nxt = (kt & 1) ? st0 : st1;
+      const bool more = kt + 1 < ksteps;
+      // This lane's 32 code bytes and 4 scale bytes of every fragment.
+      uint4 ca[kFragM][2], cb[kFragN][2];
+      half2_t sa[kFragM][2], sb[kFragN][2];
+#pragma unroll
+      for (int f = 0; f < kFragM; ++f) {
+        const int r = wm * 128 + f * 32 + r32;
+        ca[f][0] = *reinterpret_cast<const uint4 *>(cur.a + 16 * chunk_slot(r, 2 * h));
+        ca[f][1] = *reinterpret_cast<const uint4 *>(cur.a + 16 * chunk_slot(r, 2 * h + 1));
+        const uint32_t w = h ? cur.as[r].y : cur.as[r].x;
+        sa[f][0] = scale_pair2(w);
+        sa[f][1] = scale_pair2(w >> 16);
+      }
+#pragma unroll
+      for (int f = 0; f < kFragN; ++f) {
+        const int r = wn * (32 * kFragN) + f * 32 + r32;
+        cb[f][0] = *reinterpret_cast<const uint4 *>(cur.b + 16 * chunk_slot(r, 2 * h));
+        cb[f][1] = *reinterpret_cast<const uint4 *>(cur.b + 16 * chunk_slot(r, 2 * h + 1));
+        const uint32_t w = h ? cur.bs[r].y : cur.bs[r].x;
+        sb[f][0] = scale_pair2(w);
+        sb[f][1] = scale_pair2(w >> 16);
+      }
+      if (more) {
+        la.load(ac, as, g.M, g.K, m0, (int64_t)(kt + 1) * BK);
+        lb.load(bc, bs, g.N, g.K, n0, (int64_t)(kt + 1) * BK);
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        half8_t av[kFragM], bv[kFragN];
+#pragma unroll
+        for (int f = 0; f < kFragM; ++f) av[f] = decode8(word_of(ca[f][s >> 2], s & 3), sa[f][s >> 2][(s >> 1) & 1]);
+#pragma unroll
+        for (int f = 0; f < kFragN; ++f) bv[f] = decode8(word_of(cb[f][s >> 2], s & 3), sb[f][s >> 2][(s >> 1) & 1]);
+        mfma_substep<kFragN>(acc, av, bv);
+      }
+      if (more) {
+        la.store(nxt.a, nxt.as);
+        lb.store(nxt.b, nxt.bs);
+      }
+      __syncthreads();
+    }
   }
 
   // Epilogue: multiply by fl(fl(sA * sB) * alpha) and store.  Accumulator v
@@ -380,16 +587,16 @@ hipError_t launch_tiles(const GemmArgs &g, int64_t batch, bool fast, bool bf16, 
   return hipGetLastError();
 }
 
-// N-tile width: among 256, 192 and 128, the one with the least estimated
-// time, counting a partly filled last round of workgroups as a full round
-// (one workgroup per CU, 256 CUs) and costing narrower tiles by their extra
-// decode work per MFMA.
+// N-tile width (64 * kFragN): among 256, 192 and 128, the one with the least
+// estimated time, counting a partly filled last round of workgroups as a full
+// round (one workgroup per CU, 256 CUs) and costing narrower tiles by their
+// extra decode work per MFMA (measured on fprop/MLP-sized problems).
 int pick_frag_n(int64_t M, int64_t N, int64_t batch) {
   const int64_t tm = (M + BM - 1) / BM;
   double best = 1e300;
   int pick = 4;
   const int cands[3] = {4, 3, 2};
-  const double cost_per_col[3] = {1.0, 1.05, 1.15};  // relative decode overhead per output
+  const double cost_per_col[3] = {1.0, 1.02, 1.12};
   for (int c = 0; c < 3; ++c) {
     const int fn = cands[c];
     const int64_t tn = (N + 64 * fn - 1) / (64 * fn);
@@ -426,12 +633,12 @@ nvfp4_status launch_gemm(const GemmProblem &p, hipStream_t s) {
   g.ldc = p.ldc;
   g.bstride_c = p.bstride_c;
   g.alpha = p.alpha;
+  const bool fast = p.K % BK == 0;
   const int fn = pick_frag_n(p.M, p.N, p.batch);
   const int64_t tm = (p.M + BM - 1) / BM, tn = (p.N + 64 * fn - 1) / (64 * fn);
   if (tm * tn > 0x7FFFFFFF) return NVFP4_EUNSUPPORTED;
   g.tiles_m = (int)tm;
   g.tiles_n = (int)tn;
-  const bool fast = p.K % BK == 0;
   hipError_t e;
   if (fn == 4) e = launch_tiles<4>(g, p.batch, fast, p.c_bf16, s);
   else if (fn == 3) e = launch_tiles<3>(g, p.batch, fast, p.c_bf16, s);

@@ -80,3 +80,23 @@ def test_gemm_tiny_fp32_workload_full():
     assert_quant_equal(to_oracle_view(qb), oracle_quant(t["B"], axis=O.ALONG_ROWS), "B")
     stats = gemm_vs_oracle(qa, qb, out_dtype=torch.float32, what="tiny")
     assert stats["n"] == 256 * 256
+
+
+# Shapes that send the launcher down each main loop: the tile width follows
+# from filling 256 CUs in whole rounds (256 x 256 for 4000 x 4001, 256 x 192
+# for 4096 x 3072, 256 x 128 for small problems), and K % 128 selects the
+# global->LDS path or the register-staged one with a K tail.
+LOOP_SHAPES = [(4000, 4001, 256), (4096, 3072, 384), (448, 384, 384),
+               (4000, 4001, 272), (4096, 3072, 144), (448, 384, 400)]
+
+
+@pytest.mark.parametrize("M,N,K", LOOP_SHAPES)
+def test_gemm_every_main_loop(M, N, K):
+    a, b = _pair(M, N, K, 1, 7 * M + N + K)
+    qa, qb = gpu_quant(a), gpu_quant(b)
+    rng = np.random.default_rng(K)
+    edges = [r for t in range(0, M, 256) for r in (t, t + 127, t + 128, t + 255) if r < M]
+    rows = np.unique(np.concatenate([edges, [M - 1], rng.integers(0, M, 32)]))
+    for dt in (torch.float32, torch.bfloat16):
+        stats = gemm_vs_oracle(qa, qb, out_dtype=dt, rows=rows, what=f"{M}x{N}x{K}")
+        assert stats["n"] == rows.size * N
