@@ -6,14 +6,20 @@ One step is one pass of the whole path over one batch of synthetic input:
 quantize X (RNE), quantize W (RNE), GEMM Y = X^ W^^T (BF16 out), all on one
 stream with the inputs already resident in HBM.  Inputs rotate over enough
 copies to exceed twice the 256 MB Infinity Cache, so every step reads its
-operands from HBM.  Per-kernel times come from HIP events recorded on the
-stream the kernels run on; the step time from the host clock around the
-timed steps, bracketed by device synchronisation.
+operands from HBM.  The step time comes from the host clock around K timed
+steps, bracketed by device synchronisation; per-kernel times from HIP events
+recorded on the launch stream around each kernel during K further steps
+(kept out of the timed region because each event adds idle time between
+kernels).
 
 Prints one JSON line.  `value` is the whole-step NVFP4 GEMM throughput
 (2*M*N*K per step time, TFLOP/s); `roofline` describes the dominant kernel
-(the GEMM) against the dense FP16/BF16 MFMA peak; `cpu_baseline` times the
-CPU oracle (test infrastructure) on a bounded sample of the same step.
+(the GEMM) against the dense FP16/BF16 MFMA peak, with `traffic` the HBM
+bytes per launch from the committed counter summary (null once the GEMM
+source changed); `mfma_ceiling` is the sustained rate of the MFMA
+instruction itself for constant, random and NVFP4-valued operands on this
+GPU; `cpu_baseline` times the CPU oracle (test infrastructure) on a bounded
+sample of the same step.
 """
 from __future__ import annotations
 
@@ -45,10 +51,33 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="fprop_3b", choices=["fprop_3b", "mlp_up_12b"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-mfma-ceiling", action="store_true", help="skip the MFMA ceiling probe")
     p.add_argument("--cpu-rows", type=int, default=1024, help="GEMM rows in the CPU-oracle sample")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run 5 device-to-device copies of MIB MiB (calibrates HBM byte counters)")
     return p.parse_args()
+
+
+def mfma_ceiling():
+    """Sustained v_mfma_f32_32x32x16_f16 rate for three operand sets, from the
+    probe executable built next to the library (run as a child process before
+    this process touches the GPU).  The chip lowers its clock with operand
+    toggling, so the NVFP4-valued set is the attainable ceiling for the GEMM's
+    MFMA work; the datasheet peak assumes the top clock."""
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(nv.__file__)), "mfma_ceiling")
+    if not os.path.exists(exe):
+        return None
+    try:
+        out = subprocess.run([exe], check=True, capture_output=True, text=True, timeout=120).stdout
+    except (subprocess.SubprocessError, OSError):
+        return None
+    res = {}
+    for line in out.splitlines():
+        if line.startswith("{"):
+            r = json.loads(line)
+            res[r["operands"]] = {"TFLOP/s": r["TFLOP/s"], "shader_MHz": r["shader_MHz"]}
+    return res or None
 
 
 def measured_traffic(workload: str):
@@ -113,6 +142,7 @@ def main():
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+    ceiling = None if (args.copy_probe or args.no_mfma_ceiling) else mfma_ceiling()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.copy_probe:
@@ -132,30 +162,43 @@ def main():
     wsp_x = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
     wsp_w = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
 
+    # Each buffer set's three calls marshalled once, so the host enqueues a
+    # step in a few microseconds and stays ahead of the GPU; the events then
+    # time the kernels rather than launch gaps.
+    calls = [(nv.bind_quantize(xs[j], qxs[j], wsp_x), nv.bind_quantize(ws[j], qws[j], wsp_w),
+              nv.bind_gemm(qxs[j], qws[j], ys[j])) for j in range(nbuf)]
+
     def step(i, ev=None):
-        j = i % nbuf
+        qx, qw, mm = calls[i % nbuf]
         if ev is not None:
             ev[0].record()
-        nv.quantize(xs[j], out=qxs[j], workspace=wsp_x)
+        qx()
         if ev is not None:
             ev[1].record()
-        nv.quantize(ws[j], out=qws[j], workspace=wsp_w)
+        qw()
         if ev is not None:
             ev[2].record()
-        nv.gemm(qxs[j], qws[j], out=ys[j])
+        mm()
         if ev is not None:
             ev[3].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # Timed region: exactly K steps, nothing else on the stream.
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, events[i])
+        step(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # Per-kernel region: the same K steps again with HIP events recorded on the
+    # launch stream around each kernel (events add a few microseconds of
+    # idle between kernels, so they stay out of the timed region above).
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, events[i])
+    torch.cuda.synchronize()
 
     qx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     qw_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
@@ -194,6 +237,7 @@ def main():
                            "frac_hbm": round(qw_gbps / PEAK_HBM_GBPS, 4)},
             "quantize_x_w": {"GB/s": round(q_gbps, 1), "frac_hbm": round(q_gbps / PEAK_HBM_GBPS, 4)},
         },
+        "mfma_ceiling": ceiling,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -167,11 +167,9 @@ def new_workspace(nbytes: int, device) -> torch.Tensor:
     return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-def quantize(x: torch.Tensor, axis: int = ALONG_COLS, rounding: int = RNE, sr_seed: int = 0,
-             sr_stream: int = 0, rht: bool = False, rht_seed: int = 0, out: QTensor | None = None,
-             workspace: torch.Tensor | None = None) -> QTensor:
-    """Quantize a 2-D [rows][cols] or 3-D [batch][rows][cols] CUDA tensor
-    (bfloat16 or float32, last dimension contiguous)."""
+def _quantize_args(x: torch.Tensor, axis: int, rounding: int, sr_seed: int, sr_stream: int, rht: bool,
+                   rht_seed: int, out: QTensor | None, workspace: torch.Tensor | None):
+    """Validated ctypes arguments of one nvfp4_quantize call (and its output)."""
     if x.dim() == 2:
         x3 = x.unsqueeze(0)
     elif x.dim() == 3:
@@ -190,11 +188,45 @@ def quantize(x: torch.Tensor, axis: int = ALONG_COLS, rounding: int = RNE, sr_se
         workspace = new_workspace(nvfp4_quantize_workspace_size(), x.device)
     opts = QuantOptsC(rounding, int(bool(rht)), sr_seed, rht_seed, sr_stream, 0)
     q = out.c_struct()
-    st = nvfp4_quantize(x3.data_ptr(), BF16 if x3.dtype == torch.bfloat16 else F32, b, r, c,
-                        x3.stride(1) if r > 1 else c, x3.stride(0) if b > 1 else r * c, axis, opts, q,
-                        workspace.data_ptr(), workspace.numel(), _stream(x.device))
-    _check(st, "nvfp4_quantize")
+    args = (x3.data_ptr(), BF16 if x3.dtype == torch.bfloat16 else F32, b, r, c,
+            x3.stride(1) if r > 1 else c, x3.stride(0) if b > 1 else r * c, axis, ctypes.byref(opts),
+            ctypes.byref(q), workspace.data_ptr(), workspace.numel(), _stream(x.device))
+    return args, (opts, q, x3, workspace), out
+
+
+def quantize(x: torch.Tensor, axis: int = ALONG_COLS, rounding: int = RNE, sr_seed: int = 0,
+             sr_stream: int = 0, rht: bool = False, rht_seed: int = 0, out: QTensor | None = None,
+             workspace: torch.Tensor | None = None) -> QTensor:
+    """Quantize a 2-D [rows][cols] or 3-D [batch][rows][cols] CUDA tensor
+    (bfloat16 or float32, last dimension contiguous)."""
+    args, _keep, out = _quantize_args(x, axis, rounding, sr_seed, sr_stream, rht, rht_seed, out, workspace)
+    _check(lib().nvfp4_quantize(*args), "nvfp4_quantize")
     return out
+
+
+class BoundCall:
+    """One C-ABI call with its arguments marshalled once (pointers, sizes,
+    option structs and the current stream at bind time).  Calling it only
+    enqueues the kernels again; for loops that repeat the same call on the
+    same buffers, where per-call argument conversion would otherwise
+    dominate the host time."""
+
+    def __init__(self, fn, args, keep, what: str, result=None):
+        self._fn, self._args, self._keep, self._what, self.result = fn, args, keep, what, result
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != OK:
+            raise NVFP4Error(st, self._what)
+        return self.result
+
+
+def bind_quantize(x: torch.Tensor, out: QTensor, workspace: torch.Tensor, axis: int = ALONG_COLS,
+                  rounding: int = RNE, sr_seed: int = 0, sr_stream: int = 0, rht: bool = False,
+                  rht_seed: int = 0) -> BoundCall:
+    """quantize() bound to fixed buffers and the current stream."""
+    args, keep, out = _quantize_args(x, axis, rounding, sr_seed, sr_stream, rht, rht_seed, out, workspace)
+    return BoundCall(lib().nvfp4_quantize, args, keep, "nvfp4_quantize", out)
 
 
 def gemm(a: QTensor, b: QTensor, out_dtype: torch.dtype = torch.bfloat16, alpha: float = 1.0,
@@ -203,14 +235,25 @@ def gemm(a: QTensor, b: QTensor, out_dtype: torch.dtype = torch.bfloat16, alpha:
     created = out is None
     if created:
         out = torch.empty(a.batch, a.rows, b.rows, dtype=out_dtype, device=a.codes.device)
+    args, _keep = _gemm_args(a, b, out, alpha)
+    _check(lib().nvfp4_gemm(*args), "nvfp4_gemm")
+    return out[0] if created and a.batch == 1 else out
+
+
+def _gemm_args(a: QTensor, b: QTensor, out: torch.Tensor, alpha: float):
     o3 = out if out.dim() == 3 else out.unsqueeze(0)
     ca, cb = a.c_struct(), b.c_struct()
-    st = nvfp4_gemm(ca, cb, o3.data_ptr(), BF16 if o3.dtype == torch.bfloat16 else F32,
-                    o3.stride(1) if o3.size(1) > 1 else o3.size(2),
-                    o3.stride(0) if o3.size(0) > 1 else o3.size(1) * o3.size(2), alpha,
-                    _stream(a.codes.device))
-    _check(st, "nvfp4_gemm")
-    return out[0] if created and a.batch == 1 else out
+    args = (ctypes.byref(ca), ctypes.byref(cb), o3.data_ptr(), BF16 if o3.dtype == torch.bfloat16 else F32,
+            o3.stride(1) if o3.size(1) > 1 else o3.size(2),
+            o3.stride(0) if o3.size(0) > 1 else o3.size(1) * o3.size(2), ctypes.c_float(alpha),
+            _stream(a.codes.device))
+    return args, (ca, cb, o3)
+
+
+def bind_gemm(a: QTensor, b: QTensor, out: torch.Tensor, alpha: float = 1.0) -> BoundCall:
+    """gemm() bound to fixed operands, output and the current stream."""
+    args, keep = _gemm_args(a, b, out, alpha)
+    return BoundCall(lib().nvfp4_gemm, args, keep, "nvfp4_gemm", out)
 
 
 def linear_fwd_bwd(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, sr_seed: int, rht_seed: int,

@@ -3,7 +3,9 @@
     python -m bit_block_scaled_nvfp4_amd.build
 
 Compiles every csrc/*.hip to an object under build/ and links the shared
-library next to this file.  Flags that matter for bit-exact results: no FMA
+library next to this file; also builds the measurement probe
+probes/mfma_ceiling.hip into the executable `mfma_ceiling` (not part of the
+library).  Flags that matter for bit-exact results: no FMA
 contraction, correctly rounded FP32 divide, no denormal flushing, and packed
 FP32 instructions disabled."""
 from __future__ import annotations
@@ -18,6 +20,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "build")
 LIB = os.path.join(PKG, "libnvfp4.so")
+PROBE_SRC = os.path.join(PKG, "probes", "mfma_ceiling.hip")
+PROBE = os.path.join(PKG, "mfma_ceiling")
 ARCH = "gfx950"
 
 COMMON = [
@@ -49,6 +53,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     subprocess.run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], check=True)
     os.replace(tmp, LIB)
+    subprocess.run([cc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+                    "-Xclang", "-packed-fp32-ops", PROBE_SRC, "-o", PROBE + ".tmp"],
+                   check=True, stderr=None if verbose else subprocess.PIPE)
+    os.replace(PROBE + ".tmp", PROBE)
     return LIB
 
 

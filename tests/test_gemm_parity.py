@@ -100,3 +100,24 @@ def test_gemm_every_main_loop(M, N, K):
     for dt in (torch.float32, torch.bfloat16):
         stats = gemm_vs_oracle(qa, qb, out_dtype=dt, rows=rows, what=f"{M}x{N}x{K}")
         assert stats["n"] == rows.size * N
+
+
+def test_bound_calls_repeat_the_unbound_results():
+    """bind_quantize / bind_gemm marshal arguments once; repeated calls on the
+    same buffers give the same bytes as the plain wrappers."""
+    a, b = _pair(300, 200, 256, 1, 23)
+    da, db = a.to(DEV), b.to(DEV)
+    qa_ref, qb_ref = nv.quantize(da), nv.quantize(db)
+    y_ref = nv.gemm(qa_ref, qb_ref, out_dtype=torch.bfloat16)
+    qa, qb = nv.QTensor.empty(1, 300, 256, DEV), nv.QTensor.empty(1, 200, 256, DEV)
+    wa = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), DEV)
+    wb = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), DEV)
+    y = torch.empty(300, 200, dtype=torch.bfloat16, device=DEV)
+    calls = (nv.bind_quantize(da, qa, wa), nv.bind_quantize(db, qb, wb), nv.bind_gemm(qa, qb, y))
+    for _ in range(3):
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        assert torch.equal(qa.codes, qa_ref.codes) and torch.equal(qa.scales, qa_ref.scales)
+        assert torch.equal(qb.codes, qb_ref.codes) and torch.equal(qa.tensor_scale, qa_ref.tensor_scale)
+        assert torch.equal(y, y_ref)
