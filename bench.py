@@ -38,6 +38,8 @@ import bit_block_scaled_nvfp4_amd as nv
 from bit_block_scaled_nvfp4_amd import workloads as W
 
 METRIC = "NVFP4 GEMM TFLOP/s + %MFMA peak; quantize GB/s + %HBM at 8192x3072x3072"
+# (other workloads: the same line for that workload's step; `value` is its
+# whole-step TFLOP/s and `roofline` its dominant call)
 PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense FP16/BF16 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 CACHE_BYTES = 256 << 20    # Infinity Cache
@@ -49,7 +51,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="fprop_3b", choices=["fprop_3b", "mlp_up_12b"])
+    p.add_argument("--workload", default="fprop_3b",
+                   choices=["fprop_3b", "mlp_up_12b", "linear_train", "attn_scores"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-mfma-ceiling", action="store_true", help="skip the MFMA ceiling probe")
     p.add_argument("--cpu-rows", type=int, default=1024, help="GEMM rows in the CPU-oracle sample")
@@ -149,38 +152,18 @@ def main():
         copy_probe(args.copy_probe)
         return
     t = W.WORKLOADS[args.workload]()
-    x_cpu, w_cpu = t["X"], t["W"]
-    M, K = x_cpu.shape
-    N = w_cpu.shape[0]
-    in_bytes = (M * K + N * K) * 2
-    nbuf = max(2, int(np.ceil(2 * CACHE_BYTES / in_bytes)) + 1)
-    xs = [x_cpu.to(dev) for _ in range(nbuf)]
-    ws = [w_cpu.to(dev) for _ in range(nbuf)]
-    qxs = [nv.QTensor.empty(1, M, K, dev) for _ in range(nbuf)]
-    qws = [nv.QTensor.empty(1, N, K, dev) for _ in range(nbuf)]
-    ys = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(nbuf)]
-    wsp_x = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
-    wsp_w = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
-
-    # Each buffer set's three calls marshalled once, so the host enqueues a
-    # step in a few microseconds and stays ahead of the GPU; the events then
-    # time the kernels rather than launch gaps.
-    calls = [(nv.bind_quantize(xs[j], qxs[j], wsp_x), nv.bind_quantize(ws[j], qws[j], wsp_w),
-              nv.bind_gemm(qxs[j], qws[j], ys[j])) for j in range(nbuf)]
+    setup = {"fprop_3b": setup_linear_gemm, "mlp_up_12b": setup_linear_gemm,
+             "linear_train": setup_linear_train, "attn_scores": setup_attn}[args.workload]
+    S = setup(t, dev)
+    calls, nbuf, names = S["calls"], S["nbuf"], S["names"]
 
     def step(i, ev=None):
-        qx, qw, mm = calls[i % nbuf]
+        for k, c in enumerate(calls[i % nbuf]):
+            if ev is not None:
+                ev[k].record()
+            c()
         if ev is not None:
-            ev[0].record()
-        qx()
-        if ev is not None:
-            ev[1].record()
-        qw()
-        if ev is not None:
-            ev[2].record()
-        mm()
-        if ev is not None:
-            ev[3].record()
+            ev[len(names)].record()
 
     for i in range(args.warmup):
         step(i)
@@ -192,27 +175,42 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # Per-kernel region: the same K steps again with HIP events recorded on the
-    # launch stream around each kernel (events add a few microseconds of
-    # idle between kernels, so they stay out of the timed region above).
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # launch stream around each call (events add a few microseconds of idle
+    # between kernels, so they stay out of the timed region above).
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(args.warmup + args.steps + i, events[i])
     torch.cuda.synchronize()
-
-    qx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    qw_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    gemm_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    call_ms = [float(np.mean([e[k].elapsed_time(e[k + 1]) for e in events])) for k in range(len(names))]
     ms_per_step = wall / args.steps * 1e3
-    flops = 2.0 * M * N * K
-    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
-    qx_gbps = QUANT_BYTES_PER_ELEM * M * K / (qx_ms * 1e-3) / 1e9
-    qw_gbps = QUANT_BYTES_PER_ELEM * N * K / (qw_ms * 1e-3) / 1e9
-    q_gbps = QUANT_BYTES_PER_ELEM * (M + N) * K / ((qx_ms + qw_ms) * 1e-3) / 1e9
+
+    kernels = {}
+    for k, name in enumerate(names):
+        us = call_ms[k] * 1e3
+        info = {"us": round(us, 2)}
+        if name in S["flops"]:
+            tf = S["flops"][name] / (us * 1e-6) / 1e12
+            info.update({"TFLOP/s": round(tf, 2), "frac_mfma": round(tf / PEAK_MFMA_TFLOPS, 4)})
+        if name in S["bytes"]:
+            gbps = S["bytes"][name] / (us * 1e-6) / 1e9
+            info.update({"GB/s": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)})
+        kernels[name] = info
+    dom = S["dominant"]
+    dom_us = call_ms[names.index(dom)] * 1e3
+    if S["bound"] == "mfma":
+        achieved = S["flops"][dom] / (dom_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_MFMA_TFLOPS, 4), "traffic": measured_traffic(args.workload)}
+    else:
+        achieved = S["bytes"][dom] / (dom_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(args.workload)}
+    roofline["kernel"] = dom
 
     out = {
         "metric": METRIC,
-        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "value": round(S["step_flops"] / (ms_per_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -223,26 +221,94 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "x_dtype": "bf16",
-                   "y_dtype": "bf16", "rounding": "rne", "rotating_buffers": nbuf},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_MFMA_TFLOPS, 4),
-                     "traffic": measured_traffic(args.workload)},
-        "kernels": {
-            "gemm": {"us": round(gemm_ms * 1e3, 2), "TFLOP/s": round(gemm_tflops, 2),
-                     "frac_mfma": round(gemm_tflops / PEAK_MFMA_TFLOPS, 4)},
-            "quantize_x": {"us": round(qx_ms * 1e3, 2), "GB/s": round(qx_gbps, 1),
-                           "frac_hbm": round(qx_gbps / PEAK_HBM_GBPS, 4)},
-            "quantize_w": {"us": round(qw_ms * 1e3, 2), "GB/s": round(qw_gbps, 1),
-                           "frac_hbm": round(qw_gbps / PEAK_HBM_GBPS, 4)},
-            "quantize_x_w": {"GB/s": round(q_gbps, 1), "frac_hbm": round(q_gbps / PEAK_HBM_GBPS, 4)},
-        },
+        "config": dict(S["config"], workload=args.workload, rotating_buffers=nbuf),
+        "roofline": roofline,
+        "kernels": kernels,
         "mfma_ceiling": ceiling,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(x_cpu, w_cpu, args.cpu_rows)
+    if not args.no_cpu_baseline and args.workload == "fprop_3b":
+        out["cpu_baseline"] = cpu_baseline(t["X"], t["W"], args.cpu_rows)
     print(json.dumps(out), flush=True)
+
+
+def rotation(in_bytes: int) -> int:
+    """Buffer sets to rotate over so a step's inputs are not in the 256 MB
+    Infinity Cache from an earlier step."""
+    return max(2, int(np.ceil(2 * CACHE_BYTES / in_bytes)) + 1)
+
+
+def setup_linear_gemm(t, dev) -> dict:
+    """One linear layer's forward: quantize X and W (RNE), Y = X W^T (BF16)."""
+    x_cpu, w_cpu = t["X"], t["W"]
+    M, K = x_cpu.shape
+    N = w_cpu.shape[0]
+    nbuf = rotation((M * K + N * K) * 2)
+    xs = [x_cpu.to(dev) for _ in range(nbuf)]
+    ws = [w_cpu.to(dev) for _ in range(nbuf)]
+    qxs = [nv.QTensor.empty(1, M, K, dev) for _ in range(nbuf)]
+    qws = [nv.QTensor.empty(1, N, K, dev) for _ in range(nbuf)]
+    ys = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(nbuf)]
+    wsp_x = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
+    wsp_w = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
+    # Each buffer set's calls marshalled once, so the host enqueues a step in
+    # a few microseconds and stays ahead of the GPU.
+    calls = [(nv.bind_quantize(xs[j], qxs[j], wsp_x), nv.bind_quantize(ws[j], qws[j], wsp_w),
+              nv.bind_gemm(qxs[j], qws[j], ys[j])) for j in range(nbuf)]
+    flops = 2.0 * M * N * K
+    return {"calls": calls, "nbuf": nbuf, "names": ["quantize_x", "quantize_w", "gemm"],
+            "flops": {"gemm": flops}, "step_flops": flops,
+            "bytes": {"quantize_x": QUANT_BYTES_PER_ELEM * M * K, "quantize_w": QUANT_BYTES_PER_ELEM * N * K},
+            "dominant": "gemm", "bound": "mfma",
+            "config": {"M": M, "N": N, "K": K, "x_dtype": "bf16", "y_dtype": "bf16", "rounding": "rne"}}
+
+
+def setup_linear_train(t, dev) -> dict:
+    """A linear layer's training step through nvfp4_linear_fwd_bwd: six
+    quantizations (RNE, SR, RHT+SR) and the Fprop, Dgrad and Wgrad GEMMs."""
+    x_cpu, w_cpu, dy_cpu = t["X"], t["W"], t["dY"]
+    M, K = x_cpu.shape
+    N = w_cpu.shape[0]
+    nbuf = rotation((M * K + N * K + M * N) * 2)
+    wsp = nv.new_workspace(nv.nvfp4_linear_workspace_size(M, N, K), dev)
+    calls = []
+    for _ in range(nbuf):
+        x, w, dy = x_cpu.to(dev), w_cpu.to(dev), dy_cpu.to(dev)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+        dw = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+        calls.append((nv.bind_linear_fwd_bwd(x, w, dy, y, dx, dw, wsp, t["sr_seed"], t["rht_seed"]),))
+    flops = 3 * 2.0 * M * N * K
+    return {"calls": calls, "nbuf": nbuf, "names": ["linear_fwd_bwd"], "flops": {"linear_fwd_bwd": flops},
+            "step_flops": flops, "bytes": {}, "dominant": "linear_fwd_bwd", "bound": "mfma",
+            "config": {"M": M, "N": N, "K": K, "x_dtype": "bf16", "y_dtype": "bf16",
+                       "rounding": "rne fprop, sr dgrad, rht+sr wgrad"}}
+
+
+def setup_attn(t, dev) -> dict:
+    """Attention scores: quantize Q and K (RNE, one tensor scale each), then
+    S = alpha Q K^T for every (batch, head), FP32 out -- bound by writing S."""
+    q_cpu, k_cpu = t["Q"], t["K"]
+    B, H, S_, D = q_cpu.shape
+    nbuf = rotation(2 * q_cpu.numel() * 2)
+    qs = [q_cpu.reshape(B * H, S_, D).to(dev) for _ in range(nbuf)]
+    ks = [k_cpu.reshape(B * H, S_, D).to(dev) for _ in range(nbuf)]
+    qq = [nv.QTensor.empty(B * H, S_, D, dev) for _ in range(nbuf)]
+    qk = [nv.QTensor.empty(B * H, S_, D, dev) for _ in range(nbuf)]
+    s_out = torch.empty(B * H, S_, S_, dtype=torch.float32, device=dev)  # 8.6 GB, written every step
+    wsp_q = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
+    wsp_k = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
+    calls = [(nv.bind_quantize(qs[j], qq[j], wsp_q), nv.bind_quantize(ks[j], qk[j], wsp_k),
+              nv.bind_gemm(qq[j], qk[j], s_out, alpha=t["alpha"])) for j in range(nbuf)]
+    flops = 2.0 * B * H * S_ * S_ * D
+    gemm_bytes = 4.0 * B * H * S_ * S_ + 2 * B * H * S_ * D * (0.5 + 1 / 16)
+    return {"calls": calls, "nbuf": nbuf, "names": ["quantize_q", "quantize_k", "gemm"],
+            "flops": {"gemm": flops}, "step_flops": flops,
+            "bytes": {"quantize_q": QUANT_BYTES_PER_ELEM * q_cpu.numel(),
+                      "quantize_k": QUANT_BYTES_PER_ELEM * k_cpu.numel(), "gemm": gemm_bytes},
+            "dominant": "gemm", "bound": "hbm",
+            "config": {"batch": B, "heads": H, "seq": S_, "head_dim": D, "x_dtype": "bf16", "y_dtype": "fp32",
+                       "rounding": "rne", "alpha": t["alpha"]}}
 
 
 if __name__ == "__main__":

@@ -256,24 +256,41 @@ def bind_gemm(a: QTensor, b: QTensor, out: torch.Tensor, alpha: float = 1.0) -> 
     return BoundCall(lib().nvfp4_gemm, args, keep, "nvfp4_gemm", out)
 
 
-def linear_fwd_bwd(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, sr_seed: int, rht_seed: int,
-                   wgrad_sr_x: bool = True, dw_dtype: torch.dtype = torch.bfloat16,
-                   workspace: torch.Tensor | None = None):
-    """Fprop, Dgrad and Wgrad of Y = X W^T in NVFP4; returns (Y, dX, dW)."""
+def _linear_args(x, w, dy, y, dx, dw, sr_seed, rht_seed, wgrad_sr_x, workspace):
     M, K = x.shape
     N = w.shape[0]
     for t in (x, w, dy):
         if t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError("x, w, dy must be contiguous bfloat16")
-    y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
-    dx = torch.empty(M, K, dtype=torch.bfloat16, device=x.device)
-    dw = torch.empty(N, K, dtype=dw_dtype, device=x.device)
-    need = nvfp4_linear_workspace_size(M, N, K)
+    cfg = LinearCfgC(sr_seed, rht_seed, int(bool(wgrad_sr_x)), F32 if dw.dtype == torch.float32 else BF16)
+    args = (x.data_ptr(), w.data_ptr(), dy.data_ptr(), y.data_ptr(), dx.data_ptr(), dw.data_ptr(), M, N, K,
+            ctypes.byref(cfg), workspace.data_ptr(), workspace.numel(), _stream(x.device))
+    return args, (cfg, x, w, dy, y, dx, dw, workspace)
+
+
+def _linear_outputs(x, w, dw_dtype):
+    M, K = x.shape
+    N = w.shape[0]
+    return (torch.empty(M, N, dtype=torch.bfloat16, device=x.device),
+            torch.empty(M, K, dtype=torch.bfloat16, device=x.device),
+            torch.empty(N, K, dtype=dw_dtype, device=x.device))
+
+
+def linear_fwd_bwd(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, sr_seed: int, rht_seed: int,
+                   wgrad_sr_x: bool = True, dw_dtype: torch.dtype = torch.bfloat16,
+                   workspace: torch.Tensor | None = None):
+    """Fprop, Dgrad and Wgrad of Y = X W^T in NVFP4; returns (Y, dX, dW)."""
+    y, dx, dw = _linear_outputs(x, w, dw_dtype)
     if workspace is None:
-        workspace = new_workspace(need, x.device)
-    cfg = LinearCfgC(sr_seed, rht_seed, int(bool(wgrad_sr_x)), F32 if dw_dtype == torch.float32 else BF16)
-    st = nvfp4_linear_fwd_bwd(x.data_ptr(), w.data_ptr(), dy.data_ptr(), y.data_ptr(), dx.data_ptr(),
-                              dw.data_ptr(), M, N, K, cfg, workspace.data_ptr(), workspace.numel(),
-                              _stream(x.device))
-    _check(st, "nvfp4_linear_fwd_bwd")
+        workspace = new_workspace(nvfp4_linear_workspace_size(x.shape[0], w.shape[0], x.shape[1]), x.device)
+    args, _keep = _linear_args(x, w, dy, y, dx, dw, sr_seed, rht_seed, wgrad_sr_x, workspace)
+    _check(lib().nvfp4_linear_fwd_bwd(*args), "nvfp4_linear_fwd_bwd")
     return y, dx, dw
+
+
+def bind_linear_fwd_bwd(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, y: torch.Tensor, dx: torch.Tensor,
+                        dw: torch.Tensor, workspace: torch.Tensor, sr_seed: int, rht_seed: int,
+                        wgrad_sr_x: bool = True) -> BoundCall:
+    """linear_fwd_bwd() bound to fixed inputs, outputs, workspace and the current stream."""
+    args, keep = _linear_args(x, w, dy, y, dx, dw, sr_seed, rht_seed, wgrad_sr_x, workspace)
+    return BoundCall(lib().nvfp4_linear_fwd_bwd, args, keep, "nvfp4_linear_fwd_bwd", (y, dx, dw))
