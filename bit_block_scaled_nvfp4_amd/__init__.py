@@ -47,6 +47,12 @@ class QuantOptsC(ctypes.Structure):
                 ("sr_stream", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
 
+class QuantJobC(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("batch", ctypes.c_int64), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("ld", ctypes.c_int64), ("batch_stride", ctypes.c_int64),
+                ("out", QTensorC)]
+
+
 class LinearCfgC(ctypes.Structure):
     _fields_ = [("sr_seed", ctypes.c_uint64), ("rht_seed", ctypes.c_uint64),
                 ("wgrad_sr_x", ctypes.c_int32), ("dw_dtype", ctypes.c_int32)]
@@ -72,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_quantize.argtypes = [vp, i32, i64, i64, i64, i64, i64, i32,
                                      ctypes.POINTER(QuantOptsC), ctypes.POINTER(QTensorC), vp, sz, vp]
         L.nvfp4_quantize.restype = i32
+        L.nvfp4_quantize_group_workspace_size.restype = sz
+        L.nvfp4_quantize_group.argtypes = [ctypes.POINTER(QuantJobC), i32, i32, ctypes.POINTER(QuantOptsC),
+                                           vp, sz, vp]
+        L.nvfp4_quantize_group.restype = i32
         L.nvfp4_gemm.argtypes = [ctypes.POINTER(QTensorC), ctypes.POINTER(QTensorC), vp, i32, i64, i64,
                                  ctypes.c_float, vp]
         L.nvfp4_gemm.restype = i32
@@ -101,6 +111,10 @@ def nvfp4_quantize_workspace_size() -> int:
     return lib().nvfp4_quantize_workspace_size()
 
 
+def nvfp4_quantize_group_workspace_size() -> int:
+    return lib().nvfp4_quantize_group_workspace_size()
+
+
 def nvfp4_linear_workspace_size(M: int, N: int, K: int) -> int:
     return lib().nvfp4_linear_workspace_size(M, N, K)
 
@@ -111,6 +125,11 @@ def nvfp4_quantize(x_ptr, x_dtype, batch, rows, cols, ld, batch_stride, axis, op
                                 ctypes.byref(opts) if opts is not None else None,
                                 ctypes.byref(out) if out is not None else None,
                                 workspace, workspace_bytes, stream)
+
+
+def nvfp4_quantize_group(jobs, njobs, x_dtype, opts, workspace, workspace_bytes, stream) -> int:
+    return lib().nvfp4_quantize_group(jobs, njobs, x_dtype, ctypes.byref(opts) if opts is not None else None,
+                                      workspace, workspace_bytes, stream)
 
 
 def nvfp4_gemm(a, b, c_ptr, c_dtype, ldc, batch_stride_c, alpha, stream) -> int:
@@ -227,6 +246,54 @@ def bind_quantize(x: torch.Tensor, out: QTensor, workspace: torch.Tensor, axis: 
     """quantize() bound to fixed buffers and the current stream."""
     args, keep, out = _quantize_args(x, axis, rounding, sr_seed, sr_stream, rht, rht_seed, out, workspace)
     return BoundCall(lib().nvfp4_quantize, args, keep, "nvfp4_quantize", out)
+
+
+def _quantize_group_args(xs, rounding: int, sr_seed: int, sr_stream: int, rht: bool, rht_seed: int,
+                         outs, workspace: torch.Tensor | None):
+    """Validated ctypes arguments of one nvfp4_quantize_group call (and its outputs)."""
+    if not 1 <= len(xs) <= 4:
+        raise ValueError("a group holds 1 to 4 tensors")
+    if len({x.dtype for x in xs}) != 1:
+        raise TypeError("all tensors of a group must have one dtype")
+    outs = list(outs) if outs is not None else [None] * len(xs)
+    jobs = (QuantJobC * len(xs))()
+    x3s = []
+    for i, x in enumerate(xs):
+        x3 = x.unsqueeze(0) if x.dim() == 2 else x
+        if x3.dim() != 3:
+            raise ValueError("x must be 2-D or 3-D")
+        if x3.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("x must be bfloat16 or float32")
+        if x3.size(2) > 1 and x3.stride(2) != 1:
+            raise ValueError("the last dimension of x must be contiguous")
+        b, r, c = x3.shape
+        if outs[i] is None:
+            outs[i] = QTensor.empty(b, r, c, x.device)
+        jobs[i] = QuantJobC(x3.data_ptr(), b, r, c, x3.stride(1) if r > 1 else c,
+                            x3.stride(0) if b > 1 else r * c, outs[i].c_struct())
+        x3s.append(x3)
+    if workspace is None:
+        workspace = new_workspace(nvfp4_quantize_group_workspace_size(), xs[0].device)
+    opts = QuantOptsC(rounding, int(bool(rht)), sr_seed, rht_seed, sr_stream, 0)
+    args = (jobs, len(xs), BF16 if xs[0].dtype == torch.bfloat16 else F32, ctypes.byref(opts),
+            workspace.data_ptr(), workspace.numel(), _stream(xs[0].device))
+    return args, (jobs, opts, x3s, workspace), outs
+
+
+def quantize_group(xs, rounding: int = RNE, sr_seed: int = 0, sr_stream: int = 0, rht: bool = False,
+                   rht_seed: int = 0, outs=None, workspace: torch.Tensor | None = None) -> list:
+    """Quantize 1-4 tensors along their last dimension with shared options,
+    each with its own tensor scale (same results as quantize() on each)."""
+    args, _keep, outs = _quantize_group_args(xs, rounding, sr_seed, sr_stream, rht, rht_seed, outs, workspace)
+    _check(lib().nvfp4_quantize_group(*args), "nvfp4_quantize_group")
+    return outs
+
+
+def bind_quantize_group(xs, outs, workspace: torch.Tensor, rounding: int = RNE, sr_seed: int = 0,
+                        sr_stream: int = 0, rht: bool = False, rht_seed: int = 0) -> BoundCall:
+    """quantize_group() bound to fixed buffers and the current stream."""
+    args, keep, outs = _quantize_group_args(xs, rounding, sr_seed, sr_stream, rht, rht_seed, outs, workspace)
+    return BoundCall(lib().nvfp4_quantize_group, args, keep, "nvfp4_quantize_group", outs)
 
 
 def gemm(a: QTensor, b: QTensor, out_dtype: torch.dtype = torch.bfloat16, alpha: float = 1.0,

@@ -185,7 +185,7 @@ NVFP4_EXPORT const char *nvfp4_status_string(int32_t status) {
   }
 }
 
-NVFP4_EXPORT int32_t nvfp4_version(void) { return (1 << 16) | 0; }
+NVFP4_EXPORT int32_t nvfp4_version(void) { return (1 << 16) | 1; }
 
 NVFP4_EXPORT size_t nvfp4_quantize_workspace_size(void) { return sizeof(QuantCtrl); }
 
@@ -199,6 +199,35 @@ NVFP4_EXPORT nvfp4_status nvfp4_quantize(const void *x, int32_t x_dtype, int64_t
   const nvfp4::QuantProblem p = make_quant(x, x_dtype == NVFP4_BF16, batch, rows, cols, ld, batch_stride,
                                            axis == NVFP4_ALONG_ROWS, opts, out, workspace);
   return nvfp4::launch_quantize(p, static_cast<hipStream_t>(stream));
+}
+
+NVFP4_EXPORT size_t nvfp4_quantize_group_workspace_size(void) { return nvfp4::kGroupWorkspace; }
+
+NVFP4_EXPORT nvfp4_status nvfp4_quantize_group(const nvfp4_quant_job *jobs, int32_t njobs, int32_t x_dtype,
+                                               const nvfp4_quant_opts *opts, void *workspace,
+                                               size_t workspace_bytes, void *stream) {
+  if (!jobs || njobs < 1 || njobs > nvfp4::kMaxGroup) return NVFP4_EINVAL;
+  for (int i = 0; i < njobs; ++i) {
+    const nvfp4_quant_job &j = jobs[i];
+    const nvfp4_status st = validate_quantize(j.x, x_dtype, j.batch, j.rows, j.cols, j.ld, j.batch_stride,
+                                              NVFP4_ALONG_COLS, opts, &j.out, workspace, workspace_bytes);
+    if (st != NVFP4_OK) return st;
+  }
+  if (workspace_bytes < nvfp4::kGroupWorkspace) return NVFP4_EWORKSPACE;
+  nvfp4::QuantGroupProblem p{};
+  p.njobs = njobs;
+  for (int i = 0; i < njobs; ++i) {
+    const nvfp4_quant_job &j = jobs[i];
+    p.job[i] = make_quant(j.x, x_dtype == NVFP4_BF16, j.batch, j.rows, j.cols, j.ld, j.batch_stride, false, opts,
+                          &j.out, workspace);
+  }
+  uint8_t *base = static_cast<uint8_t *>(workspace);
+  p.ctrl_seq = reinterpret_cast<QuantCtrl *>(base);
+  p.ctrl_group = reinterpret_cast<QuantCtrl *>(base + sizeof(QuantCtrl));
+  for (int i = 0; i < nvfp4::kMaxGroup; ++i)
+    p.amax[i] = reinterpret_cast<QuantCtrl::Slot(*)[8]>(base + 2 * sizeof(QuantCtrl) +
+                                                        i * 2 * 8 * sizeof(QuantCtrl::Slot));
+  return nvfp4::launch_quantize_group(p, static_cast<hipStream_t>(stream));
 }
 
 NVFP4_EXPORT nvfp4_status nvfp4_gemm(const nvfp4_qtensor *a, const nvfp4_qtensor *b, void *c, int32_t c_dtype,

@@ -48,6 +48,19 @@ struct QuantProblem {
   QuantCtrl *ctrl;
 };
 
+// Several tensors quantized along their contiguous dimension with the same
+// dtype and options.  Workspace: ctrl_seq serves the per-tensor fallback,
+// ctrl_group the single-launch barrier, amax[j] (2 parities x 8 slots) the
+// maxima of tensor j in that launch.
+constexpr int kMaxGroup = 4;
+struct QuantGroupProblem {
+  int njobs;
+  QuantProblem job[kMaxGroup];
+  QuantCtrl *ctrl_seq, *ctrl_group;
+  QuantCtrl::Slot (*amax[kMaxGroup])[8];
+};
+constexpr size_t kGroupWorkspace = 2 * sizeof(QuantCtrl) + kMaxGroup * 2 * 8 * sizeof(QuantCtrl::Slot);
+
 struct GemmProblem {
   const uint8_t *a_codes, *a_scales;
   const float *a_st;
@@ -61,6 +74,7 @@ struct GemmProblem {
 };
 
 nvfp4_status launch_quantize(const QuantProblem &p, hipStream_t stream);
+nvfp4_status launch_quantize_group(const QuantGroupProblem &p, hipStream_t stream);
 nvfp4_status launch_gemm(const GemmProblem &p, hipStream_t stream);
 
 }  // namespace nvfp4

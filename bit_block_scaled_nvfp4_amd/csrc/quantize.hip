@@ -53,11 +53,12 @@ constexpr uint32_t kSpinLimit = 1u << 22;  // polls before a barrier wait gives 
 #define NVFP4_FUSED_DISABLE 0
 #endif
 
-template <bool kBF16>
+template <bool kBF16, bool kRHT, bool kSR>
 struct Fused {
-  // blocks held per lane: 33.5M BF16 (16.8M FP32) elements on 256 CUs,
-  // within the register budget of the workgroup size
-  static constexpr int kMaxBlocks = (kBF16 ? 16 : 8) * 512 / kFusedThreads;
+  // Blocks held per lane: 37.7M BF16 (16.8M FP32) elements on 256 CUs, the
+  // most that fits the 128-VGPR budget of 1024-thread workgroups without
+  // spilling (BF16 with both the transform and stochastic rounding: 33.5M).
+  static constexpr int kMaxBlocks = kBF16 ? (kRHT && kSR ? 8 : 9) : 4;
 };
 
 // ---------------------------------------------------------------------------
@@ -211,7 +212,29 @@ struct RowArgs {
   QuantCtrl *ctrl;
   uint64_t sr_seed, rht_seed;
   uint32_t sr_stream;
-  uint32_t nseg_iters;  // single pass: segments per wavefront
+};
+
+// Single pass: up to kMaxJobs contiguous tensors in one launch, each with
+// its own tensor scale.  Global segment g belongs to the job whose
+// [seg_begin, next seg_begin) range holds it.
+constexpr int kMaxJobs = 4;
+static_assert(kMaxJobs == kMaxGroup, "the group API and the kernel table hold the same number of jobs");
+struct RowJob {
+  const void *x;
+  uint64_t nblocks;
+  uint64_t seg_begin;
+  uint8_t *codes, *scales;
+  float *tensor_scale;
+  QuantCtrl::Slot (*amax)[8];  // [2][8]: per epoch parity, per workgroup-index slot
+};
+struct FusedArgs {
+  RowJob job[kMaxJobs];
+  int njobs;
+  uint64_t nseg;     // segments over all jobs
+  QuantCtrl *ctrl;   // barrier counters
+  uint64_t sr_seed, rht_seed;
+  uint32_t sr_stream;
+  uint32_t nseg_iters;  // segments per wavefront
 };
 
 // Element offset of block `blk` (row-major over [batch*rows][cols/16]).
@@ -259,6 +282,16 @@ __device__ __forceinline__ uint64_t load_segment(const RowArgs &a, uint64_t seg,
   }
 }
 
+// load_segment for a contiguous tensor given by pointer and block count.
+template <bool kBF16>
+__device__ __forceinline__ uint64_t load_segment_contig(const void *x, uint64_t nblocks, uint64_t seg, int lane,
+                                                        RawBlock<kBF16> &raw) {
+  RowArgs v{};
+  v.x = x;
+  v.nblocks = nblocks;
+  return load_segment<kBF16, true>(v, seg, lane, raw);
+}
+
 // Encode one block (values already transformed) and store codes + scale.
 template <bool kSR>
 __device__ __forceinline__ void row_store_block(const RowArgs &a, uint64_t blk, const float (&v)[16], uint32_t S,
@@ -269,66 +302,94 @@ __device__ __forceinline__ void row_store_block(const RowArgs &a, uint64_t blk, 
 }
 
 template <bool kBF16, bool kRHT, bool kSR>
-__global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_kernel(RowArgs a) {
-  constexpr int kMax = Fused<kBF16>::kMaxBlocks;
+__global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_kernel(FusedArgs a) {
+  constexpr int kMax = Fused<kBF16, kRHT, kSR>::kMaxBlocks;
   constexpr int kWaves = kFusedThreads / 64;
-  __shared__ float recip[128];
-  __shared__ uint32_t part[kWaves];
+  __shared__ float recip[kMaxJobs][128];
+  __shared__ uint32_t part[kWaves][kMaxJobs];
   __shared__ uint32_t s_epoch;
-  __shared__ float s_amax;
+  __shared__ float s_st[kMaxJobs];
   QuantCtrl *ctrl = a.ctrl;
   const int slot = blockIdx.x & 7;
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int njobs = a.njobs;
 
   // The epoch (completed single-pass calls on this workspace) cannot advance
   // before this workgroup arrives, so reading it here is race free.
   if (threadIdx.x == 0) s_epoch = (uint32_t)atomic_load_dev(&ctrl->release.v);
 
   const uint64_t nwaves = (uint64_t)gridDim.x * kWaves;
-  const uint64_t gwave = (uint64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const uint64_t gwave = (uint64_t)blockIdx.x * kWaves + wave;
   const uint32_t mask = kRHT ? rht_sign_mask(a.rht_seed) : 0u;
 
-  // Phase 1: all loads first, then the block maxima.
+  // Phase 1: all loads first, then the block maxima.  A segment belongs to
+  // one job, so the job index is uniform across the wavefront.
   RawBlock<kBF16> raw[kMax];
   uint64_t blk[kMax];
+  int jb[kMax];
   uint32_t bmax[kMax];
 #pragma unroll
   for (int it = 0; it < kMax; ++it) {
-    if (it < (int)a.nseg_iters) blk[it] = load_segment<kBF16, true>(a, it * nwaves + gwave, lane, raw[it]);
-    else { raw[it].zero(); blk[it] = a.nblocks; }
+    const uint64_t g = it * nwaves + gwave;
+    if (it < (int)a.nseg_iters && g < a.nseg) {
+      const int j = (njobs > 1 && g >= a.job[1].seg_begin) + (njobs > 2 && g >= a.job[2].seg_begin) +
+                    (njobs > 3 && g >= a.job[3].seg_begin);
+      jb[it] = j;
+      blk[it] = load_segment_contig<kBF16>(a.job[j].x, a.job[j].nblocks, g - a.job[j].seg_begin, lane, raw[it]);
+    } else {
+      raw[it].zero();
+      jb[it] = 0;
+      blk[it] = ~0ull;
+    }
   }
-  uint32_t m = 0;
+  uint32_t mj[kMaxJobs] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int it = 0; it < kMax; ++it) {
     float v[16];
     raw[it].values(v);
     if (kRHT) rht16(v, mask);
     bmax[it] = max_abs16(v);
-    m = max(m, bmax[it]);
+#pragma unroll
+    for (int j = 0; j < kMaxJobs; ++j)
+      if (jb[it] == j) mj[j] = max(mj[j], bmax[it]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  m = wave_max_u32(m);
-  if (lane == 0) part[threadIdx.x >> 6] = m;
+#pragma unroll
+  for (int j = 0; j < kMaxJobs; ++j) {
+    if (j < njobs) {
+      const uint32_t m = wave_max_u32(mj[j]);
+      if (lane == 0) part[wave][j] = m;
+    }
+  }
   __syncthreads();
 
-  // Grid barrier: publish the workgroup max, arrive, wait for the epoch to
-  // complete, then read the tensor max.  All control words are device-scope
-  // atomics at the coherence point, so relaxed ordering plus explicit
-  // completion waits suffice (acquire/release would flush and invalidate the
-  // L2 on every poll).  The wait is bounded; on expiry the timeout word is
-  // set and the kernel still finishes.
+  // Grid barrier: publish the workgroup maxima, arrive, wait for the epoch
+  // to complete, then read the tensor maxima.  All control words are
+  // device-scope atomics at the coherence point, so relaxed ordering plus
+  // explicit completion waits suffice (acquire/release would flush and
+  // invalidate the L2 on every poll).  The wait is bounded; on expiry the
+  // timeout word is set and the kernel still finishes.
   if (threadIdx.x == 0) {
-    uint32_t wm = part[0];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) wm = max(wm, part[i]);
     const uint32_t e = s_epoch;
-    if (blockIdx.x == 0) {  // slots of the next epoch: unused since the call before this one ended
+    // Slots of the next epoch are unused since the call before this one
+    // ended.  Every table entry that has slots is cleared, not only this
+    // call's jobs: a later call on the workspace may have more jobs.
+    if (blockIdx.x == 0) {
+      for (int j = 0; j < kMaxJobs; ++j) {
+        if (a.job[j].amax == nullptr) continue;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) atomic_store_dev(&ctrl->amax[(e + 1) & 1][i].v, 0u);
+        for (int i = 0; i < 8; ++i) atomic_store_dev(&a.job[j].amax[(e + 1) & 1][i].v, 0u);
+      }
     }
-    const uint32_t prev = __hip_atomic_fetch_max(&ctrl->amax[e & 1][slot].v, wm, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    wait_for(prev);  // the max is performed before this workgroup counts as arrived
+    for (int j = 0; j < njobs; ++j) {
+      uint32_t wm = part[0][j];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) wm = max(wm, part[w][j]);
+      const uint32_t prev = __hip_atomic_fetch_max(&a.job[j].amax[e & 1][slot].v, wm, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      wait_for(prev);  // the max is performed before this workgroup counts as arrived
+    }
     // Arrive: the last workgroup of each slot bumps `top`; the last of those
     // releases the epoch.  Slot i holds the workgroups with index = i mod 8.
     const unsigned n_slots = min(gridDim.x, 8u);
@@ -348,15 +409,21 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    uint32_t am = 0;
+    for (int j = 0; j < njobs; ++j) {
+      uint32_t am = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) am = max(am, atomic_load_dev(&ctrl->amax[e & 1][i].v));
-    s_amax = __uint_as_float(am);
+      for (int i = 0; i < 8; ++i) am = max(am, atomic_load_dev(&a.job[j].amax[e & 1][i].v));
+      s_st[j] = __uint_as_float(am) / 2688.0f;
+    }
   }
   __syncthreads();
-  const float st = s_amax / 2688.0f;
-  const float d6 = 6.0f * st;
-  build_recip_table(recip, st);
+  for (int t = threadIdx.x; t < njobs * 128; t += kFusedThreads) {
+    const int j = t >> 7, sc = t & 127;
+    if (sc < 127) {
+      const float e = e4m3_value((uint32_t)sc) * s_st[j];
+      recip[j][sc] = (e == 0.0f) ? 0.0f : 1.0f / e;
+    }
+  }
   __syncthreads();
 
   // Phase 2: encode from registers.
@@ -364,18 +431,22 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
   for (int it = 0; it < kMax; ++it) raw[it].opaque();
 #pragma unroll
   for (int it = 0; it < kMax; ++it) {
-    if (blk[it] < a.nblocks) {
-      const uint32_t S = block_scale_code(bmax[it], st, d6);
+    const int j = jb[it];
+    if (blk[it] < a.job[j].nblocks) {
+      const float st = s_st[j];
+      const uint32_t S = block_scale_code(bmax[it], st, 6.0f * st);
       float v[16];
       raw[it].values(v);
       if (kRHT) rht16(v, mask);
-      row_store_block<kSR>(a, blk[it], v, S, recip);
+      const uint2 c = encode16<kSR>(v, recip[j][S], 16 * blk[it], a.sr_stream, a.sr_seed);
+      st_stream(a.job[j].codes + 8 * blk[it], c);
+      a.job[j].scales[blk[it]] = (uint8_t)S;
     }
     // Keep blocks from being interleaved by the scheduler: hoisting every
     // block's unpacked values at once would exceed the register budget.
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.tensor_scale = st;
+  if (blockIdx.x == 0 && threadIdx.x < (unsigned)njobs) *a.job[threadIdx.x].tensor_scale = s_st[threadIdx.x];
 }
 
 template <bool kBF16, bool kRHT, bool kContig>
@@ -618,10 +689,10 @@ int cu_count() {
   return n;
 }
 
-// Single-pass row-wise quantize if the tensor fits the on-chip capacity of a
-// co-resident grid; returns false (nothing launched) otherwise.
+// Single-pass row-wise quantize of the jobs in `a` if they fit the on-chip
+// capacity of a co-resident grid; returns false (nothing launched) otherwise.
 template <bool kBF16, bool kRHT, bool kSR>
-bool try_row_fused(RowArgs a, hipStream_t s, hipError_t &err) {
+bool try_row_fused(FusedArgs a, hipStream_t s, hipError_t &err) {
   const int cus = cu_count();
   if (cus <= 0) return false;
   auto kernel = row_fused_kernel<kBF16, kRHT, kSR>;
@@ -631,9 +702,8 @@ bool try_row_fused(RowArgs a, hipStream_t s, hipError_t &err) {
     return false;
   const uint64_t grid = (uint64_t)cus * kFusedPerCU;
   const uint64_t nwaves = grid * (kFusedThreads / 64);
-  const uint64_t nseg = (a.nblocks + 63) / 64;
-  const uint64_t iters = (nseg + nwaves - 1) / nwaves;
-  if (iters > (uint64_t)Fused<kBF16>::kMaxBlocks) return false;
+  const uint64_t iters = (a.nseg + nwaves - 1) / nwaves;
+  if (iters > (uint64_t)Fused<kBF16, kRHT, kSR>::kMaxBlocks) return false;
   a.nseg_iters = (uint32_t)iters;
 #if NVFP4_FUSED_COOPERATIVE
   void *args[] = {&a};
@@ -651,6 +721,25 @@ bool try_row_fused(RowArgs a, hipStream_t s, hipError_t &err) {
   return err == hipSuccess;
 }
 
+// The single-pass arguments of one contiguous tensor.
+FusedArgs fused_single(const RowArgs &r) {
+  FusedArgs a{};
+  a.job[0].x = r.x;
+  a.job[0].nblocks = r.nblocks;
+  a.job[0].seg_begin = 0;
+  a.job[0].codes = r.codes;
+  a.job[0].scales = r.scales;
+  a.job[0].tensor_scale = r.tensor_scale;
+  a.job[0].amax = r.ctrl->amax;
+  a.njobs = 1;
+  a.nseg = (r.nblocks + 63) / 64;
+  a.ctrl = r.ctrl;
+  a.sr_seed = r.sr_seed;
+  a.rht_seed = r.rht_seed;
+  a.sr_stream = r.sr_stream;
+  return a;
+}
+
 template <bool kBF16, bool kRHT, bool kSR, bool kContig>
 hipError_t run_row_two_pass(const RowArgs &a, hipStream_t s) {
   const int g = grid_for((a.nblocks + 63) / 64, (kThreads / 64) * kBatch, 256ull * 4);
@@ -663,7 +752,7 @@ template <bool kBF16, bool kRHT, bool kSR>
 hipError_t run_row(const RowArgs &a, bool contig, hipStream_t s) {
   if (contig) {
     hipError_t err = hipSuccess;
-    if (!NVFP4_FUSED_DISABLE && try_row_fused<kBF16, kRHT, kSR>(a, s, err)) return hipSuccess;
+    if (!NVFP4_FUSED_DISABLE && try_row_fused<kBF16, kRHT, kSR>(fused_single(a), s, err)) return hipSuccess;
     (void)hipGetLastError();  // a refused cooperative launch falls back to two passes
     return run_row_two_pass<kBF16, kRHT, kSR, true>(a, s);
   }
@@ -693,7 +782,64 @@ hipError_t dispatch_col(const ColArgs &a, bool rht, bool sr, hipStream_t s) {
 
 __global__ void store_zero_scale(float *p) { *p = 0.0f; }
 
+template <bool kBF16>
+bool dispatch_group_fused(const FusedArgs &a, bool rht, bool sr, hipStream_t s, hipError_t &err) {
+  if (rht) return sr ? try_row_fused<kBF16, true, true>(a, s, err) : try_row_fused<kBF16, true, false>(a, s, err);
+  return sr ? try_row_fused<kBF16, false, true>(a, s, err) : try_row_fused<kBF16, false, false>(a, s, err);
+}
+
 }  // namespace
+
+nvfp4_status launch_quantize_group(const QuantGroupProblem &p, hipStream_t s) {
+  // One launch when every tensor is contiguous and all fit the single-pass
+  // capacity together; otherwise the tensors one after the other.
+  FusedArgs a{};
+  bool contig = true;
+  uint64_t seg = 0;
+  int n = 0;
+  for (int i = 0; i < p.njobs; ++i) {
+    const QuantProblem &q = p.job[i];
+    if (q.batch == 0 || q.rows == 0 || q.cols == 0) continue;
+    contig = contig && q.ld == q.cols && (q.batch == 1 || q.bstride == q.rows * q.cols);
+    RowJob &j = a.job[n];
+    j.x = q.x;
+    j.nblocks = (uint64_t)(q.batch * q.rows * q.cols / 16);
+    j.seg_begin = seg;
+    j.codes = q.codes;
+    j.scales = q.scales;
+    j.tensor_scale = q.tensor_scale;
+    seg += (j.nblocks + 63) / 64;
+    ++n;
+  }
+  for (int i = 0; i < kMaxGroup; ++i) a.job[i].amax = p.amax[i];  // all four, see row_fused_kernel
+  if (contig && n > 0 && !NVFP4_FUSED_DISABLE) {
+    a.njobs = n;
+    a.nseg = seg;
+    a.ctrl = p.ctrl_group;
+    a.sr_seed = p.job[0].sr_seed;
+    a.rht_seed = p.job[0].rht_seed;
+    a.sr_stream = p.job[0].sr_stream;
+    hipError_t err = hipSuccess;
+    const bool launched = p.job[0].bf16 ? dispatch_group_fused<true>(a, p.job[0].rht, p.job[0].sr, s, err)
+                                        : dispatch_group_fused<false>(a, p.job[0].rht, p.job[0].sr, s, err);
+    if (launched) {
+      for (int i = 0; i < p.njobs; ++i) {  // empty tensors: tensor scale 0
+        const QuantProblem &q = p.job[i];
+        if (q.batch == 0 || q.rows == 0 || q.cols == 0)
+          hipLaunchKernelGGL(store_zero_scale, dim3(1), dim3(1), 0, s, q.tensor_scale);
+      }
+      return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+    }
+    (void)hipGetLastError();
+  }
+  for (int i = 0; i < p.njobs; ++i) {
+    QuantProblem q = p.job[i];
+    q.ctrl = p.ctrl_seq;
+    const nvfp4_status st = launch_quantize(q, s);
+    if (st != NVFP4_OK) return st;
+  }
+  return NVFP4_OK;
+}
 
 nvfp4_status launch_quantize(const QuantProblem &p, hipStream_t s) {
   const int64_t qr = p.along_rows ? p.cols : p.rows;

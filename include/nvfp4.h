@@ -132,6 +132,32 @@ nvfp4_status nvfp4_quantize(const void *x, int32_t x_dtype, int64_t batch, int64
                             const nvfp4_quant_opts *opts, const nvfp4_qtensor *out,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* One tensor of a grouped quantization: the input view and its destination,
+ * with the meaning nvfp4_quantize gives them for axis ALONG_COLS. */
+typedef struct nvfp4_quant_job {
+  const void *x;
+  int64_t batch, rows, cols, ld, batch_stride;
+  nvfp4_qtensor out;
+} nvfp4_quant_job;
+
+/* Bytes of workspace nvfp4_quantize_group needs (16 KiB). */
+size_t nvfp4_quantize_group_workspace_size(void);
+
+/* Quantize 1..4 tensors along their contiguous dimension with the same input
+ * dtype and options, each with its own tensor scale: the result equals
+ * nvfp4_quantize on every job in turn (axis ALONG_COLS, same opts), bit for
+ * bit.  Contiguous inputs (ld == cols, dense batches) whose blocks fit the
+ * single-pass capacity together (on 256 CUs 37.7M BF16 elements, 33.5M
+ * with both the transform and stochastic rounding, 16.8M FP32) are
+ * quantized in one launch that reads every input once; other groups run as
+ * separate calls.  Each job is validated as for
+ * nvfp4_quantize.  The workspace (>= nvfp4_quantize_group_workspace_size(),
+ * 256-byte aligned) follows the same rules: zeroed before first use, left
+ * reusable by each call, one per concurrently running call. */
+nvfp4_status nvfp4_quantize_group(const nvfp4_quant_job *jobs, int32_t njobs, int32_t x_dtype,
+                                  const nvfp4_quant_opts *opts, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
 /* Block-scaled GEMM, both operands quantized along K ("NT" form):
  *   C[b][i][j] = alpha * sA * sB * sum_k A^[b][i][k] * B^[b][j][k]
  * with A^ = E2M1 * E4M3 (exact), sA/sB the tensor scales read on the device.

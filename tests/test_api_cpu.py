@@ -31,6 +31,7 @@ def test_status_strings_and_version():
     assert nv.status_string(99) == "unknown status"
     assert nv.nvfp4_version() >> 16 == 1
     assert nv.nvfp4_quantize_workspace_size() == 4096
+    assert nv.nvfp4_quantize_group_workspace_size() == 16384
 
 
 def _q(batch, rows, cols, codes=FAKE, scales=FAKE, st=FAKE):
@@ -70,6 +71,29 @@ def test_quantize_argument_errors():
     assert _quant(wsb=4095) == nv.EWORKSPACE
     assert _quant(ws=FAKE + 64) == nv.EALIGN
     assert nv.nvfp4_quantize(FAKE, nv.BF16, 1, 32, 64, 64, 0, 0, None, None, FAKE, 4096, None) == nv.EINVAL
+
+
+def _job(x=FAKE, b=1, r=32, c=64, ld=64, bs=32 * 64, out=None):
+    return nv.QuantJobC(x, b, r, c, ld, bs, out if out is not None else _q(b, r, c))
+
+
+def _group(jobs, dt=nv.BF16, opts=None, ws=FAKE, wsb=16384):
+    arr = (nv.QuantJobC * max(len(jobs), 1))(*jobs)
+    return nv.nvfp4_quantize_group(arr, len(jobs), dt, opts or nv.QuantOptsC(0, 0, 0, 0, 0, 0), ws, wsb, None)
+
+
+def test_quantize_group_argument_errors():
+    assert _group([]) == nv.EINVAL                                        # no jobs
+    assert _group([_job()] * 5) == nv.EINVAL                              # more than 4
+    assert nv.nvfp4_quantize_group(None, 1, nv.BF16, nv.QuantOptsC(), FAKE, 16384, None) == nv.EINVAL
+    assert _group([_job()], dt=3) == nv.EINVAL
+    assert _group([_job()], opts=nv.QuantOptsC(2, 0, 0, 0, 0, 0)) == nv.EINVAL
+    assert _group([_job(), _job(c=40, ld=40)]) == nv.ESHAPE               # second job: K % 16 != 0
+    assert _group([_job(), _job(x=FAKE + 2)]) == nv.EALIGN
+    assert _group([_job(out=_q(1, 32, 48))]) == nv.EINVAL                 # view shape mismatch
+    assert _group([_job()], ws=0) == nv.EWORKSPACE
+    assert _group([_job()], wsb=16383) == nv.EWORKSPACE                   # one-tensor size is not enough
+    assert _group([_job()], ws=FAKE + 64) == nv.EALIGN
 
 
 def test_gemm_argument_errors():

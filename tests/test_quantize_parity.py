@@ -107,12 +107,12 @@ def test_workspace_reuse_across_calls():
 
 def test_single_pass_and_two_pass_share_a_workspace():
     """Alternate tensors that fit the single-pass kernel with ones that take
-    the two-pass path (more than 2^25 BF16 elements) and with transposing
+    the two-pass path (more than 37.7M BF16 elements) and with transposing
     calls, all on one workspace: every result stays bit-exact, and neither
     the two-pass words nor the barrier-timeout word are left set."""
     import bit_block_scaled_nvfp4_amd as nv
     ws = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), "cuda:0")
-    big = _input((4608, 8192), 40, "bf16")  # 37.7M elements: over the single-pass capacity
+    big = _input((4864, 8192), 40, "bf16")  # 39.8M elements: over the single-pass capacity
     small = [(_input((256, 512), 41 + i, "f32") * 10.0 ** (i - 2)).to(torch.bfloat16) for i in range(4)]
     seq = [small[0], big, small[1], small[2], big, small[3]]
     for i, x in enumerate(seq):
