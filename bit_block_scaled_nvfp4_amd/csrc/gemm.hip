@@ -40,20 +40,28 @@
 //    (into the idle stage, no VGPRs), then decodes and multiplies.
 //  * Other K: register-staged loads with the K tail read as zero codes and
 //    scales (zero products).
-// The launcher picks the tile width so that the tile count fills the 256
-// CUs in whole rounds.
+// A second kernel runs two wavefronts per SIMD (8 per workgroup, 512 x 192
+// or 256 x 384 tiles, three LDS stages); see its section below.  The
+// launcher costs every kernel and tile shape by its rounds of workgroups over
+// the 256 CUs and picks the cheapest.
 //
 // Workgroups are mapped to tiles so that each XCD (blockIdx mod 8 under the
 // round-robin dispatch) works on a contiguous range of tiles, in groups of
 // kGroupM tile rows, to keep A and B panels in that XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
+#include <cstdlib>
 #include <type_traits>
+#include <utility>
 
 #include "internal.hpp"
 
 #ifndef NVFP4_GEMM_INTERLEAVE
 #define NVFP4_GEMM_INTERLEAVE 5
+#endif
+#ifndef NVFP4_GEMM_W8
+#define NVFP4_GEMM_W8 1
 #endif
 #ifndef NVFP4_GEMM_SWIZZLE
 #define NVFP4_GEMM_SWIZZLE 2
@@ -364,6 +372,50 @@ __device__ __forceinline__ void pipelined_kstep(Stage<kBN> &cur, const Stage<kBN
   mfma_and_decode<0>(r0, sc_nxt, av, bv, acc);
 }
 
+// Epilogue of one wavefront's 128 x (32 * kFragN) region at (row0, col0):
+// multiply by fl(fl(sA * sB) * alpha) and store, masking the M and N edges.
+// Accumulator v of lane l in a 32x32 tile holds row 8*(v/4) + 4*(l/32) + v%4,
+// column l%32.
+template <int kFragN, bool kBF16Out>
+__device__ __forceinline__ void store_tile(const floatx16 (&acc)[kFragM][kFragN], const GemmArgs &g, int64_t batch,
+                                           int64_t wrow0, int64_t wcol0) {
+  using OutT = typename std::conditional<kBF16Out, uint16_t, float>::type;
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, r32 = lane & 31;
+  const float sc = (*g.a_st * *g.b_st) * g.alpha;
+  OutT *cb_ptr = static_cast<OutT *>(g.c) + batch * g.bstride_c;
+  const int64_t row0 = wrow0 + 4 * h;
+  const int64_t col0 = wcol0 + r32;
+  const bool full = wrow0 + 128 <= g.M && wcol0 + 32 * kFragN <= g.N;
+  // One accumulator row pair at a time, so no table of row offsets stays
+  // live beside the accumulators.
+#pragma unroll
+  for (int v = 0; v < 16; v += 2) {
+    const int64_t rv = row0 + 8 * (v >> 2) + (v & 3);
+    OutT *p0 = cb_ptr + rv * g.ldc + col0;
+#pragma unroll
+    for (int i = 0; i < kFragM; ++i) {
+      const int64_t r = rv + 32 * i;
+      OutT *pr = p0 + 32 * i * g.ldc;
+#pragma unroll
+      for (int j = 0; j < kFragN; ++j) {
+        const bool col_ok = full || col0 + 32 * j < g.N;
+        const bool ok0 = col_ok && (full || r < g.M), ok1 = col_ok && (full || r + 1 < g.M);
+        if constexpr (kBF16Out) {
+          // v_cvt_pk_bf16_f32: two FP32 -> BF16, round to nearest even
+          const float2_t y2 = {acc[i][j][v] * sc, acc[i][j][v + 1] * sc};
+          const uint32_t b2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(y2, bf16x2_t));
+          if (ok0) pr[32 * j] = (uint16_t)b2;
+          if (ok1) pr[g.ldc + 32 * j] = (uint16_t)(b2 >> 16);
+        } else {
+          if (ok0) pr[32 * j] = acc[i][j][v] * sc;
+          if (ok1) pr[g.ldc + 32 * j] = acc[i][j][v + 1] * sc;
+        }
+      }
+    }
+  }
+}
+
 template <int kFragN, bool kFast, bool kBF16Out>
 __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
   constexpr int kBN = 64 * kFragN;
@@ -537,40 +589,312 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
     }
   }
 
-  // Epilogue: multiply by fl(fl(sA * sB) * alpha) and store.  Accumulator v
-  // of lane l in a 32x32 tile holds row 8*(v/4) + 4*(l/32) + v%4, column l%32.
-  using OutT = typename std::conditional<kBF16Out, uint16_t, float>::type;
-  const float sc = (*g.a_st * *g.b_st) * g.alpha;
-  OutT *cb_ptr = static_cast<OutT *>(g.c) + batch * g.bstride_c;
-  const int64_t row0 = m0 + wm * 128 + 4 * h;
-  const int64_t col0 = n0 + wn * (32 * kFragN) + r32;
-  int64_t roff[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) roff[v] = (int64_t)(8 * (v >> 2) + (v & 3)) * g.ldc;
-  const bool full = m0 + BM <= g.M && n0 + kBN <= g.N;
-#pragma unroll
-  for (int i = 0; i < kFragM; ++i) {
-    OutT *prow = cb_ptr + (row0 + 32 * i) * g.ldc + col0;
-#pragma unroll
-    for (int j = 0; j < kFragN; ++j) {
-      const bool col_ok = full || col0 + 32 * j < g.N;
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        const int64_t r = row0 + 32 * i + 8 * (v >> 2) + (v & 3);
-        const bool ok0 = col_ok && (full || r < g.M), ok1 = col_ok && (full || r + 1 < g.M);
-        if constexpr (kBF16Out) {
-          // v_cvt_pk_bf16_f32: two FP32 -> BF16, round to nearest even
-          const float2_t y2 = {acc[i][j][v] * sc, acc[i][j][v + 1] * sc};
-          const uint32_t b2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(y2, bf16x2_t));
-          if (ok0) prow[roff[v] + 32 * j] = (uint16_t)b2;
-          if (ok1) prow[roff[v + 1] + 32 * j] = (uint16_t)(b2 >> 16);
-        } else {
-          if (ok0) prow[roff[v] + 32 * j] = acc[i][j][v] * sc;
-          if (ok1) prow[roff[v + 1] + 32 * j] = acc[i][j][v + 1] * sc;
-        }
-      }
+  store_tile<kFragN, kBF16Out>(acc, g, batch, m0 + wm * 128, n0 + wn * (32 * kFragN));
+}
+
+// ---------------------------------------------------------------------------
+// Two wavefronts per SIMD.  A workgroup of 8 wavefronts computes a
+// (128 kWM) x (96 kWN) tile; each wavefront still owns a 128 x 96 region
+// (4 x 3 MFMA tiles), so the decode work per MFMA is that of the 256 x 192
+// kernel above.  With two wavefronts on every SIMD, one wavefront's decode
+// and LDS reads issue while the other's MFMAs run, and a wavefront waiting
+// at the step barrier or for an LDS read leaves the matrix pipe to the
+// other.  The 192 accumulators leave 64 registers per wavefront for
+// everything else, so a step holds little: the scale words of its seven
+// fragments, then per half step the seven scale pairs, per two sub-steps
+// the seven code words, the three B operands and one A operand.
+//
+// Three LDS stages: the global->LDS loads of step k + 2 are issued right
+// after the barrier that opens step k, into the stage step k - 1 used, and
+// each wavefront waits only for its own loads of step k (those of step
+// k + 1, issued later, stay in flight).
+// ---------------------------------------------------------------------------
+constexpr int kW8Threads = 512;
+
+template <int kBM, int kBN>
+struct alignas(16) W8Stage {
+  uint8_t a[kBM * kRowBytes];
+  uint8_t b[kBN * kRowBytes];
+  uint2 as[kBM];
+  uint2 bs[kBN];
+};
+
+// s_waitcnt immediate for vmcnt(n), expcnt and lgkmcnt left at their maxima.
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// The global->LDS loads of one stage, split into jobs of one instruction:
+// code jobs move 16 rows (1 KB, 16 bytes per lane), scale jobs 32 rows
+// (256 B, one dword per lane).  Jobs are numbered A codes, A scales, B codes,
+// B scales, and job j belongs to wavefront j mod 8, so a wavefront's i-th job
+// has a kind known at compile time unless its group of eight straddles a
+// kind boundary.  A lane's global offset is recomputed at every issue (rows
+// clamped to the last row, code chunks unswizzled): holding it across the
+// step would cost registers the accumulators need.  Offsets are 32-bit; the
+// launcher only picks this kernel for operands under 2 GiB.
+template <int kWM, int kWN>
+struct W8Loader {
+  static constexpr int kBM = 128 * kWM, kBN = 96 * kWN;
+  static constexpr int kCodeA = kBM / 16, kScaleA = kBM / 32, kCodeB = kBN / 16, kScaleB = kBN / 32;
+  static constexpr int kJobs = kCodeA + kScaleA + kCodeB + kScaleB;
+  static constexpr int kPerWave = (kJobs + 7) / 8;
+  static_assert(kBM % 32 == 0 && kBN % 32 == 0, "scale jobs cover 32 rows of one operand");
+  static_assert(sizeof(W8Stage<kBM, kBN>) == (kBM + kBN) * (kRowBytes + 8), "stage members are packed");
+
+  const uint8_t *ac, *as, *bc, *bs;
+  int64_t M, N, m0, n0;
+  uint32_t kb2, kb16;  // bytes per code row, per scale row
+
+  // global_load_lds of 16 / 4 bytes per lane into the 64 consecutive lane
+  // slots at LDS byte address `lds` (wavefront-uniform, through M0), from the
+  // scalar base `base` plus the lane's 32-bit offset.  Written as assembly so
+  // that the compiler does not track these loads: its own waits for loads
+  // that write LDS drain all of them before unrelated LDS reads.  The kernel
+  // waits for them explicitly (wait_oldest, then the barrier).  M0 is set in
+  // the same statement, and nothing else in this kernel keeps a value in M0.
+  template <int kBytes>
+  __device__ __forceinline__ static void dma(const uint8_t *base, uint32_t off, uint32_t lds) {
+    if constexpr (kBytes == 16)
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+                   "s"(lds)
+                   : "memory");
+    else
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
+                   : "memory");
+  }
+
+  // Byte offsets of the stage members (W8Stage has no padding between them).
+  static constexpr uint32_t kOffB = kBM * kRowBytes, kOffAs = (kBM + kBN) * kRowBytes,
+                            kOffBs = kOffAs + kBM * 8;
+
+  // kind 0: A codes, 1: A scales, 2: B codes, 3: B scales; jj: job within its
+  // kind; sbase: the stage's LDS address (scalar).
+  template <int kKind>
+  __device__ __forceinline__ void job(uint32_t sbase, int jj, int lane, int64_t k0) const {
+    if constexpr (kKind == 0 || kKind == 2) {
+      const int row = 16 * jj + (lane >> 2);
+      const int part = chunk_slot(row, lane & 3) & 3;  // the XOR swizzle is its own inverse
+      const uint32_t gr = kKind == 0 ? (uint32_t)min(m0 + row, M - 1) : (uint32_t)min(n0 + row, N - 1);
+      dma<16>((kKind == 0 ? ac : bc) + k0 / 2, gr * kb2 + 16 * part, sbase + (kKind == 0 ? 0u : kOffB) + 1024u * jj);
+    } else {
+      const int row = 32 * jj + (lane >> 1);
+      const uint32_t gr = kKind == 1 ? (uint32_t)min(m0 + row, M - 1) : (uint32_t)min(n0 + row, N - 1);
+      dma<4>((kKind == 1 ? as : bs) + k0 / 16, gr * kb16 + 4 * (lane & 1),
+             sbase + (kKind == 1 ? kOffAs : kOffBs) + 256u * jj);
     }
   }
+
+  template <int kI>
+  __device__ __forceinline__ void issue_one(uint32_t st, int wave, int lane, int64_t k0) const {
+    constexpr int lo = 8 * kI, hi = 8 * kI + 7;
+    constexpr int e0 = kCodeA, e1 = e0 + kScaleA, e2 = e1 + kCodeB, e3 = e2 + kScaleB;
+    const int j = lo + wave;
+    if constexpr (hi < e0) {
+      job<0>(st, j, lane, k0);
+    } else if constexpr (lo >= e0 && hi < e1) {
+      job<1>(st, j - e0, lane, k0);
+    } else if constexpr (lo >= e1 && hi < e2) {
+      job<2>(st, j - e1, lane, k0);
+    } else if constexpr (lo >= e2 && hi < e3) {
+      job<3>(st, j - e2, lane, k0);
+    } else {  // the group straddles a kind boundary: branch on the (uniform) job index
+      if (j < e0) job<0>(st, j, lane, k0);
+      else if (j < e1) job<1>(st, j - e0, lane, k0);
+      else if (j < e2) job<2>(st, j - e1, lane, k0);
+      else if (j < e3) job<3>(st, j - e2, lane, k0);
+    }
+  }
+
+  template <int... kIs>
+  __device__ __forceinline__ void issue_all(uint32_t st, int wave, int lane, int64_t k0,
+                                            std::integer_sequence<int, kIs...>) const {
+    (issue_one<kIs>(st, wave, lane, k0), ...);
+  }
+
+  __device__ __forceinline__ void issue(W8Stage<kBM, kBN> &st, int wave, int lane, int64_t k0) const {
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&st);
+    issue_all(sbase, wave, lane, k0, std::make_integer_sequence<int, kPerWave>{});
+  }
+
+  // Wait until this wavefront's loads of the oldest stage in flight have
+  // landed while the next stage's (issued after them) stay in flight.  Any
+  // other vector-memory operation issued later only makes the wait stricter.
+  __device__ __forceinline__ static void wait_oldest(int wave) {
+    constexpr int kFull = kJobs / 8, kRem = kJobs % 8;  // wavefronts < kRem issue one more job
+    __builtin_amdgcn_sched_barrier(0);
+    if (kRem != 0 && wave < kRem)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kFull + 1));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kFull));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+};
+
+// Two E4M3 scale bytes (bits 0..7 and 8..15 of w) -> two FP16 values S * 2^-8
+// in one dword: an E4M3 code shifted left by 7 and read as FP16 is its value
+// times 2^-8 (exponent fields line up; subnormal codes become FP16
+// subnormals).  The converter's scale of 256 supplies the missing 2^8.
+__device__ __forceinline__ half2_t scale_pair_lo(uint32_t w) {
+  return __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, w, 0x0C010C00u) << 7);
+}
+
+// Eight E2M1 codes times (S * 2^-8): the converter at scale 2^8 (exact, a
+// power of two) gives code * 256, and one packed multiply per pair gives
+// code * S, exact in FP16 (at most 6 significant bits, at least 2^-10).
+__device__ __forceinline__ half8_t decode8_s256(uint32_t codes, _Float16 s) {
+  const half2_t s2 = {s, s};
+  const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * s2;
+  const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * s2;
+  const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * s2;
+  const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * s2;
+  return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// The MFMAs of one K step for one wavefront's 128 x 96 region.
+template <int kBM, int kBN>
+__device__ __forceinline__ void w8_compute(const W8Stage<kBM, kBN> &st, int arow, int brow, int h, int qa, int qb,
+                                           floatx16 (&acc)[kFragM][3]) {
+  const uint32_t *as32 = reinterpret_cast<const uint32_t *>(st.as);
+  const uint32_t *bs32 = reinterpret_cast<const uint32_t *>(st.bs);
+  uint32_t wa[kFragM], wb[3];
+#pragma unroll
+  for (int f = 0; f < kFragM; ++f) wa[f] = as32[(arow + 32 * f) * 2 + h];
+#pragma unroll
+  for (int f = 0; f < 3; ++f) wb[f] = bs32[(brow + 32 * f) * 2 + h];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    // blocks 4h + 2 half (low) and 4h + 2 half + 1 (high) of every fragment
+    half2_t sa[kFragM], sb[3];
+#pragma unroll
+    for (int f = 0; f < kFragM; ++f) sa[f] = scale_pair_lo(wa[f] >> (16 * half));
+#pragma unroll
+    for (int f = 0; f < 3; ++f) sb[f] = scale_pair_lo(wb[f] >> (16 * half));
+    const int ca_off = 16 * ((2 * h + half) ^ qa), cb_off = 16 * ((2 * h + half) ^ qb);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      uint2 ca[kFragM], cb[3];
+#pragma unroll
+      for (int f = 0; f < kFragM; ++f)
+        ca[f] = *reinterpret_cast<const uint2 *>(st.a + (arow + 32 * f) * kRowBytes + ca_off + 8 * p);
+#pragma unroll
+      for (int f = 0; f < 3; ++f)
+        cb[f] = *reinterpret_cast<const uint2 *>(st.b + (brow + 32 * f) * kRowBytes + cb_off + 8 * p);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        half8_t bv[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) bv[j] = decode8_s256(e ? cb[j].y : cb[j].x, sb[j][p]);
+#pragma unroll
+        for (int i = 0; i < kFragM; ++i) {
+          const half8_t av = decode8_s256(e ? ca[i].y : ca[i].x, sa[i][p]);
+#pragma unroll
+          for (int j = 0; j < 3; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv[j], acc[i][j], 0, 0, 0);
+        }
+      }
+      // Keep the scheduler from hoisting later sub-steps' reads and decodes
+      // into this one: the other wavefront on the SIMD hides the latency,
+      // and the registers are not there.
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+struct W8Lane {
+  int wave, lane, h, arow, brow, qa, qb;
+};
+
+// Fill a stage with K step `kstep`.  The stage comes in as a restrict
+// pointer so that, once inlined, its loads carry alias-scope information: the
+// compiler then tells them apart from reads of the other stages instead of
+// waiting for every load that writes LDS before any LDS read.
+template <int kWM, int kWN>
+__device__ __forceinline__ void w8_fill(W8Stage<128 * kWM, 96 * kWN> *__restrict__ dst, const W8Loader<kWM, kWN> &ld,
+                                        const W8Lane &c, int kstep) {
+  // Offsets are recomputed per issue; an opaque copy of the lane index keeps
+  // them from being hoisted out of the loop (and spilled).
+  int lane_k = c.lane;
+  asm volatile("" : "+v"(lane_k));
+  ld.issue(*dst, c.wave, lane_k, (int64_t)kstep * BK);
+}
+
+// One K step: wait for this step's stage, barrier, refill the stage the step
+// before used, multiply.  The refill is issued at every step, for step
+// kt + 2 or, past the end, again for the last step (into a stage nobody reads
+// any more): a fixed number of loads per step lets the compiler's own wait
+// before the reads of `cur` be exact instead of draining every load.
+template <int kWM, int kWN>
+__device__ __forceinline__ void w8_step(const W8Stage<128 * kWM, 96 * kWN> *__restrict__ cur,
+                                        W8Stage<128 * kWM, 96 * kWN> *__restrict__ dst,
+                                        const W8Loader<kWM, kWN> &ld, const W8Lane &c, int kt, int ksteps,
+                                        floatx16 (&acc)[kFragM][3]) {
+  W8Loader<kWM, kWN>::wait_oldest(c.wave);
+  // A bare barrier: __syncthreads() would also wait for the loads of the
+  // next stage, still in flight.  This wavefront's LDS reads of the step
+  // before have all returned (lgkmcnt(0)) before it arrives, so the stage
+  // they read can be refilled once every wavefront has arrived.
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  w8_fill<kWM, kWN>(dst, ld, c, min(kt + 2, ksteps - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  w8_compute<128 * kWM, 96 * kWN>(*cur, c.arow, c.brow, c.h, c.qa, c.qb, acc);
+}
+
+template <int kWM, int kWN, bool kBF16Out>
+__global__ __launch_bounds__(kW8Threads) void gemm_nvfp4_w8_kernel(GemmArgs g) {
+  using L = W8Loader<kWM, kWN>;
+  constexpr int kBM = L::kBM, kBN = L::kBN;
+  // Three stages as separate objects, so the compiler can tell reads of one
+  // from the global->LDS loads in flight into the others.
+  __shared__ W8Stage<kBM, kBN> st0, st1, st2;
+
+  const int ntiles = g.tiles_m * g.tiles_n;
+  const int bid = blockIdx.x;
+  const int per_xcd = ntiles / 8;
+  const int t = (ntiles % 8 == 0) ? (bid % 8) * per_xcd + bid / 8 : bid;
+  const int group = t / (kGroupM * g.tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(g.tiles_m - first_m, kGroupM);
+  const int in_group = t - group * kGroupM * g.tiles_n;
+  const int tm = first_m + in_group % gm;
+  const int tn = in_group / gm;
+
+  const int64_t batch = blockIdx.y;
+  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % kWM, wn = wave / kWM;
+  const int h = lane >> 5, r32 = lane & 31;
+  const int arow = wm * 128 + r32, brow = wn * 96 + r32;
+  // The chunk swizzle of the lane's rows (the same for rows 32 apart).
+  const int qa = chunk_slot(arow, 0) & 3, qb = chunk_slot(brow, 0) & 3;
+  static_assert(NVFP4_GEMM_SWIZZLE >= 0 && NVFP4_GEMM_SWIZZLE <= 2, "XOR swizzles on row bits below 5");
+
+  const uint8_t *ac = g.a_codes + batch * g.M * (g.K / 2);
+  const uint8_t *as = g.a_scales + batch * g.M * (g.K / 16);
+  const uint8_t *bc = g.b_codes + batch * g.N * (g.K / 2);
+  const uint8_t *bs = g.b_scales + batch * g.N * (g.K / 16);
+
+  floatx16 acc[kFragM][3];
+#pragma unroll
+  for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const L ld{ac, as, bc, bs, g.M, g.N, m0, n0, (uint32_t)(g.K / 2), (uint32_t)(g.K / 16)};
+  const int ksteps = (int)(g.K / BK);
+  const W8Lane c{wave, lane, h, arow, brow, qa, qb};
+  if (ksteps > 0) {  // steps 0 and 1 (or the last step again): one stage in flight per step from here on
+    w8_fill<kWM, kWN>(&st0, ld, c, 0);
+    w8_fill<kWM, kWN>(&st1, ld, c, min(1, ksteps - 1));
+  }
+  for (int kt = 0; kt < ksteps; kt += 3) {
+    w8_step<kWM, kWN>(&st0, &st2, ld, c, kt, ksteps, acc);
+    if (kt + 1 < ksteps) w8_step<kWM, kWN>(&st1, &st0, ld, c, kt + 1, ksteps, acc);
+    if (kt + 2 < ksteps) w8_step<kWM, kWN>(&st2, &st1, ld, c, kt + 2, ksteps, acc);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the refills issued past the last step
+  store_tile<3, kBF16Out>(acc, g, batch, m0 + wm * 128, n0 + wn * 96);
 }
 
 template <int kFragN>
@@ -587,30 +911,53 @@ hipError_t launch_tiles(const GemmArgs &g, int64_t batch, bool fast, bool bf16, 
   return hipGetLastError();
 }
 
-// N-tile width (64 * kFragN): among 256, 192 and 128, the one with the least
-// estimated time, counting a partly filled last round of workgroups as a full
-// round (one workgroup per CU, 256 CUs) and costing narrower tiles by their
-// extra decode work per MFMA (measured on fprop/MLP-sized problems).
-int pick_frag_n(int64_t M, int64_t N, int64_t batch) {
-  const int64_t tm = (M + BM - 1) / BM;
+template <int kWM, int kWN>
+hipError_t launch_w8(const GemmArgs &g, int64_t batch, bool bf16, hipStream_t s) {
+  const dim3 grid((unsigned)(g.tiles_m * g.tiles_n), (unsigned)batch);
+  if (bf16)
+    hipLaunchKernelGGL((gemm_nvfp4_w8_kernel<kWM, kWN, true>), grid, dim3(kW8Threads), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_nvfp4_w8_kernel<kWM, kWN, false>), grid, dim3(kW8Threads), 0, s, g);
+  return hipGetLastError();
+}
+
+// Kernel and tile choice.  Candidates: the 4-wavefront kernel with 256 x 256,
+// 256 x 192 and 256 x 128 tiles, and (K % 128 == 0) the 8-wavefront kernel
+// with 512 x 192 and 256 x 384 tiles.  Each is costed as its rounds of
+// workgroups (one workgroup per CU, 256 CUs; a partly filled last round
+// counts in full) times its tile area times a per-element cost measured on
+// fprop/MLP-sized problems.
+struct TilePick {
+  int kind;  // 4-wavefront kFragN (4, 3, 2), or 8-wavefront: 10 (512 x 192), 11 (256 x 384)
+  int bm, bn;
+};
+
+TilePick pick_tiles(int64_t M, int64_t N, int64_t batch, bool fast) {
+  struct Cand {
+    int kind, bm, bn;
+    double cost;
+    bool need_fast;
+  };
+  const Cand cands[5] = {{10, 512, 192, 0.96, true}, {11, 256, 384, 0.96, true},
+                         {4, 256, 256, 1.0, false},  {3, 256, 192, 1.02, false}, {2, 256, 128, 1.12, false}};
   double best = 1e300;
-  int pick = 4;
-  const int cands[3] = {4, 3, 2};
-  const double cost_per_col[3] = {1.0, 1.02, 1.12};
-  for (int c = 0; c < 3; ++c) {
-    const int fn = cands[c];
-    const int64_t tn = (N + 64 * fn - 1) / (64 * fn);
-    const int64_t tiles = tm * tn * batch;
-    const int64_t rounds = (tiles + 255) / 256;
-    const double t = (double)rounds * (double)(64 * fn) * cost_per_col[c];
+  TilePick pick{4, 256, 256};
+  for (const Cand &c : cands) {
+    if (c.need_fast && (!fast || !NVFP4_GEMM_W8)) continue;
+    const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * batch;
+    const double t = (double)((tiles + 255) / 256) * c.bm * c.bn * c.cost;
     if (t < best - 1e-9) {
       best = t;
-      pick = fn;
+      pick = TilePick{c.kind, c.bm, c.bn};
     }
   }
-#ifdef NVFP4_GEMM_FORCE_FRAG_N
-  pick = NVFP4_GEMM_FORCE_FRAG_N;
-#endif
+  // Testing / tuning override, e.g. NVFP4_GEMM_TILE=512x192.
+  if (const char *env = std::getenv("NVFP4_GEMM_TILE")) {
+    int bm = 0, bn = 0;
+    if (std::sscanf(env, "%dx%d", &bm, &bn) == 2)
+      for (const Cand &c : cands)
+        if (c.bm == bm && c.bn == bn && (fast || !c.need_fast)) pick = TilePick{c.kind, c.bm, c.bn};
+  }
   return pick;
 }
 
@@ -633,15 +980,19 @@ nvfp4_status launch_gemm(const GemmProblem &p, hipStream_t s) {
   g.ldc = p.ldc;
   g.bstride_c = p.bstride_c;
   g.alpha = p.alpha;
+  // The 8-wavefront kernel's loads use 32-bit offsets within an operand.
   const bool fast = p.K % BK == 0;
-  const int fn = pick_frag_n(p.M, p.N, p.batch);
-  const int64_t tm = (p.M + BM - 1) / BM, tn = (p.N + 64 * fn - 1) / (64 * fn);
+  const bool small = p.M * (p.K / 2) < ((int64_t)1 << 31) && p.N * (p.K / 2) < ((int64_t)1 << 31);
+  const TilePick tp = pick_tiles(p.M, p.N, p.batch, fast && small);
+  const int64_t tm = (p.M + tp.bm - 1) / tp.bm, tn = (p.N + tp.bn - 1) / tp.bn;
   if (tm * tn > 0x7FFFFFFF) return NVFP4_EUNSUPPORTED;
   g.tiles_m = (int)tm;
   g.tiles_n = (int)tn;
   hipError_t e;
-  if (fn == 4) e = launch_tiles<4>(g, p.batch, fast, p.c_bf16, s);
-  else if (fn == 3) e = launch_tiles<3>(g, p.batch, fast, p.c_bf16, s);
+  if (tp.kind == 10) e = launch_w8<4, 2>(g, p.batch, p.c_bf16, s);
+  else if (tp.kind == 11) e = launch_w8<2, 4>(g, p.batch, p.c_bf16, s);
+  else if (tp.kind == 4) e = launch_tiles<4>(g, p.batch, fast, p.c_bf16, s);
+  else if (tp.kind == 3) e = launch_tiles<3>(g, p.batch, fast, p.c_bf16, s);
   else e = launch_tiles<2>(g, p.batch, fast, p.c_bf16, s);
   return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }

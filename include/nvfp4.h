@@ -166,7 +166,14 @@ nvfp4_status nvfp4_quantize_group(const nvfp4_quant_job *jobs, int32_t njobs, in
  *   a, b         host structs: a is [batch][M][K], b is [batch][N][K].
  *   c            device, c_dtype elements, row stride ldc >= N, batch stride
  *                batch_stride_c >= M*ldc (elements), aligned to the element.
- * Any M, N >= 0 and K a multiple of 16 (K = 0 gives zeros). */
+ * Any M, N >= 0 and K a multiple of 16 (K = 0 gives zeros).
+ * The kernel and tile shape are chosen per problem.  The environment
+ * variable NVFP4_GEMM_TILE, read at every call, overrides that choice for
+ * testing and tuning: "512x192" or "256x384" (eight-wavefront kernel, used
+ * only where K % 128 == 0 and each operand's codes are under 2 GiB),
+ * "256x256", "256x192" or "256x128" (four-wavefront kernel); unset, empty or
+ * anything else keeps the automatic choice.  Results agree to the FP32
+ * accumulation-order tolerance whatever the tile. */
 nvfp4_status nvfp4_gemm(const nvfp4_qtensor *a, const nvfp4_qtensor *b, void *c, int32_t c_dtype,
                         int64_t ldc, int64_t batch_stride_c, float alpha, void *stream);
 
