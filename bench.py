@@ -93,7 +93,7 @@ def measured_traffic(workload: str):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m_bytes = re.search(r"gemm_nvfp4_kernel HBM bytes per launch: (\d+)", text)
+    m_bytes = re.search(r"gemm_nvfp4\w* HBM bytes per launch: (\d+)", text)
     m_sha = re.search(r"gemm_source_sha256_16: ([0-9a-f]+)", text)
     if not (m_bytes and m_sha):
         return None
