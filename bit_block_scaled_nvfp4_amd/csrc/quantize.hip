@@ -57,8 +57,8 @@ template <bool kBF16, bool kRHT, bool kSR>
 struct Fused {
   // Blocks held per lane: 37.7M BF16 (16.8M FP32) elements on 256 CUs, the
   // most that fits the 128-VGPR budget of 1024-thread workgroups without
-  // spilling (BF16 with both the transform and stochastic rounding: 33.5M).
-  static constexpr int kMaxBlocks = kBF16 ? (kRHT && kSR ? 8 : 9) : 4;
+  // spilling (BF16 with both the transform and stochastic rounding: 29.4M).
+  static constexpr int kMaxBlocks = kBF16 ? (kRHT && kSR ? 7 : 9) : 4;
 };
 
 // ---------------------------------------------------------------------------

@@ -147,7 +147,7 @@ size_t nvfp4_quantize_group_workspace_size(void);
  * dtype and options, each with its own tensor scale: the result equals
  * nvfp4_quantize on every job in turn (axis ALONG_COLS, same opts), bit for
  * bit.  Contiguous inputs (ld == cols, dense batches) whose blocks fit the
- * single-pass capacity together (on 256 CUs 37.7M BF16 elements, 33.5M
+ * single-pass capacity together (on 256 CUs 37.7M BF16 elements, 29.4M
  * with both the transform and stochastic rounding, 16.8M FP32) are
  * quantized in one launch that reads every input once; other groups run as
  * separate calls.  Each job is validated as for
