@@ -19,7 +19,7 @@ namespace nvfp4 {
 // Per-epoch-parity amax slots are cleared one call ahead.  Every word sits
 // on its own 128-byte line so the atomics spread over memory channels.
 struct QuantCtrl {
-  uint32_t amax_bits;  // two-pass: max |v| as FP32 bits (atomicMax)
+  uint32_t reserved;   // zero
   uint32_t done;       // two-pass: workgroups finished with the encode pass
   uint32_t timeout;    // single-pass: nonzero if a bounded barrier wait expired
   uint32_t pad0[29];
@@ -31,7 +31,14 @@ struct QuantCtrl {
     uint32_t v;
     uint32_t pad[31];
   } amax[2][8];
-  uint32_t pad1[160];
+  // Two-pass: per-workgroup maxima go to slot blockIdx mod 8, so the atomics
+  // of a pass that ends in one burst spread over four cache lines instead of
+  // queueing on one word; readers take the max of the eight.
+  struct alignas(64) Part {
+    uint32_t v;
+    uint32_t pad[15];
+  } part[8];
+  uint32_t pad1[32];
 };
 static_assert(sizeof(QuantCtrl) == 4096, "quantize control block is 4 KB");
 

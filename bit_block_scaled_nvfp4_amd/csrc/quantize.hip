@@ -167,9 +167,16 @@ __device__ __forceinline__ void wait_for(T v) {
   asm volatile("" ::"v"(v));
 }
 
-__device__ __forceinline__ uint32_t load_amax(const QuantCtrl *ctrl) { return atomic_load_dev(&ctrl->amax_bits); }
+// Two-pass tensor max as FP32 bits: the max of the eight partial slots.
+__device__ __forceinline__ uint32_t load_amax(const QuantCtrl *ctrl) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = max(m, atomic_load_dev(&ctrl->part[i].v));
+  return m;
+}
 
-// Workgroup max -> one atomicMax per workgroup (two-pass amax kernels).
+// Workgroup max -> one atomicMax per workgroup into slot blockIdx mod 8
+// (two-pass amax kernels).
 __device__ __forceinline__ void block_amax_commit(uint32_t m, QuantCtrl *ctrl) {
   __shared__ uint32_t part[16];
   m = wave_max_u32(m);
@@ -179,7 +186,7 @@ __device__ __forceinline__ void block_amax_commit(uint32_t m, QuantCtrl *ctrl) {
   if (threadIdx.x == 0) {
     uint32_t r = part[0];
     for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = max(r, part[i]);
-    __hip_atomic_fetch_max(&ctrl->amax_bits, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_max(&ctrl->part[blockIdx.x & 7].v, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -192,7 +199,7 @@ __device__ __forceinline__ void encode_finish(QuantCtrl *ctrl, float *tensor_sca
     // arrive (seen through the returned count) clears the two-pass words.
     const uint32_t old = __hip_atomic_fetch_add(&ctrl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == gridDim.x - 1) {
-      atomic_store_dev(&ctrl->amax_bits, 0u);
+      for (int i = 0; i < 8; ++i) atomic_store_dev(&ctrl->part[i].v, 0u);
       atomic_store_dev(&ctrl->done, 0u);
     }
   }

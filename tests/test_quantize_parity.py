@@ -124,6 +124,10 @@ def test_single_pass_and_two_pass_share_a_workspace():
             assert_quant_equal(to_oracle_view(qt), oracle_quant(x, axis=O.ALONG_ROWS), f"col call {i}")
     torch.cuda.synchronize()
     assert int(ws[:16].sum().item()) == 0
+    # the eight two-pass partial maxima (64-byte slots after the 128-byte
+    # header, 10 counter lines and 16 single-pass slot lines) are cleared too
+    part0 = 128 + 10 * 128 + 16 * 128
+    assert int(ws[part0:part0 + 8 * 64].sum().item()) == 0
 
 
 @pytest.mark.parametrize("name", ["fprop_3b"])
