@@ -667,24 +667,39 @@ struct W8Loader {
                             kOffBs = kOffAs + kBM * 8;
 
   // kind 0: A codes, 1: A scales, 2: B codes, 3: B scales; jj: job within its
-  // kind; sbase: the stage's LDS address (scalar).
+  // kind; sbase: the stage's LDS address (scalar).  Lane terms shared by all
+  // jobs of a kind: a code job's lane takes row 16 jj + lane / 4 and, since
+  // 16 jj leaves row bits 2..3 alone, the same unswizzled chunk; a scale
+  // job's lane takes row 32 jj + lane / 2, dword lane & 1.  Rows are clamped
+  // to the last row; all of it in 32 bits (operands under 2 GiB, fewer than
+  // 2^24 rows and code bytes per row, which the launcher checks).
+  struct LaneTerms {
+    int code_row, code_off, scale_row, scale_off;
+  };
+  __device__ __forceinline__ static LaneTerms lane_terms(int lane) {
+    const int code_row = lane >> 2;
+    return LaneTerms{code_row, 16 * (chunk_slot(code_row, lane & 3) & 3), lane >> 1, 4 * (lane & 1)};
+  }
+
   template <int kKind>
-  __device__ __forceinline__ void job(uint32_t sbase, int jj, int lane, int64_t k0) const {
+  __device__ __forceinline__ void job(uint32_t sbase, int jj, const LaneTerms &t, int64_t k0) const {
     if constexpr (kKind == 0 || kKind == 2) {
-      const int row = 16 * jj + (lane >> 2);
-      const int part = chunk_slot(row, lane & 3) & 3;  // the XOR swizzle is its own inverse
-      const uint32_t gr = kKind == 0 ? (uint32_t)min(m0 + row, M - 1) : (uint32_t)min(n0 + row, N - 1);
-      dma<16>((kKind == 0 ? ac : bc) + k0 / 2, gr * kb2 + 16 * part, sbase + (kKind == 0 ? 0u : kOffB) + 1024u * jj);
+      const int last = (int)(kKind == 0 ? M - 1 - m0 : N - 1 - n0);  // last row relative to the tile
+      const uint32_t r0 = (uint32_t)(kKind == 0 ? m0 : n0);
+      const uint32_t gr = r0 + (uint32_t)min(16 * jj + t.code_row, last);
+      dma<16>((kKind == 0 ? ac : bc) + k0 / 2, __umul24(gr, kb2) + (uint32_t)t.code_off,
+              sbase + (kKind == 0 ? 0u : kOffB) + 1024u * jj);
     } else {
-      const int row = 32 * jj + (lane >> 1);
-      const uint32_t gr = kKind == 1 ? (uint32_t)min(m0 + row, M - 1) : (uint32_t)min(n0 + row, N - 1);
-      dma<4>((kKind == 1 ? as : bs) + k0 / 16, gr * kb16 + 4 * (lane & 1),
+      const int last = (int)(kKind == 1 ? M - 1 - m0 : N - 1 - n0);
+      const uint32_t r0 = (uint32_t)(kKind == 1 ? m0 : n0);
+      const uint32_t gr = r0 + (uint32_t)min(32 * jj + t.scale_row, last);
+      dma<4>((kKind == 1 ? as : bs) + k0 / 16, __umul24(gr, kb16) + (uint32_t)t.scale_off,
              sbase + (kKind == 1 ? kOffAs : kOffBs) + 256u * jj);
     }
   }
 
   template <int kI>
-  __device__ __forceinline__ void issue_one(uint32_t st, int wave, int lane, int64_t k0) const {
+  __device__ __forceinline__ void issue_one(uint32_t st, int wave, const LaneTerms &lane, int64_t k0) const {
     constexpr int lo = 8 * kI, hi = 8 * kI + 7;
     constexpr int e0 = kCodeA, e1 = e0 + kScaleA, e2 = e1 + kCodeB, e3 = e2 + kScaleB;
     const int j = lo + wave;
@@ -705,14 +720,15 @@ struct W8Loader {
   }
 
   template <int... kIs>
-  __device__ __forceinline__ void issue_all(uint32_t st, int wave, int lane, int64_t k0,
+  __device__ __forceinline__ void issue_all(uint32_t st, int wave, const LaneTerms &lane, int64_t k0,
                                             std::integer_sequence<int, kIs...>) const {
     (issue_one<kIs>(st, wave, lane, k0), ...);
   }
 
   __device__ __forceinline__ void issue(W8Stage<kBM, kBN> &st, int wave, int lane, int64_t k0) const {
     const uint32_t sbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&st);
-    issue_all(sbase, wave, lane, k0, std::make_integer_sequence<int, kPerWave>{});
+    const LaneTerms t = lane_terms(lane);
+    issue_all(sbase, wave, t, k0, std::make_integer_sequence<int, kPerWave>{});
   }
 
   // Wait until this wavefront's loads of the oldest stage in flight have
@@ -980,9 +996,11 @@ nvfp4_status launch_gemm(const GemmProblem &p, hipStream_t s) {
   g.ldc = p.ldc;
   g.bstride_c = p.bstride_c;
   g.alpha = p.alpha;
-  // The 8-wavefront kernel's loads use 32-bit offsets within an operand.
+  // The 8-wavefront kernel's loads use 32-bit offsets within an operand and
+  // 24-bit row and row-size factors.
   const bool fast = p.K % BK == 0;
-  const bool small = p.M * (p.K / 2) < ((int64_t)1 << 31) && p.N * (p.K / 2) < ((int64_t)1 << 31);
+  const bool small = p.M * (p.K / 2) < ((int64_t)1 << 31) && p.N * (p.K / 2) < ((int64_t)1 << 31) &&
+                     p.M < (1 << 24) && p.N < (1 << 24) && p.K / 2 < (1 << 24);
   const TilePick tp = pick_tiles(p.M, p.N, p.batch, fast && small);
   const int64_t tm = (p.M + tp.bm - 1) / tp.bm, tn = (p.N + tp.bn - 1) / tp.bn;
   if (tm * tn > 0x7FFFFFFF) return NVFP4_EUNSUPPORTED;
