@@ -84,25 +84,24 @@ __device__ __forceinline__ uint32_t e2m1_rne8(const float *q) {
 }
 
 // Stochastic rounding onto the same grid with a 16-bit uniform word u: the
-// magnitude rounds up iff u < 2^16 * (|q| - lo) / step.  For |q| in [1, 6)
-// lo is |q| truncated to one mantissa bit and (|q| - lo) / step is the
-// remaining 22 mantissa bits over 2^22, so the test is an integer compare.
-// For |q| < 1 the step is 0.5: t = 2|q| is exact and lo = floor(t).  At 6 the
-// truncated code is already 7 and the fraction is 0, so no special case.
+// magnitude rounds up iff u < 2^16 * (|q| - lo) / step, lo the grid point
+// at or below |q| (saturated at 6).  Written without a branch on the range,
+// so that the lanes of a wavefront do not take both paths in turn: with
+// e' = max(exponent(|q|), 0), t = |q| * 2^(1 - e') is exact and lies in
+// [0, 2) for |q| < 1 (step 0.5, t = 2|q|) and in [2, 4) for |q| >= 1 (step
+// 2^(e' - 1)); the grid point below is code 2e' + floor(t) and
+// (|q| - lo) / step = t - floor(t), also exact.  For |q| >= 1 the test
+// equals comparing u << 6 with the low 22 mantissa bits of |q|.  At 6 the
+// fraction is 0, so no special case.
 __device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t u16) {
-  uint32_t sign = (__float_as_uint(q) >> 28) & 8u;
-  float a = fminf(fabsf(q), 6.0f);
-  uint32_t ua = __float_as_uint(a);
-  uint32_t code;
-  if (a >= 1.0f) {
-    uint32_t lo = (ua >> 22) - 252u;
-    code = lo + (((u16 << 6) < (ua & 0x3FFFFFu)) ? 1u : 0u);
-  } else {
-    float t = a * 2.0f;
-    float fl = __builtin_floorf(t);
-    code = (uint32_t)fl + (((float)u16 < (t - fl) * 65536.0f) ? 1u : 0u);
-  }
-  return sign | code;
+  const uint32_t sign = (__float_as_uint(q) >> 28) & 8u;
+  const float a = fminf(fabsf(q), 6.0f);
+  const uint32_t ebits = __float_as_uint(a) >> 23;          // biased exponent (sign bit is 0)
+  const uint32_t e = (ebits > 127u ? ebits : 127u) - 127u;  // 0, 1 or 2
+  const float t = a * __uint_as_float((128u - e) << 23);    // a * 2^(1 - e)
+  const float fl = __builtin_floorf(t);
+  const uint32_t up = ((float)u16 < (t - fl) * 65536.0f) ? 1u : 0u;
+  return sign | (2u * e + (uint32_t)fl + up);
 }
 
 // ---------------------------------------------------------------------------

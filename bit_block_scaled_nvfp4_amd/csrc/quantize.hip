@@ -102,6 +102,18 @@ struct RawBlock {
 #pragma unroll
     for (int i = 0; i < (kBF16 ? 8 : 16); ++i) asm volatile("" : "+v"(w[i]));
   }
+  // max |v| over the block as FP32 bits, straight from BF16 words: |x|
+  // orders like the unsigned 15-bit magnitude field, so packed 16-bit maxima
+  // of (w & 0x7FFF7FFF) give the largest magnitude, whose FP32 bits are its
+  // BF16 bits shifted left by 16.  Equal to max_abs16 of the unpacked values.
+  __device__ __forceinline__ uint32_t max_abs_bf16() const {
+    static_assert(kBF16, "BF16 blocks only");
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 m = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+    return (uint32_t)(m.x > m.y ? m.x : m.y) << 16;
+  }
   __device__ __forceinline__ void values(float (&v)[16]) const {
 #pragma unroll
     for (int j = 0; j < 16; ++j)
@@ -289,14 +301,34 @@ __device__ __forceinline__ uint64_t load_segment(const RowArgs &a, uint64_t seg,
   }
 }
 
-// load_segment for a contiguous tensor given by pointer and block count.
+// load_segment for a contiguous tensor in the single-pass kernel, whose
+// capacity (tens of millions of elements) keeps every segment, chunk and
+// block index within 32 bits: the same loads and lane exchange as
+// load_segment, with 32-bit bounds arithmetic.
 template <bool kBF16>
-__device__ __forceinline__ uint64_t load_segment_contig(const void *x, uint64_t nblocks, uint64_t seg, int lane,
-                                                        RawBlock<kBF16> &raw) {
-  RowArgs v{};
-  v.x = x;
-  v.nblocks = nblocks;
-  return load_segment<kBF16, true>(v, seg, lane, raw);
+__device__ __forceinline__ uint32_t load_segment_fused(const void *x, uint32_t nblocks, uint32_t seg, int lane,
+                                                       RawBlock<kBF16> &raw) {
+  if constexpr (kBF16) {
+    const uint4 *p = static_cast<const uint4 *>(x);
+    const uint32_t nchunks = 2 * nblocks;
+    const uint32_t c0 = seg * 128 + lane, c1 = c0 + 64;
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    const uint4 x0 = c0 < nchunks ? ld_stream(p + c0) : zero;
+    const uint4 x1 = c1 < nchunks ? ld_stream(p + c1) : zero;
+    const bool odd = lane & 1;
+    const uint4 send = odd ? x0 : x1;
+    const uint4 recv = make_uint4(__shfl_xor(send.x, 1), __shfl_xor(send.y, 1), __shfl_xor(send.z, 1),
+                                  __shfl_xor(send.w, 1));
+    const uint4 lo = odd ? recv : x0, hi = odd ? x1 : recv;
+    raw.w[0] = lo.x; raw.w[1] = lo.y; raw.w[2] = lo.z; raw.w[3] = lo.w;
+    raw.w[4] = hi.x; raw.w[5] = hi.y; raw.w[6] = hi.z; raw.w[7] = hi.w;
+    return seg * 64 + (uint32_t)((lane & 1) * 32 + (lane >> 1));
+  } else {
+    const uint32_t blk = seg * 64 + lane;
+    if (blk < nblocks) raw.load(x, (int64_t)16 * blk);
+    else raw.zero();
+    return blk;
+  }
 }
 
 // Encode one block (values already transformed) and store codes + scale.
@@ -326,37 +358,45 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
   // before this workgroup arrives, so reading it here is race free.
   if (threadIdx.x == 0) s_epoch = (uint32_t)atomic_load_dev(&ctrl->release.v);
 
-  const uint64_t nwaves = (uint64_t)gridDim.x * kWaves;
-  const uint64_t gwave = (uint64_t)blockIdx.x * kWaves + wave;
+  // 32-bit indices throughout: the launcher only runs this kernel within its
+  // capacity (at most kMax segments per wavefront of one grid).
+  const uint32_t nwaves = gridDim.x * kWaves;
+  const uint32_t gwave = blockIdx.x * kWaves + wave;
+  const uint32_t nseg = (uint32_t)a.nseg;
   const uint32_t mask = kRHT ? rht_sign_mask(a.rht_seed) : 0u;
 
   // Phase 1: all loads first, then the block maxima.  A segment belongs to
   // one job, so the job index is uniform across the wavefront.
   RawBlock<kBF16> raw[kMax];
-  uint64_t blk[kMax];
+  uint32_t blk[kMax];
   int jb[kMax];
   uint32_t bmax[kMax];
 #pragma unroll
   for (int it = 0; it < kMax; ++it) {
-    const uint64_t g = it * nwaves + gwave;
-    if (it < (int)a.nseg_iters && g < a.nseg) {
-      const int j = (njobs > 1 && g >= a.job[1].seg_begin) + (njobs > 2 && g >= a.job[2].seg_begin) +
-                    (njobs > 3 && g >= a.job[3].seg_begin);
+    const uint32_t g = it * nwaves + gwave;
+    if (it < (int)a.nseg_iters && g < nseg) {
+      const int j = (njobs > 1 && g >= (uint32_t)a.job[1].seg_begin) + (njobs > 2 && g >= (uint32_t)a.job[2].seg_begin) +
+                    (njobs > 3 && g >= (uint32_t)a.job[3].seg_begin);
       jb[it] = j;
-      blk[it] = load_segment_contig<kBF16>(a.job[j].x, a.job[j].nblocks, g - a.job[j].seg_begin, lane, raw[it]);
+      blk[it] = load_segment_fused<kBF16>(a.job[j].x, (uint32_t)a.job[j].nblocks, g - (uint32_t)a.job[j].seg_begin,
+                                          lane, raw[it]);
     } else {
       raw[it].zero();
       jb[it] = 0;
-      blk[it] = ~0ull;
+      blk[it] = ~0u;
     }
   }
   uint32_t mj[kMaxJobs] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int it = 0; it < kMax; ++it) {
-    float v[16];
-    raw[it].values(v);
-    if (kRHT) rht16(v, mask);
-    bmax[it] = max_abs16(v);
+    if constexpr (kBF16 && !kRHT) {
+      bmax[it] = raw[it].max_abs_bf16();
+    } else {
+      float v[16];
+      raw[it].values(v);
+      if (kRHT) rht16(v, mask);
+      bmax[it] = max_abs16(v);
+    }
 #pragma unroll
     for (int j = 0; j < kMaxJobs; ++j)
       if (jb[it] == j) mj[j] = max(mj[j], bmax[it]);
@@ -439,14 +479,14 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
 #pragma unroll
   for (int it = 0; it < kMax; ++it) {
     const int j = jb[it];
-    if (blk[it] < a.job[j].nblocks) {
+    if (blk[it] < (uint32_t)a.job[j].nblocks) {
       const float st = s_st[j];
       const uint32_t S = block_scale_code(bmax[it], st, 6.0f * st);
       float v[16];
       raw[it].values(v);
       if (kRHT) rht16(v, mask);
-      const uint2 c = encode16<kSR>(v, recip[j][S], 16 * blk[it], a.sr_stream, a.sr_seed);
-      st_stream(a.job[j].codes + 8 * blk[it], c);
+      const uint2 c = encode16<kSR>(v, recip[j][S], (uint64_t)16 * blk[it], a.sr_stream, a.sr_seed);
+      st_stream(a.job[j].codes + (size_t)8 * blk[it], c);
       a.job[j].scales[blk[it]] = (uint8_t)S;
     }
     // Keep blocks from being interleaved by the scheduler: hoisting every
