@@ -63,6 +63,9 @@
 #ifndef NVFP4_GEMM_W8
 #define NVFP4_GEMM_W8 1
 #endif
+#ifndef NVFP4_GEMM_F4_PIPE
+#define NVFP4_GEMM_F4_PIPE 1
+#endif
 #ifndef NVFP4_GEMM_SWIZZLE
 #define NVFP4_GEMM_SWIZZLE 2
 #endif
@@ -148,8 +151,9 @@ __device__ __forceinline__ half8_t decode8(uint32_t codes, _Float16 s) {
 template <int kRows>
 __device__ __forceinline__ void lds_load_operand(const uint8_t *codes_g, const uint8_t *scales_g,
                                                  int64_t rows, int64_t K, int64_t r0, int64_t k0,
-                                                 uint8_t *lds_codes, uint2 *lds_scales) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                                                 uint8_t *lds_codes, uint2 *lds_scales, int tid = -1) {
+  if (tid < 0) tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t kblocks = K / 16;
   constexpr int kCodeLoads = kRows * 4 / kThreads;  // 16-byte chunks per lane
 #pragma unroll
@@ -376,6 +380,51 @@ __device__ __forceinline__ void pipelined_kstep(Stage<kBN> &cur, const Stage<kBN
 // multiply by fl(fl(sA * sB) * alpha) and store, masking the M and N edges.
 // Accumulator v of lane l in a 32x32 tile holds row 8*(v/4) + 4*(l/32) + v%4,
 // column l%32.
+// The pipelined K step for 256 x 256 tiles, whose 256 accumulators leave
+// room for one code buffer and one scale buffer only (two of each spill).
+// The decoded operands are still double-buffered, so every sub-step's MFMAs
+// run while the next sub-step is decoded; the cost is one exposed LDS read
+// latency at each half step.  On entry r holds this step's first-half
+// codes, sc its scales and av/bv sub-step 0; stage `cur` holds this step and
+// `nxt` the next one, landed or in flight.
+template <int kFragN, int kBN>
+__device__ __forceinline__ void pipelined_kstep_lite(Stage<kBN> &cur, const Stage<kBN> &nxt, const TileSrc &t, int kt,
+                                                     int ksteps, const LaneCoord &c, HalfCodes<kFragN> &r,
+                                                     StepScales<kFragN> &sc, half8_t (&av)[kFragM],
+                                                     half8_t (&bv)[kFragN], floatx16 (&acc)[kFragM][kFragN]) {
+  // Opaque copies of the lane coordinates: addresses derived from them are
+  // rebuilt where used instead of being hoisted out of the loop, where they
+  // would take the registers the operands need.
+  LaneCoord cl = c;
+  asm volatile("" : "+v"(cl.r32), "+v"(cl.h));
+  mfma_and_decode<1>(r, sc, av, bv, acc);
+  mfma_and_decode<2>(r, sc, av, bv, acc);
+  mfma_and_decode<3>(r, sc, av, bv, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  read_codes<kFragN>(cur, 1, cl, r);  // the first half's codes are dead
+  mfma_and_decode<4>(r, sc, av, bv, acc);
+  mfma_and_decode<5>(r, sc, av, bv, acc);
+  mfma_and_decode<6>(r, sc, av, bv, acc);
+  mfma_and_decode<7>(r, sc, av, bv, acc);
+  // Every read of `cur` is done: wait for this wave's loads of `nxt`, then
+  // the barrier makes `nxt` visible and frees `cur` for the step after next.
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  read_codes<kFragN>(nxt, 0, cl, r);  // past the last step: stale but in-bounds LDS, never used
+  read_scales<kFragN>(nxt, cl, sc);
+  if (kt + 2 < ksteps) {
+    const int64_t k0 = (int64_t)(kt + 2) * BK;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    lds_load_operand<BM>(t.ac, t.as, t.M, t.K, t.m0, k0, cur.a, cur.as, tid);
+    lds_load_operand<kBN>(t.bc, t.bs, t.N, t.K, t.n0, k0, cur.b, cur.bs, tid);
+  }
+  mfma_and_decode<0>(r, sc, av, bv, acc);
+}
+
 template <int kFragN, bool kBF16Out>
 __device__ __forceinline__ void store_tile(const floatx16 (&acc)[kFragM][kFragN], const GemmArgs &g, int64_t batch,
                                            int64_t wrow0, int64_t wcol0) {
@@ -477,6 +526,28 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
     for (int kt = 0; kt < ksteps; kt += 2) {
       pipelined_kstep<kFragN>(st0, st1, src, kt, ksteps, c, r0, r1, sc0, sc1, av, bv, acc);
       if (kt + 1 < ksteps) pipelined_kstep<kFragN>(st1, st0, src, kt + 1, ksteps, c, r0, r1, sc1, sc0, av, bv, acc);
+    }
+  } else if constexpr (kFast && NVFP4_GEMM_F4_PIPE) {
+    const TileSrc src{ac, as, bc, bs, g.M, g.N, g.K, m0, n0};
+    const LaneCoord c{wm, wn, h, r32};
+    if (ksteps > 0) {
+      lds_load_operand<BM>(ac, as, g.M, g.K, m0, 0, st0.a, st0.as);
+      lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, 0, st0.b, st0.bs);
+      if (ksteps > 1) {
+        lds_load_operand<BM>(ac, as, g.M, g.K, m0, BK, st1.a, st1.as);
+        lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, BK, st1.b, st1.bs);
+      }
+    }
+    __syncthreads();
+    HalfCodes<kFragN> r;
+    StepScales<kFragN> sc;
+    half8_t av[kFragM], bv[kFragN];
+    read_codes<kFragN>(st0, 0, c, r);
+    read_scales<kFragN>(st0, c, sc);
+    decode_substep<0, kFragN>(r, sc, av, bv);
+    for (int kt = 0; kt < ksteps; kt += 2) {
+      pipelined_kstep_lite<kFragN>(st0, st1, src, kt, ksteps, c, r, sc, av, bv, acc);
+      if (kt + 1 < ksteps) pipelined_kstep_lite<kFragN>(st1, st0, src, kt + 1, ksteps, c, r, sc, av, bv, acc);
     }
   } else if constexpr (kFast) {
     // 256 x 256 tiles: the accumulators take all 256 AGPRs, which leaves no
