@@ -123,24 +123,23 @@ struct alignas(16) Stage {
   uint2 bs[kBN];
 };
 
-// Two E4M3 scale bytes (bits 0..6 and 8..14 of w) -> two FP16 scales in one
-// dword.  An E4M3 code c shifted left by 7 and read as FP16 is c's value
-// times 2^-8 (the exponent fields line up; subnormal codes become FP16
-// subnormals), so one packed multiply by 256 gives the exact values.
-__device__ __forceinline__ half2_t scale_pair2(uint32_t w) {
-  const uint32_t spread = __builtin_amdgcn_perm(0u, w, 0x0C010C00u);  // [s0, 0, s1, 0]
-  const half2_t k256 = {(_Float16)256.0f, (_Float16)256.0f};
-  return __builtin_bit_cast(half2_t, spread << 7) * k256;
+// Two E4M3 scale bytes (bits 0..7 and 8..15 of w) -> two FP16 values S * 2^-8
+// in one dword: an E4M3 code shifted left by 7 and read as FP16 is its value
+// times 2^-8 (exponent fields line up; subnormal codes become FP16
+// subnormals).  The converter's scale of 256 supplies the missing 2^8.
+__device__ __forceinline__ half2_t scale_pair_lo(uint32_t w) {
+  return __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, w, 0x0C010C00u) << 7);
 }
 
-// Eight E2M1 codes (element 2j in the low nibble of byte j) times one FP16
-// block scale -> eight FP16 values in element order.
-__device__ __forceinline__ half8_t decode8(uint32_t codes, _Float16 s) {
+// Eight E2M1 codes times (S * 2^-8): the converter at scale 2^8 (exact, a
+// power of two) gives code * 256, and one packed multiply per pair gives
+// code * S, exact in FP16 (at most 6 significant bits, at least 2^-10).
+__device__ __forceinline__ half8_t decode8_s256(uint32_t codes, _Float16 s) {
   const half2_t s2 = {s, s};
-  const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s2;
-  const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s2;
-  const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s2;
-  const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s2;
+  const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * s2;
+  const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * s2;
+  const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * s2;
+  const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * s2;
   return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
@@ -148,7 +147,7 @@ __device__ __forceinline__ half8_t decode8(uint32_t codes, _Float16 s) {
 // wavefront's global_load_lds fills 64 consecutive lane slots, which keeps
 // the row-major [rows][64 B] code and [rows][8 B] scale layout.  Rows past
 // the end are clamped; their products only reach output rows never stored.
-template <int kRows>
+template <int kRows, bool kOff32>
 __device__ __forceinline__ void lds_load_operand(const uint8_t *codes_g, const uint8_t *scales_g,
                                                  int64_t rows, int64_t K, int64_t r0, int64_t k0,
                                                  uint8_t *lds_codes, uint2 *lds_scales, int tid = -1) {
@@ -156,27 +155,55 @@ __device__ __forceinline__ void lds_load_operand(const uint8_t *codes_g, const u
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t kblocks = K / 16;
   constexpr int kCodeLoads = kRows * 4 / kThreads;  // 16-byte chunks per lane
-#pragma unroll
-  for (int i = 0; i < kCodeLoads; ++i) {
-    const int slot = (kCodeLoads * wave + i) * 64;
-    const int p = slot + lane;  // physical chunk: row p/4, position p%4
-    const int row = p >> 2;
-    const int part = (chunk_slot(row, p & 3)) & 3;  // the XOR swizzle is its own inverse
-    const int64_t gr = min(r0 + row, rows - 1);
-    const uint8_t *src = codes_g + gr * (K / 2) + k0 / 2 + 16 * part;
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds_codes + 16 * slot), 16, 0, 0);
-  }
   constexpr int kScaleLoads = (kRows * 2 + kThreads - 1) / kThreads;  // dwords per lane
+  if constexpr (kOff32) {
+    // Operands under 2 GiB with fewer than 2^24 rows and code bytes per row:
+    // 32-bit offsets and 24-bit products.  A code load's lane takes row
+    // 16 (job) + lane / 4, whose swizzle bits (2..3) come from the lane
+    // alone; a scale load's lane takes row 32 (job) + lane / 2.
+    const int last = (int)(rows - 1 - r0);
+    const uint32_t base = (uint32_t)r0, kb2 = (uint32_t)(K / 2), kb16 = (uint32_t)kblocks;
+    const uint32_t part16 = 16u * (uint32_t)(chunk_slot(lane >> 2, lane & 3) & 3);
 #pragma unroll
-  for (int i = 0; i < kScaleLoads; ++i) {
-    const int slot = (kScaleLoads * wave + i) * 64;
-    const int p = slot + lane;
-    if (slot < kRows * 2) {  // wave-uniform
-      const int64_t gr = min(r0 + (p >> 1), rows - 1);
-      const uint8_t *src = scales_g + gr * kblocks + k0 / 16 + 4 * (p & 1);
-      if (p < kRows * 2)
-        __builtin_amdgcn_global_load_lds(src, (lds_void *)(reinterpret_cast<uint8_t *>(lds_scales) + 4 * slot), 4,
-                                         0, 0);
+    for (int i = 0; i < kCodeLoads; ++i) {
+      const int job = kCodeLoads * wave + i;
+      const uint32_t gr = base + (uint32_t)min(16 * job + (lane >> 2), last);
+      const uint8_t *src = codes_g + k0 / 2 + (__umul24(gr, kb2) + part16);
+      __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds_codes + 1024 * job), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kScaleLoads; ++i) {
+      const int job = kScaleLoads * wave + i;
+      if (64 * job < kRows * 2) {  // wave-uniform
+        const uint32_t gr = base + (uint32_t)min(32 * job + (lane >> 1), last);
+        const uint8_t *src = scales_g + k0 / 16 + (__umul24(gr, kb16) + 4u * (uint32_t)(lane & 1));
+        if (64 * job + lane < kRows * 2)
+          __builtin_amdgcn_global_load_lds(src, (lds_void *)(reinterpret_cast<uint8_t *>(lds_scales) + 256 * job),
+                                           4, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kCodeLoads; ++i) {
+      const int slot = (kCodeLoads * wave + i) * 64;
+      const int p = slot + lane;  // physical chunk: row p/4, position p%4
+      const int row = p >> 2;
+      const int part = (chunk_slot(row, p & 3)) & 3;  // the XOR swizzle is its own inverse
+      const int64_t gr = min(r0 + row, rows - 1);
+      const uint8_t *src = codes_g + gr * (K / 2) + k0 / 2 + 16 * part;
+      __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds_codes + 16 * slot), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kScaleLoads; ++i) {
+      const int slot = (kScaleLoads * wave + i) * 64;
+      const int p = slot + lane;
+      if (slot < kRows * 2) {  // wave-uniform
+        const int64_t gr = min(r0 + (p >> 1), rows - 1);
+        const uint8_t *src = scales_g + gr * kblocks + k0 / 16 + 4 * (p & 1);
+        if (p < kRows * 2)
+          __builtin_amdgcn_global_load_lds(src, (lds_void *)(reinterpret_cast<uint8_t *>(lds_scales) + 4 * slot), 4,
+                                           0, 0);
+      }
     }
   }
 }
@@ -266,15 +293,15 @@ __device__ __forceinline__ void read_scales(const Stage<kBN> &st, const LaneCoor
   for (int f = 0; f < kFragM; ++f) {
     const int row = c.wm * 128 + f * 32 + c.r32;
     const uint32_t w = c.h ? st.as[row].y : st.as[row].x;
-    sc.a[f][0] = scale_pair2(w);
-    sc.a[f][1] = scale_pair2(w >> 16);
+    sc.a[f][0] = scale_pair_lo(w);
+    sc.a[f][1] = scale_pair_lo(w >> 16);
   }
 #pragma unroll
   for (int f = 0; f < kFragN; ++f) {
     const int row = c.wn * (32 * kFragN) + f * 32 + c.r32;
     const uint32_t w = c.h ? st.bs[row].y : st.bs[row].x;
-    sc.b[f][0] = scale_pair2(w);
-    sc.b[f][1] = scale_pair2(w >> 16);
+    sc.b[f][0] = scale_pair_lo(w);
+    sc.b[f][1] = scale_pair_lo(w >> 16);
   }
 }
 
@@ -288,9 +315,9 @@ template <int kS, int kFragN>
 __device__ __forceinline__ void decode_substep(const HalfCodes<kFragN> &r, const StepScales<kFragN> &sc,
                                                half8_t (&av)[kFragM], half8_t (&bv)[kFragN]) {
 #pragma unroll
-  for (int f = 0; f < kFragM; ++f) av[f] = decode8(word_at<kS & 3>(r.a[f]), sc.a[f][kS >> 2][(kS >> 1) & 1]);
+  for (int f = 0; f < kFragM; ++f) av[f] = decode8_s256(word_at<kS & 3>(r.a[f]), sc.a[f][kS >> 2][(kS >> 1) & 1]);
 #pragma unroll
-  for (int f = 0; f < kFragN; ++f) bv[f] = decode8(word_at<kS & 3>(r.b[f]), sc.b[f][kS >> 2][(kS >> 1) & 1]);
+  for (int f = 0; f < kFragN; ++f) bv[f] = decode8_s256(word_at<kS & 3>(r.b[f]), sc.b[f][kS >> 2][(kS >> 1) & 1]);
 }
 
 template <int kFragN>
@@ -343,7 +370,7 @@ struct TileSrc {
 // then the next step's first half and scales are read into r0 and sc_nxt,
 // and the step after next is fetched into `cur`, whose reads every wave has
 // completed before the barrier.
-template <int kFragN, int kBN>
+template <int kFragN, bool kOff32, int kBN>
 __device__ __forceinline__ void pipelined_kstep(Stage<kBN> &cur, const Stage<kBN> &nxt, const TileSrc &t, int kt,
                                                 int ksteps, const LaneCoord &c, HalfCodes<kFragN> &r0,
                                                 HalfCodes<kFragN> &r1, const StepScales<kFragN> &sc_cur,
@@ -367,8 +394,8 @@ __device__ __forceinline__ void pipelined_kstep(Stage<kBN> &cur, const Stage<kBN
   read_scales<kFragN>(nxt, c, sc_nxt);
   if (kt + 2 < ksteps) {
     const int64_t k0 = (int64_t)(kt + 2) * BK;
-    lds_load_operand<BM>(t.ac, t.as, t.M, t.K, t.m0, k0, cur.a, cur.as);
-    lds_load_operand<kBN>(t.bc, t.bs, t.N, t.K, t.n0, k0, cur.b, cur.bs);
+    lds_load_operand<BM, kOff32>(t.ac, t.as, t.M, t.K, t.m0, k0, cur.a, cur.as);
+    lds_load_operand<kBN, kOff32>(t.bc, t.bs, t.N, t.K, t.n0, k0, cur.b, cur.bs);
   }
   mfma_and_decode<5>(r1, sc_cur, av, bv, acc);
   mfma_and_decode<6>(r1, sc_cur, av, bv, acc);
@@ -387,7 +414,7 @@ __device__ __forceinline__ void pipelined_kstep(Stage<kBN> &cur, const Stage<kBN
 // latency at each half step.  On entry r holds this step's first-half
 // codes, sc its scales and av/bv sub-step 0; stage `cur` holds this step and
 // `nxt` the next one, landed or in flight.
-template <int kFragN, int kBN>
+template <int kFragN, bool kOff32, int kBN>
 __device__ __forceinline__ void pipelined_kstep_lite(Stage<kBN> &cur, const Stage<kBN> &nxt, const TileSrc &t, int kt,
                                                      int ksteps, const LaneCoord &c, HalfCodes<kFragN> &r,
                                                      StepScales<kFragN> &sc, half8_t (&av)[kFragM],
@@ -419,8 +446,8 @@ __device__ __forceinline__ void pipelined_kstep_lite(Stage<kBN> &cur, const Stag
     const int64_t k0 = (int64_t)(kt + 2) * BK;
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    lds_load_operand<BM>(t.ac, t.as, t.M, t.K, t.m0, k0, cur.a, cur.as, tid);
-    lds_load_operand<kBN>(t.bc, t.bs, t.N, t.K, t.n0, k0, cur.b, cur.bs, tid);
+    lds_load_operand<BM, kOff32>(t.ac, t.as, t.M, t.K, t.m0, k0, cur.a, cur.as, tid);
+    lds_load_operand<kBN, kOff32>(t.bc, t.bs, t.N, t.K, t.n0, k0, cur.b, cur.bs, tid);
   }
   mfma_and_decode<0>(r, sc, av, bv, acc);
 }
@@ -465,7 +492,7 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[kFragM][kFragN]
   }
 }
 
-template <int kFragN, bool kFast, bool kBF16Out>
+template <int kFragN, bool kFast, bool kBF16Out, bool kOff32>
 __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
   constexpr int kBN = 64 * kFragN;
   // Two stages as separate objects: the compiler can then tell a read of one
@@ -509,11 +536,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
     const TileSrc src{ac, as, bc, bs, g.M, g.N, g.K, m0, n0};
     const LaneCoord c{wm, wn, h, r32};
     if (ksteps > 0) {
-      lds_load_operand<BM>(ac, as, g.M, g.K, m0, 0, st0.a, st0.as);
-      lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, 0, st0.b, st0.bs);
+      lds_load_operand<BM, kOff32>(ac, as, g.M, g.K, m0, 0, st0.a, st0.as);
+      lds_load_operand<kBN, kOff32>(bc, bs, g.N, g.K, n0, 0, st0.b, st0.bs);
       if (ksteps > 1) {
-        lds_load_operand<BM>(ac, as, g.M, g.K, m0, BK, st1.a, st1.as);
-        lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, BK, st1.b, st1.bs);
+        lds_load_operand<BM, kOff32>(ac, as, g.M, g.K, m0, BK, st1.a, st1.as);
+        lds_load_operand<kBN, kOff32>(bc, bs, g.N, g.K, n0, BK, st1.b, st1.bs);
       }
     }
     __syncthreads();
@@ -524,18 +551,18 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
     read_scales<kFragN>(st0, c, sc0);
     decode_substep<0, kFragN>(r0, sc0, av, bv);
     for (int kt = 0; kt < ksteps; kt += 2) {
-      pipelined_kstep<kFragN>(st0, st1, src, kt, ksteps, c, r0, r1, sc0, sc1, av, bv, acc);
-      if (kt + 1 < ksteps) pipelined_kstep<kFragN>(st1, st0, src, kt + 1, ksteps, c, r0, r1, sc1, sc0, av, bv, acc);
+      pipelined_kstep<kFragN, kOff32>(st0, st1, src, kt, ksteps, c, r0, r1, sc0, sc1, av, bv, acc);
+      if (kt + 1 < ksteps) pipelined_kstep<kFragN, kOff32>(st1, st0, src, kt + 1, ksteps, c, r0, r1, sc1, sc0, av, bv, acc);
     }
   } else if constexpr (kFast && NVFP4_GEMM_F4_PIPE) {
     const TileSrc src{ac, as, bc, bs, g.M, g.N, g.K, m0, n0};
     const LaneCoord c{wm, wn, h, r32};
     if (ksteps > 0) {
-      lds_load_operand<BM>(ac, as, g.M, g.K, m0, 0, st0.a, st0.as);
-      lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, 0, st0.b, st0.bs);
+      lds_load_operand<BM, kOff32>(ac, as, g.M, g.K, m0, 0, st0.a, st0.as);
+      lds_load_operand<kBN, kOff32>(bc, bs, g.N, g.K, n0, 0, st0.b, st0.bs);
       if (ksteps > 1) {
-        lds_load_operand<BM>(ac, as, g.M, g.K, m0, BK, st1.a, st1.as);
-        lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, BK, st1.b, st1.bs);
+        lds_load_operand<BM, kOff32>(ac, as, g.M, g.K, m0, BK, st1.a, st1.as);
+        lds_load_operand<kBN, kOff32>(bc, bs, g.N, g.K, n0, BK, st1.b, st1.bs);
       }
     }
     __syncthreads();
@@ -546,8 +573,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
     read_scales<kFragN>(st0, c, sc);
     decode_substep<0, kFragN>(r, sc, av, bv);
     for (int kt = 0; kt < ksteps; kt += 2) {
-      pipelined_kstep_lite<kFragN>(st0, st1, src, kt, ksteps, c, r, sc, av, bv, acc);
-      if (kt + 1 < ksteps) pipelined_kstep_lite<kFragN>(st1, st0, src, kt + 1, ksteps, c, r, sc, av, bv, acc);
+      pipelined_kstep_lite<kFragN, kOff32>(st0, st1, src, kt, ksteps, c, r, sc, av, bv, acc);
+      if (kt + 1 < ksteps) pipelined_kstep_lite<kFragN, kOff32>(st1, st0, src, kt + 1, ksteps, c, r, sc, av, bv, acc);
     }
   } else if constexpr (kFast) {
     // 256 x 256 tiles: the accumulators take all 256 AGPRs, which leaves no
@@ -555,8 +582,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
     // step reads its codes from LDS, issues the global->LDS loads of the
     // next step, then decodes and multiplies.
     if (ksteps > 0) {
-      lds_load_operand<BM>(ac, as, g.M, g.K, m0, 0, st0.a, st0.as);
-      lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, 0, st0.b, st0.bs);
+      lds_load_operand<BM, kOff32>(ac, as, g.M, g.K, m0, 0, st0.a, st0.as);
+      lds_load_operand<kBN, kOff32>(bc, bs, g.N, g.K, n0, 0, st0.b, st0.bs);
     }
     __syncthreads();
     for (int kt = 0; kt < ksteps; ++kt) {
@@ -570,8 +597,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
         ca[f][0] = *reinterpret_cast<const uint4 *>(cur.a + 16 * chunk_slot(r, 2 * h));
         ca[f][1] = *reinterpret_cast<const uint4 *>(cur.a + 16 * chunk_slot(r, 2 * h + 1));
         const uint32_t w = h ? cur.as[r].y : cur.as[r].x;
-        sa[f][0] = scale_pair2(w);
-        sa[f][1] = scale_pair2(w >> 16);
+        sa[f][0] = scale_pair_lo(w);
+        sa[f][1] = scale_pair_lo(w >> 16);
       }
 #pragma unroll
       for (int f = 0; f < kFragN; ++f) {
@@ -579,21 +606,21 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
         cb[f][0] = *reinterpret_cast<const uint4 *>(cur.b + 16 * chunk_slot(r, 2 * h));
         cb[f][1] = *reinterpret_cast<const uint4 *>(cur.b + 16 * chunk_slot(r, 2 * h + 1));
         const uint32_t w = h ? cur.bs[r].y : cur.bs[r].x;
-        sb[f][0] = scale_pair2(w);
-        sb[f][1] = scale_pair2(w >> 16);
+        sb[f][0] = scale_pair_lo(w);
+        sb[f][1] = scale_pair_lo(w >> 16);
       }
       // Issued after this step's LDS reads, so no read waits on them.
       if (kt + 1 < ksteps) {
-        lds_load_operand<BM>(ac, as, g.M, g.K, m0, (int64_t)(kt + 1) * BK, nxt.a, nxt.as);
-        lds_load_operand<kBN>(bc, bs, g.N, g.K, n0, (int64_t)(kt + 1) * BK, nxt.b, nxt.bs);
+        lds_load_operand<BM, kOff32>(ac, as, g.M, g.K, m0, (int64_t)(kt + 1) * BK, nxt.a, nxt.as);
+        lds_load_operand<kBN, kOff32>(bc, bs, g.N, g.K, n0, (int64_t)(kt + 1) * BK, nxt.b, nxt.bs);
       }
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         half8_t av[kFragM], bv[kFragN];
 #pragma unroll
-        for (int f = 0; f < kFragM; ++f) av[f] = decode8(word_of(ca[f][s >> 2], s & 3), sa[f][s >> 2][(s >> 1) & 1]);
+        for (int f = 0; f < kFragM; ++f) av[f] = decode8_s256(word_of(ca[f][s >> 2], s & 3), sa[f][s >> 2][(s >> 1) & 1]);
 #pragma unroll
-        for (int f = 0; f < kFragN; ++f) bv[f] = decode8(word_of(cb[f][s >> 2], s & 3), sb[f][s >> 2][(s >> 1) & 1]);
+        for (int f = 0; f < kFragN; ++f) bv[f] = decode8_s256(word_of(cb[f][s >> 2], s & 3), sb[f][s >> 2][(s >> 1) & 1]);
         mfma_substep<kFragN>(acc, av, bv);
       }
       // The next stage must have landed before the barrier.  The scheduling
@@ -627,8 +654,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
         ca[f][0] = *reinterpret_cast<const uint4 *>(cur.a + 16 * chunk_slot(r, 2 * h));
         ca[f][1] = *reinterpret_cast<const uint4 *>(cur.a + 16 * chunk_slot(r, 2 * h + 1));
         const uint32_t w = h ? cur.as[r].y : cur.as[r].x;
-        sa[f][0] = scale_pair2(w);
-        sa[f][1] = scale_pair2(w >> 16);
+        sa[f][0] = scale_pair_lo(w);
+        sa[f][1] = scale_pair_lo(w >> 16);
       }
 #pragma unroll
       for (int f = 0; f < kFragN; ++f) {
@@ -636,8 +663,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
         cb[f][0] = *reinterpret_cast<const uint4 *>(cur.b + 16 * chunk_slot(r, 2 * h));
         cb[f][1] = *reinterpret_cast<const uint4 *>(cur.b + 16 * chunk_slot(r, 2 * h + 1));
         const uint32_t w = h ? cur.bs[r].y : cur.bs[r].x;
-        sb[f][0] = scale_pair2(w);
-        sb[f][1] = scale_pair2(w >> 16);
+        sb[f][0] = scale_pair_lo(w);
+        sb[f][1] = scale_pair_lo(w >> 16);
       }
       if (more) {
         la.load(ac, as, g.M, g.K, m0, (int64_t)(kt + 1) * BK);
@@ -647,9 +674,9 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
       for (int s = 0; s < 8; ++s) {
         half8_t av[kFragM], bv[kFragN];
 #pragma unroll
-        for (int f = 0; f < kFragM; ++f) av[f] = decode8(word_of(ca[f][s >> 2], s & 3), sa[f][s >> 2][(s >> 1) & 1]);
+        for (int f = 0; f < kFragM; ++f) av[f] = decode8_s256(word_of(ca[f][s >> 2], s & 3), sa[f][s >> 2][(s >> 1) & 1]);
 #pragma unroll
-        for (int f = 0; f < kFragN; ++f) bv[f] = decode8(word_of(cb[f][s >> 2], s & 3), sb[f][s >> 2][(s >> 1) & 1]);
+        for (int f = 0; f < kFragN; ++f) bv[f] = decode8_s256(word_of(cb[f][s >> 2], s & 3), sb[f][s >> 2][(s >> 1) & 1]);
         mfma_substep<kFragN>(acc, av, bv);
       }
       if (more) {
@@ -816,26 +843,6 @@ struct W8Loader {
   }
 };
 
-// Two E4M3 scale bytes (bits 0..7 and 8..15 of w) -> two FP16 values S * 2^-8
-// in one dword: an E4M3 code shifted left by 7 and read as FP16 is its value
-// times 2^-8 (exponent fields line up; subnormal codes become FP16
-// subnormals).  The converter's scale of 256 supplies the missing 2^8.
-__device__ __forceinline__ half2_t scale_pair_lo(uint32_t w) {
-  return __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, w, 0x0C010C00u) << 7);
-}
-
-// Eight E2M1 codes times (S * 2^-8): the converter at scale 2^8 (exact, a
-// power of two) gives code * 256, and one packed multiply per pair gives
-// code * S, exact in FP16 (at most 6 significant bits, at least 2^-10).
-__device__ __forceinline__ half8_t decode8_s256(uint32_t codes, _Float16 s) {
-  const half2_t s2 = {s, s};
-  const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * s2;
-  const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * s2;
-  const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * s2;
-  const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * s2;
-  return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
 // The MFMAs of one K step for one wavefront's 128 x 96 region.
 template <int kBM, int kBN>
 __device__ __forceinline__ void w8_compute(const W8Stage<kBM, kBN> &st, int arow, int brow, int h, int qa, int qb,
@@ -985,16 +992,20 @@ __global__ __launch_bounds__(kW8Threads) void gemm_nvfp4_w8_kernel(GemmArgs g) {
 }
 
 template <int kFragN>
-hipError_t launch_tiles(const GemmArgs &g, int64_t batch, bool fast, bool bf16, hipStream_t s) {
+hipError_t launch_tiles(const GemmArgs &g, int64_t batch, bool fast, bool bf16, bool off32, hipStream_t s) {
   const dim3 grid((unsigned)(g.tiles_m * g.tiles_n), (unsigned)batch);
-  if (fast && bf16)
-    hipLaunchKernelGGL((gemm_nvfp4_kernel<kFragN, true, true>), grid, dim3(kThreads), 0, s, g);
-  else if (fast)
-    hipLaunchKernelGGL((gemm_nvfp4_kernel<kFragN, true, false>), grid, dim3(kThreads), 0, s, g);
-  else if (bf16)
-    hipLaunchKernelGGL((gemm_nvfp4_kernel<kFragN, false, true>), grid, dim3(kThreads), 0, s, g);
-  else
-    hipLaunchKernelGGL((gemm_nvfp4_kernel<kFragN, false, false>), grid, dim3(kThreads), 0, s, g);
+  const dim3 block(kThreads);
+  if (fast && off32) {
+    if (bf16) hipLaunchKernelGGL((gemm_nvfp4_kernel<kFragN, true, true, true>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((gemm_nvfp4_kernel<kFragN, true, false, true>), grid, block, 0, s, g);
+  } else if (fast) {
+    if (bf16) hipLaunchKernelGGL((gemm_nvfp4_kernel<kFragN, true, true, false>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((gemm_nvfp4_kernel<kFragN, true, false, false>), grid, block, 0, s, g);
+  } else if (bf16) {
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<kFragN, false, true, false>), grid, block, 0, s, g);
+  } else {
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<kFragN, false, false, false>), grid, block, 0, s, g);
+  }
   return hipGetLastError();
 }
 
@@ -1080,9 +1091,9 @@ nvfp4_status launch_gemm(const GemmProblem &p, hipStream_t s) {
   hipError_t e;
   if (tp.kind == 10) e = launch_w8<4, 2>(g, p.batch, p.c_bf16, s);
   else if (tp.kind == 11) e = launch_w8<2, 4>(g, p.batch, p.c_bf16, s);
-  else if (tp.kind == 4) e = launch_tiles<4>(g, p.batch, fast, p.c_bf16, s);
-  else if (tp.kind == 3) e = launch_tiles<3>(g, p.batch, fast, p.c_bf16, s);
-  else e = launch_tiles<2>(g, p.batch, fast, p.c_bf16, s);
+  else if (tp.kind == 4) e = launch_tiles<4>(g, p.batch, fast, p.c_bf16, small, s);
+  else if (tp.kind == 3) e = launch_tiles<3>(g, p.batch, fast, p.c_bf16, small, s);
+  else e = launch_tiles<2>(g, p.batch, fast, p.c_bf16, small, s);
   return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 
