@@ -25,19 +25,18 @@
 // i.e. one scale block (4h + s/2) per lane.  A and B use the same
 // assignment, so each K index meets its partner once.
 //
-// The decode is the VALU cost: the FP4 -> FP16 converter issues at about half
-// the rate of a plain VALU instruction, so decoding one fragment's sub-step
-// (8 elements per lane) costs about as much issue time as 1.5 MFMAs, and with
-// one wavefront per SIMD it only overlaps the matrix pipe when it sits
-// between MFMAs of other operands.  Three main loops:
+// The decode is the VALU cost (a convert and a packed multiply per two
+// elements), and with one wavefront per SIMD it only overlaps the matrix
+// pipe when it sits between MFMAs of other operands.  Three main loops:
 //  * K % 128 == 0, tiles 256 x 192 / 256 x 128: software pipelined.  The next
 //    sub-step is decoded while the current one's MFMAs run (grouped one MFMA
 //    to a few VALU instructions), codes are read from LDS half a step ahead,
 //    and global_load_lds fills the stage of the step after next, so global
 //    latency has a whole step and LDS latency half a step to hide.
-//  * K % 128 == 0, tiles 256 x 256: the accumulators fill the AGPR file, so
-//    a step reads its codes from LDS, issues the next step's global_load_lds
-//    (into the idle stage, no VGPRs), then decodes and multiplies.
+//  * K % 128 == 0, tiles 256 x 256: the accumulators fill the AGPR file,
+//    which leaves room for double-buffered decoded operands but for one code
+//    and one scale buffer only: the same overlap of decode and MFMAs, with
+//    each half step's codes read once the previous half's are dead.
 //  * Other K: register-staged loads with the K tail read as zero codes and
 //    scales (zero products).
 // A second kernel runs two wavefronts per SIMD (8 per workgroup, 512 x 192
