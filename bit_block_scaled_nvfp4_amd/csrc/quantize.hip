@@ -187,6 +187,33 @@ __device__ __forceinline__ uint32_t load_amax(const QuantCtrl *ctrl) {
   return m;
 }
 
+// Single-pass grid barrier, thread 0 of each workgroup: arrive at epoch e
+// and wait for its release.  The last workgroup of each slot (workgroups
+// with index = slot mod 8) bumps `top`; the last of those publishes e + 1.
+// All control words are device-scope atomics at the coherence point, so
+// relaxed ordering plus the caller's explicit completion waits suffice
+// (acquire/release would flush and invalidate the L2 on every poll).  The
+// wait is bounded; on expiry the timeout word is set and the kernel still
+// finishes.
+__device__ __forceinline__ void fused_arrive_wait(QuantCtrl *ctrl, uint32_t e, int slot) {
+  const unsigned n_slots = min(gridDim.x, 8u);
+  const unsigned long long in_slot = gridDim.x / 8 + ((unsigned)slot < gridDim.x % 8 ? 1 : 0);
+  const unsigned long long old =
+      __hip_atomic_fetch_add(&ctrl->arrive[slot].v, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((old + 1) % in_slot == 0) {
+    const unsigned long long t = __hip_atomic_fetch_add(&ctrl->top.v, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((t + 1) % n_slots == 0) atomic_store_dev(&ctrl->release.v, (unsigned long long)e + 1);
+  }
+  for (uint32_t spin = 0;; ++spin) {
+    if (atomic_load_dev(&ctrl->release.v) > e) break;
+    if (spin >= kSpinLimit) {
+      atomic_store_dev(&ctrl->timeout, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
 // Workgroup max -> one atomicMax per workgroup into slot blockIdx mod 8
 // (two-pass amax kernels).
 __device__ __forceinline__ void block_amax_commit(uint32_t m, QuantCtrl *ctrl) {
@@ -437,25 +464,7 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
                                                    __HIP_MEMORY_SCOPE_AGENT);
       wait_for(prev);  // the max is performed before this workgroup counts as arrived
     }
-    // Arrive: the last workgroup of each slot bumps `top`; the last of those
-    // releases the epoch.  Slot i holds the workgroups with index = i mod 8.
-    const unsigned n_slots = min(gridDim.x, 8u);
-    const unsigned long long in_slot = gridDim.x / 8 + ((unsigned)slot < gridDim.x % 8 ? 1 : 0);
-    const unsigned long long old =
-        __hip_atomic_fetch_add(&ctrl->arrive[slot].v, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((old + 1) % in_slot == 0) {
-      const unsigned long long t =
-          __hip_atomic_fetch_add(&ctrl->top.v, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((t + 1) % n_slots == 0) atomic_store_dev(&ctrl->release.v, (unsigned long long)e + 1);
-    }
-    for (uint32_t spin = 0;; ++spin) {
-      if (atomic_load_dev(&ctrl->release.v) > e) break;
-      if (spin >= kSpinLimit) {
-        atomic_store_dev(&ctrl->timeout, 1u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
+    fused_arrive_wait(ctrl, e, slot);
     for (int j = 0; j < njobs; ++j) {
       uint32_t am = 0;
 #pragma unroll
@@ -720,6 +729,131 @@ __global__ __launch_bounds__(kThreads) void col_encode_kernel(ColArgs a) {
   encode_finish(a.ctrl, a.tensor_scale, st);
 }
 
+// Single-pass transposing quantize (BF16): one 1024-thread workgroup per CU,
+// each covering 1024 input rows x 128 columns, i.e. 64 x 16 units of 16 rows
+// x 8 columns, one unit per thread held in registers (64 dwords).  Phase 1
+// takes the eight column blocks' maxima (after the transform), then the grid
+// barrier of the row kernel yields the tensor max; phase 2 re-derives each
+// column block from the held words and encodes it exactly as
+// col_encode_kernel does, staging the tile's codes in LDS so each transposed
+// row gets 512 contiguous bytes.  The input is read once.
+constexpr int kColFusedThreads = 1024;
+constexpr int kColFusedRB = 64;  // row blocks per tile
+constexpr int kColFusedCG = 16;  // column groups per tile
+
+template <bool kRHT, bool kSR>
+__global__ __launch_bounds__(kColFusedThreads) void col_fused_kernel(ColArgs a) {
+  __shared__ float recip[128];
+  __shared__ uint2 tile_codes[kColFusedCG * 8][kColFusedRB + 1];
+  __shared__ uint8_t tile_scales[kColFusedCG * 8][kColFusedRB + 4];
+  __shared__ uint32_t part[kColFusedThreads / 64];
+  __shared__ uint32_t s_epoch;
+  __shared__ float s_st;
+  QuantCtrl *ctrl = a.ctrl;
+  const int slot = blockIdx.x & 7;
+  // The epoch cannot advance before this workgroup arrives: race free.
+  if (threadIdx.x == 0) s_epoch = (uint32_t)atomic_load_dev(&ctrl->release.v);
+  const uint32_t mask = kRHT ? rht_sign_mask(a.rht_seed) : 0u;
+
+  const int64_t bid = blockIdx.x;
+  const int64_t tc = bid % a.tiles_c, trb = bid / a.tiles_c;
+  const int64_t tr = trb % a.tiles_r, b = trb / a.tiles_r;
+  const int cgl = threadIdx.x % kColFusedCG, rbl = threadIdx.x / kColFusedCG;
+  const int64_t cg = tc * kColFusedCG + cgl, rb = tr * kColFusedRB + rbl;
+  const bool valid = rb < a.R / 16 && 8 * cg < a.C;
+
+  // Phase 1: load the unit, block maxima of its (transformed) columns.
+  ColTile<true> t;
+  if (valid) {
+    col_load<true>(a, b, rb, cg, t);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t.w[j][i] = 0u;
+  }
+  uint32_t bm[8];
+  uint32_t m = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = t.at(j, e);
+    if (kRHT) rht16(v, mask);
+    bm[e] = max_abs16(v);  // columns past C hold zeros: maximum 0
+    m = max(m, bm[e]);
+    // One column's unpacked values at a time: the unit's 64 words and the
+    // eight maxima are what the register budget holds across the barrier.
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t e = s_epoch;
+    if (blockIdx.x == 0) {  // slots of the next epoch: unused since the call before this one ended
+#pragma unroll
+      for (int i = 0; i < 8; ++i) atomic_store_dev(&ctrl->amax[(e + 1) & 1][i].v, 0u);
+    }
+    uint32_t wm = part[0];
+    for (int w = 1; w < kColFusedThreads / 64; ++w) wm = max(wm, part[w]);
+    const uint32_t prev =
+        __hip_atomic_fetch_max(&ctrl->amax[e & 1][slot].v, wm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_for(prev);  // the max is performed before this workgroup counts as arrived
+    fused_arrive_wait(ctrl, e, slot);
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = max(am, atomic_load_dev(&ctrl->amax[e & 1][i].v));
+    s_st = __uint_as_float(am) / 2688.0f;
+  }
+  __syncthreads();
+  const float st = s_st;
+  const float d6 = 6.0f * st;
+  build_recip_table(recip, st);
+  __syncthreads();
+
+  // Phase 2: encode from registers into the LDS tile.  The words are hidden
+  // from value numbering so that phase 1's unpacked values are recomputed
+  // here rather than kept alive across the barrier.
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(t.w[j][i]));
+  if (valid) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t c = 8 * cg + e;  // row of the transposed view
+      if (c >= a.C) break;
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = t.at(j, e);
+      if (kRHT) rht16(v, mask);
+      const uint32_t S = block_scale_code(bm[e], st, d6);
+      const int64_t vrow = b * a.C + c;  // row index in the [batch*C][R] view
+      tile_codes[cgl * 8 + e][rbl] = encode16<kSR>(v, recip[S], (uint64_t)(vrow * a.R + 16 * rb), a.sr_stream,
+                                                   a.sr_seed);
+      tile_scales[cgl * 8 + e][rbl] = (uint8_t)S;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __syncthreads();
+  // Write out: 128 transposed rows x 64 row blocks of 8 code bytes and one
+  // scale byte; consecutive threads take consecutive row blocks of a row.
+  const int64_t RB = a.R / 16;
+  const int64_t rb_n = min((int64_t)kColFusedRB, RB - tr * kColFusedRB);
+  for (int i = threadIdx.x; i < kColFusedCG * 8 * kColFusedRB; i += kColFusedThreads) {
+    const int tcol = i / kColFusedRB, trbl = i % kColFusedRB;
+    const int64_t c = tc * kColFusedCG * 8 + tcol;
+    if (c < a.C && trbl < rb_n) {
+      const int64_t vrow = b * a.C + c;
+      const int64_t r = tr * kColFusedRB + trbl;
+      st_stream(a.codes + vrow * (a.R / 2) + 8 * r, tile_codes[tcol][trbl]);
+      a.scales[vrow * RB + r] = tile_scales[tcol][trbl];
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.tensor_scale = st;
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -812,8 +946,35 @@ hipError_t dispatch_row(const RowArgs &a, bool rht, bool sr, bool contig, hipStr
   return sr ? run_row<kBF16, false, true>(a, contig, s) : run_row<kBF16, false, false>(a, contig, s);
 }
 
+// Single-pass transposing quantize if the grid of 1024-row x 128-column
+// tiles fits one workgroup per CU (BF16 only: an FP32 unit would not fit the
+// register budget); returns false (nothing launched) otherwise.
+template <bool kRHT, bool kSR>
+bool try_col_fused(ColArgs a, hipStream_t s, hipError_t &err) {
+  const int cus = cu_count();
+  if (cus <= 0) return false;
+  auto kernel = col_fused_kernel<kRHT, kSR>;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kColFusedThreads, 0) != hipSuccess || per_cu < 1)
+    return false;
+  a.tiles_r = (a.R / 16 + kColFusedRB - 1) / kColFusedRB;
+  a.tiles_c = (a.C + 8 * kColFusedCG - 1) / (8 * kColFusedCG);
+  const int64_t grid = a.batch * a.tiles_r * a.tiles_c;
+  if (grid < 1 || grid > (int64_t)cus) return false;
+  // A plain launch: with at most one workgroup per CU every workgroup
+  // becomes resident, so the grid barrier completes (bounded wait besides).
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kColFusedThreads), 0, s, a);
+  err = hipGetLastError();
+  return err == hipSuccess;
+}
+
 template <bool kBF16, bool kRHT, bool kSR>
 hipError_t run_col(const ColArgs &a, hipStream_t s) {
+  if constexpr (kBF16) {
+    hipError_t err = hipSuccess;
+    if (!NVFP4_FUSED_DISABLE && try_col_fused<kRHT, kSR>(a, s, err)) return hipSuccess;
+    (void)hipGetLastError();
+  }
   const uint64_t g = (uint64_t)(a.batch * a.tiles_r * a.tiles_c);
   if (g > 0x7FFFFFFFull) return hipErrorInvalidValue;
   hipLaunchKernelGGL((col_amax_kernel<kBF16, kRHT>), dim3((unsigned)g), dim3(kThreads), 0, s, a);

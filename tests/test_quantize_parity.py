@@ -130,6 +130,16 @@ def test_single_pass_and_two_pass_share_a_workspace():
     assert int(ws[part0:part0 + 8 * 64].sum().item()) == 0
 
 
+@pytest.mark.parametrize("rows", [8192, 16384])
+def test_transposing_single_pass_and_two_pass(rows):
+    """Transposing BF16 quantize with RHT + SR: 8192 x 4096 fills the
+    single-pass kernel's grid exactly (256 tiles of 1024 x 128); 16384 x 4096
+    needs 512 tiles and takes the two-pass kernels.  Both bit-exact."""
+    x = (_input((rows, 4096), 50 + rows // 8192, "f32") * 0.01).to(torch.bfloat16)
+    kw = dict(axis=O.ALONG_ROWS, rounding=O.SR, sr_seed=0x5EED0003, sr_stream=3, rht=True, rht_seed=0x4AD40004)
+    assert_quant_equal(to_oracle_view(gpu_quant(x, **kw)), oracle_quant(x, **kw), f"{rows}x4096 transposed")
+
+
 @pytest.mark.parametrize("name", ["fprop_3b"])
 def test_quantize_fprop_full_size(name):
     t = W.fprop_3b()
