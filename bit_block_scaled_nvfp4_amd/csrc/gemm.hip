@@ -142,6 +142,25 @@ __device__ __forceinline__ half8_t decode8_s256(uint32_t codes, _Float16 s) {
   return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// global_load_lds of 16 / 4 bytes per lane into the 64 consecutive lane
+// slots at LDS byte address `lds` (wavefront-uniform, through M0), from the
+// scalar base `base` plus the lane's 32-bit offset.  Written as assembly so
+// that the compiler does not track these loads: its own waits for loads that
+// write LDS drain all of them before unrelated LDS reads.  Every kernel that
+// uses it waits for these loads explicitly (s_waitcnt vmcnt) before the
+// barrier that publishes a stage, and issues them only after its last read
+// of the stage they refill.  M0 is set in the same statement; nothing else
+// in these kernels keeps a value in M0 (checked in the generated code).
+template <int kBytes>
+__device__ __forceinline__ void dma(const uint8_t *base, uint32_t off, uint32_t lds) {
+  if constexpr (kBytes == 16)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
+                 : "memory");
+}
+
 // Direct global -> LDS loads of one operand's K step (K % 128 == 0): each
 // wavefront's global_load_lds fills 64 consecutive lane slots, which keeps
 // the row-major [rows][64 B] code and [rows][8 B] scale layout.  Rows past
@@ -163,22 +182,21 @@ __device__ __forceinline__ void lds_load_operand(const uint8_t *codes_g, const u
     const int last = (int)(rows - 1 - r0);
     const uint32_t base = (uint32_t)r0, kb2 = (uint32_t)(K / 2), kb16 = (uint32_t)kblocks;
     const uint32_t part16 = 16u * (uint32_t)(chunk_slot(lane >> 2, lane & 3) & 3);
+    const uint32_t lds_codes_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_codes);
+    const uint32_t lds_scales_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_scales);
 #pragma unroll
     for (int i = 0; i < kCodeLoads; ++i) {
       const int job = kCodeLoads * wave + i;
       const uint32_t gr = base + (uint32_t)min(16 * job + (lane >> 2), last);
-      const uint8_t *src = codes_g + k0 / 2 + (__umul24(gr, kb2) + part16);
-      __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds_codes + 1024 * job), 16, 0, 0);
+      dma<16>(codes_g + k0 / 2, __umul24(gr, kb2) + part16, lds_codes_base + 1024u * job);
     }
 #pragma unroll
     for (int i = 0; i < kScaleLoads; ++i) {
       const int job = kScaleLoads * wave + i;
       if (64 * job < kRows * 2) {  // wave-uniform
         const uint32_t gr = base + (uint32_t)min(32 * job + (lane >> 1), last);
-        const uint8_t *src = scales_g + k0 / 16 + (__umul24(gr, kb16) + 4u * (uint32_t)(lane & 1));
         if (64 * job + lane < kRows * 2)
-          __builtin_amdgcn_global_load_lds(src, (lds_void *)(reinterpret_cast<uint8_t *>(lds_scales) + 256 * job),
-                                           4, 0, 0);
+          dma<4>(scales_g + k0 / 16, __umul24(gr, kb16) + 4u * (uint32_t)(lane & 1), lds_scales_base + 256u * job);
       }
     }
   } else {
@@ -542,6 +560,9 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
         lds_load_operand<kBN, kOff32>(bc, bs, g.N, g.K, n0, BK, st1.b, st1.bs);
       }
     }
+    // Stage loads issued as assembly are not seen by the compiler's own
+    // wait before a barrier: wait for them explicitly.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     HalfCodes<kFragN> r0, r1;
     StepScales<kFragN> sc0, sc1;  // scales of even / odd steps
@@ -564,6 +585,9 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
         lds_load_operand<kBN, kOff32>(bc, bs, g.N, g.K, n0, BK, st1.b, st1.bs);
       }
     }
+    // Stage loads issued as assembly are not seen by the compiler's own
+    // wait before a barrier: wait for them explicitly.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     HalfCodes<kFragN> r;
     StepScales<kFragN> sc;
@@ -584,6 +608,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
       lds_load_operand<BM, kOff32>(ac, as, g.M, g.K, m0, 0, st0.a, st0.as);
       lds_load_operand<kBN, kOff32>(bc, bs, g.N, g.K, n0, 0, st0.b, st0.bs);
     }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // assembly stage loads: see above
     __syncthreads();
     for (int kt = 0; kt < ksteps; ++kt) {
       const Stage<kBN> &cur = (kt & 1) ? st1 : st0;
@@ -740,24 +765,6 @@ struct W8Loader {
   const uint8_t *ac, *as, *bc, *bs;
   int64_t M, N, m0, n0;
   uint32_t kb2, kb16;  // bytes per code row, per scale row
-
-  // global_load_lds of 16 / 4 bytes per lane into the 64 consecutive lane
-  // slots at LDS byte address `lds` (wavefront-uniform, through M0), from the
-  // scalar base `base` plus the lane's 32-bit offset.  Written as assembly so
-  // that the compiler does not track these loads: its own waits for loads
-  // that write LDS drain all of them before unrelated LDS reads.  The kernel
-  // waits for them explicitly (wait_oldest, then the barrier).  M0 is set in
-  // the same statement, and nothing else in this kernel keeps a value in M0.
-  template <int kBytes>
-  __device__ __forceinline__ static void dma(const uint8_t *base, uint32_t off, uint32_t lds) {
-    if constexpr (kBytes == 16)
-      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
-                   "s"(lds)
-                   : "memory");
-    else
-      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
-                   : "memory");
-  }
 
   // Byte offsets of the stage members (W8Stage has no padding between them).
   static constexpr uint32_t kOffB = kBM * kRowBytes, kOffAs = (kBM + kBN) * kRowBytes,
