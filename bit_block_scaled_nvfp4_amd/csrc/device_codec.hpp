@@ -147,6 +147,17 @@ __device__ __forceinline__ uint32_t sr_word(const u32x4 &r, int j) {
 }
 
 // ---------------------------------------------------------------------------
+// Lane-pair exchange
+// ---------------------------------------------------------------------------
+
+// The value of the other lane of the pair (2k, 2k + 1): a DPP quad
+// permutation [1, 0, 3, 2], i.e. a VALU move with no LDS traffic.
+__device__ __forceinline__ uint32_t lane_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float lane_xor1(float v) { return __uint_as_float(lane_xor1(__float_as_uint(v))); }
+
+// ---------------------------------------------------------------------------
 // Random Hadamard transform on 16 values held by one lane
 // ---------------------------------------------------------------------------
 
@@ -188,7 +199,7 @@ __device__ __forceinline__ void rht16_pair(float (&v)[8], uint32_t mask, bool od
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float p = __shfl_xor(v[j], 1);
+    const float p = lane_xor1(v[j]);
     v[j] = odd ? (p - v[j]) : (v[j] + p);
   }
 #pragma unroll

@@ -299,62 +299,71 @@ __device__ __forceinline__ int64_t row_block_offset(const RowArgs &a, uint64_t b
 // 16-byte loads per lane (chunks lane and 64 + lane), after which each even /
 // odd lane pair swaps one half so that even lane 2k owns block 64 seg + k and
 // odd lane 2k+1 owns block 64 seg + 32 + k.  Otherwise lane l owns block
-// 64 seg + l and loads it directly.  Returns the lane's block index.
-// kStream: non-temporal loads (data read once); the two-pass amax kernel
-// uses cached loads instead so the encode pass can re-read from the
-// Infinity Cache.
-template <bool kBF16, bool kContig, bool kStream = true>
-__device__ __forceinline__ uint64_t load_segment(const RowArgs &a, uint64_t seg, int lane, RawBlock<kBF16> &raw) {
-  if constexpr (kBF16 && kContig) {
-    const uint4 *p = static_cast<const uint4 *>(a.x);
-    const uint64_t nchunks = 2 * a.nblocks;
-    const uint64_t c0 = seg * 128 + lane, c1 = c0 + 64;
-    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    const uint4 x0 = c0 < nchunks ? (kStream ? ld_stream(p + c0) : p[c0]) : zero;
-    const uint4 x1 = c1 < nchunks ? (kStream ? ld_stream(p + c1) : p[c1]) : zero;
-    const bool odd = lane & 1;
-    const uint4 send = odd ? x0 : x1;
-    const uint4 recv = make_uint4(__shfl_xor(send.x, 1), __shfl_xor(send.y, 1), __shfl_xor(send.z, 1),
-                                  __shfl_xor(send.w, 1));
-    const uint4 lo = odd ? recv : x0, hi = odd ? x1 : recv;
-    raw.w[0] = lo.x; raw.w[1] = lo.y; raw.w[2] = lo.z; raw.w[3] = lo.w;
-    raw.w[4] = hi.x; raw.w[5] = hi.y; raw.w[6] = hi.z; raw.w[7] = hi.w;
-    return seg * 64 + (uint64_t)((lane & 1) * 32 + (lane >> 1));
-  } else {
-    const uint64_t blk = seg * 64 + lane;
-    if (blk < a.nblocks) raw.template load<kStream>(a.x, row_block_offset<kContig>(a, blk));
-    else raw.zero();
-    return blk;
-  }
+// 64 seg + l and loads it directly.
+//
+// Loading is split in two so that a wavefront can have all of its segments'
+// loads in flight before it waits for the first: issue_* only computes
+// addresses and issues loads, finish_* (after the data arrived) does the lane
+// exchange and returns the lane's block index.  Out-of-range chunks and
+// blocks are not branched around (a branch whose other side writes the same
+// registers makes the compiler wait for each load in turn): their indices
+// are clamped to the last valid one, and the caller ignores blocks whose
+// index is past the end.  kStream: non-temporal loads (data read once); the
+// two-pass amax kernel uses cached loads instead so the encode pass can
+// re-read from the Infinity Cache.
+struct SegChunks {
+  uint4 c0, c1;
+};
+
+template <bool kStream, typename Idx>
+__device__ __forceinline__ SegChunks issue_segment_bf16(const void *x, Idx nchunks, Idx seg, int lane) {
+  const uint4 *p = static_cast<const uint4 *>(x);
+  const Idx last = nchunks - 1;
+  const Idx c0 = seg * 128 + (Idx)lane, c1 = c0 + 64;
+  const uint4 *p0 = p + (c0 < last ? c0 : last), *p1 = p + (c1 < last ? c1 : last);
+  SegChunks r;
+  r.c0 = kStream ? ld_stream(p0) : *p0;
+  r.c1 = kStream ? ld_stream(p1) : *p1;
+  return r;
 }
 
-// load_segment for a contiguous tensor in the single-pass kernel, whose
-// capacity (tens of millions of elements) keeps every segment, chunk and
-// block index within 32 bits: the same loads and lane exchange as
-// load_segment, with 32-bit bounds arithmetic.
-template <bool kBF16>
-__device__ __forceinline__ uint32_t load_segment_fused(const void *x, uint32_t nblocks, uint32_t seg, int lane,
-                                                       RawBlock<kBF16> &raw) {
-  if constexpr (kBF16) {
-    const uint4 *p = static_cast<const uint4 *>(x);
-    const uint32_t nchunks = 2 * nblocks;
-    const uint32_t c0 = seg * 128 + lane, c1 = c0 + 64;
-    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    const uint4 x0 = c0 < nchunks ? ld_stream(p + c0) : zero;
-    const uint4 x1 = c1 < nchunks ? ld_stream(p + c1) : zero;
-    const bool odd = lane & 1;
-    const uint4 send = odd ? x0 : x1;
-    const uint4 recv = make_uint4(__shfl_xor(send.x, 1), __shfl_xor(send.y, 1), __shfl_xor(send.z, 1),
-                                  __shfl_xor(send.w, 1));
-    const uint4 lo = odd ? recv : x0, hi = odd ? x1 : recv;
-    raw.w[0] = lo.x; raw.w[1] = lo.y; raw.w[2] = lo.z; raw.w[3] = lo.w;
-    raw.w[4] = hi.x; raw.w[5] = hi.y; raw.w[6] = hi.z; raw.w[7] = hi.w;
-    return seg * 64 + (uint32_t)((lane & 1) * 32 + (lane >> 1));
+template <typename Idx>
+__device__ __forceinline__ Idx finish_segment_bf16(const SegChunks &s, Idx seg, int lane, RawBlock<true> &raw) {
+  const bool odd = lane & 1;
+  const uint4 send = odd ? s.c0 : s.c1;
+  const uint4 recv = make_uint4(lane_xor1(send.x), lane_xor1(send.y), lane_xor1(send.z), lane_xor1(send.w));
+  const uint4 lo = odd ? recv : s.c0, hi = odd ? s.c1 : recv;
+  raw.w[0] = lo.x; raw.w[1] = lo.y; raw.w[2] = lo.z; raw.w[3] = lo.w;
+  raw.w[4] = hi.x; raw.w[5] = hi.y; raw.w[6] = hi.z; raw.w[7] = hi.w;
+  return seg * 64 + (Idx)((lane & 1) * 32 + (lane >> 1));
+}
+
+// Segment of any other layout (FP32, or rows with a stride): lane l loads
+// block 64 seg + l whole, clamped to the last block.
+template <bool kBF16, bool kContig, bool kStream>
+__device__ __forceinline__ uint64_t issue_segment_direct(const RowArgs &a, uint64_t seg, int lane,
+                                                         RawBlock<kBF16> &raw) {
+  const uint64_t blk = seg * 64 + lane;
+  raw.template load<kStream>(a.x, row_block_offset<kContig>(a, blk < a.nblocks ? blk : a.nblocks - 1));
+  return blk;
+}
+
+// Segments of the two-pass row kernels: raw[i] and the block index of
+// segment s0 + i * stride, all loads issued before any is waited for.
+template <bool kBF16, bool kContig, bool kStream, int kN>
+__device__ __forceinline__ void load_segments(const RowArgs &a, uint64_t s0, uint64_t stride, int lane,
+                                              RawBlock<kBF16> (&raw)[kN], uint64_t (&blk)[kN]) {
+  if constexpr (kBF16 && kContig) {
+    SegChunks ch[kN];
+#pragma unroll
+    for (int i = 0; i < kN; ++i) ch[i] = issue_segment_bf16<kStream, uint64_t>(a.x, 2 * a.nblocks, s0 + i * stride, lane);
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first exchange
+#pragma unroll
+    for (int i = 0; i < kN; ++i) blk[i] = finish_segment_bf16<uint64_t>(ch[i], s0 + i * stride, lane, raw[i]);
   } else {
-    const uint32_t blk = seg * 64 + lane;
-    if (blk < nblocks) raw.load(x, (int64_t)16 * blk);
-    else raw.zero();
-    return blk;
+#pragma unroll
+    for (int i = 0; i < kN; ++i) blk[i] = issue_segment_direct<kBF16, kContig, kStream>(a, s0 + i * stride, lane, raw[i]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -392,25 +401,58 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
   const uint32_t nseg = (uint32_t)a.nseg;
   const uint32_t mask = kRHT ? rht_sign_mask(a.rht_seed) : 0u;
 
-  // Phase 1: all loads first, then the block maxima.  A segment belongs to
-  // one job, so the job index is uniform across the wavefront.
+  // Phase 1: every segment's loads are issued before the first is waited
+  // for, then the block maxima.  A segment belongs to one job, so the job
+  // index is uniform across the wavefront.  Iterations at or past nseg_iters
+  // (uniform over the grid) load nothing; within them, a segment past the
+  // end of the last job loads that job's final chunk again (clamped, in
+  // bounds) and is marked invalid.
   RawBlock<kBF16> raw[kMax];
   uint32_t blk[kMax];
   int jb[kMax];
   uint32_t bmax[kMax];
+  {
+    uint32_t seg[kMax];
+    const void *xs[kMax];
 #pragma unroll
-  for (int it = 0; it < kMax; ++it) {
-    const uint32_t g = it * nwaves + gwave;
-    if (it < (int)a.nseg_iters && g < nseg) {
+    for (int it = 0; it < kMax; ++it) {
+      const uint32_t g = it * nwaves + gwave;
       const int j = (njobs > 1 && g >= (uint32_t)a.job[1].seg_begin) + (njobs > 2 && g >= (uint32_t)a.job[2].seg_begin) +
                     (njobs > 3 && g >= (uint32_t)a.job[3].seg_begin);
       jb[it] = j;
-      blk[it] = load_segment_fused<kBF16>(a.job[j].x, (uint32_t)a.job[j].nblocks, g - (uint32_t)a.job[j].seg_begin,
-                                          lane, raw[it]);
+      xs[it] = j == 0 ? a.job[0].x : j == 1 ? a.job[1].x : j == 2 ? a.job[2].x : a.job[3].x;
+      const uint32_t sb = (uint32_t)(j == 0 ? a.job[0].seg_begin : j == 1 ? a.job[1].seg_begin
+                                     : j == 2 ? a.job[2].seg_begin : a.job[3].seg_begin);
+      seg[it] = g - sb;
+    }
+    auto job_nblocks = [&](int j) -> uint32_t {
+      return (uint32_t)(j == 0 ? a.job[0].nblocks : j == 1 ? a.job[1].nblocks : j == 2 ? a.job[2].nblocks
+                                                                                       : a.job[3].nblocks);
+    };
+    if constexpr (kBF16) {
+      SegChunks ch[kMax];
+#pragma unroll
+      for (int it = 0; it < kMax; ++it)
+        if (it < (int)a.nseg_iters)
+          ch[it] = issue_segment_bf16<true, uint32_t>(xs[it], 2 * job_nblocks(jb[it]), seg[it], lane);
+#pragma unroll
+      for (int it = 0; it < kMax; ++it) {
+        if (it < (int)a.nseg_iters) blk[it] = finish_segment_bf16<uint32_t>(ch[it], seg[it], lane, raw[it]);
+        else raw[it].zero();
+      }
     } else {
-      raw[it].zero();
-      jb[it] = 0;
-      blk[it] = ~0u;
+#pragma unroll
+      for (int it = 0; it < kMax; ++it) {
+        const uint32_t nb = job_nblocks(jb[it]);
+        blk[it] = seg[it] * 64 + lane;
+        if (it < (int)a.nseg_iters) raw[it].load(xs[it], (int64_t)16 * (blk[it] < nb ? blk[it] : nb - 1));
+        else raw[it].zero();
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < kMax; ++it) {
+      const uint32_t g = it * nwaves + gwave;
+      if (!(it < (int)a.nseg_iters && g < nseg) || blk[it] >= job_nblocks(jb[it])) blk[it] = ~0u;
     }
   }
   uint32_t mj[kMaxJobs] = {0u, 0u, 0u, 0u};
@@ -424,6 +466,7 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
       if (kRHT) rht16(v, mask);
       bmax[it] = max_abs16(v);
     }
+    if (blk[it] == ~0u) bmax[it] = 0u;
 #pragma unroll
     for (int j = 0; j < kMaxJobs; ++j)
       if (jb[it] == j) mj[j] = max(mj[j], bmax[it]);
@@ -515,18 +558,20 @@ __global__ __launch_bounds__(kThreads) void row_amax_kernel(RowArgs a) {
   for (uint64_t s0 = (uint64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); s0 < nseg;
        s0 += kBatch * nwaves) {
     RawBlock<kBF16> raw[kBatch];
+    uint64_t blk[kBatch];
+    load_segments<kBF16, kContig, false>(a, s0, nwaves, lane, raw, blk);
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      const uint64_t seg = s0 + i * nwaves;
-      if (seg < nseg) load_segment<kBF16, kContig, false>(a, seg, lane, raw[i]);
-      else raw[i].zero();
-    }
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      float v[16];
-      raw[i].values(v);
-      if (kRHT) rht16(v, mask);
-      m = max(m, max_abs16(v));
+      uint32_t bm;
+      if constexpr (kBF16 && !kRHT) {
+        bm = raw[i].max_abs_bf16();
+      } else {
+        float v[16];
+        raw[i].values(v);
+        if (kRHT) rht16(v, mask);
+        bm = max_abs16(v);
+      }
+      m = max(m, blk[i] < a.nblocks ? bm : 0u);
     }
   }
   block_amax_commit(m, a.ctrl);
@@ -548,12 +593,7 @@ __global__ __launch_bounds__(kThreads) void row_encode_kernel(RowArgs a) {
        s0 += kBatch * nwaves) {
     RawBlock<kBF16> raw[kBatch];
     uint64_t blk[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const uint64_t seg = s0 + i * nwaves;
-      if (seg < nseg) blk[i] = load_segment<kBF16, kContig>(a, seg, lane, raw[i]);
-      else { raw[i].zero(); blk[i] = a.nblocks; }
-    }
+    load_segments<kBF16, kContig, true>(a, s0, nwaves, lane, raw, blk);
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       if (blk[i] < a.nblocks) {
@@ -604,46 +644,59 @@ struct ColTile {
   }
 };
 
+// Load a lane's 16 rows x 8 columns.  `full` (uniform over the workgroup:
+// the whole tile lies inside the tensor's columns and rows start on 16-byte
+// boundaries) takes one or two 16-byte loads per row, all issued before any
+// is waited for; otherwise element loads with columns at or beyond C read as
+// zero.  Lanes outside the tensor pass clamped, in-bounds coordinates and
+// ignore what they load.
 template <bool kBF16>
-__device__ __forceinline__ void col_load(const ColArgs &a, int64_t b, int64_t rb, int64_t cg,
+__device__ __forceinline__ void col_load(const ColArgs &a, int64_t b, int64_t rb, int64_t cg, bool full,
                                          ColTile<kBF16> &t) {
   const int64_t c0 = 8 * cg;
-  const bool full = a.vec_ok && c0 + 8 <= a.C;
+  const uint8_t *base = static_cast<const uint8_t *>(a.x) + (b * a.bstride + 16 * rb * a.ld + c0) * (kBF16 ? 2 : 4);
+  const int64_t ldb = a.ld * (kBF16 ? 2 : 4);
+  if (full) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint8_t *p = base + j * ldb;
+      const uint4 q = *reinterpret_cast<const uint4 *>(p);
+      t.w[j][0] = q.x; t.w[j][1] = q.y; t.w[j][2] = q.z; t.w[j][3] = q.w;
+      if (!kBF16) {
+        const uint4 q1 = *reinterpret_cast<const uint4 *>(p + 16);
+        t.w[j][4] = q1.x; t.w[j][5] = q1.y; t.w[j][6] = q1.z; t.w[j][7] = q1.w;
+      }
+    }
+    return;
+  }
+  // Element loads at clamped column offsets (c0 < C), masked afterwards.
+  const int lim = (int)min((int64_t)7, a.C - 1 - c0);
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int64_t off = b * a.bstride + (16 * rb + j) * a.ld + c0;
     if (kBF16) {
-      const uint16_t *p = static_cast<const uint16_t *>(a.x) + off;
-      if (full) {
-        const uint4 q = *reinterpret_cast<const uint4 *>(p);
-        t.w[j][0] = q.x; t.w[j][1] = q.y; t.w[j][2] = q.z; t.w[j][3] = q.w;
-      } else {
-        uint32_t e[8];
+      const uint16_t *p = reinterpret_cast<const uint16_t *>(base + j * ldb);
+      uint32_t e[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = (c0 + i < a.C) ? p[i] : 0u;
+      for (int i = 0; i < 8; ++i) e[i] = p[min(i, lim)];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) t.w[j][i] = e[2 * i] | (e[2 * i + 1] << 16);
-      }
+      for (int i = 0; i < 8; ++i) e[i] = i <= lim ? e[i] : 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t.w[j][i] = e[2 * i] | (e[2 * i + 1] << 16);
     } else {
-      const float *p = static_cast<const float *>(a.x) + off;
-      if (full) {
-        const float4 q0 = *reinterpret_cast<const float4 *>(p);
-        const float4 q1 = *reinterpret_cast<const float4 *>(p + 4);
-        t.w[j][0] = __float_as_uint(q0.x); t.w[j][1] = __float_as_uint(q0.y);
-        t.w[j][2] = __float_as_uint(q0.z); t.w[j][3] = __float_as_uint(q0.w);
-        t.w[j][4] = __float_as_uint(q1.x); t.w[j][5] = __float_as_uint(q1.y);
-        t.w[j][6] = __float_as_uint(q1.z); t.w[j][7] = __float_as_uint(q1.w);
-      } else {
+      const uint32_t *p = reinterpret_cast<const uint32_t *>(base + j * ldb);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) t.w[j][i] = (c0 + i < a.C) ? __float_as_uint(p[i]) : 0u;
-      }
+      for (int i = 0; i < 8; ++i) t.w[j][i] = p[min(i, lim)];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t.w[j][i] = i <= lim ? t.w[j][i] : 0u;
     }
   }
 }
 
+// A lane's unit of the two-pass tiles: row block rb, column group cg; ld_rb
+// and ld_cg are the same clamped into the tensor (what the lane loads).
 struct ColLane {
-  int64_t b, tr, tc, rb, cg;
-  bool valid;
+  int64_t b, tr, tc, rb, cg, ld_rb, ld_cg;
+  bool valid, full;
 };
 
 __device__ __forceinline__ ColLane col_lane(const ColArgs &a) {
@@ -656,6 +709,9 @@ __device__ __forceinline__ ColLane col_lane(const ColArgs &a) {
   l.cg = l.tc * kColTileCG + (threadIdx.x % kColTileCG);
   l.rb = l.tr * kColTileRB + (threadIdx.x / kColTileCG);
   l.valid = l.rb < a.R / 16 && 8 * l.cg < a.C;
+  l.ld_rb = min(l.rb, a.R / 16 - 1);
+  l.ld_cg = min(l.cg, (a.C - 1) / 8);
+  l.full = a.vec_ok && (l.tc + 1) * (8 * kColTileCG) <= a.C;
   return l;
 }
 
@@ -664,19 +720,17 @@ __global__ __launch_bounds__(kThreads) void col_amax_kernel(ColArgs a) {
   const uint32_t mask = kRHT ? rht_sign_mask(a.rht_seed) : 0u;
   const ColLane l = col_lane(a);
   uint32_t m = 0;
-  if (l.valid) {
-    ColTile<kBF16> t;
-    col_load<kBF16>(a, l.b, l.rb, l.cg, t);
+  ColTile<kBF16> t;
+  col_load<kBF16>(a, l.b, l.ld_rb, l.ld_cg, l.full, t);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v[16];
+  for (int e = 0; e < 8; ++e) {
+    float v[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = t.at(j, e);
-      if (kRHT) rht16(v, mask);
-      m = max(m, max_abs16(v));
-    }
+    for (int j = 0; j < 16; ++j) v[j] = t.at(j, e);
+    if (kRHT) rht16(v, mask);
+    m = max(m, max_abs16(v));  // columns past C hold zeros
   }
-  block_amax_commit(m, a.ctrl);
+  block_amax_commit(l.valid ? m : 0u, a.ctrl);
 }
 
 template <bool kBF16, bool kRHT, bool kSR>
@@ -693,9 +747,9 @@ __global__ __launch_bounds__(kThreads) void col_encode_kernel(ColArgs a) {
   __syncthreads();
   const ColLane l = col_lane(a);
   const int cgl = threadIdx.x % kColTileCG, rbl = threadIdx.x / kColTileCG;
+  ColTile<kBF16> t;
+  col_load<kBF16>(a, l.b, l.ld_rb, l.ld_cg, l.full, t);
   if (l.valid) {
-    ColTile<kBF16> t;
-    col_load<kBF16>(a, l.b, l.rb, l.cg, t);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int64_t c = 8 * l.cg + e;  // row of the transposed view
@@ -761,17 +815,13 @@ __global__ __launch_bounds__(kColFusedThreads) void col_fused_kernel(ColArgs a) 
   const int cgl = threadIdx.x % kColFusedCG, rbl = threadIdx.x / kColFusedCG;
   const int64_t cg = tc * kColFusedCG + cgl, rb = tr * kColFusedRB + rbl;
   const bool valid = rb < a.R / 16 && 8 * cg < a.C;
+  const bool full = a.vec_ok && (tc + 1) * (8 * kColFusedCG) <= a.C;
 
-  // Phase 1: load the unit, block maxima of its (transformed) columns.
+  // Phase 1: load the unit (clamped into the tensor for lanes outside it,
+  // whose maxima are then dropped), block maxima of its (transformed)
+  // columns.
   ColTile<true> t;
-  if (valid) {
-    col_load<true>(a, b, rb, cg, t);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) t.w[j][i] = 0u;
-  }
+  col_load<true>(a, b, min(rb, a.R / 16 - 1), min(cg, (a.C - 1) / 8), full, t);
   uint32_t bm[8];
   uint32_t m = 0;
 #pragma unroll
@@ -781,7 +831,7 @@ __global__ __launch_bounds__(kColFusedThreads) void col_fused_kernel(ColArgs a) 
     for (int j = 0; j < 16; ++j) v[j] = t.at(j, e);
     if (kRHT) rht16(v, mask);
     bm[e] = max_abs16(v);  // columns past C hold zeros: maximum 0
-    m = max(m, bm[e]);
+    m = max(m, valid ? bm[e] : 0u);
     // One column's unpacked values at a time: the unit's 64 words and the
     // eight maxima are what the register budget holds across the barrier.
     __builtin_amdgcn_sched_barrier(0);
