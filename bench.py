@@ -84,24 +84,34 @@ def mfma_ceiling():
     return res or None
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size), or None when
-    the GEMM source has changed since those counters were taken."""
+def source_digest() -> str:
+    """First 16 hex digits of the SHA-256 over the library's sources (every
+    file under csrc/, in name order): counter summaries record it, and their
+    figures are used only while it still matches."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(here, "bit_block_scaled_nvfp4_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` (a name of the `kernels` table) from
+    the committed rocprofv3 counter summary of this workload (FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy of known size), or None when the library
+    sources have changed since those counters were taken."""
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", f"hbm_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m_bytes = re.search(r"gemm_nvfp4\w* HBM bytes per launch: (\d+)", text)
-    m_sha = re.search(r"gemm_source_sha256_16: ([0-9a-f]+)", text)
+    m_bytes = re.search(r"^%s HBM bytes per launch: (\d+)$" % re.escape(kernel), text, re.M)
+    m_sha = re.search(r"^source_sha256_16: ([0-9a-f]+)$", text, re.M)
     if not (m_bytes and m_sha):
         return None
-    h = hashlib.sha256()
-    for f in ("gemm.hip", "internal.hpp"):
-        with open(os.path.join(here, "bit_block_scaled_nvfp4_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return int(m_bytes.group(1)) if h.hexdigest()[:16] == m_sha.group(1) else None
+    return int(m_bytes.group(1)) if source_digest() == m_sha.group(1) else None
 
 
 def copy_probe(mib: int) -> None:
@@ -202,11 +212,11 @@ def main():
     if S["bound"] == "mfma":
         achieved = S["flops"][dom] / (dom_us * 1e-6) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_MFMA_TFLOPS, 4), "traffic": measured_traffic(args.workload)}
+                    "frac": round(achieved / PEAK_MFMA_TFLOPS, 4), "traffic": measured_traffic(args.workload, dom)}
     else:
         achieved = S["bytes"][dom] / (dom_us * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(args.workload)}
+                    "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(args.workload, dom)}
     roofline["kernel"] = dom
 
     out = {
