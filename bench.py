@@ -154,7 +154,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     ceiling = None if (args.copy_probe or args.no_mfma_ceiling) else mfma_ceiling()
     dev = torch.device("cuda:0")

@@ -59,7 +59,7 @@ typedef enum nvfp4_status {
   NVFP4_EINVAL = 1,      /* null pointer, unknown enum value, inconsistent views */
   NVFP4_ESHAPE = 2,      /* contraction length not a multiple of 16, negative or oversized extents */
   NVFP4_EALIGN = 3,      /* a pointer or stride breaks the alignment stated below */
-  NVFP4_EUNSUPPORTED = 4,/* a valid request this build does not implement */
+  NVFP4_EUNSUPPORTED = 4,/* a valid request the library does not implement */
   NVFP4_EHIP = 5,        /* the HIP runtime refused a launch */
   NVFP4_EWORKSPACE = 6   /* workspace missing or smaller than the *_workspace_size() figure */
 } nvfp4_status;
