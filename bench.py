@@ -50,8 +50,8 @@ QUANT_BYTES_PER_ELEM = 2 + 0.5 + 1.0 / 16  # BF16 in, E2M1 codes + E4M3 scales o
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="fprop_3b",
                    choices=["fprop_3b", "mlp_up_12b", "linear_train", "attn_scores"])
     p.add_argument("--no-cpu-baseline", action="store_true")
