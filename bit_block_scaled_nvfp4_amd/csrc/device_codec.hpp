@@ -112,16 +112,26 @@ struct u32x4 {
   uint32_t x, y, z, w;
 };
 
+// a ^ b ^ k in one VALU instruction (gfx950's three-input bit operation,
+// truth table 0x96); k is uniform over the wavefront (a key word), so it is
+// taken from a scalar register.
+__device__ __forceinline__ uint32_t xor3_key(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
+
 // Each round's two 32 x 32 -> 64-bit products are written as one 64-bit
 // multiply each, which the compiler emits as a single v_mad_u64_u32 (the
-// high and low words at once) instead of a mul_lo / mul_hi pair.
+// high and low words at once) instead of a mul_lo / mul_hi pair.  The key
+// must be uniform over the wavefront (it is a kernel argument here).
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int i = 0; i < 10; ++i) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c.x, p1 = (uint64_t)0xCD9E8D57u * c.z;
     const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
     const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
-    c = u32x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    c = u32x4{xor3_key(hi1, c.y, k0), lo1, xor3_key(hi0, c.w, k1), lo0};
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }

@@ -31,6 +31,8 @@
 // a Philox word for stochastic rounding).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "device_codec.hpp"
 #include "internal.hpp"
 
@@ -913,11 +915,46 @@ int grid_for(uint64_t items, int threads, uint64_t cap) {
   return (int)(want < 1 ? 1 : (want > cap ? cap : want));
 }
 
+// Device properties the single-pass launchers need, queried once per device
+// and kept (a device's CU count and a kernel's occupancy do not change
+// while the process runs).  Concurrent first calls may both query; they
+// store the same value.
+constexpr int kMaxDevices = 64;
+
+int current_device() {
+  int dev = 0;
+  return hipGetDevice(&dev) == hipSuccess ? dev : -1;
+}
+
 int cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  static std::atomic<int> cache[kMaxDevices];
+  const int dev = current_device();
+  if (dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < kMaxDevices && n > 0) cache[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+// Resident workgroups per CU of kKernel at kThreadsPerGroup threads (0 if
+// the query fails), cached per device; one table per kernel instance.
+template <auto kKernel, int kThreadsPerGroup>
+int occupancy() {
+  static std::atomic<int> cache[kMaxDevices];  // value + 1, 0 = unknown
+  const int dev = current_device();
+  if (dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v - 1;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kKernel, kThreadsPerGroup, 0) != hipSuccess) return 0;
+  if (dev < kMaxDevices) cache[dev].store(per_cu + 1, std::memory_order_relaxed);
+  return per_cu;
 }
 
 // Single-pass row-wise quantize of the jobs in `a` if they fit the on-chip
@@ -927,10 +964,7 @@ bool try_row_fused(FusedArgs a, hipStream_t s, hipError_t &err) {
   const int cus = cu_count();
   if (cus <= 0) return false;
   auto kernel = row_fused_kernel<kBF16, kRHT, kSR>;
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kFusedThreads, 0) != hipSuccess ||
-      per_cu < kFusedPerCU)
-    return false;
+  if (occupancy<row_fused_kernel<kBF16, kRHT, kSR>, kFusedThreads>() < kFusedPerCU) return false;
   const uint64_t grid = (uint64_t)cus * kFusedPerCU;
   const uint64_t nwaves = grid * (kFusedThreads / 64);
   const uint64_t iters = (a.nseg + nwaves - 1) / nwaves;
@@ -1004,9 +1038,7 @@ bool try_col_fused(ColArgs a, hipStream_t s, hipError_t &err) {
   const int cus = cu_count();
   if (cus <= 0) return false;
   auto kernel = col_fused_kernel<kRHT, kSR>;
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kColFusedThreads, 0) != hipSuccess || per_cu < 1)
-    return false;
+  if (occupancy<col_fused_kernel<kRHT, kSR>, kColFusedThreads>() < 1) return false;
   a.tiles_r = (a.R / 16 + kColFusedRB - 1) / kColFusedRB;
   a.tiles_c = (a.C + 8 * kColFusedCG - 1) / (8 * kColFusedCG);
   const int64_t grid = a.batch * a.tiles_r * a.tiles_c;
