@@ -92,16 +92,17 @@ __device__ __forceinline__ uint32_t e2m1_rne8(const float *q) {
 // 2^(e' - 1)); the grid point below is code 2e' + floor(t) and
 // (|q| - lo) / step = t - floor(t), also exact.  For |q| >= 1 the test
 // equals comparing u << 6 with the low 22 mantissa bits of |q|.  At 6 the
-// fraction is 0, so no special case.
+// fraction is 0, so no special case.  t - floor(t) is one v_fract_f32
+// (exact for t in [0, 4), where it never reaches its clamp below 1) and
+// floor(t) the truncating convert.
 __device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t u16) {
   const uint32_t sign = (__float_as_uint(q) >> 28) & 8u;
   const float a = fminf(fabsf(q), 6.0f);
   const uint32_t ebits = __float_as_uint(a) >> 23;          // biased exponent (sign bit is 0)
   const uint32_t e = (ebits > 127u ? ebits : 127u) - 127u;  // 0, 1 or 2
-  const float t = a * __uint_as_float((128u - e) << 23);    // a * 2^(1 - e)
-  const float fl = __builtin_floorf(t);
-  const uint32_t up = ((float)u16 < (t - fl) * 65536.0f) ? 1u : 0u;
-  return sign | (2u * e + (uint32_t)fl + up);
+  const float t = __builtin_ldexpf(a, 1 - (int)e);          // a * 2^(1 - e), in [0, 4), exact
+  const uint32_t up = ((float)u16 < __builtin_amdgcn_fractf(t) * 65536.0f) ? 1u : 0u;
+  return sign | (2u * e + (uint32_t)t + up);
 }
 
 // ---------------------------------------------------------------------------
@@ -171,9 +172,9 @@ __device__ __forceinline__ float lane_xor1(float v) { return __uint_as_float(lan
 // Random Hadamard transform on 16 values held by one lane
 // ---------------------------------------------------------------------------
 
-// v <- (1/4) H16 diag(s) v; signs flip by XOR of the sign bit (exact), the
+// v <- H16 diag(s) v; signs flip by XOR of the sign bit (exact), the
 // butterflies run with span 1, 2, 4, 8 in that order in FP32.
-__device__ __forceinline__ void rht16(float (&v)[16], uint32_t mask) {
+__device__ __forceinline__ void rht16_unscaled(float (&v)[16], uint32_t mask) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((mask >> j) & 1u) << 31));
 #pragma unroll
@@ -186,8 +187,20 @@ __device__ __forceinline__ void rht16(float (&v)[16], uint32_t mask) {
       v[i + h] = a - b;
     }
   }
+}
+
+// v <- (1/4) H16 diag(s) v: the butterflies, then the product by 1/4 of each
+// value (rounded, which matters only for subnormal results).
+__device__ __forceinline__ void rht16(float (&v)[16], uint32_t mask) {
+  rht16_unscaled(v, mask);
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.25f;
+}
+
+// max |v'| over a block of v' = fl(w / 4), as FP32 bits, from the maximum of
+// |w| (bits m): rounding is monotone, so fl(max|w| / 4) = max fl(|w| / 4).
+__device__ __forceinline__ uint32_t quarter_max_bits(uint32_t m) {
+  return __float_as_uint(__uint_as_float(m) * 0.25f);
 }
 
 // The same transform when a 16-block is split over a lane pair (even lane:

@@ -465,8 +465,12 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
     } else {
       float v[16];
       raw[it].values(v);
-      if (kRHT) rht16(v, mask);
-      bmax[it] = max_abs16(v);
+      if (kRHT) {
+        rht16_unscaled(v, mask);
+        bmax[it] = quarter_max_bits(max_abs16(v));
+      } else {
+        bmax[it] = max_abs16(v);
+      }
     }
     if (blk[it] == ~0u) bmax[it] = 0u;
 #pragma unroll
@@ -570,8 +574,12 @@ __global__ __launch_bounds__(kThreads) void row_amax_kernel(RowArgs a) {
       } else {
         float v[16];
         raw[i].values(v);
-        if (kRHT) rht16(v, mask);
-        bm = max_abs16(v);
+        if (kRHT) {
+          rht16_unscaled(v, mask);
+          bm = quarter_max_bits(max_abs16(v));
+        } else {
+          bm = max_abs16(v);
+        }
       }
       m = max(m, blk[i] < a.nblocks ? bm : 0u);
     }
@@ -729,8 +737,12 @@ __global__ __launch_bounds__(kThreads) void col_amax_kernel(ColArgs a) {
     float v[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = t.at(j, e);
-    if (kRHT) rht16(v, mask);
-    m = max(m, max_abs16(v));  // columns past C hold zeros
+    if (kRHT) {
+      rht16_unscaled(v, mask);
+      m = max(m, quarter_max_bits(max_abs16(v)));  // columns past C hold zeros
+    } else {
+      m = max(m, max_abs16(v));
+    }
   }
   block_amax_commit(l.valid ? m : 0u, a.ctrl);
 }
@@ -831,8 +843,12 @@ __global__ __launch_bounds__(kColFusedThreads) void col_fused_kernel(ColArgs a) 
     float v[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = t.at(j, e);
-    if (kRHT) rht16(v, mask);
-    bm[e] = max_abs16(v);  // columns past C hold zeros: maximum 0
+    if (kRHT) {
+      rht16_unscaled(v, mask);
+      bm[e] = quarter_max_bits(max_abs16(v));  // columns past C hold zeros: maximum 0
+    } else {
+      bm[e] = max_abs16(v);
+    }
     m = max(m, valid ? bm[e] : 0u);
     // One column's unpacked values at a time: the unit's 64 words and the
     // eight maxima are what the register budget holds across the barrier.
