@@ -75,7 +75,9 @@ __device__ __forceinline__ uint32_t e2m1_rne(float q) {
 // instruction.  Its results equal e2m1_rne() on every non-NaN FP32 input
 // (checked exhaustively on the hardware over all 2^32 bit patterns).
 __device__ __forceinline__ uint32_t e2m1_rne8(const float *q) {
-  uint32_t w = 0;
+  // The four converts write bytes 0..3, so the word's initial value never
+  // shows; any live register will do (no zeroing move needed).
+  uint32_t w = __float_as_uint(q[0]);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[0], q[1], 1.0f, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);

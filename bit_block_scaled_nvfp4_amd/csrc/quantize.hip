@@ -544,8 +544,10 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
       raw[it].values(v);
       if (kRHT) rht16(v, mask);
       const uint2 c = encode16<kSR>(v, recip[j][S], (uint64_t)16 * blk[it], a.sr_stream, a.sr_seed);
-      st_stream(a.job[j].codes + (size_t)8 * blk[it], c);
-      a.job[j].scales[blk[it]] = (uint8_t)S;
+      // Uniform base plus a 32-bit lane offset (the capacity keeps 8 * blk
+      // within 32 bits): the stores take their base from scalar registers.
+      st_stream(a.job[j].codes + (uint32_t)(8u * blk[it]), c);
+      a.job[j].scales[(uint32_t)blk[it]] = (uint8_t)S;
     }
     // Keep blocks from being interleaved by the scheduler: hoisting every
     // block's unpacked values at once would exceed the register budget.
