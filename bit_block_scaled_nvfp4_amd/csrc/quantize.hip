@@ -799,20 +799,22 @@ __global__ __launch_bounds__(kThreads) void col_encode_kernel(ColArgs a) {
   encode_finish(a.ctrl, a.tensor_scale, st);
 }
 
-// Single-pass transposing quantize (BF16): one 1024-thread workgroup per CU,
-// each covering 1024 input rows x 128 columns, i.e. 64 x 16 units of 16 rows
-// x 8 columns, one unit per thread held in registers (64 dwords).  Phase 1
+// Single-pass transposing quantize (BF16): at most one workgroup per CU, each
+// covering 16 kRB input rows x 128 columns, i.e. kRB x 16 units of 16 rows
+// x 8 columns, one unit per thread held in registers (64 dwords); kRB = 64
+// (1024 threads) for large tensors, 32 (512 threads, twice the workgroups)
+// where the grid of 64-row-block tiles would leave CUs idle.  Phase 1
 // takes the eight column blocks' maxima (after the transform), then the grid
 // barrier of the row kernel yields the tensor max; phase 2 re-derives each
 // column block from the held words and encodes it exactly as
 // col_encode_kernel does, staging the tile's codes in LDS so each transposed
 // row gets 512 contiguous bytes.  The input is read once.
-constexpr int kColFusedThreads = 1024;
-constexpr int kColFusedRB = 64;  // row blocks per tile
 constexpr int kColFusedCG = 16;  // column groups per tile
 
-template <bool kRHT, bool kSR>
-__global__ __launch_bounds__(kColFusedThreads) void col_fused_kernel(ColArgs a) {
+template <int kRB, bool kRHT, bool kSR>
+__global__ __launch_bounds__(kRB * kColFusedCG) void col_fused_kernel(ColArgs a) {
+  constexpr int kColFusedRB = kRB;  // row blocks per tile
+  constexpr int kColFusedThreads = kRB * kColFusedCG;
   __shared__ float recip[128];
   __shared__ uint2 tile_codes[kColFusedCG * 8][kColFusedRB + 1];
   __shared__ uint8_t tile_scales[kColFusedCG * 8][kColFusedRB + 4];
@@ -1048,24 +1050,31 @@ hipError_t dispatch_row(const RowArgs &a, bool rht, bool sr, bool contig, hipStr
   return sr ? run_row<kBF16, false, true>(a, contig, s) : run_row<kBF16, false, false>(a, contig, s);
 }
 
-// Single-pass transposing quantize if the grid of 1024-row x 128-column
+// Single-pass transposing quantize if a grid of 16 kRB-row x 128-column
 // tiles fits one workgroup per CU (BF16 only: an FP32 unit would not fit the
-// register budget); returns false (nothing launched) otherwise.
-template <bool kRHT, bool kSR>
-bool try_col_fused(ColArgs a, hipStream_t s, hipError_t &err) {
-  const int cus = cu_count();
-  if (cus <= 0) return false;
-  auto kernel = col_fused_kernel<kRHT, kSR>;
-  if (occupancy<col_fused_kernel<kRHT, kSR>, kColFusedThreads>() < 1) return false;
-  a.tiles_r = (a.R / 16 + kColFusedRB - 1) / kColFusedRB;
+// register budget): 512-row tiles when those fit (more workgroups for the
+// same tensor), else 1024-row tiles.  Returns false (nothing launched) if
+// neither fits.
+template <int kRB, bool kRHT, bool kSR>
+bool launch_col_fused(ColArgs a, int cus, hipStream_t s, hipError_t &err) {
+  constexpr int kThreadsPerGroup = kRB * kColFusedCG;
+  if (occupancy<col_fused_kernel<kRB, kRHT, kSR>, kThreadsPerGroup>() < 1) return false;
+  a.tiles_r = (a.R / 16 + kRB - 1) / kRB;
   a.tiles_c = (a.C + 8 * kColFusedCG - 1) / (8 * kColFusedCG);
   const int64_t grid = a.batch * a.tiles_r * a.tiles_c;
   if (grid < 1 || grid > (int64_t)cus) return false;
   // A plain launch: with at most one workgroup per CU every workgroup
   // becomes resident, so the grid barrier completes (bounded wait besides).
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kColFusedThreads), 0, s, a);
+  hipLaunchKernelGGL((col_fused_kernel<kRB, kRHT, kSR>), dim3((unsigned)grid), dim3(kThreadsPerGroup), 0, s, a);
   err = hipGetLastError();
   return err == hipSuccess;
+}
+
+template <bool kRHT, bool kSR>
+bool try_col_fused(const ColArgs &a, hipStream_t s, hipError_t &err) {
+  const int cus = cu_count();
+  if (cus <= 0) return false;
+  return launch_col_fused<32, kRHT, kSR>(a, cus, s, err) || launch_col_fused<64, kRHT, kSR>(a, cus, s, err);
 }
 
 template <bool kBF16, bool kRHT, bool kSR>
