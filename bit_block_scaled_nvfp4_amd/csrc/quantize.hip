@@ -891,35 +891,38 @@ __global__ __launch_bounds__(kRB * kColFusedCG) void col_fused_kernel(ColArgs a)
   for (int j = 0; j < 16; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(t.w[j][i]));
+  // Element, code and scale indices in 32 bits: the grid covers at most one
+  // tile per CU, so the whole tensor has fewer than 2^25 elements.
+  const uint32_t R32 = (uint32_t)a.R, C32 = (uint32_t)a.C;
   if (valid) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int64_t c = 8 * cg + e;  // row of the transposed view
-      if (c >= a.C) break;
+      const uint32_t c = 8u * (uint32_t)cg + e;  // row of the transposed view
+      if (c >= C32) break;
       float v[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) v[j] = t.at(j, e);
       if (kRHT) rht16(v, mask);
       const uint32_t S = block_scale_code(bm[e], st, d6);
-      const int64_t vrow = b * a.C + c;  // row index in the [batch*C][R] view
-      tile_codes[cgl * 8 + e][rbl] = encode16<kSR>(v, recip[S], (uint64_t)(vrow * a.R + 16 * rb), a.sr_stream,
-                                                   a.sr_seed);
+      const uint32_t vrow = (uint32_t)b * C32 + c;  // row index in the [batch*C][R] view
+      tile_codes[cgl * 8 + e][rbl] =
+          encode16<kSR>(v, recip[S], (uint64_t)(vrow * R32 + 16u * (uint32_t)rb), a.sr_stream, a.sr_seed);
       tile_scales[cgl * 8 + e][rbl] = (uint8_t)S;
       __builtin_amdgcn_sched_barrier(0);
     }
   }
   __syncthreads();
-  // Write out: 128 transposed rows x 64 row blocks of 8 code bytes and one
+  // Write out: 128 transposed rows x kRB row blocks of 8 code bytes and one
   // scale byte; consecutive threads take consecutive row blocks of a row.
-  const int64_t RB = a.R / 16;
-  const int64_t rb_n = min((int64_t)kColFusedRB, RB - tr * kColFusedRB);
+  const uint32_t RB = R32 / 16;
+  const uint32_t rb_n = min((uint32_t)kColFusedRB, RB - (uint32_t)tr * kColFusedRB);
   for (int i = threadIdx.x; i < kColFusedCG * 8 * kColFusedRB; i += kColFusedThreads) {
-    const int tcol = i / kColFusedRB, trbl = i % kColFusedRB;
-    const int64_t c = tc * kColFusedCG * 8 + tcol;
-    if (c < a.C && trbl < rb_n) {
-      const int64_t vrow = b * a.C + c;
-      const int64_t r = tr * kColFusedRB + trbl;
-      st_stream(a.codes + vrow * (a.R / 2) + 8 * r, tile_codes[tcol][trbl]);
+    const uint32_t tcol = i / kColFusedRB, trbl = i % kColFusedRB;
+    const uint32_t c = (uint32_t)tc * kColFusedCG * 8 + tcol;
+    if (c < C32 && trbl < rb_n) {
+      const uint32_t vrow = (uint32_t)b * C32 + c;
+      const uint32_t r = (uint32_t)tr * kColFusedRB + trbl;
+      st_stream(a.codes + (vrow * (R32 / 2) + 8u * r), tile_codes[tcol][trbl]);
       a.scales[vrow * RB + r] = tile_scales[tcol][trbl];
     }
   }
