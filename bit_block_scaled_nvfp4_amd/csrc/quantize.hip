@@ -11,19 +11,22 @@
 // owns one whole 16-element block (two 16-byte BF16 loads), so the transform,
 // the block maximum and the block scale stay in the lane.
 //  * Single pass (tensors that fit in the register files): a grid of one
-//    1024-thread workgroup per CU loads every lane's blocks (up to 8 per
-//    lane for BF16, 33.5M elements on 256 CUs) into registers, reduces the amax per
-//    wavefront and workgroup, meets the rest of the grid at an epoch
-//    barrier, then encodes from registers.  HBM sees one read of the input
-//    and one write of codes and scales.
-//  * Two passes (larger tensors or when the grid cannot be co-resident): an
-//    amax kernel and an encode kernel over the same block order; the second
-//    read largely hits the 256 MB Infinity Cache for tensors that fit it.
+//    1024-thread workgroup per CU loads every lane's blocks (up to 9 per
+//    lane for BF16, 37.7M elements on 256 CUs) into registers, every load
+//    issued before the first wait, reduces the amax per wavefront and
+//    workgroup, meets the rest of the grid at an epoch barrier, then encodes
+//    from registers.  HBM sees one read of the input and one write of codes
+//    and scales.  Up to four tensors (a GEMM's operands) share one launch.
+//  * Two passes (larger tensors or strided rows): an amax kernel and an
+//    encode kernel over the same block order; the second read largely hits
+//    the 256 MB Infinity Cache for tensors that fit it.
 // Transposing ("along rows"): one lane owns 8 input columns x 16 input rows,
 // i.e. 8 complete blocks of the transposed view, so the transform and the
-// block maximum stay in the lane; a workgroup covers 256 input rows x 128
-// columns and stages its codes in LDS so each transposed row's 128-byte code
-// line is written by one workgroup.  Two passes.
+// block maximum stay in the lane, and codes are staged in LDS so each
+// transposed row's code line is written by one workgroup.
+//  * Single pass (BF16, grids of at most one workgroup per CU): 512- or
+//    1024-row x 128-column tiles held in registers across the same barrier.
+//  * Two passes otherwise: 256-row x 128-column tiles.
 //
 // Encode of a block: S = E4M3(fl(max|v| / fl(6 s_t))), q = fl(v * r_S) with
 // r_S = fl(1 / fl(E4M3(S) * s_t)) from a 127-entry LDS table built once per

@@ -39,10 +39,18 @@
  *     inputs must be finite and the tensor amax either 0 or >= 2^-100; a
  *     non-finite input leaves a non-finite tensor scale and unspecified codes.
  *   - Workspaces must be zero-filled before their first use.  Each call leaves
- *     the control words it used zero again, so a workspace can be reused by
- *     later calls on the same stream without clearing.  Calls that are in
- *     flight at the same time need separate workspaces.  After an
- *     NVFP4_EHIP error, zero the workspace again.
+ *     the workspace ready for the next one (two-pass words are restored to
+ *     zero; the single-pass barrier's counters only grow and need no reset),
+ *     so a workspace can be reused by later calls on the same stream without
+ *     clearing.  Calls that are in flight at the same time need separate
+ *     workspaces.  After an NVFP4_EHIP error, zero the workspace again.
+ *   - Single-pass quantize launches (one workgroup per CU) meet at a
+ *     grid-wide barrier for the tensor amax, so they need every CU to become
+ *     free while they run.  The wait is bounded (about a second): if other
+ *     work holds CUs for longer, the 32-bit word at byte offset 8 of the
+ *     workspace (of the group launch's control block for
+ *     nvfp4_quantize_group) becomes nonzero and that call's results are
+ *     unspecified.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
