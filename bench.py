@@ -56,7 +56,8 @@ def parse():
                    choices=["fprop_3b", "mlp_up_12b", "linear_train", "attn_scores"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-mfma-ceiling", action="store_true", help="skip the MFMA ceiling probe")
-    p.add_argument("--cpu-rows", type=int, default=1024, help="GEMM rows in the CPU-oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=2048,
+                   help="GEMM rows in the CPU-oracle sample (about 10 s of one core at the fprop_3b shape)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run 5 device-to-device copies of MIB MiB (calibrates HBM byte counters)")
     return p.parse_args()
