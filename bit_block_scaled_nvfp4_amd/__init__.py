@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "nvfp4.h")
 
 # enums of include/nvfp4.h
-OK, EINVAL, ESHAPE, EALIGN, EUNSUPPORTED, EHIP, EWORKSPACE = range(7)
+OK, EINVAL, ESHAPE, EALIGN, EUNSUPPORTED, EHIP, EWORKSPACE, ETIMEOUT = range(8)
 F32, BF16 = 0, 1
 RNE, SR = 0, 1
 ALONG_COLS, ALONG_ROWS = 0, 1
@@ -85,6 +85,13 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_gemm.argtypes = [ctypes.POINTER(QTensorC), ctypes.POINTER(QTensorC), vp, i32, i64, i64,
                                  ctypes.c_float, vp]
         L.nvfp4_gemm.restype = i32
+        L.nvfp4_gemm_ex.argtypes = [ctypes.POINTER(QTensorC), ctypes.POINTER(QTensorC), vp, i32, i64, i64,
+                                    ctypes.c_float, i32, i32, vp]
+        L.nvfp4_gemm_ex.restype = i32
+        L.nvfp4_quantize_workspace_check.argtypes = [vp, sz, vp]
+        L.nvfp4_quantize_workspace_check.restype = i32
+        L.nvfp4_linear_view.argtypes = [vp, sz, i64, i64, i64, i32, ctypes.POINTER(QTensorC)]
+        L.nvfp4_linear_view.restype = i32
         L.nvfp4_linear_workspace_size.argtypes = [i64, i64, i64]
         L.nvfp4_linear_workspace_size.restype = sz
         L.nvfp4_linear_fwd_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64,
@@ -136,6 +143,21 @@ def nvfp4_gemm(a, b, c_ptr, c_dtype, ldc, batch_stride_c, alpha, stream) -> int:
     return lib().nvfp4_gemm(ctypes.byref(a) if a is not None else None,
                             ctypes.byref(b) if b is not None else None,
                             c_ptr, c_dtype, ldc, batch_stride_c, ctypes.c_float(alpha), stream)
+
+
+def nvfp4_gemm_ex(a, b, c_ptr, c_dtype, ldc, batch_stride_c, alpha, tile_m, tile_n, stream) -> int:
+    return lib().nvfp4_gemm_ex(ctypes.byref(a) if a is not None else None,
+                               ctypes.byref(b) if b is not None else None,
+                               c_ptr, c_dtype, ldc, batch_stride_c, ctypes.c_float(alpha), tile_m, tile_n, stream)
+
+
+def nvfp4_quantize_workspace_check(workspace, workspace_bytes, stream) -> int:
+    return lib().nvfp4_quantize_workspace_check(workspace, workspace_bytes, stream)
+
+
+def nvfp4_linear_view(workspace, workspace_bytes, M, N, K, which, out) -> int:
+    return lib().nvfp4_linear_view(workspace, workspace_bytes, M, N, K, which,
+                                   ctypes.byref(out) if out is not None else None)
 
 
 def nvfp4_linear_fwd_bwd(x_ptr, w_ptr, dy_ptr, y_ptr, dx_ptr, dw_ptr, M, N, K, cfg, workspace,
@@ -297,13 +319,17 @@ def bind_quantize_group(xs, outs, workspace: torch.Tensor, rounding: int = RNE, 
 
 
 def gemm(a: QTensor, b: QTensor, out_dtype: torch.dtype = torch.bfloat16, alpha: float = 1.0,
-         out: torch.Tensor | None = None) -> torch.Tensor:
-    """C[b] = alpha * A^[b] . B^[b]^T -> [batch][M][N] (squeezed to 2-D when batch == 1)."""
+         out: torch.Tensor | None = None, tile: tuple[int, int] | None = None) -> torch.Tensor:
+    """C[b] = alpha * A^[b] . B^[b]^T -> [batch][M][N] (squeezed to 2-D when batch == 1).
+    ``tile`` = (tile_m, tile_n) requests a workgroup tile (nvfp4_gemm_ex)."""
     created = out is None
     if created:
         out = torch.empty(a.batch, a.rows, b.rows, dtype=out_dtype, device=a.codes.device)
     args, _keep = _gemm_args(a, b, out, alpha)
-    _check(lib().nvfp4_gemm(*args), "nvfp4_gemm")
+    if tile is None:
+        _check(lib().nvfp4_gemm(*args), "nvfp4_gemm")
+    else:
+        _check(lib().nvfp4_gemm_ex(*args[:-1], int(tile[0]), int(tile[1]), args[-1]), "nvfp4_gemm_ex")
     return out[0] if created and a.batch == 1 else out
 
 
@@ -315,6 +341,13 @@ def _gemm_args(a: QTensor, b: QTensor, out: torch.Tensor, alpha: float):
             o3.stride(0) if o3.size(0) > 1 else o3.size(1) * o3.size(2), ctypes.c_float(alpha),
             _stream(a.codes.device))
     return args, (ca, cb, o3)
+
+
+def quantize_workspace_check(workspace: torch.Tensor) -> int:
+    """Status of a quantize workspace (waits for the current stream):
+    OK, or ETIMEOUT once a single-pass barrier wait on it has expired."""
+    return lib().nvfp4_quantize_workspace_check(workspace.data_ptr(), workspace.numel(),
+                                                _stream(workspace.device))
 
 
 def bind_gemm(a: QTensor, b: QTensor, out: torch.Tensor, alpha: float = 1.0) -> BoundCall:
@@ -353,6 +386,27 @@ def linear_fwd_bwd(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, sr_seed: 
     args, _keep = _linear_args(x, w, dy, y, dx, dw, sr_seed, rht_seed, wgrad_sr_x, workspace)
     _check(lib().nvfp4_linear_fwd_bwd(*args), "nvfp4_linear_fwd_bwd")
     return y, dx, dw
+
+
+LINEAR_VIEWS = ("X", "W", "dY", "W^T", "dY^T", "X^T")
+
+
+def linear_view(workspace: torch.Tensor, M: int, N: int, K: int, which: int) -> QTensor:
+    """Quantized view `which` (index into LINEAR_VIEWS) that nvfp4_linear_fwd_bwd
+    left in `workspace`, as tensors aliasing the workspace memory."""
+    q = QTensorC()
+    _check(lib().nvfp4_linear_view(workspace.data_ptr(), workspace.numel(), M, N, K, which, ctypes.byref(q)),
+           "nvfp4_linear_view")
+    base = workspace.data_ptr()
+    rows, cols = q.rows, q.cols
+
+    def sub(ptr, n):
+        off = ptr - base
+        return workspace[off:off + n]
+
+    return QTensor(sub(q.codes, rows * cols // 2).view(1, rows, cols // 2),
+                   sub(q.scales, rows * cols // 16).view(1, rows, cols // 16),
+                   sub(q.tensor_scale, 4).view(torch.float32), 1, rows, cols)
 
 
 def bind_linear_fwd_bwd(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, y: torch.Tensor, dx: torch.Tensor,

@@ -42,14 +42,18 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
-    objs = []
+    objs, procs = [], []
     for src in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
         obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
         cmd = [cc, *COMMON, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
+        procs.append((cmd, subprocess.Popen(cmd, stderr=None if verbose else subprocess.PIPE)))
         objs.append(obj)
+    for cmd, p in procs:  # the translation units compile side by side
+        _, err = p.communicate()
+        if p.returncode != 0:
+            raise subprocess.CalledProcessError(p.returncode, cmd, stderr=err)
     tmp = LIB + ".tmp"
     subprocess.run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], check=True)
     os.replace(tmp, LIB)
@@ -58,6 +62,17 @@ def build(verbose: bool = False) -> str:
                    check=True, stderr=None if verbose else subprocess.PIPE)
     os.replace(PROBE + ".tmp", PROBE)
     return LIB
+
+
+def build_shared(src: str, out: str, verbose: bool = False) -> str:
+    """One HIP source -> a shared library `out`, with the library's flags
+    (used for test probes that exercise the library's device functions)."""
+    cmd = [hipcc(), *COMMON, "-shared", src, "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -121,7 +121,8 @@ nvfp4_status validate_gemm(const nvfp4_qtensor *a, const nvfp4_qtensor *b, const
 }
 
 nvfp4::GemmProblem make_gemm(const nvfp4_qtensor *a, const nvfp4_qtensor *b, void *c, int32_t c_dtype,
-                             int64_t ldc, int64_t batch_stride_c, float alpha) {
+                             int64_t ldc, int64_t batch_stride_c, float alpha, int32_t tile_m = 0,
+                             int32_t tile_n = 0) {
   nvfp4::GemmProblem p{};
   p.a_codes = a->codes;
   p.a_scales = a->scales;
@@ -138,6 +139,8 @@ nvfp4::GemmProblem make_gemm(const nvfp4_qtensor *a, const nvfp4_qtensor *b, voi
   p.ldc = ldc;
   p.bstride_c = batch_stride_c;
   p.alpha = alpha;
+  p.tile_m = tile_m;
+  p.tile_n = tile_n;
   return p;
 }
 
@@ -181,11 +184,12 @@ NVFP4_EXPORT const char *nvfp4_status_string(int32_t status) {
     case NVFP4_EUNSUPPORTED: return "unsupported request";
     case NVFP4_EHIP: return "HIP launch failed";
     case NVFP4_EWORKSPACE: return "workspace missing or too small";
+    case NVFP4_ETIMEOUT: return "a single-pass quantize gave up waiting at its grid barrier (results unreliable)";
     default: return "unknown status";
   }
 }
 
-NVFP4_EXPORT int32_t nvfp4_version(void) { return (1 << 16) | 1; }
+NVFP4_EXPORT int32_t nvfp4_version(void) { return (1 << 16) | 2; }
 
 NVFP4_EXPORT size_t nvfp4_quantize_workspace_size(void) { return sizeof(QuantCtrl); }
 
@@ -238,9 +242,54 @@ NVFP4_EXPORT nvfp4_status nvfp4_gemm(const nvfp4_qtensor *a, const nvfp4_qtensor
                             static_cast<hipStream_t>(stream));
 }
 
+NVFP4_EXPORT nvfp4_status nvfp4_gemm_ex(const nvfp4_qtensor *a, const nvfp4_qtensor *b, void *c, int32_t c_dtype,
+                                        int64_t ldc, int64_t batch_stride_c, float alpha, int32_t tile_m,
+                                        int32_t tile_n, void *stream) {
+  nvfp4_status st = validate_gemm(a, b, c, c_dtype, ldc, batch_stride_c);
+  if (st != NVFP4_OK) return st;
+  if (tile_m < 0 || tile_n < 0 || (tile_m == 0) != (tile_n == 0)) return NVFP4_EINVAL;
+  return nvfp4::launch_gemm(make_gemm(a, b, c, c_dtype, ldc, batch_stride_c, alpha, tile_m, tile_n),
+                            static_cast<hipStream_t>(stream));
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_quantize_workspace_check(const void *workspace, size_t workspace_bytes,
+                                                         void *stream) {
+  if (!workspace || workspace_bytes < sizeof(QuantCtrl)) return NVFP4_EWORKSPACE;
+  if (!aligned(workspace, 256)) return NVFP4_EALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // The control blocks a workspace of this size holds: the per-tensor one,
+  // and for a group workspace the single-launch one after it.
+  const int nblocks = workspace_bytes >= nvfp4::kGroupWorkspace ? 2 : 1;
+  uint32_t words[2] = {0u, 0u};
+  for (int i = 0; i < nblocks; ++i) {
+    const QuantCtrl *c = static_cast<const QuantCtrl *>(workspace) + i;
+    if (hipMemcpyAsync(&words[i], &c->timeout, sizeof(uint32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+      return NVFP4_EHIP;
+  }
+  if (hipStreamSynchronize(s) != hipSuccess) return NVFP4_EHIP;
+  return (words[0] | words[1]) ? NVFP4_ETIMEOUT : NVFP4_OK;
+}
+
 NVFP4_EXPORT size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0 || M > kMaxExtent || N > kMaxExtent || K > kMaxExtent) return 0;
   return linear_layout(M, N, K).total;
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_linear_view(void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                                            int64_t K, int32_t which, nvfp4_qtensor *out) {
+  if (!workspace || !out || which < 0 || which > 5) return NVFP4_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0 || M % 16 || N % 16 || K % 16) return NVFP4_ESHAPE;
+  if (M > kMaxExtent || N > kMaxExtent || K > kMaxExtent) return NVFP4_ESHAPE;
+  const LinearLayout L = linear_layout(M, N, K);
+  if (workspace_bytes < L.total) return NVFP4_EWORKSPACE;
+  uint8_t *base = static_cast<uint8_t *>(workspace);
+  out->codes = base + L.codes[which];
+  out->scales = base + L.scales[which];
+  out->tensor_scale = reinterpret_cast<float *>(base + L.st[which]);
+  out->batch = 1;
+  out->rows = L.rows[which];
+  out->cols = L.cols[which];
+  return NVFP4_OK;
 }
 
 NVFP4_EXPORT nvfp4_status nvfp4_linear_fwd_bwd(const void *x, const void *w, const void *dy, void *y,

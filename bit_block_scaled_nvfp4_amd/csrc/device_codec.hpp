@@ -22,13 +22,6 @@ namespace nvfp4 {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// FP32 -> BF16 bits, round to nearest even (inputs here are finite).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // ---------------------------------------------------------------------------
 // E4M3FN block scale (only non-negative codes 0x00..0x7E are produced)
 // ---------------------------------------------------------------------------
@@ -56,24 +49,11 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
 // E2M1 element encode
 // ---------------------------------------------------------------------------
 
-// Round-to-nearest-even onto {0, .5, 1, 1.5, 2, 3, 4, 6}, saturating at 6,
-// returning the 4-bit code (sign in bit 3, kept for zero results).
-// |q| >= 1 is a normal E2M1 number: round the FP32 mantissa to 1 bit with the
-// usual bias trick and rebias the exponent (127 -> 1).  |q| < 1 is the
-// subnormal range with step 0.5: round 2|q| to an integer (0, 1 or 2).
-__device__ __forceinline__ uint32_t e2m1_rne(float q) {
-  uint32_t sign = (__float_as_uint(q) >> 28) & 8u;
-  float a = fminf(fabsf(q), 6.0f);
-  uint32_t ua = __float_as_uint(a);
-  uint32_t nrm = ((ua + 0x1FFFFFu + ((ua >> 22) & 1u)) >> 22) - 252u;
-  uint32_t sub = (uint32_t)__builtin_rintf(a * 2.0f);
-  return sign | ((a < 1.0f) ? sub : nrm);
-}
-
 // Eight values -> eight RNE codes packed into a dword (element j in nibble j)
 // with gfx950's FP32 -> FP4 converter at unit scale, two values per
-// instruction.  Its results equal e2m1_rne() on every non-NaN FP32 input
-// (checked exhaustively on the hardware over all 2^32 bit patterns).
+// instruction.  Its results equal the oracle's round-to-nearest-even encoder
+// on every non-NaN FP32 input: tests/test_hw_converters.py sweeps all 2^32
+// bit patterns through this function on the GPU.
 __device__ __forceinline__ uint32_t e2m1_rne8(const float *q) {
   // The four converts write bytes 0..3, so the word's initial value never
   // shows; any live register will do (no zeroing move needed).
@@ -105,6 +85,44 @@ __device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t u16) {
   const float t = __builtin_ldexpf(a, 1 - (int)e);          // a * 2^(1 - e), in [0, 4), exact
   const uint32_t up = ((float)u16 < __builtin_amdgcn_fractf(t) * 65536.0f) ? 1u : 0u;
   return sign | (2u * e + (uint32_t)t + up);
+}
+
+// ---------------------------------------------------------------------------
+// GEMM operand decode (E2M1 code x E4M3 block scale -> FP16, exact)
+// ---------------------------------------------------------------------------
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+// Two E4M3 scale bytes (bits 0..7 and 8..15 of w) -> two FP16 values S * 2^-8
+// in one dword: an E4M3 code shifted left by 7 and read as FP16 is its value
+// times 2^-8 (exponent fields line up; subnormal codes become FP16
+// subnormals).  The converter's scale of 256 below supplies the missing 2^8.
+__device__ __forceinline__ half2_t scale_pair_lo(uint32_t w) {
+  return __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, w, 0x0C010C00u) << 7);
+}
+
+// Eight E2M1 codes times (S * 2^-8): the converter at scale 2^8 (exact, a
+// power of two) gives code * 256, and one packed multiply per pair gives
+// code * S, exact in FP16 (at most 6 significant bits, at least 2^-10).
+// tests/test_hw_converters.py checks every code against every scale byte.
+__device__ __forceinline__ half8_t decode8_s256(uint32_t codes, _Float16 s) {
+  const half2_t s2 = {s, s};
+  const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * s2;
+  const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * s2;
+  const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * s2;
+  const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * s2;
+  return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Two FP32 values -> two BF16 (round to nearest even) in one dword, the
+// first in the low half: gfx950's v_cvt_pk_bf16_f32 (the GEMM epilogue's
+// convert; tests/test_hw_converters.py sweeps every FP32 pattern through it).
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  typedef float float2_v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  const float2_v y2 = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(y2, bf16x2_v));
 }
 
 // ---------------------------------------------------------------------------
@@ -203,32 +221,6 @@ __device__ __forceinline__ void rht16(float (&v)[16], uint32_t mask) {
 // |w| (bits m): rounding is monotone, so fl(max|w| / 4) = max fl(|w| / 4).
 __device__ __forceinline__ uint32_t quarter_max_bits(uint32_t m) {
   return __float_as_uint(__uint_as_float(m) * 0.25f);
-}
-
-// The same transform when a 16-block is split over a lane pair (even lane:
-// elements 0..7, odd lane: 8..15).  Spans 1, 2, 4 stay inside the lane; span 8
-// pairs element j of the even lane with element j of the odd lane.
-__device__ __forceinline__ void rht16_pair(float (&v)[8], uint32_t mask, bool odd) {
-  const uint32_t m = odd ? (mask >> 8) : mask;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((m >> j) & 1u) << 31));
-#pragma unroll
-  for (int h = 1; h < 8; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i & h) continue;
-      const float a = v[i], b = v[i + h];
-      v[i] = a + b;
-      v[i + h] = a - b;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float p = lane_xor1(v[j]);
-    v[j] = odd ? (p - v[j]) : (v[j] + p);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = v[j] * 0.25f;
 }
 
 // ---------------------------------------------------------------------------

@@ -49,34 +49,17 @@
 // kGroupM tile rows, to keep A and B panels in that XCD's L2.
 #include <hip/hip_runtime.h>
 
-#include <cstdio>
-#include <cstdlib>
 #include <type_traits>
 #include <utility>
 
+#include "device_codec.hpp"
 #include "internal.hpp"
 
-#ifndef NVFP4_GEMM_INTERLEAVE
-#define NVFP4_GEMM_INTERLEAVE 5
-#endif
-#ifndef NVFP4_GEMM_W8
-#define NVFP4_GEMM_W8 1
-#endif
-#ifndef NVFP4_GEMM_F4_PIPE
-#define NVFP4_GEMM_F4_PIPE 1
-#endif
-#ifndef NVFP4_GEMM_SWIZZLE
-#define NVFP4_GEMM_SWIZZLE 2
-#endif
 
 namespace nvfp4 {
 namespace {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BM = 256, BK = 128;
@@ -84,6 +67,9 @@ constexpr int kThreads = 256;
 constexpr int kRowBytes = BK / 2;  // 64 code bytes per row per K step
 constexpr int kFragM = 4;          // 32-row A fragments per wavefront
 constexpr int kGroupM = 8;         // tile rows per L2 group
+// VALU instructions the scheduler places after each MFMA of a pipelined
+// sub-step (the decode of the next sub-step); 4 and 5 measured best.
+constexpr int kInterleave = 5;
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
 // maxima (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -91,15 +77,7 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // LDS placement of the 16-byte code chunk `part` (0..3) of tile row `row`.
 // Fragment reads take the same part from 32 consecutive rows; XOR-ing the
 // part with row bits spreads those reads over all LDS banks.
-__device__ __forceinline__ int chunk_slot(int row, int part) {
-#if NVFP4_GEMM_SWIZZLE == 1
-  return row * 4 + (part ^ ((row >> 1) & 3));
-#elif NVFP4_GEMM_SWIZZLE == 2
-  return row * 4 + (part ^ ((row >> 2) & 3));
-#else
-  return row * 4 + part;
-#endif
-}
+__device__ __forceinline__ int chunk_slot(int row, int part) { return row * 4 + (part ^ ((row >> 2) & 3)); }
 
 struct GemmArgs {
   const uint8_t *a_codes, *a_scales;
@@ -121,26 +99,6 @@ struct alignas(16) Stage {
   uint2 as[BM];
   uint2 bs[kBN];
 };
-
-// Two E4M3 scale bytes (bits 0..7 and 8..15 of w) -> two FP16 values S * 2^-8
-// in one dword: an E4M3 code shifted left by 7 and read as FP16 is its value
-// times 2^-8 (exponent fields line up; subnormal codes become FP16
-// subnormals).  The converter's scale of 256 supplies the missing 2^8.
-__device__ __forceinline__ half2_t scale_pair_lo(uint32_t w) {
-  return __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, w, 0x0C010C00u) << 7);
-}
-
-// Eight E2M1 codes times (S * 2^-8): the converter at scale 2^8 (exact, a
-// power of two) gives code * 256, and one packed multiply per pair gives
-// code * S, exact in FP16 (at most 6 significant bits, at least 2^-10).
-__device__ __forceinline__ half8_t decode8_s256(uint32_t codes, _Float16 s) {
-  const half2_t s2 = {s, s};
-  const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * s2;
-  const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * s2;
-  const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * s2;
-  const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * s2;
-  return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
 
 // global_load_lds of 16 / 4 bytes per lane into the 64 consecutive lane
 // slots at LDS byte address `lds` (wavefront-uniform, through M0), from the
@@ -356,16 +314,14 @@ __device__ __forceinline__ void mfma_and_decode(const HalfCodes<kFragN> &r, cons
   half8_t na[kFragM], nb[kFragN];
   decode_substep<kNext, kFragN>(r, sc, na, nb);
   mfma_substep<kFragN>(acc, av, bv);
-#if NVFP4_GEMM_INTERLEAVE
   // One wavefront per SIMD issues in order, so VALU work only overlaps an
   // MFMA if it sits between MFMAs: ask for kFragM * kFragN groups of one
   // MFMA followed by a few VALU instructions.
 #pragma unroll
   for (int i = 0; i < kFragM * kFragN; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_GEMM_INTERLEAVE, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kInterleave, 0);
   }
-#endif
 #pragma unroll
   for (int f = 0; f < kFragM; ++f) av[f] = na[f];
 #pragma unroll
@@ -496,8 +452,7 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[kFragM][kFragN]
         const bool ok0 = col_ok && (full || r < g.M), ok1 = col_ok && (full || r + 1 < g.M);
         if constexpr (kBF16Out) {
           // v_cvt_pk_bf16_f32: two FP32 -> BF16, round to nearest even
-          const float2_t y2 = {acc[i][j][v] * sc, acc[i][j][v + 1] * sc};
-          const uint32_t b2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(y2, bf16x2_t));
+          const uint32_t b2 = pack_bf16x2_rne(acc[i][j][v] * sc, acc[i][j][v + 1] * sc);
           if (ok0) pr[32 * j] = (uint16_t)b2;
           if (ok1) pr[g.ldc + 32 * j] = (uint16_t)(b2 >> 16);
         } else {
@@ -574,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
       pipelined_kstep<kFragN, kOff32>(st0, st1, src, kt, ksteps, c, r0, r1, sc0, sc1, av, bv, acc);
       if (kt + 1 < ksteps) pipelined_kstep<kFragN, kOff32>(st1, st0, src, kt + 1, ksteps, c, r0, r1, sc1, sc0, av, bv, acc);
     }
-  } else if constexpr (kFast && NVFP4_GEMM_F4_PIPE) {
+  } else if constexpr (kFast) {
     const TileSrc src{ac, as, bc, bs, g.M, g.N, g.K, m0, n0};
     const LaneCoord c{wm, wn, h, r32};
     if (ksteps > 0) {
@@ -598,62 +553,6 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
     for (int kt = 0; kt < ksteps; kt += 2) {
       pipelined_kstep_lite<kFragN, kOff32>(st0, st1, src, kt, ksteps, c, r, sc, av, bv, acc);
       if (kt + 1 < ksteps) pipelined_kstep_lite<kFragN, kOff32>(st1, st0, src, kt + 1, ksteps, c, r, sc, av, bv, acc);
-    }
-  } else if constexpr (kFast) {
-    // 256 x 256 tiles: the accumulators take all 256 AGPRs, which leaves no
-    // room for the pipelined loop's second code and operand buffers.  A K
-    // step reads its codes from LDS, issues the global->LDS loads of the
-    // next step, then decodes and multiplies.
-    if (ksteps > 0) {
-      lds_load_operand<BM, kOff32>(ac, as, g.M, g.K, m0, 0, st0.a, st0.as);
-      lds_load_operand<kBN, kOff32>(bc, bs, g.N, g.K, n0, 0, st0.b, st0.bs);
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // assembly stage loads: see above
-    __syncthreads();
-    for (int kt = 0; kt < ksteps; ++kt) {
-      const Stage<kBN> &cur = (kt & 1) ? st1 : st0;
-      Stage<kBN> &nxt = (kt & 1) ? st0 : st1;
-      uint4 ca[kFragM][2], cb[kFragN][2];
-      half2_t sa[kFragM][2], sb[kFragN][2];
-#pragma unroll
-      for (int f = 0; f < kFragM; ++f) {
-        const int r = wm * 128 + f * 32 + r32;
-        ca[f][0] = *reinterpret_cast<const uint4 *>(cur.a + 16 * chunk_slot(r, 2 * h));
-        ca[f][1] = *reinterpret_cast<const uint4 *>(cur.a + 16 * chunk_slot(r, 2 * h + 1));
-        const uint32_t w = h ? cur.as[r].y : cur.as[r].x;
-        sa[f][0] = scale_pair_lo(w);
-        sa[f][1] = scale_pair_lo(w >> 16);
-      }
-#pragma unroll
-      for (int f = 0; f < kFragN; ++f) {
-        const int r = wn * (32 * kFragN) + f * 32 + r32;
-        cb[f][0] = *reinterpret_cast<const uint4 *>(cur.b + 16 * chunk_slot(r, 2 * h));
-        cb[f][1] = *reinterpret_cast<const uint4 *>(cur.b + 16 * chunk_slot(r, 2 * h + 1));
-        const uint32_t w = h ? cur.bs[r].y : cur.bs[r].x;
-        sb[f][0] = scale_pair_lo(w);
-        sb[f][1] = scale_pair_lo(w >> 16);
-      }
-      // Issued after this step's LDS reads, so no read waits on them.
-      if (kt + 1 < ksteps) {
-        lds_load_operand<BM, kOff32>(ac, as, g.M, g.K, m0, (int64_t)(kt + 1) * BK, nxt.a, nxt.as);
-        lds_load_operand<kBN, kOff32>(bc, bs, g.N, g.K, n0, (int64_t)(kt + 1) * BK, nxt.b, nxt.bs);
-      }
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        half8_t av[kFragM], bv[kFragN];
-#pragma unroll
-        for (int f = 0; f < kFragM; ++f) av[f] = decode8_s256(word_of(ca[f][s >> 2], s & 3), sa[f][s >> 2][(s >> 1) & 1]);
-#pragma unroll
-        for (int f = 0; f < kFragN; ++f) bv[f] = decode8_s256(word_of(cb[f][s >> 2], s & 3), sb[f][s >> 2][(s >> 1) & 1]);
-        mfma_substep<kFragN>(acc, av, bv);
-      }
-      // The next stage must have landed before the barrier.  The scheduling
-      // fences keep the wait below this step's math (hoisted, it would wait
-      // for the loads just issued) and the MFMAs above the barrier.
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
     }
   } else {
     StagedLoad<BM> la;
@@ -966,7 +865,6 @@ __global__ __launch_bounds__(kW8Threads) void gemm_nvfp4_w8_kernel(GemmArgs g) {
   const int arow = wm * 128 + r32, brow = wn * 96 + r32;
   // The chunk swizzle of the lane's rows (the same for rows 32 apart).
   const int qa = chunk_slot(arow, 0) & 3, qb = chunk_slot(brow, 0) & 3;
-  static_assert(NVFP4_GEMM_SWIZZLE >= 0 && NVFP4_GEMM_SWIZZLE <= 2, "XOR swizzles on row bits below 5");
 
   const uint8_t *ac = g.a_codes + batch * g.M * (g.K / 2);
   const uint8_t *as = g.a_scales + batch * g.M * (g.K / 16);
@@ -1036,7 +934,7 @@ struct TilePick {
   int bm, bn;
 };
 
-TilePick pick_tiles(int64_t M, int64_t N, int64_t batch, bool fast) {
+TilePick pick_tiles(int64_t M, int64_t N, int64_t batch, bool fast, int force_bm, int force_bn) {
   struct Cand {
     int kind, bm, bn;
     double cost;
@@ -1047,7 +945,7 @@ TilePick pick_tiles(int64_t M, int64_t N, int64_t batch, bool fast) {
   double best = 1e300;
   TilePick pick{4, 256, 256};
   for (const Cand &c : cands) {
-    if (c.need_fast && (!fast || !NVFP4_GEMM_W8)) continue;
+    if (c.need_fast && !fast) continue;
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * batch;
     const double t = (double)((tiles + 255) / 256) * c.bm * c.bn * c.cost;
     if (t < best - 1e-9) {
@@ -1055,12 +953,12 @@ TilePick pick_tiles(int64_t M, int64_t N, int64_t batch, bool fast) {
       pick = TilePick{c.kind, c.bm, c.bn};
     }
   }
-  // Testing / tuning override, e.g. NVFP4_GEMM_TILE=512x192.
-  if (const char *env = std::getenv("NVFP4_GEMM_TILE")) {
-    int bm = 0, bn = 0;
-    if (std::sscanf(env, "%dx%d", &bm, &bn) == 2)
-      for (const Cand &c : cands)
-        if (c.bm == bm && c.bn == bn && (fast || !c.need_fast)) pick = TilePick{c.kind, c.bm, c.bn};
+  // A requested tile (tuning and tests) replaces the choice where its
+  // kernel applies; otherwise the request is refused.
+  if (force_bm != 0 || force_bn != 0) {
+    pick = TilePick{-1, 0, 0};
+    for (const Cand &c : cands)
+      if (c.bm == force_bm && c.bn == force_bn && (fast || !c.need_fast)) pick = TilePick{c.kind, c.bm, c.bn};
   }
   return pick;
 }
@@ -1089,7 +987,8 @@ nvfp4_status launch_gemm(const GemmProblem &p, hipStream_t s) {
   const bool fast = p.K % BK == 0;
   const bool small = p.M * (p.K / 2) < ((int64_t)1 << 31) && p.N * (p.K / 2) < ((int64_t)1 << 31) &&
                      p.M < (1 << 24) && p.N < (1 << 24) && p.K / 2 < (1 << 24);
-  const TilePick tp = pick_tiles(p.M, p.N, p.batch, fast && small);
+  const TilePick tp = pick_tiles(p.M, p.N, p.batch, fast && small, p.tile_m, p.tile_n);
+  if (tp.kind < 0) return NVFP4_EUNSUPPORTED;
   const int64_t tm = (p.M + tp.bm - 1) / tp.bm, tn = (p.N + tp.bn - 1) / tp.bn;
   if (tm * tn > 0x7FFFFFFF) return NVFP4_EUNSUPPORTED;
   g.tiles_m = (int)tm;

@@ -10,22 +10,28 @@
 namespace nvfp4 {
 
 // Control words of one quantize workspace (4 KB, zero before first use).
-// Two-pass path: the amax accumulator and the encode-pass completion counter
-// are restored to zero by the last workgroup of each call.  Single-pass
-// path: counters that only grow, so nothing needs clearing.  `release`
-// counts completed single-pass calls (the current call's epoch); `arrive`
-// spreads the arrivals of one call over 8 counters, the last arrival at each
-// bumps `top`, and the last of those publishes the next epoch in `release`.
-// Per-epoch-parity amax slots are cleared one call ahead.  Every word sits
-// on its own 128-byte line so the atomics spread over memory channels.
+// Two-pass path: the amax slots and the encode-pass completion counter are
+// restored to zero by the last workgroup of each call.  Single-pass path: a
+// grid barrier in two levels -- a workgroup adds one to arrive[blockIdx mod 8],
+// the last arrival at a slot (it knows the launch's slot sizes) stores the
+// slot back to zero and adds one to `top`, and the last of those stores `top`
+// back to zero and publishes the next epoch in `release`.  Every call thus
+// starts from zero counters whatever the grid size of the call before it.
+// `release` counts completed single-pass calls (the current call's epoch);
+// per-epoch-parity amax slots are cleared one call ahead.  The `fin` words
+// count finished workgroups the same way, so that the last workgroup of the
+// grid writes the tensor scale once every barrier wait of the call has either
+// completed or expired.  Every word sits on its own 128-byte line so the
+// atomics spread over memory channels.
 struct QuantCtrl {
-  uint32_t reserved;   // zero
+  uint32_t spin_limit; // single-pass: polls before a barrier wait gives up; 0 = the default (about 1 s)
   uint32_t done;       // two-pass: workgroups finished with the encode pass
-  uint32_t timeout;    // single-pass: nonzero if a bounded barrier wait expired
+  uint32_t timeout;    // single-pass: nonzero once a barrier wait expired (kept until the caller clears it)
   uint32_t pad0[29];
   struct alignas(128) Counter {
     unsigned long long v;
-    uint32_t pad[30];
+    uint32_t fin;
+    uint32_t pad[29];
   } arrive[8], top, release;
   struct alignas(128) Slot {
     uint32_t v;
@@ -78,6 +84,7 @@ struct GemmProblem {
   bool c_bf16;
   int64_t ldc, bstride_c;
   float alpha;
+  int tile_m, tile_n;  // 0, 0: automatic choice; otherwise a requested workgroup tile
 };
 
 nvfp4_status launch_quantize(const QuantProblem &p, hipStream_t stream);

@@ -43,20 +43,9 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;           // two-pass kernels
-#ifndef NVFP4_FUSED_THREADS
-#define NVFP4_FUSED_THREADS 1024
-#endif
-constexpr int kFusedThreads = NVFP4_FUSED_THREADS;  // single-pass kernel, one workgroup per CU
-constexpr int kFusedPerCU = 1;
+constexpr int kFusedThreads = 1024;     // single-pass kernel, one workgroup per CU
 constexpr int kBatch = 4;               // two-pass row kernels: blocks loaded per lane before use
 constexpr uint32_t kSpinLimit = 1u << 22;  // polls before a barrier wait gives up (~1 s)
-
-#ifndef NVFP4_FUSED_COOPERATIVE
-#define NVFP4_FUSED_COOPERATIVE 0
-#endif
-#ifndef NVFP4_FUSED_DISABLE
-#define NVFP4_FUSED_DISABLE 0
-#endif
 
 template <bool kBF16, bool kRHT, bool kSR>
 struct Fused {
@@ -192,31 +181,68 @@ __device__ __forceinline__ uint32_t load_amax(const QuantCtrl *ctrl) {
   return m;
 }
 
-// Single-pass grid barrier, thread 0 of each workgroup: arrive at epoch e
-// and wait for its release.  The last workgroup of each slot (workgroups
-// with index = slot mod 8) bumps `top`; the last of those publishes e + 1.
-// All control words are device-scope atomics at the coherence point, so
-// relaxed ordering plus the caller's explicit completion waits suffice
-// (acquire/release would flush and invalidate the L2 on every poll).  The
-// wait is bounded; on expiry the timeout word is set and the kernel still
-// finishes.
-__device__ __forceinline__ void fused_arrive_wait(QuantCtrl *ctrl, uint32_t e, int slot) {
-  const unsigned n_slots = min(gridDim.x, 8u);
-  const unsigned long long in_slot = gridDim.x / 8 + ((unsigned)slot < gridDim.x % 8 ? 1 : 0);
+// Workgroups per barrier slot (slot = blockIdx mod 8) and slots in use, for
+// the launch's own grid size.
+__device__ __forceinline__ unsigned slots_in_use() { return min(gridDim.x, 8u); }
+__device__ __forceinline__ unsigned per_slot(int slot) {
+  return gridDim.x / 8 + ((unsigned)slot < gridDim.x % 8 ? 1u : 0u);
+}
+
+// Single-pass grid barrier, thread 0 of each workgroup: arrive at epoch e and
+// wait for its release.  The last arrival at a slot stores the slot's counter
+// back to zero and bumps `top`; the last of those stores `top` back to zero
+// and publishes e + 1.  Nothing else touches these counters until the kernel
+// ends, so the next call (ordered after this one on its stream) starts from
+// zero whatever its grid size.  All control words are device-scope atomics at
+// the coherence point, so relaxed ordering plus the caller's explicit
+// completion waits suffice (acquire/release would flush and invalidate the L2
+// on every poll).  The wait is bounded: on expiry the sticky timeout word is
+// set (completed before the workgroup goes on) and true is returned; the
+// kernel still finishes, and its last workgroup then writes a NaN tensor
+// scale.
+__device__ __forceinline__ bool fused_arrive_wait(QuantCtrl *ctrl, unsigned long long e, int slot) {
   const unsigned long long old =
       __hip_atomic_fetch_add(&ctrl->arrive[slot].v, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if ((old + 1) % in_slot == 0) {
+  if (old + 1 == per_slot(slot)) {
+    atomic_store_dev(&ctrl->arrive[slot].v, 0ull);
     const unsigned long long t = __hip_atomic_fetch_add(&ctrl->top.v, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((t + 1) % n_slots == 0) atomic_store_dev(&ctrl->release.v, (unsigned long long)e + 1);
+    if (t + 1 == slots_in_use()) {
+      atomic_store_dev(&ctrl->top.v, 0ull);
+      atomic_store_dev(&ctrl->release.v, e + 1);
+    }
   }
+  const uint32_t lim = atomic_load_dev(&ctrl->spin_limit);
+  const uint32_t limit = lim ? lim : kSpinLimit;
   for (uint32_t spin = 0;; ++spin) {
-    if (atomic_load_dev(&ctrl->release.v) > e) break;
-    if (spin >= kSpinLimit) {
-      atomic_store_dev(&ctrl->timeout, 1u);
-      break;
+    if (atomic_load_dev(&ctrl->release.v) > e) return false;
+    if (spin >= limit) {
+      wait_for(__hip_atomic_fetch_or(&ctrl->timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      return true;
     }
     __builtin_amdgcn_s_sleep(2);
   }
+}
+
+// Thread 0 of each workgroup at the end of a single-pass kernel: true for the
+// last workgroup of the grid to get here (counted like the barrier's
+// arrivals, in the `fin` words, each restored to zero by its last arrival).
+// Every workgroup has passed or given up its barrier wait before it counts,
+// and a workgroup that gave up set the timeout word before that, so the last
+// one sees every expiry of the call.
+__device__ __forceinline__ bool fused_last_to_finish(QuantCtrl *ctrl, int slot) {
+  const uint32_t old = __hip_atomic_fetch_add(&ctrl->arrive[slot].fin, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (old + 1 != per_slot(slot)) return false;
+  atomic_store_dev(&ctrl->arrive[slot].fin, 0u);
+  const uint32_t t = __hip_atomic_fetch_add(&ctrl->top.fin, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (t + 1 != slots_in_use()) return false;
+  atomic_store_dev(&ctrl->top.fin, 0u);
+  return true;
+}
+
+// The tensor scale a single-pass call publishes: s_t, or NaN once any barrier
+// wait on this workspace has expired (the codes are then unreliable).
+__device__ __forceinline__ float published_scale(const QuantCtrl *ctrl, float st) {
+  return atomic_load_dev(&ctrl->timeout) != 0u ? __builtin_nanf("") : st;
 }
 
 // Workgroup max -> one atomicMax per workgroup into slot blockIdx mod 8
@@ -387,7 +413,7 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
   constexpr int kWaves = kFusedThreads / 64;
   __shared__ float recip[kMaxJobs][128];
   __shared__ uint32_t part[kWaves][kMaxJobs];
-  __shared__ uint32_t s_epoch;
+  __shared__ unsigned long long s_epoch;
   __shared__ float s_st[kMaxJobs];
   QuantCtrl *ctrl = a.ctrl;
   const int slot = blockIdx.x & 7;
@@ -397,7 +423,7 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
 
   // The epoch (completed single-pass calls on this workspace) cannot advance
   // before this workgroup arrives, so reading it here is race free.
-  if (threadIdx.x == 0) s_epoch = (uint32_t)atomic_load_dev(&ctrl->release.v);
+  if (threadIdx.x == 0) s_epoch = atomic_load_dev(&ctrl->release.v);
 
   // 32-bit indices throughout: the launcher only runs this kernel within its
   // capacity (at most kMax segments per wavefront of one grid).
@@ -497,7 +523,7 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
   // invalidate the L2 on every poll).  The wait is bounded; on expiry the
   // timeout word is set and the kernel still finishes.
   if (threadIdx.x == 0) {
-    const uint32_t e = s_epoch;
+    const unsigned long long e = s_epoch;
     // Slots of the next epoch are unused since the call before this one
     // ended.  Every table entry that has slots is cleared, not only this
     // call's jobs: a later call on the workspace may have more jobs.
@@ -516,7 +542,7 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
                                                    __HIP_MEMORY_SCOPE_AGENT);
       wait_for(prev);  // the max is performed before this workgroup counts as arrived
     }
-    fused_arrive_wait(ctrl, e, slot);
+    (void)fused_arrive_wait(ctrl, e, slot);
     for (int j = 0; j < njobs; ++j) {
       uint32_t am = 0;
 #pragma unroll
@@ -556,7 +582,8 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
     // block's unpacked values at once would exceed the register budget.
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (blockIdx.x == 0 && threadIdx.x < (unsigned)njobs) *a.job[threadIdx.x].tensor_scale = s_st[threadIdx.x];
+  if (threadIdx.x == 0 && fused_last_to_finish(ctrl, slot))
+    for (int j = 0; j < njobs; ++j) *a.job[j].tensor_scale = published_scale(ctrl, s_st[j]);
 }
 
 template <bool kBF16, bool kRHT, bool kContig>
@@ -822,12 +849,12 @@ __global__ __launch_bounds__(kRB * kColFusedCG) void col_fused_kernel(ColArgs a)
   __shared__ uint2 tile_codes[kColFusedCG * 8][kColFusedRB + 1];
   __shared__ uint8_t tile_scales[kColFusedCG * 8][kColFusedRB + 4];
   __shared__ uint32_t part[kColFusedThreads / 64];
-  __shared__ uint32_t s_epoch;
+  __shared__ unsigned long long s_epoch;
   __shared__ float s_st;
   QuantCtrl *ctrl = a.ctrl;
   const int slot = blockIdx.x & 7;
   // The epoch cannot advance before this workgroup arrives: race free.
-  if (threadIdx.x == 0) s_epoch = (uint32_t)atomic_load_dev(&ctrl->release.v);
+  if (threadIdx.x == 0) s_epoch = atomic_load_dev(&ctrl->release.v);
   const uint32_t mask = kRHT ? rht_sign_mask(a.rht_seed) : 0u;
 
   const int64_t bid = blockIdx.x;
@@ -865,7 +892,7 @@ __global__ __launch_bounds__(kRB * kColFusedCG) void col_fused_kernel(ColArgs a)
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t e = s_epoch;
+    const unsigned long long e = s_epoch;
     if (blockIdx.x == 0) {  // slots of the next epoch: unused since the call before this one ended
 #pragma unroll
       for (int i = 0; i < 8; ++i) atomic_store_dev(&ctrl->amax[(e + 1) & 1][i].v, 0u);
@@ -875,7 +902,7 @@ __global__ __launch_bounds__(kRB * kColFusedCG) void col_fused_kernel(ColArgs a)
     const uint32_t prev =
         __hip_atomic_fetch_max(&ctrl->amax[e & 1][slot].v, wm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wait_for(prev);  // the max is performed before this workgroup counts as arrived
-    fused_arrive_wait(ctrl, e, slot);
+    (void)fused_arrive_wait(ctrl, e, slot);
     uint32_t am = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) am = max(am, atomic_load_dev(&ctrl->amax[e & 1][i].v));
@@ -929,7 +956,7 @@ __global__ __launch_bounds__(kRB * kColFusedCG) void col_fused_kernel(ColArgs a)
       a.scales[vrow * RB + r] = tile_scales[tcol][trbl];
     }
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.tensor_scale = st;
+  if (threadIdx.x == 0 && fused_last_to_finish(ctrl, slot)) *a.tensor_scale = published_scale(ctrl, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -990,17 +1017,12 @@ bool try_row_fused(FusedArgs a, hipStream_t s, hipError_t &err) {
   const int cus = cu_count();
   if (cus <= 0) return false;
   auto kernel = row_fused_kernel<kBF16, kRHT, kSR>;
-  if (occupancy<row_fused_kernel<kBF16, kRHT, kSR>, kFusedThreads>() < kFusedPerCU) return false;
-  const uint64_t grid = (uint64_t)cus * kFusedPerCU;
+  if (occupancy<row_fused_kernel<kBF16, kRHT, kSR>, kFusedThreads>() < 1) return false;
+  const uint64_t grid = (uint64_t)cus;
   const uint64_t nwaves = grid * (kFusedThreads / 64);
   const uint64_t iters = (a.nseg + nwaves - 1) / nwaves;
   if (iters > (uint64_t)Fused<kBF16, kRHT, kSR>::kMaxBlocks) return false;
   a.nseg_iters = (uint32_t)iters;
-#if NVFP4_FUSED_COOPERATIVE
-  void *args[] = {&a};
-  err = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)grid),
-                                   dim3(kFusedThreads), args, 0, s);
-#else
   // A plain launch: with one workgroup per CU every workgroup becomes
   // resident once kernels already running on other streams drain, so the
   // grid barrier completes; the bounded wait only guards against a kernel
@@ -1008,7 +1030,6 @@ bool try_row_fused(FusedArgs a, hipStream_t s, hipError_t &err) {
   // guarantee up front but costs ~18 us per call on MI355X.)
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kFusedThreads), 0, s, a);
   err = hipGetLastError();
-#endif
   return err == hipSuccess;
 }
 
@@ -1043,8 +1064,8 @@ template <bool kBF16, bool kRHT, bool kSR>
 hipError_t run_row(const RowArgs &a, bool contig, hipStream_t s) {
   if (contig) {
     hipError_t err = hipSuccess;
-    if (!NVFP4_FUSED_DISABLE && try_row_fused<kBF16, kRHT, kSR>(fused_single(a), s, err)) return hipSuccess;
-    (void)hipGetLastError();  // a refused cooperative launch falls back to two passes
+    if (try_row_fused<kBF16, kRHT, kSR>(fused_single(a), s, err)) return hipSuccess;
+    if (err != hipSuccess) return err;  // a launch that was refused is reported, not retried
     return run_row_two_pass<kBF16, kRHT, kSR, true>(a, s);
   }
   return run_row_two_pass<kBF16, kRHT, kSR, false>(a, s);
@@ -1080,15 +1101,16 @@ template <bool kRHT, bool kSR>
 bool try_col_fused(const ColArgs &a, hipStream_t s, hipError_t &err) {
   const int cus = cu_count();
   if (cus <= 0) return false;
-  return launch_col_fused<32, kRHT, kSR>(a, cus, s, err) || launch_col_fused<64, kRHT, kSR>(a, cus, s, err);
+  if (launch_col_fused<32, kRHT, kSR>(a, cus, s, err)) return true;
+  return err == hipSuccess && launch_col_fused<64, kRHT, kSR>(a, cus, s, err);
 }
 
 template <bool kBF16, bool kRHT, bool kSR>
 hipError_t run_col(const ColArgs &a, hipStream_t s) {
   if constexpr (kBF16) {
     hipError_t err = hipSuccess;
-    if (!NVFP4_FUSED_DISABLE && try_col_fused<kRHT, kSR>(a, s, err)) return hipSuccess;
-    (void)hipGetLastError();
+    if (try_col_fused<kRHT, kSR>(a, s, err)) return hipSuccess;
+    if (err != hipSuccess) return err;
   }
   const uint64_t g = (uint64_t)(a.batch * a.tiles_r * a.tiles_c);
   if (g > 0x7FFFFFFFull) return hipErrorInvalidValue;
@@ -1135,7 +1157,7 @@ nvfp4_status launch_quantize_group(const QuantGroupProblem &p, hipStream_t s) {
     ++n;
   }
   for (int i = 0; i < kMaxGroup; ++i) a.job[i].amax = p.amax[i];  // all four, see row_fused_kernel
-  if (contig && n > 0 && !NVFP4_FUSED_DISABLE) {
+  if (contig && n > 0) {
     a.njobs = n;
     a.nseg = seg;
     a.ctrl = p.ctrl_group;
@@ -1153,7 +1175,7 @@ nvfp4_status launch_quantize_group(const QuantGroupProblem &p, hipStream_t s) {
       }
       return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
     }
-    (void)hipGetLastError();
+    if (err != hipSuccess) return NVFP4_EHIP;
   }
   for (int i = 0; i < p.njobs; ++i) {
     QuantProblem q = p.job[i];

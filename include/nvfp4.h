@@ -2,18 +2,21 @@
  * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 quantize + block-scaled GEMM
  * library (libnvfp4.so).
  *
- * What the library computes.  The pages this follows describe NVFP4 as a
- * 4-bit floating-point format for the weights and activations that enter the
- * GEMMs of LLM linear layers, with BF16/FP32 kept for the accumulators and a
- * dedicated scaling scheme because the 4-bit grid is sparse
- * ("NVIDIA acelera o pre-treinamento de LLM: NVFP4 no Blackwell em conjunto
- * com JAX e MaxText", sections "Por Que Cada Porcento E Importante" and
- * "Como o Treinamento Mixed-Precision Funciona com NVFP4"); Hadamard mixing
- * and stochastic rounding appear in "Full-Stack FP4: Stable LLM Pretraining
- * with Quantized Projections, Optimizers, and Attention", section 2.2, and
- * NVFP4 GEMMs for linear-layer training in the same page's section 1 and in
- * "NVFP4 Treina com Precisao de 16 Bits ...", section "Contexto e
- * background".  The concrete encoding used here:
+ * Pages cited below, by title:
+ *   [P1] "NVFP4 Treina com Precisao de 16 Bits e a Velocidade de 4 Bits para
+ *        Pre-treinamento em Grande Escala"
+ *   [P2] "NVIDIA acelera o pre-treinamento de LLM: NVFP4 no Blackwell em
+ *        conjunto com JAX e MaxText"
+ *   [P3] "Full-Stack FP4: Stable LLM Pretraining with Quantized Projections,
+ *        Optimizers, and Attention"
+ *
+ * What the library computes.  NVFP4 is a 4-bit floating-point format for the
+ * weights and activations that enter the GEMMs of LLM training, with BF16 or
+ * FP32 kept for the accumulators ([P2] "Como o Treinamento Mixed-Precision
+ * Funciona com NVFP4"); the 4-bit grid is sparse, so it comes with its own
+ * scaling scheme ([P2] "Por Que Cada Porcento E Importante").  Hadamard
+ * mixing before quantization and stochastic rounding come from [P3] section
+ * 2.2.  The pages leave the encoding open; the one used here:
  *   - element: OCP MX E2M1 (values +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}), two codes
  *     per byte, element 2j in the low nibble of byte j;
  *   - block scale: OCP FP8 E4M3FN, one per 16 consecutive elements along the
@@ -32,25 +35,31 @@
  *   - Pointers named in a struct or argument as "device" are device memory of
  *     the current HIP device; the structs themselves are host memory read
  *     during the call only.  The caller owns every buffer.
- *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
- *     enqueues work on `stream`; it never synchronises and never allocates.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call except
+ *     nvfp4_quantize_workspace_check only enqueues work on `stream`; none
+ *     allocates.
  *   - Synchronous return codes report argument errors (checked before any HIP
- *     call) and launch failures.  Data-dependent problems are not reported:
- *     inputs must be finite and the tensor amax either 0 or >= 2^-100; a
- *     non-finite input leaves a non-finite tensor scale and unspecified codes.
- *   - Workspaces must be zero-filled before their first use.  Each call leaves
- *     the workspace ready for the next one (two-pass words are restored to
- *     zero; the single-pass barrier's counters only grow and need no reset),
- *     so a workspace can be reused by later calls on the same stream without
- *     clearing.  Calls that are in flight at the same time need separate
- *     workspaces.  After an NVFP4_EHIP error, zero the workspace again.
+ *     call) and launch failures.  Inputs must be finite and the tensor amax
+ *     either 0 or >= 2^-100; a non-finite input leaves a non-finite tensor
+ *     scale and unspecified codes.
+ *   - Workspaces must be zero-filled before their first use.  Each call
+ *     leaves the workspace ready for the next one (every counter a call uses
+ *     is restored to zero by that call, whatever the grid size of the calls
+ *     before or after it), so a workspace can be reused by later calls on the
+ *     same stream without clearing.  Calls in flight at the same time need
+ *     separate workspaces.  After NVFP4_EHIP or a barrier time-out (below),
+ *     zero the workspace again.
  *   - Single-pass quantize launches (one workgroup per CU) meet at a
  *     grid-wide barrier for the tensor amax, so they need every CU to become
  *     free while they run.  The wait is bounded (about a second): if other
- *     work holds CUs for longer, the 32-bit word at byte offset 8 of the
- *     workspace (of the group launch's control block for
- *     nvfp4_quantize_group) becomes nonzero and that call's results are
- *     unspecified.
+ *     work holds CUs for longer, the call's tensor scale is written as NaN
+ *     (so every GEMM output that uses it is NaN) and the 32-bit time-out
+ *     word at byte offset 8 of the control block becomes nonzero.  The word
+ *     stays set, and every later single-pass call on that workspace also
+ *     writes a NaN tensor scale, until the caller zeroes the workspace;
+ *     nvfp4_quantize_workspace_check reports it.  The 32-bit word at byte
+ *     offset 0 of a control block, if nonzero, replaces the default poll
+ *     limit of that wait (for tests that force the time-out).
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -68,8 +77,9 @@ typedef enum nvfp4_status {
   NVFP4_ESHAPE = 2,      /* contraction length not a multiple of 16, negative or oversized extents */
   NVFP4_EALIGN = 3,      /* a pointer or stride breaks the alignment stated below */
   NVFP4_EUNSUPPORTED = 4,/* a valid request the library does not implement */
-  NVFP4_EHIP = 5,        /* the HIP runtime refused a launch */
-  NVFP4_EWORKSPACE = 6   /* workspace missing or smaller than the *_workspace_size() figure */
+  NVFP4_EHIP = 5,        /* the HIP runtime refused a launch or a copy */
+  NVFP4_EWORKSPACE = 6,  /* workspace missing or smaller than the *_workspace_size() figure */
+  NVFP4_ETIMEOUT = 7     /* a single-pass barrier wait on this workspace expired (results unreliable) */
 } nvfp4_status;
 
 typedef enum nvfp4_dtype { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
@@ -80,20 +90,27 @@ typedef enum nvfp4_rounding { NVFP4_RNE = 0, NVFP4_SR = 1 } nvfp4_rounding;
 typedef enum nvfp4_axis { NVFP4_ALONG_COLS = 0, NVFP4_ALONG_ROWS = 1 } nvfp4_axis;
 
 /* One quantized view [batch][rows][cols], cols = contraction length (a
- * multiple of 16).  All three arrays are dense and owned by the caller:
+ * multiple of 16): the 4-bit weights or activations of [P2] "Como o
+ * Treinamento Mixed-Precision Funciona com NVFP4" with their scaling scheme
+ * ([P2] "Por Que Cada Porcento E Importante").  All three arrays are dense
+ * and owned by the caller:
  *   codes        device, batch*rows*cols/2 bytes, 16-byte aligned;
  *   scales       device, batch*rows*cols/16 bytes (E4M3FN bit patterns,
  *                row-major, no swizzle), 4-byte aligned;
- *   tensor_scale device, one float: written by nvfp4_quantize, read on the
- *                device by nvfp4_gemm (no host round trip). */
+ *   tensor_scale device, one float (s_t), 4-byte aligned; written by the
+ *                quantizer and read by the GEMM on the device (never copied
+ *                to the host). */
 typedef struct nvfp4_qtensor {
   uint8_t *codes;
   uint8_t *scales;
   float *tensor_scale;
-  int64_t batch, rows, cols;
+  int64_t batch;
+  int64_t rows;
+  int64_t cols;
 } nvfp4_qtensor;
 
-/* Quantizer options.  rounding: an nvfp4_rounding.  rht: 0/1, apply the
+/* Quantizer options ([P3] section 2.2: Hadamard mixing before quantization,
+ * stochastic rounding).  rounding: an nvfp4_rounding.  rht: 0/1, apply the
  * 16-point random Hadamard transform along the contraction dimension first;
  * its +-1 diagonal is bit j of word 0 of Philox4x32-10(counter = (0, 0,
  * 0xFFFFFFFF, 0), key = rht_seed).  Stochastic rounding of logical element n
@@ -116,10 +133,13 @@ const char *nvfp4_status_string(int32_t status);
 /* Library ABI version, (major << 16) | minor. */
 int32_t nvfp4_version(void);
 
-/* Bytes of workspace nvfp4_quantize needs (a small control block). */
+/* Bytes of workspace nvfp4_quantize needs (one 4 KiB control block). */
 size_t nvfp4_quantize_workspace_size(void);
 
-/* Quantize x to NVFP4.
+/* Quantize x to NVFP4: the per-tensor / per-block scaling of [P2] "Por Que
+ * Cada Porcento E Importante" applied to a weight, activation or gradient
+ * that enters a GEMM ([P2] "Como o Treinamento Mixed-Precision Funciona com
+ * NVFP4"), with the options of [P3] section 2.2.
  *   x            device, [batch][rows][cols] elements of x_dtype with row
  *                stride ld >= cols and batch stride batch_stride >= rows*ld
  *                (elements).  ALONG_COLS: x, ld*esize and batch_stride*esize
@@ -133,15 +153,15 @@ size_t nvfp4_quantize_workspace_size(void);
  *                and cols must equal the view's shape.
  *   workspace    device, >= nvfp4_quantize_workspace_size() bytes, zeroed
  *                before first use, 256-byte aligned.
- * Empty tensors (batch, rows or cols = 0) are valid: nothing is written
- * except tensor_scale = 0. */
+ * One tensor scale covers the whole view, all batches included (also for
+ * batched attention operands).  Empty tensors (batch, rows or cols = 0) are
+ * valid: nothing is written except tensor_scale = 0. */
 nvfp4_status nvfp4_quantize(const void *x, int32_t x_dtype, int64_t batch, int64_t rows,
                             int64_t cols, int64_t ld, int64_t batch_stride, int32_t axis,
                             const nvfp4_quant_opts *opts, const nvfp4_qtensor *out,
                             void *workspace, size_t workspace_bytes, void *stream);
 
-/* One tensor of a grouped quantization: the input view and its destination,
- * with the meaning nvfp4_quantize gives them for axis ALONG_COLS. */
+/* One tensor of nvfp4_quantize_group: x as for nvfp4_quantize (ALONG_COLS). */
 typedef struct nvfp4_quant_job {
   const void *x;
   int64_t batch, rows, cols, ld, batch_stride;
@@ -151,41 +171,64 @@ typedef struct nvfp4_quant_job {
 /* Bytes of workspace nvfp4_quantize_group needs (16 KiB). */
 size_t nvfp4_quantize_group_workspace_size(void);
 
-/* Quantize 1..4 tensors along their contiguous dimension with the same input
- * dtype and options, each with its own tensor scale: the result equals
+/* Quantize the operands of one GEMM -- the weights and activations of [P2]
+ * "Como o Treinamento Mixed-Precision Funciona com NVFP4" -- together: 1..4
+ * tensors along their contiguous dimension with the same input dtype and
+ * options, each with its own tensor scale.  The result equals
  * nvfp4_quantize on every job in turn (axis ALONG_COLS, same opts), bit for
  * bit.  Contiguous inputs (ld == cols, dense batches) whose blocks fit the
  * single-pass capacity together (on 256 CUs 37.7M BF16 elements, 29.4M
  * with both the transform and stochastic rounding, 16.8M FP32) are
  * quantized in one launch that reads every input once; other groups run as
- * separate calls.  Each job is validated as for
- * nvfp4_quantize.  The workspace (>= nvfp4_quantize_group_workspace_size(),
- * 256-byte aligned) follows the same rules: zeroed before first use, left
- * reusable by each call, one per concurrently running call. */
+ * separate calls.  Each job is validated as for nvfp4_quantize.  The
+ * workspace (>= nvfp4_quantize_group_workspace_size(), 256-byte aligned)
+ * follows the same rules: zeroed before first use, left reusable by each
+ * call, one per concurrently running call. */
 nvfp4_status nvfp4_quantize_group(const nvfp4_quant_job *jobs, int32_t njobs, int32_t x_dtype,
                                   const nvfp4_quant_opts *opts, void *workspace, size_t workspace_bytes,
                                   void *stream);
 
-/* Block-scaled GEMM, both operands quantized along K ("NT" form):
+/* Diagnostic, and the one call that synchronises: waits for `stream`, then
+ * reads the time-out word(s) of a quantize workspace (the one control block
+ * of a >= 4 KiB workspace, both of a >= 16 KiB group workspace).  Returns
+ * NVFP4_OK, NVFP4_ETIMEOUT if a single-pass barrier wait on it expired since
+ * it was last zeroed, or an argument / NVFP4_EHIP error. */
+nvfp4_status nvfp4_quantize_workspace_check(const void *workspace, size_t workspace_bytes, void *stream);
+
+/* Block-scaled GEMM of two NVFP4 operands with wide accumulation, the GEMM
+ * of [P2] "Como o Treinamento Mixed-Precision Funciona com NVFP4" (NVFP4
+ * weights and activations, BF16/FP32 accumulators) and of [P3] section 1
+ * (linear projections); batched, it is the QK^T scores product that [P3]
+ * section 2.4 runs in NVFP4.  Both operands are quantized along K ("NT"):
  *   C[b][i][j] = alpha * sA * sB * sum_k A^[b][i][k] * B^[b][j][k]
  * with A^ = E2M1 * E4M3 (exact), sA/sB the tensor scales read on the device.
  * Accumulation is FP32; the epilogue multiplies by fl(fl(sA*sB)*alpha) and
  * stores FP32, or BF16 rounded to nearest even.
- *   a, b         host structs: a is [batch][M][K], b is [batch][N][K].
+ *   a, b         host structs: a is [batch][M][K], b is [batch][N][K]
+ *                (batch <= 65535 when the output is not empty).
  *   c            device, c_dtype elements, row stride ldc >= N, batch stride
  *                batch_stride_c >= M*ldc (elements), aligned to the element.
- * Any M, N >= 0 and K a multiple of 16 (K = 0 gives zeros).
- * The kernel and tile shape are chosen per problem.  The environment
- * variable NVFP4_GEMM_TILE, read at every call, overrides that choice for
- * testing and tuning: "512x192" or "256x384" (eight-wavefront kernel, used
- * only where K % 128 == 0 and each operand's codes are under 2 GiB),
- * "256x256", "256x192" or "256x128" (four-wavefront kernel); unset, empty or
- * anything else keeps the automatic choice.  Results agree to the FP32
- * accumulation-order tolerance whatever the tile. */
+ * Any M, N >= 0 and K a multiple of 16 (K = 0 gives zeros).  The kernel and
+ * tile shape are chosen per problem; results agree with the exact product
+ * to the FP32 accumulation-order tolerance whatever the tile. */
 nvfp4_status nvfp4_gemm(const nvfp4_qtensor *a, const nvfp4_qtensor *b, void *c, int32_t c_dtype,
                         int64_t ldc, int64_t batch_stride_c, float alpha, void *stream);
 
-/* Linear-layer training step in NVFP4 (all operands BF16, row-major):
+/* nvfp4_gemm with a requested workgroup tile (tile_m x tile_n), for tuning
+ * and tests; the same product as nvfp4_gemm ([P2] "Como o Treinamento
+ * Mixed-Precision Funciona com NVFP4").  tile_m = tile_n = 0 is the automatic
+ * choice.  Tiles: 512x192 and 256x384 (eight-wavefront kernel; only where
+ * K % 128 == 0 and each operand's codes are under 2 GiB), 256x256, 256x192
+ * and 256x128 (four-wavefront kernel).  A tile that is not in this list or
+ * does not apply to the problem returns NVFP4_EUNSUPPORTED. */
+nvfp4_status nvfp4_gemm_ex(const nvfp4_qtensor *a, const nvfp4_qtensor *b, void *c, int32_t c_dtype,
+                           int64_t ldc, int64_t batch_stride_c, float alpha, int32_t tile_m,
+                           int32_t tile_n, void *stream);
+
+/* Linear-layer training step in NVFP4: the quantized linear projections of
+ * [P3] sections 1 and 2.1 (forward and backward GEMMs in NVFP4), stochastic
+ * rounding and Hadamard mixing of [P3] section 2.2 on the gradient-side
+ * operands; all inputs BF16, row-major:
  *   Fprop  Y  = X W^T  : X [M][K] and W [N][K] along K, RNE.
  *   Dgrad  dX = dY W   : dY [M][N] along N with stochastic rounding
  *                        (stream 1); W^T along N (transposing), RNE.
@@ -194,7 +237,8 @@ nvfp4_status nvfp4_gemm(const nvfp4_qtensor *a, const nvfp4_qtensor *b, void *c,
  *                        rounding on dY^T (stream 2) and, when wgrad_sr_x is
  *                        nonzero, on X^T (stream 3; RNE otherwise).
  * Y [M][N] and dX [M][K] are BF16; dW [N][K] has dtype dw_dtype.
- * M, N, K must be multiples of 16; all pointers 16-byte aligned. */
+ * M, N, K must be multiples of 16; all pointers 16-byte aligned.  The six
+ * quantized views stay in the workspace after the call (nvfp4_linear_view). */
 typedef struct nvfp4_linear_cfg {
   uint64_t sr_seed;
   uint64_t rht_seed;
@@ -203,13 +247,24 @@ typedef struct nvfp4_linear_cfg {
 } nvfp4_linear_cfg;
 
 /* Bytes of workspace for nvfp4_linear_fwd_bwd: the six quantized views and
- * their control blocks.  Zero it before first use. */
+ * their control blocks (0 for invalid sizes).  Zero it before first use. */
 size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K);
 
 nvfp4_status nvfp4_linear_fwd_bwd(const void *x, const void *w, const void *dy, void *y,
                                   void *dx, void *dw, int64_t M, int64_t N, int64_t K,
                                   const nvfp4_linear_cfg *cfg, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/* Describe quantized view `which` of a linear workspace (host computation
+ * only, no HIP call), so that the views the step made can be reused instead
+ * of quantized again -- the reuse of quantized views between forward and
+ * backward of [P3] section 2.4:
+ *   0: X [M][K]   1: W [N][K]   2: dY [M][N] (SR, stream 1)   3: W^T [K][N]
+ *   4: dY^T [N][M] (RHT + SR, stream 2)   5: X^T [K][M] (RHT, SR stream 3
+ *   or RNE).  Contents are defined once an nvfp4_linear_fwd_bwd call on this
+ *   workspace has run on its stream. */
+nvfp4_status nvfp4_linear_view(void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                               int64_t K, int32_t which, nvfp4_qtensor *out);
 
 #ifdef __cplusplus
 }

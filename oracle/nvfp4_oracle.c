@@ -154,6 +154,14 @@ void oracle_e4m3_encode_rne_sat_array(const float *y, int64_t n, uint8_t *out) {
     out[i] = (uint8_t)oracle_e4m3_encode_rne_sat(y[i]);
 }
 
+/* Stochastic rounding of each of nq values under every 16-bit word:
+ * out[i * 65536 + u] = oracle_e2m1_encode_sr(q[i], u). */
+void oracle_e2m1_encode_sr_all_words(const float *q, int64_t nq, uint8_t *out) {
+  for (int64_t i = 0; i < nq; ++i)
+    for (uint32_t u = 0; u < 65536u; ++u)
+      out[i * 65536 + u] = (uint8_t)oracle_e2m1_encode_sr(q[i], u);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As   */
 /* Easy as 1, 2, 3", SC'11): 10 rounds of two 32x32->64 multiplies with an   */

@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_e4m3_encode_rne_sat.restype = ctypes.c_int
         L.oracle_e2m1_encode_rne_array.argtypes = [vp, i64, vp]
         L.oracle_e4m3_encode_rne_sat_array.argtypes = [vp, i64, vp]
+        L.oracle_e2m1_encode_sr_all_words.argtypes = [vp, i64, vp]
         L.oracle_philox4x32_10.argtypes = [vp, vp, vp]
         L.oracle_sr_word.argtypes = [u64, u32, u64]
         L.oracle_sr_word.restype = u32
@@ -111,6 +112,14 @@ def e4m3_encode_array(y: np.ndarray) -> np.ndarray:
     y = np.ascontiguousarray(y, dtype=np.float32)
     out = np.empty(y.shape, dtype=np.uint8)
     lib().oracle_e4m3_encode_rne_sat_array(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def e2m1_encode_sr_all_words(q: np.ndarray) -> np.ndarray:
+    """[len(q)][65536] codes: every value of q under every 16-bit word."""
+    q = np.ascontiguousarray(q, dtype=np.float32).reshape(-1)
+    out = np.empty((q.size, 65536), dtype=np.uint8)
+    lib().oracle_e2m1_encode_sr_all_words(_ptr(q), q.size, _ptr(out))
     return out
 
 

@@ -11,6 +11,9 @@ Acceptance (the reading used throughout):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -66,7 +69,8 @@ def bf16_rne_bits(y: np.ndarray) -> np.ndarray:
     y = np.asarray(y, dtype=np.float64)
     out = np.zeros(y.shape, dtype=np.int64)
     nz = y != 0
-    e = np.floor(np.log2(np.abs(y[nz])))
+    # BF16 shares FP32's exponent range: below 2^-126 the spacing stays 2^-133
+    e = np.maximum(np.floor(np.log2(np.abs(y[nz]))), -126.0)
     scale = np.exp2(e - 7)
     r = np.round(y[nz] / scale) * scale  # half-to-even on an exact quotient
     out[nz] = (np.float32(r).view(np.uint32) >> 16).astype(np.int64)
@@ -97,19 +101,63 @@ def check_gemm(y: np.ndarray, y_ref: np.ndarray, sabs: np.ndarray, bf16: bool, w
     return {"n": y.size, "ulp_ok": int(ulp_ok.sum()), "cancel_only": int((~ulp_ok & cancel_ok).sum())}
 
 
+def host_threads() -> int:
+    """CPU threads for the oracle (the box's share: at most 16)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def gemm_ref_tasks(qa: O.QTensor, qb: O.QTensor, alpha: float, tasks, mem_cap: float = 8e9):
+    """O.gemm_ref over a list of (batch index, row array) tasks, each task
+    split into row chunks, in threads (ctypes releases the GIL).  The number
+    of threads keeps the oracle's per-call decoded copy of B (N*K doubles)
+    under mem_cap bytes in total.  Returns [(y_ref, sabs)] in task order."""
+    per_call = 8.0 * qb.rows * qb.cols
+    nthr = max(1, min(host_threads(), int(mem_cap // max(per_call, 1.0))))
+    jobs = []
+    for ti, (bi, rows) in enumerate(tasks):
+        rows = np.asarray(rows, dtype=np.int64)
+        nchunk = max(1, min(nthr, rows.size // 16)) if len(tasks) < nthr else 1
+        for part in np.array_split(rows, nchunk):
+            if part.size:
+                jobs.append((ti, int(bi), part))
+    with ThreadPoolExecutor(nthr) as ex:
+        res = list(ex.map(lambda j: O.gemm_ref(qa, qb, alpha, j[1], j[2]), jobs))
+    out = []
+    for ti in range(len(tasks)):
+        parts = [r for j, r in zip(jobs, res) if j[0] == ti]
+        out.append((np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])))
+    return out
+
+
 def gemm_vs_oracle(qa_gpu: nv.QTensor, qb_gpu: nv.QTensor, out_dtype=torch.bfloat16, alpha=1.0,
-                   rows=None, batches=None, what: str = "") -> dict:
+                   rows=None, batches=None, what: str = "", tile=None, rows_per_batch=None) -> dict:
     """Run the GPU GEMM on device views, compare selected rows of selected
-    batch entries with the oracle reference computed from the same codes."""
-    y = nv.gemm(qa_gpu, qb_gpu, out_dtype=out_dtype, alpha=alpha)
+    batch entries with the oracle reference computed from the same codes.
+    ``rows_per_batch`` (dict batch -> rows) overrides ``rows``/``batches``."""
+    y = nv.gemm(qa_gpu, qb_gpu, out_dtype=out_dtype, alpha=alpha, tile=tile)
     y3 = y if y.dim() == 3 else y.unsqueeze(0)
     qa, qb = to_oracle_view(qa_gpu), to_oracle_view(qb_gpu)
-    stats = {"n": 0}
-    for bi in (range(qa.batch) if batches is None else batches):
+    return compare_output(y3, qa, qb, alpha, out_dtype == torch.bfloat16, what, rows=rows, batches=batches,
+                          rows_per_batch=rows_per_batch)
+
+
+def compare_output(y3: torch.Tensor, qa: O.QTensor, qb: O.QTensor, alpha: float, bf16: bool, what: str,
+                   rows=None, batches=None, rows_per_batch=None) -> dict:
+    """Check rows of a [batch][M][N] device output against the oracle."""
+    if rows_per_batch is None:
         sel = np.arange(qa.rows) if rows is None else np.asarray(rows)
-        y_ref, sabs = O.gemm_ref(qa, qb, alpha, int(bi), sel)
+        rows_per_batch = {int(bi): sel for bi in (range(qa.batch) if batches is None else batches)}
+    tasks = [(bi, np.asarray(r, dtype=np.int64)) for bi, r in rows_per_batch.items()]
+    refs = gemm_ref_tasks(qa, qb, alpha, tasks)
+    stats = {"n": 0, "rows": 0}
+    for (bi, sel), (y_ref, sabs) in zip(tasks, refs):
         got = y3[bi][torch.as_tensor(sel, device=y3.device)].float().cpu().numpy()
-        s = check_gemm(got, y_ref, sabs, out_dtype == torch.bfloat16, f"{what} batch {bi}")
+        s = check_gemm(got, y_ref, sabs, bf16, f"{what} batch {bi}")
         for k, v in s.items():
             stats[k] = stats.get(k, 0) + v
+        stats["rows"] += sel.size
     return stats

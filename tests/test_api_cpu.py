@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    for s in range(7):
+    for s in range(8):
         assert nv.status_string(s) and nv.status_string(s) != "unknown status"
     assert nv.status_string(99) == "unknown status"
     assert nv.nvfp4_version() >> 16 == 1
@@ -109,6 +109,47 @@ def test_gemm_argument_errors():
     assert nv.nvfp4_gemm(_q(1, 64, 128, st=0), b, FAKE, nv.F32, 32, 0, 1.0, None) == nv.EINVAL
     assert nv.nvfp4_gemm(_q(2, 64, 128), _q(2, 32, 128), FAKE, nv.F32, 32, 10, 1.0, None) == nv.ESHAPE
     assert nv.nvfp4_gemm(_q(70000, 1, 16), _q(70000, 1, 16), FAKE, nv.F32, 1, 1, 1.0, None) == nv.EUNSUPPORTED
+
+
+def test_gemm_ex_argument_errors():
+    a, b = _q(1, 64, 128), _q(1, 32, 128)
+    f = nv.nvfp4_gemm_ex
+    assert f(None, b, FAKE, nv.F32, 32, 0, 1.0, 0, 0, None) == nv.EINVAL
+    assert f(a, b, FAKE, nv.F32, 32, 0, 1.0, -1, 192, None) == nv.EINVAL     # negative tile
+    assert f(a, b, FAKE, nv.F32, 32, 0, 1.0, 0, 192, None) == nv.EINVAL      # half a request
+    assert f(a, b, FAKE, nv.F32, 16, 0, 1.0, 0, 0, None) == nv.ESHAPE        # ldc < N (validated first)
+
+
+def test_quantize_workspace_check_argument_errors():
+    f = nv.nvfp4_quantize_workspace_check
+    assert f(None, 4096, None) == nv.EWORKSPACE
+    assert f(FAKE, 4095, None) == nv.EWORKSPACE
+    assert f(FAKE + 64, 4096, None) == nv.EALIGN
+
+
+def test_linear_view_describes_the_workspace_layout():
+    """nvfp4_linear_view is host arithmetic only: the six views' shapes, and
+    codes / scales / tensor-scale regions that are 256-byte aligned, in
+    order, disjoint and inside the workspace."""
+    M, N, K = 8192, 4096, 4096
+    need = nv.nvfp4_linear_workspace_size(M, N, K)
+    base = 1 << 20
+    shapes = [(M, K), (N, K), (M, N), (K, N), (N, M), (K, M)]
+    end = base
+    for i, (r, c) in enumerate(shapes):
+        q = nv.QTensorC()
+        assert nv.nvfp4_linear_view(base, need, M, N, K, i, q) == nv.OK
+        assert (q.batch, q.rows, q.cols) == (1, r, c)
+        regions = [(q.codes, r * c // 2), (q.scales, r * c // 16), (q.tensor_scale, 4)]
+        for p, n in regions:
+            assert p % 256 == 0 and p >= end
+            end = p + n
+    assert end <= base + need
+    q = nv.QTensorC()
+    assert nv.nvfp4_linear_view(base, need, M, N, K, 6, q) == nv.EINVAL
+    assert nv.nvfp4_linear_view(base, need - 1, M, N, K, 0, q) == nv.EWORKSPACE
+    assert nv.nvfp4_linear_view(base, need, M, N, 40, 0, q) == nv.ESHAPE
+    assert nv.nvfp4_linear_view(0, need, M, N, K, 0, q) == nv.EINVAL
 
 
 def test_linear_argument_errors_and_workspace_size():

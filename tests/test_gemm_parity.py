@@ -123,42 +123,44 @@ def test_bound_calls_repeat_the_unbound_results():
         assert torch.equal(y, y_ref)
 
 
-# Forced tiles (NVFP4_GEMM_TILE): every kernel and tile shape on ragged
+# Forced tiles (nvfp4_gemm_ex): every kernel and tile shape on ragged
 # problems.  The eight-wavefront kernel (512 x 192 and 256 x 384) keeps three
 # LDS stages in flight and unrolls the K loop by three, so K steps of 1..5
 # cover every remainder and the refills issued past the last step.
-FORCED = [("512x192", 520, 200, 128, 1), ("512x192", 1000, 700, 256, 1), ("512x192", 1030, 390, 384, 1),
-          ("512x192", 600, 800, 512, 2), ("512x192", 700, 500, 640, 1), ("256x384", 300, 770, 384, 1),
-          ("256x384", 520, 400, 640, 2), ("256x256", 300, 300, 384, 1), ("256x192", 300, 200, 256, 1),
-          ("256x128", 300, 200, 272, 1)]
+FORCED = [((512, 192), 520, 200, 128, 1), ((512, 192), 1000, 700, 256, 1), ((512, 192), 1030, 390, 384, 1),
+          ((512, 192), 600, 800, 512, 2), ((512, 192), 700, 500, 640, 1), ((256, 384), 300, 770, 384, 1),
+          ((256, 384), 520, 400, 640, 2), ((256, 256), 300, 300, 384, 1), ((256, 192), 300, 200, 256, 1),
+          ((256, 128), 300, 200, 272, 1), ((256, 256), 300, 300, 272, 1), ((256, 192), 260, 200, 400, 1)]
 
 
 @pytest.mark.parametrize("tile,M,N,K,batch", FORCED)
-def test_gemm_forced_tiles(tile, M, N, K, batch, monkeypatch):
-    monkeypatch.setenv("NVFP4_GEMM_TILE", tile)
+def test_gemm_forced_tiles(tile, M, N, K, batch):
     a, b = _pair(M, N, K, batch, 11 * M + N + K)
     qa, qb = gpu_quant(a), gpu_quant(b)
     for dt in (torch.float32, torch.bfloat16):
-        stats = gemm_vs_oracle(qa, qb, out_dtype=dt, alpha=0.5, what=f"{tile} {M}x{N}x{K}x{batch}")
+        stats = gemm_vs_oracle(qa, qb, out_dtype=dt, alpha=0.5, what=f"{tile} {M}x{N}x{K}x{batch}", tile=tile)
         assert stats["n"] == M * N * batch
 
 
-@pytest.mark.parametrize("tile", ["512x192", "256x384"])
-def test_gemm_forced_tiles_wide_range(tile, monkeypatch):
+@pytest.mark.parametrize("tile", [(512, 192), (256, 384)])
+def test_gemm_forced_tiles_wide_range(tile):
     """Per-row magnitudes over 2^-12..2^5 give subnormal block scales, whose
     FP16 form (S * 2^-8) is an FP16 subnormal in the eight-wavefront decode."""
-    monkeypatch.setenv("NVFP4_GEMM_TILE", tile)
     a, b = _pair(640, 420, 512, 1, 29, wide=True)
     qa, qb = gpu_quant(a), gpu_quant(b)
     assert int(to_oracle_view(qa).scales.min()) < 8  # subnormal E4M3 scales present
     for dt in (torch.float32, torch.bfloat16):
-        gemm_vs_oracle(qa, qb, out_dtype=dt, what=f"wide {tile}")
+        gemm_vs_oracle(qa, qb, out_dtype=dt, what=f"wide {tile}", tile=tile)
 
 
-def test_gemm_tile_override_ignored_where_not_applicable(monkeypatch):
-    """The eight-wavefront tiles need K % 128 == 0; elsewhere the override is
-    ignored and the automatic choice runs."""
-    monkeypatch.setenv("NVFP4_GEMM_TILE", "512x192")
+def test_gemm_tile_request_refused_where_not_applicable():
+    """The eight-wavefront tiles need K % 128 == 0, and only the listed tiles
+    exist: other requests are refused before any launch; the automatic
+    choice (0, 0) still runs."""
     a, b = _pair(200, 100, 272, 1, 31)
     qa, qb = gpu_quant(a), gpu_quant(b)
-    gemm_vs_oracle(qa, qb, out_dtype=torch.float32, what="override ignored")
+    for tile in [(512, 192), (256, 384), (128, 128), (0, 64)]:
+        with pytest.raises(nv.NVFP4Error) as e:
+            nv.gemm(qa, qb, out_dtype=torch.float32, tile=tile)
+        assert e.value.status in (nv.EUNSUPPORTED, nv.EINVAL)
+    gemm_vs_oracle(qa, qb, out_dtype=torch.float32, what="automatic", tile=(0, 0))

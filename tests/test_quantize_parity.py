@@ -146,3 +146,76 @@ def test_quantize_fprop_full_size(name):
     for key in ("X", "W"):
         got = to_oracle_view(gpu_quant(t[key]))
         assert_quant_equal(got, oracle_quant(t[key]), key)
+
+
+def test_barrier_counters_start_from_zero_whatever_the_grid():
+    """Single-pass calls with different grid sizes on one workspace: a
+    transposing call of 8 workgroups, a full-size row call (one workgroup
+    per CU, every one holding data), a transposing call of 32 workgroups, a
+    row call again.  Each call's barrier counters start from zero, so every
+    result is bit-exact, and the arrival and finish counters are back at
+    zero afterwards."""
+    import bit_block_scaled_nvfp4_amd as nv
+    ws = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), "cuda:0")
+    full = W.fprop_3b()["X"]                           # 8192 x 3072: six segments per wavefront
+    small = _input((512, 1024), 60, "bf16")            # transposed: 8 tiles of 512 x 128
+    medium = (_input((2048, 2048), 61, "f32") * 3.0).to(torch.bfloat16)  # transposed: 64 tiles
+    seq = [(small, O.ALONG_ROWS), (full, O.ALONG_COLS), (medium, O.ALONG_ROWS), (full, O.ALONG_COLS),
+           (small, O.ALONG_COLS)]
+    for i, (x, axis) in enumerate(seq):
+        kw = dict(axis=axis, rounding=O.SR if i % 2 else O.RNE, sr_seed=17, sr_stream=i)
+        q = nv.quantize(x.to("cuda:0"), workspace=ws, **kw)
+        assert_quant_equal(to_oracle_view(q), oracle_quant(x, **kw), f"call {i} {tuple(x.shape)} axis {axis}")
+    torch.cuda.synchronize()
+    w = ws.cpu()
+    counters = w[128:128 + 9 * 128].view(-1, 128)      # arrive[0..7] and top: value and finish words
+    assert int(counters[:, :12].sum()) == 0
+    assert int(w[8:12].view(torch.int32)[0]) == 0       # no time-out
+    assert nv.quantize_workspace_check(ws) == nv.OK
+
+
+def _force_timeout(ws: torch.Tensor, base: int) -> None:
+    """Make the single-pass barrier of the control block at byte `base` give
+    up at once: poll limit 8, and slot 0's arrival counter preset far beyond
+    any grid's slot size, so slot 0 never completes and the release is never
+    published.  Every workgroup still runs to its end."""
+    ws[base:base + 4].view(torch.int32)[0] = 8
+    ws[base + 128:base + 136].view(torch.int64)[0] = 1 << 40
+
+
+@pytest.mark.parametrize("path", ["row", "col", "group"])
+def test_barrier_timeout_poisons_the_tensor_scale(path):
+    """A single-pass call whose barrier wait expires (forced from the host
+    with a tiny poll limit) returns, finishes every kernel, sets the time-out
+    word and publishes a NaN tensor scale, so the GEMM output is NaN; the
+    word stays set for later calls on that workspace until it is zeroed."""
+    import math
+    import bit_block_scaled_nvfp4_amd as nv
+    x = _input((512, 1024), 70, "bf16").to("cuda:0")
+    if path == "group":
+        ws = nv.new_workspace(nv.nvfp4_quantize_group_workspace_size(), "cuda:0")
+        _force_timeout(ws, 4096)
+        run = lambda: nv.quantize_group([x, x[:256]], workspace=ws)[0]
+        word = 4096 + 8
+    else:
+        ws = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), "cuda:0")
+        _force_timeout(ws, 0)
+        axis = O.ALONG_ROWS if path == "col" else O.ALONG_COLS
+        run = lambda: nv.quantize(x, axis=axis, workspace=ws)
+        word = 8
+    q = run()
+    torch.cuda.synchronize()
+    assert math.isnan(q.tensor_scale.item())
+    assert int(ws[word:word + 4].view(torch.int32)[0].item()) == 1
+    assert nv.quantize_workspace_check(ws) == nv.ETIMEOUT
+    y = nv.gemm(q, q, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(y).all())
+    q2 = run()  # sticky: still poisoned
+    torch.cuda.synchronize()
+    assert math.isnan(q2.tensor_scale.item())
+    ws.zero_()  # zeroed, the workspace is good again
+    q3 = run()
+    torch.cuda.synchronize()
+    assert not math.isnan(q3.tensor_scale.item())
+    assert nv.quantize_workspace_check(ws) == nv.OK
