@@ -5,22 +5,31 @@
 One step is one pass of the whole path over one batch of synthetic input:
 quantize X and W (RNE, one grouped call: a single launch when both fit the
 single-pass kernel), GEMM Y = X^ W^^T (BF16 out), all on one stream with the
-inputs already resident in HBM.  Inputs rotate over enough
-copies to exceed twice the 256 MB Infinity Cache, so every step reads its
-operands from HBM.  The step time comes from the host clock around K timed
-steps, bracketed by device synchronisation; per-kernel times from HIP events
-recorded on the launch stream around each kernel during K further steps
-(kept out of the timed region because each event adds idle time between
-kernels).
+inputs already resident in HBM.  Inputs rotate over enough copies to exceed
+twice the 256 MB Infinity Cache, so every step reads its operands from HBM.
+
+Order of work:
+  1. per-call timing: each call of the step launched alone, back to back
+     (`reps` launches over the rotating buffers between two HIP events on the
+     launch stream; the mean is the kernel duration plus the launch gap), and
+     isolated (one launch between events after a device synchronisation);
+  2. W untimed warm-up steps, then exactly K timed steps bracketed by device
+     synchronisation, timed by the host clock;
+  3. the CPU oracle on the same step (the `cpu_baseline` leg), which also
+     checks this run's outputs against the oracle.
 
 Prints one JSON line.  `value` is the whole-step NVFP4 GEMM throughput
-(2*M*N*K per step time, TFLOP/s); `roofline` describes the dominant kernel
-(the GEMM) against the dense FP16/BF16 MFMA peak, with `traffic` the HBM
-bytes per launch from the committed counter summary (null once the GEMM
-source changed); `mfma_ceiling` is the sustained rate of the MFMA
-instruction itself for constant, random and NVFP4-valued operands on this
-GPU; `cpu_baseline` times the CPU oracle (test infrastructure) on a bounded
-sample of the same step.
+(2*M*N*K per step time, TFLOP/s).  `roofline` describes the dominant kernel
+(the GEMM, or the attention-scores write) from its back-to-back duration:
+achieved = algorithmic flops (or bytes) per launch / duration, against the
+dense FP16 MFMA peak (or HBM), with `traffic` the HBM bytes per launch from
+the committed rocprofv3 counter summary (null once the library sources have
+changed since).  `kernels` has every call's back-to-back and isolated times
+and its rates, also as a fraction of the copy bandwidth measured in the same
+run.  `mfma_ceiling` is the sustained rate of the MFMA instruction itself
+for constant, random and NVFP4-valued operands on this GPU.  `cpu_baseline`
+times the oracle (test infrastructure) on the same step over the host's
+cores and reports the parity of this run's outputs against it.
 """
 from __future__ import annotations
 
@@ -45,6 +54,7 @@ PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense FP16/BF16 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 CACHE_BYTES = 256 << 20    # Infinity Cache
 QUANT_BYTES_PER_ELEM = 2 + 0.5 + 1.0 / 16  # BF16 in, E2M1 codes + E4M3 scales out
+MAX_HOST_THREADS = 16      # the CPU share of one GPU on the measurement boxes
 
 
 def parse():
@@ -54,13 +64,20 @@ def parse():
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="fprop_3b",
                    choices=["fprop_3b", "mlp_up_12b", "linear_train", "attn_scores"])
+    p.add_argument("--reps", type=int, default=50, help="back-to-back launches per call in the per-call timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-mfma-ceiling", action="store_true", help="skip the MFMA ceiling probe")
-    p.add_argument("--cpu-rows", type=int, default=2048,
-                   help="GEMM rows in the CPU-oracle sample (about 10 s of one core at the fprop_3b shape)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run 5 device-to-device copies of MIB MiB (calibrates HBM byte counters)")
     return p.parse_args()
+
+
+def host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(MAX_HOST_THREADS, n))
 
 
 def mfma_ceiling():
@@ -128,27 +145,53 @@ def copy_probe(mib: int) -> None:
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
 
 
-def cpu_baseline(x_cpu: torch.Tensor, w_cpu: torch.Tensor, rows: int) -> dict:
-    """The oracle as it stands, single-threaded: full quantization of X and W
-    plus the FP64 reference GEMM on `rows` rows of X, extrapolated linearly in
-    rows to the full step."""
-    from oracle import oracle as O
-    M, K = x_cpu.shape
-    N = w_cpu.shape[0]
-    xb, wb = W.bf16_bits(x_cpu), W.bf16_bits(w_cpu)
-    t0 = time.perf_counter()
-    qx = O.quantize(xb, O.BF16)
-    qw = O.quantize(wb, O.BF16)
-    t_quant = time.perf_counter() - t0
-    sel = np.linspace(0, M - 1, rows).astype(np.int64)
-    t0 = time.perf_counter()
-    O.gemm_ref(qx, qw, 1.0, 0, sel)
-    t_gemm = time.perf_counter() - t0
-    t_step = t_quant + t_gemm * (M / rows)
-    return {"value": 2.0 * M * N * K / t_step / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle quantize of all of X ({M}x{K}) and W ({N}x{K}) in {t_quant:.2f} s plus "
-                      f"the FP64 reference GEMM on {rows} of {M} rows in {t_gemm:.2f} s, "
-                      f"extrapolated linearly to the full step ({t_step:.1f} s)"}
+def copy_bandwidth(nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Device-to-device copy rate in GB/s (bytes read + bytes written per
+    second), the practical bandwidth the HBM-bound kernels compare with."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+
+
+def time_back_to_back(calls, reps: int) -> float:
+    """Mean microseconds per call of `reps` launches (cycling over the
+    rotating buffer sets' `calls`) between two events on the launch stream."""
+    for c in calls[:2]:
+        c()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        calls[i % len(calls)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def time_isolated(calls, reps: int) -> float:
+    """Mean microseconds of one launch between two events, the device idle
+    before each (cold clocks and caches aside from what the call reads)."""
+    ts = []
+    for i in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        calls[i % len(calls)]()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    return float(np.median(ts))
 
 
 def main():
@@ -163,53 +206,46 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
+    copy_gbps = copy_bandwidth()
     t = W.WORKLOADS[args.workload]()
     setup = {"fprop_3b": setup_linear_gemm, "mlp_up_12b": setup_linear_gemm,
              "linear_train": setup_linear_train, "attn_scores": setup_attn}[args.workload]
     S = setup(t, dev)
-    calls, nbuf, names = S["calls"], S["nbuf"], S["names"]
+    steps, nbuf = S["steps"], S["nbuf"]
 
-    def step(i, ev=None):
-        for k, c in enumerate(calls[i % nbuf]):
-            if ev is not None:
-                ev[k].record()
+    # 1. per-call timing
+    kernels = {}
+    for name, calls in S["calls"].items():
+        b2b = time_back_to_back(calls, args.reps)
+        iso = time_isolated(calls, max(5, args.reps // 5))
+        info = {"us": round(b2b, 2), "us_isolated": round(iso, 2)}
+        if name in S["flops"]:
+            tf = S["flops"][name] / (b2b * 1e-6) / 1e12
+            info.update({"TFLOP/s": round(tf, 2), "frac_mfma": round(tf / PEAK_MFMA_TFLOPS, 4)})
+        if name in S["bytes"]:
+            gbps = S["bytes"][name] / (b2b * 1e-6) / 1e9
+            info.update({"GB/s": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)})
+            if copy_gbps:
+                info["frac_copy"] = round(gbps / copy_gbps, 4)
+        kernels[name] = info
+
+    def step(i):
+        for c in steps[i % nbuf]:
             c()
-        if ev is not None:
-            ev[len(names)].record()
 
+    # 2. warm-up and the timed region: exactly K steps, nothing else on the stream
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # Timed region: exactly K steps, nothing else on the stream.
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # Per-kernel region: the same K steps again with HIP events recorded on the
-    # launch stream around each call (events add a few microseconds of idle
-    # between kernels, so they stay out of the timed region above).
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(args.warmup + args.steps + i, events[i])
-    torch.cuda.synchronize()
-    call_ms = [float(np.mean([e[k].elapsed_time(e[k + 1]) for e in events])) for k in range(len(names))]
     ms_per_step = wall / args.steps * 1e3
 
-    kernels = {}
-    for k, name in enumerate(names):
-        us = call_ms[k] * 1e3
-        info = {"us": round(us, 2)}
-        if name in S["flops"]:
-            tf = S["flops"][name] / (us * 1e-6) / 1e12
-            info.update({"TFLOP/s": round(tf, 2), "frac_mfma": round(tf / PEAK_MFMA_TFLOPS, 4)})
-        if name in S["bytes"]:
-            gbps = S["bytes"][name] / (us * 1e-6) / 1e9
-            info.update({"GB/s": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)})
-        kernels[name] = info
     dom = S["dominant"]
-    dom_us = call_ms[names.index(dom)] * 1e3
+    dom_us = kernels[dom]["us"]
     if S["bound"] == "mfma":
         achieved = S["flops"][dom] / (dom_us * 1e-6) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
@@ -219,6 +255,7 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(args.workload, dom)}
     roofline["kernel"] = dom
+    roofline["duration_us"] = dom_us
 
     out = {
         "metric": METRIC,
@@ -236,11 +273,13 @@ def main():
         "config": dict(S["config"], workload=args.workload, rotating_buffers=nbuf),
         "roofline": roofline,
         "kernels": kernels,
+        "copy_GB/s": round(copy_gbps, 1) if copy_gbps else None,
         "mfma_ceiling": ceiling,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and args.workload == "fprop_3b":
-        out["cpu_baseline"] = cpu_baseline(t["X"], t["W"], args.cpu_rows)
+    # 3. the oracle on the same step, and this run's outputs against it
+    if not args.no_cpu_baseline and "baseline" in S:
+        out["cpu_baseline"] = S["baseline"]()
     print(json.dumps(out), flush=True)
 
 
@@ -262,17 +301,79 @@ def setup_linear_gemm(t, dev) -> dict:
     qws = [nv.QTensor.empty(1, N, K, dev) for _ in range(nbuf)]
     ys = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(nbuf)]
     wsp = nv.new_workspace(nv.nvfp4_quantize_group_workspace_size(), dev)
+    wsx = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
+    wsw = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
     # Each buffer set's calls marshalled once, so the host enqueues a step in
     # a few microseconds and stays ahead of the GPU.  X and W are quantized
     # by one grouped call (one launch when both fit the single-pass kernel).
-    calls = [(nv.bind_quantize_group([xs[j], ws[j]], [qxs[j], qws[j]], wsp),
-              nv.bind_gemm(qxs[j], qws[j], ys[j])) for j in range(nbuf)]
+    qxw = [nv.bind_quantize_group([xs[j], ws[j]], [qxs[j], qws[j]], wsp) for j in range(nbuf)]
+    gem = [nv.bind_gemm(qxs[j], qws[j], ys[j]) for j in range(nbuf)]
+    calls = {"quantize_xw": qxw,
+             "quantize_x": [nv.bind_quantize(xs[j], qxs[j], wsx) for j in range(nbuf)],
+             "quantize_w": [nv.bind_quantize(ws[j], qws[j], wsw) for j in range(nbuf)],
+             "gemm": gem}
     flops = 2.0 * M * N * K
-    return {"calls": calls, "nbuf": nbuf, "names": ["quantize_xw", "gemm"],
+
+    def baseline():
+        # the step's results on buffer set 0 come from a fresh call, then the oracle
+        qxw[0]()
+        gem[0]()
+        torch.cuda.synchronize()
+        return cpu_baseline_linear(x_cpu, w_cpu, qxs[0], qws[0], ys[0])
+
+    return {"steps": list(zip(qxw, gem)), "calls": calls, "nbuf": nbuf,
             "flops": {"gemm": flops}, "step_flops": flops,
-            "bytes": {"quantize_xw": QUANT_BYTES_PER_ELEM * (M * K + N * K)},
-            "dominant": "gemm", "bound": "mfma",
+            "bytes": {"quantize_xw": QUANT_BYTES_PER_ELEM * (M * K + N * K),
+                      "quantize_x": QUANT_BYTES_PER_ELEM * M * K, "quantize_w": QUANT_BYTES_PER_ELEM * N * K},
+            "dominant": "gemm", "bound": "mfma", "baseline": baseline,
             "config": {"M": M, "N": N, "K": K, "x_dtype": "bf16", "y_dtype": "bf16", "rounding": "rne"}}
+
+
+def cpu_baseline_linear(x_cpu, w_cpu, qx, qw, y) -> dict:
+    """The oracle as it stands on the whole step: quantize X and W (one host
+    thread each, as the oracle quantizes a tensor in one call), then the FP64
+    reference GEMM of every output row, split over the host's threads; also
+    the one-core time of the two quantizations.  The GPU's quantized views
+    and output from this run are checked against it (codes, scales and tensor
+    scales bit for bit; Y by the G3 rule)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import oracle as O
+    M, K = x_cpu.shape
+    N = w_cpu.shape[0]
+    nthr = host_threads()
+    xb, wb = W.bf16_bits(x_cpu), W.bf16_bits(w_cpu)
+    t0 = time.perf_counter()
+    O.quantize(xb, O.BF16)
+    O.quantize(wb, O.BF16)
+    t_quant_1core = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(nthr) as ex:
+        fx, fw = ex.submit(O.quantize, xb, O.BF16), ex.submit(O.quantize, wb, O.BF16)
+        ox, ow = fx.result(), fw.result()
+        t_quant = time.perf_counter() - t0
+        chunks = np.array_split(np.arange(M, dtype=np.int64), nthr)
+        t1 = time.perf_counter()
+        parts = list(ex.map(lambda r: O.gemm_ref(ox, ow, 1.0, 0, r), chunks))
+        t_gemm = time.perf_counter() - t1
+    t_step = time.perf_counter() - t0
+    y_ref = np.concatenate([p[0] for p in parts])
+    sabs = np.concatenate([p[1] for p in parts])
+
+    def same(q, o):
+        return bool(np.array_equal(q.codes.cpu().numpy().reshape(-1), o.codes.reshape(-1)) and
+                    np.array_equal(q.scales.cpu().numpy().reshape(-1), o.scales.reshape(-1)) and
+                    np.float32(q.tensor_scale.item()).view(np.uint32) == np.float32(o.tensor_scale).view(np.uint32))
+
+    acc = O.gemm_accept(y.float().cpu().numpy(), y_ref, sabs, bf16=True)
+    return {"value": 2.0 * M * N * K / t_step / 1e12, "unit": "TFLOP/s", "cores": nthr, "kind": "oracle",
+            "sample": f"the whole step on {nthr} host threads: oracle quantize of X ({M}x{K}) and W ({N}x{K}) "
+                      f"in {t_quant:.2f} s (one thread per tensor; {t_quant_1core:.2f} s on one core), FP64 "
+                      f"reference GEMM of all {M} rows in {t_gemm:.2f} s",
+            "seconds": round(t_step, 3), "quantize_seconds_1core": round(t_quant_1core, 3),
+            "parity": {"x_view_bit_exact": same(qx, ox), "w_view_bit_exact": same(qw, ow),
+                       "y_rows": M, "y_ulp_ok": acc["ok"], "y_cancel_only": acc["cancel_only"],
+                       "y_fail": acc["fail"]}}
 
 
 def setup_linear_train(t, dev) -> dict:
@@ -289,10 +390,11 @@ def setup_linear_train(t, dev) -> dict:
         y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
         dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
         dw = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
-        calls.append((nv.bind_linear_fwd_bwd(x, w, dy, y, dx, dw, wsp, t["sr_seed"], t["rht_seed"]),))
+        calls.append(nv.bind_linear_fwd_bwd(x, w, dy, y, dx, dw, wsp, t["sr_seed"], t["rht_seed"]))
     flops = 3 * 2.0 * M * N * K
-    return {"calls": calls, "nbuf": nbuf, "names": ["linear_fwd_bwd"], "flops": {"linear_fwd_bwd": flops},
-            "step_flops": flops, "bytes": {}, "dominant": "linear_fwd_bwd", "bound": "mfma",
+    return {"steps": [(c,) for c in calls], "calls": {"linear_fwd_bwd": calls}, "nbuf": nbuf,
+            "flops": {"linear_fwd_bwd": flops}, "step_flops": flops, "bytes": {},
+            "dominant": "linear_fwd_bwd", "bound": "mfma",
             "config": {"M": M, "N": N, "K": K, "x_dtype": "bf16", "y_dtype": "bf16",
                        "rounding": "rne fprop, sr dgrad, rht+sr wgrad"}}
 
@@ -310,12 +412,13 @@ def setup_attn(t, dev) -> dict:
     s_out = torch.empty(B * H, S_, S_, dtype=torch.float32, device=dev)  # 8.6 GB, written every step
     wsp_q = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
     wsp_k = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
-    calls = [(nv.bind_quantize(qs[j], qq[j], wsp_q), nv.bind_quantize(ks[j], qk[j], wsp_k),
-              nv.bind_gemm(qq[j], qk[j], s_out, alpha=t["alpha"])) for j in range(nbuf)]
+    cq = [nv.bind_quantize(qs[j], qq[j], wsp_q) for j in range(nbuf)]
+    ck = [nv.bind_quantize(ks[j], qk[j], wsp_k) for j in range(nbuf)]
+    cg = [nv.bind_gemm(qq[j], qk[j], s_out, alpha=t["alpha"]) for j in range(nbuf)]
     flops = 2.0 * B * H * S_ * S_ * D
     gemm_bytes = 4.0 * B * H * S_ * S_ + 2 * B * H * S_ * D * (0.5 + 1 / 16)
-    return {"calls": calls, "nbuf": nbuf, "names": ["quantize_q", "quantize_k", "gemm"],
-            "flops": {"gemm": flops}, "step_flops": flops,
+    return {"steps": list(zip(cq, ck, cg)), "calls": {"quantize_q": cq, "quantize_k": ck, "gemm": cg},
+            "nbuf": nbuf, "flops": {"gemm": flops}, "step_flops": flops,
             "bytes": {"quantize_q": QUANT_BYTES_PER_ELEM * q_cpu.numel(),
                       "quantize_k": QUANT_BYTES_PER_ELEM * k_cpu.numel(), "gemm": gemm_bytes},
             "dominant": "gemm", "bound": "hbm",

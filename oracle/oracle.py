@@ -222,3 +222,50 @@ def gemm_ref(a: QTensor, b: QTensor, alpha: float = 1.0, batch_index: int = 0,
     if rc != 0:
         raise ValueError(f"oracle_gemm_ref failed (rc={rc})")
     return y, s
+
+
+# --- G3: acceptance of a GEMM output against the reference ---------------
+
+FP32_TOL = 1e-5
+
+
+def bf16_rne_bits(y: np.ndarray) -> np.ndarray:
+    """Exact round-to-nearest-even of float64 values to BF16 bit patterns."""
+    y = np.asarray(y, dtype=np.float64)
+    out = np.zeros(y.shape, dtype=np.int64)
+    nz = y != 0
+    # BF16 shares FP32's exponent range: below 2^-126 the spacing stays 2^-133
+    e = np.maximum(np.floor(np.log2(np.abs(y[nz]))), -126.0)
+    scale = np.exp2(e - 7)
+    r = np.round(y[nz] / scale) * scale  # half-to-even on an exact quotient
+    out[nz] = (np.float32(r).view(np.uint32) >> 16).astype(np.int64)
+    out[~nz] = (np.signbit(y[~nz]).astype(np.int64) << 15)
+    return out
+
+
+def gemm_accept(y: np.ndarray, y_ref: np.ndarray, sabs: np.ndarray, bf16: bool) -> dict:
+    """Counts of the G3 rule over the elements of y (FP32 values, or BF16
+    values widened to FP32):
+      FP32 out: |y - y_ref| <= 1e-5 * sabs                      -> "ok";
+      BF16 out: y is RNE_bf16(y_ref) or one of its two BF16 neighbours
+                (1 ulp)                                         -> "ok";
+                otherwise |y - y_ref| <= 1e-5 * sabs + ulp_bf16(y) / 2 (FP32
+                accumulation error near cancellation)           -> "cancel_only";
+      anything else                                             -> "fail"."""
+    y = np.asarray(y)
+    if not bf16:
+        err = np.abs(y.astype(np.float64) - y_ref)
+        ok = err <= FP32_TOL * sabs
+        return {"n": int(y.size), "ok": int(ok.sum()), "cancel_only": 0, "fail": int((~ok).sum())}
+    ybits = (np.asarray(y, dtype=np.float32).view(np.uint32) >> 16).astype(np.int64)
+    rbits = bf16_rne_bits(y_ref)
+
+    def mono(b):  # signed magnitude -> a monotone integer, so neighbours differ by 1
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+    ulp_ok = np.abs(mono(ybits) - mono(rbits)) <= 1
+    yv = np.asarray(y, dtype=np.float64)
+    ulp_y = np.exp2(np.floor(np.log2(np.maximum(np.abs(yv), 1e-300))) - 7)
+    cancel_ok = np.abs(yv - y_ref) <= FP32_TOL * sabs + 0.5 * ulp_y
+    return {"n": int(y.size), "ok": int(ulp_ok.sum()), "cancel_only": int((~ulp_ok & cancel_ok).sum()),
+            "fail": int((~(ulp_ok | cancel_ok)).sum())}

@@ -275,3 +275,32 @@ def test_gemm_ref_identity_and_single_nonzero():
     want[1, 1] = d[1, 17] ** 2
     np.testing.assert_allclose(y, want, rtol=1e-15)
     np.testing.assert_allclose(sabs, want, rtol=1e-15)
+
+
+def test_bf16_rne_bits_vs_torch_cast():
+    """The acceptance rule's BF16 rounding equals torch's round-to-nearest-even
+    cast on random FP32 patterns, FP32 subnormals and values near the top."""
+    import torch
+    rng = np.random.default_rng(12)
+    p = np.concatenate([rng.integers(0, 2 ** 32, 1 << 18, dtype=np.uint64).astype(np.uint32),
+                        np.arange(1, 1 << 16, dtype=np.uint32), np.arange(0x7F7F0000, 0x7F7FFFFF, 7, dtype=np.uint32)])
+    f = p.view(np.float32)
+    keep = np.isfinite(f) & (np.abs(f) < np.float32(3.38e38))
+    f = f[keep]
+    want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = (O.bf16_rne_bits(f.astype(np.float64)) & 0xFFFF).astype(np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_gemm_accept_counts():
+    y_ref = np.array([1.0, 1.0, 1.0, 1e-3], np.float64)
+    sabs = np.array([1.0, 1.0, 1.0, 1e3], np.float64)
+    one = np.float32(1.0)
+    up1 = np.float32(1.0078125)   # one BF16 ulp above 1
+    up2 = np.float32(1.015625)    # two BF16 ulps above 1
+    # exact, 1 ulp, 2 ulps (fails), and a small value far off but inside 1e-5 * sabs (cancellation)
+    y = np.array([one, up1, up2, np.float32(1e-3 + 9e-3)], np.float32)
+    c = O.gemm_accept(y, y_ref, sabs, bf16=True)
+    assert c == {"n": 4, "ok": 2, "cancel_only": 1, "fail": 1}
+    c = O.gemm_accept(np.float32([1.0, 1.0 + 2e-5]), np.array([1.0, 1.0]), np.array([1.0, 1.0]), bf16=False)
+    assert c == {"n": 2, "ok": 1, "cancel_only": 0, "fail": 1}
