@@ -78,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_quantize.argtypes = [vp, i32, i64, i64, i64, i64, i64, i32,
                                      ctypes.POINTER(QuantOptsC), ctypes.POINTER(QTensorC), vp, sz, vp]
         L.nvfp4_quantize.restype = i32
+        L.nvfp4_quantize_noalloc.argtypes = [vp, i32, i64, i64, i64, i64, i64, i32,
+                                             ctypes.POINTER(QuantOptsC), ctypes.POINTER(QTensorC), vp]
+        L.nvfp4_quantize_noalloc.restype = i32
         L.nvfp4_quantize_group_workspace_size.restype = sz
         L.nvfp4_quantize_group.argtypes = [ctypes.POINTER(QuantJobC), i32, i32, ctypes.POINTER(QuantOptsC),
                                            vp, sz, vp]
@@ -132,6 +135,12 @@ def nvfp4_quantize(x_ptr, x_dtype, batch, rows, cols, ld, batch_stride, axis, op
                                 ctypes.byref(opts) if opts is not None else None,
                                 ctypes.byref(out) if out is not None else None,
                                 workspace, workspace_bytes, stream)
+
+
+def nvfp4_quantize_noalloc(x_ptr, x_dtype, batch, rows, cols, ld, batch_stride, axis, opts, out, stream) -> int:
+    return lib().nvfp4_quantize_noalloc(x_ptr, x_dtype, batch, rows, cols, ld, batch_stride, axis,
+                                        ctypes.byref(opts) if opts is not None else None,
+                                        ctypes.byref(out) if out is not None else None, stream)
 
 
 def nvfp4_quantize_group(jobs, njobs, x_dtype, opts, workspace, workspace_bytes, stream) -> int:
@@ -242,6 +251,18 @@ def quantize(x: torch.Tensor, axis: int = ALONG_COLS, rounding: int = RNE, sr_se
     (bfloat16 or float32, last dimension contiguous)."""
     args, _keep, out = _quantize_args(x, axis, rounding, sr_seed, sr_stream, rht, rht_seed, out, workspace)
     _check(lib().nvfp4_quantize(*args), "nvfp4_quantize")
+    return out
+
+
+def quantize_noalloc(x: torch.Tensor, axis: int = ALONG_COLS, rounding: int = RNE, sr_seed: int = 0,
+                     sr_stream: int = 0, rht: bool = False, rht_seed: int = 0,
+                     out: QTensor | None = None) -> QTensor:
+    """quantize() through nvfp4_quantize_noalloc: no workspace (the library's
+    per-GPU static control block); `out` must be given to allocate nothing."""
+    args, _keep, out = _quantize_args(x, axis, rounding, sr_seed, sr_stream, rht, rht_seed, out,
+                                      torch.empty(0, dtype=torch.uint8, device=x.device))
+    # nvfp4_quantize's arguments without the workspace pointer and size
+    _check(lib().nvfp4_quantize_noalloc(*args[:10], args[12]), "nvfp4_quantize_noalloc")
     return out
 
 

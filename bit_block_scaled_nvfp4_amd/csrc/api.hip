@@ -7,6 +7,7 @@
 // the Hadamard mixing of section 2.2.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "../../include/nvfp4.h"
@@ -173,6 +174,32 @@ LinearLayout linear_layout(int64_t M, int64_t N, int64_t K) {
   return L;
 }
 
+// Scratch of nvfp4_quantize_noalloc: one quantize control block (4 KiB) in
+// the library's own device memory, one copy per GPU, zero when the module is
+// loaded.  Every call leaves it ready for the next (the control block's own
+// rule), so nothing is cleared between calls.  Host code never uses the
+// array's name as an address: each device's copy is looked up once with
+// hipGetSymbolAddress, with that device current, and kept.
+constexpr size_t kScratchBytes = sizeof(QuantCtrl);
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+
+nvfp4_status scratch_of_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return NVFP4_EHIP;
+  if (dev >= kMaxDevices) return NVFP4_EUNSUPPORTED;
+  void *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // Concurrent first calls on one device look up the same address.
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return NVFP4_EHIP;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return NVFP4_OK;
+}
+
 }  // namespace
 
 NVFP4_EXPORT const char *nvfp4_status_string(int32_t status) {
@@ -202,6 +229,24 @@ NVFP4_EXPORT nvfp4_status nvfp4_quantize(const void *x, int32_t x_dtype, int64_t
   if (st != NVFP4_OK) return st;
   const nvfp4::QuantProblem p = make_quant(x, x_dtype == NVFP4_BF16, batch, rows, cols, ld, batch_stride,
                                            axis == NVFP4_ALONG_ROWS, opts, out, workspace);
+  return nvfp4::launch_quantize(p, static_cast<hipStream_t>(stream));
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_quantize_noalloc(const void *x, int32_t x_dtype, int64_t batch, int64_t rows,
+                                                 int64_t cols, int64_t ld, int64_t batch_stride, int32_t axis,
+                                                 const nvfp4_quant_opts *opts, const nvfp4_qtensor *out,
+                                                 void *stream) {
+  // Arguments first, as for nvfp4_quantize (the workspace check is passed a
+  // stand-in of the scratch's size; no HIP call happens before this).
+  static_assert(kScratchBytes >= sizeof(QuantCtrl), "the scratch holds one control block");
+  nvfp4_status st = validate_quantize(x, x_dtype, batch, rows, cols, ld, batch_stride, axis, opts, out,
+                                      reinterpret_cast<const void *>(uintptr_t(256)), kScratchBytes);
+  if (st != NVFP4_OK) return st;
+  void *ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != NVFP4_OK) return st;
+  const nvfp4::QuantProblem p = make_quant(x, x_dtype == NVFP4_BF16, batch, rows, cols, ld, batch_stride,
+                                           axis == NVFP4_ALONG_ROWS, opts, out, ws);
   return nvfp4::launch_quantize(p, static_cast<hipStream_t>(stream));
 }
 

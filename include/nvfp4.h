@@ -161,6 +161,25 @@ nvfp4_status nvfp4_quantize(const void *x, int32_t x_dtype, int64_t batch, int64
                             const nvfp4_quant_opts *opts, const nvfp4_qtensor *out,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* nvfp4_quantize without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments (minus the
+ * workspace), checks and results, bit for bit.  Its scratch is one 4 KiB
+ * control block, a static array of the library: one copy per GPU, zero
+ * when the library's code is loaded, held until the process ends, looked up
+ * once per device on that device's first call.  The call itself allocates
+ * nothing.  Every quantize needs exactly one control block whatever its
+ * size, so no size is refused for lack of scratch.  All calls of this entry
+ * point on one GPU within a process share the block: calls that overlap in
+ * time on one GPU (on different streams) race and give unspecified results,
+ * so serialise them, or use nvfp4_quantize with separate workspaces.  A
+ * barrier time-out (see the conventions) leaves the block's time-out word
+ * set, after which every call of this entry point on that GPU publishes NaN
+ * tensor scales for the rest of the process. */
+nvfp4_status nvfp4_quantize_noalloc(const void *x, int32_t x_dtype, int64_t batch, int64_t rows,
+                                    int64_t cols, int64_t ld, int64_t batch_stride, int32_t axis,
+                                    const nvfp4_quant_opts *opts, const nvfp4_qtensor *out, void *stream);
+
 /* One tensor of nvfp4_quantize_group: x as for nvfp4_quantize (ALONG_COLS). */
 typedef struct nvfp4_quant_job {
   const void *x;
