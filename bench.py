@@ -9,7 +9,9 @@ inputs already resident in HBM.  Inputs rotate over enough copies to exceed
 twice the 256 MB Infinity Cache, so every step reads its operands from HBM.
 
 Order of work:
-  1. per-call timing: each call of the step launched alone, back to back
+  1. per-call timing, after --settle-ms of untimed steps (the shader clock
+     ramps over the first tens of milliseconds of load): each call of the
+     step launched alone, back to back
      (`reps` launches over the rotating buffers between two HIP events on the
      launch stream; the mean is the kernel duration plus the launch gap), and
      isolated (one launch between events after a device synchronisation);
@@ -64,7 +66,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="fprop_3b",
                    choices=["fprop_3b", "mlp_up_12b", "linear_train", "attn_scores"])
-    p.add_argument("--reps", type=int, default=50, help="back-to-back launches per call in the per-call timing")
+    p.add_argument("--reps", type=int, default=100, help="back-to-back launches per call in the per-call timing")
+    p.add_argument("--settle-ms", type=float, default=300.0,
+                   help="wall time of untimed steps before the per-call timing (lets the shader clock settle)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-mfma-ceiling", action="store_true", help="skip the MFMA ceiling probe")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -213,7 +217,17 @@ def main():
     S = setup(t, dev)
     steps, nbuf = S["steps"], S["nbuf"]
 
-    # 1. per-call timing
+    # 1. per-call timing, after the step has run long enough for the shader
+    #    clock to settle (it ramps over the first ~10-20 ms of load)
+    settle_end = time.perf_counter() + args.settle_ms * 1e-3
+    i = 0
+    while time.perf_counter() < settle_end or i < 2 * nbuf:
+        for c in steps[i % nbuf]:
+            c()
+        i += 1
+        if i % nbuf == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
     kernels = {}
     for name, calls in S["calls"].items():
         b2b = time_back_to_back(calls, args.reps)
