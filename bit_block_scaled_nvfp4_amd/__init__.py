@@ -53,6 +53,10 @@ class QuantJobC(ctypes.Structure):
                 ("out", QTensorC)]
 
 
+class AttnCfgC(ctypes.Structure):
+    _fields_ = [("sr_seed", ctypes.c_uint64), ("ds_rounding", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class LinearCfgC(ctypes.Structure):
     _fields_ = [("sr_seed", ctypes.c_uint64), ("rht_seed", ctypes.c_uint64),
                 ("wgrad_sr_x", ctypes.c_int32), ("dw_dtype", ctypes.c_int32)]
@@ -81,6 +85,16 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_quantize_noalloc.argtypes = [vp, i32, i64, i64, i64, i64, i64, i32,
                                              ctypes.POINTER(QuantOptsC), ctypes.POINTER(QTensorC), vp]
         L.nvfp4_quantize_noalloc.restype = i32
+        L.nvfp4_quantize_dual.argtypes = [vp, i32, i64, i64, i64, i64, i64, ctypes.POINTER(QuantOptsC),
+                                          ctypes.POINTER(QTensorC), ctypes.POINTER(QuantOptsC),
+                                          ctypes.POINTER(QTensorC), vp, sz, vp]
+        L.nvfp4_quantize_dual.restype = i32
+        L.nvfp4_attention_ds_workspace_size.argtypes = [i64, i64, i64]
+        L.nvfp4_attention_ds_workspace_size.restype = sz
+        L.nvfp4_attention_ds_grads.argtypes = [vp, i32, ctypes.POINTER(QTensorC), ctypes.POINTER(QTensorC), vp, vp,
+                                               i32, i64, i64, i64, i64, ctypes.c_float, ctypes.POINTER(AttnCfgC),
+                                               vp, sz, vp]
+        L.nvfp4_attention_ds_grads.restype = i32
         L.nvfp4_quantize_group_workspace_size.restype = sz
         L.nvfp4_quantize_group.argtypes = [ctypes.POINTER(QuantJobC), i32, i32, ctypes.POINTER(QuantOptsC),
                                            vp, sz, vp]
@@ -141,6 +155,24 @@ def nvfp4_quantize_noalloc(x_ptr, x_dtype, batch, rows, cols, ld, batch_stride, 
     return lib().nvfp4_quantize_noalloc(x_ptr, x_dtype, batch, rows, cols, ld, batch_stride, axis,
                                         ctypes.byref(opts) if opts is not None else None,
                                         ctypes.byref(out) if out is not None else None, stream)
+
+
+def nvfp4_quantize_dual(x_ptr, x_dtype, batch, rows, cols, ld, batch_stride, row_opts, row_out, col_opts, col_out,
+                        workspace, workspace_bytes, stream) -> int:
+    ref = lambda o: ctypes.byref(o) if o is not None else None
+    return lib().nvfp4_quantize_dual(x_ptr, x_dtype, batch, rows, cols, ld, batch_stride, ref(row_opts), ref(row_out),
+                                     ref(col_opts), ref(col_out), workspace, workspace_bytes, stream)
+
+
+def nvfp4_attention_ds_workspace_size(bh: int, sq: int, sk: int) -> int:
+    return lib().nvfp4_attention_ds_workspace_size(bh, sq, sk)
+
+
+def nvfp4_attention_ds_grads(ds_ptr, ds_dtype, q_seq, k_seq, dq_ptr, dk_ptr, out_dtype, bh, sq, sk, d, alpha, cfg,
+                             workspace, workspace_bytes, stream) -> int:
+    ref = lambda o: ctypes.byref(o) if o is not None else None
+    return lib().nvfp4_attention_ds_grads(ds_ptr, ds_dtype, ref(q_seq), ref(k_seq), dq_ptr, dk_ptr, out_dtype, bh, sq,
+                                          sk, d, ctypes.c_float(alpha), ref(cfg), workspace, workspace_bytes, stream)
 
 
 def nvfp4_quantize_group(jobs, njobs, x_dtype, opts, workspace, workspace_bytes, stream) -> int:
@@ -264,6 +296,102 @@ def quantize_noalloc(x: torch.Tensor, axis: int = ALONG_COLS, rounding: int = RN
     # nvfp4_quantize's arguments without the workspace pointer and size
     _check(lib().nvfp4_quantize_noalloc(*args[:10], args[12]), "nvfp4_quantize_noalloc")
     return out
+
+
+def _dual_args(x: torch.Tensor, row_rounding: int, col_rounding: int, sr_seed: int, row_stream: int,
+               col_stream: int, outs, workspace: torch.Tensor | None):
+    x3 = x.unsqueeze(0) if x.dim() == 2 else x
+    if x3.dim() != 3 or x3.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be a 2-D or 3-D bfloat16 or float32 tensor")
+    if x3.size(2) > 1 and x3.stride(2) != 1:
+        raise ValueError("the last dimension of x must be contiguous")
+    b, r, c = x3.shape
+    if outs is None:
+        outs = (QTensor.empty(b, r, c, x.device), QTensor.empty(b, c, r, x.device))
+    if workspace is None:
+        workspace = new_workspace(nvfp4_quantize_workspace_size(), x.device)
+    ro = QuantOptsC(row_rounding, 0, sr_seed, 0, row_stream, 0)
+    co = QuantOptsC(col_rounding, 0, sr_seed, 0, col_stream, 0)
+    rq, cq = outs[0].c_struct(), outs[1].c_struct()
+    args = (x3.data_ptr(), BF16 if x3.dtype == torch.bfloat16 else F32, b, r, c, x3.stride(1) if r > 1 else c,
+            x3.stride(0) if b > 1 else r * c, ctypes.byref(ro), ctypes.byref(rq), ctypes.byref(co), ctypes.byref(cq),
+            workspace.data_ptr(), workspace.numel(), _stream(x.device))
+    return args, (ro, co, rq, cq, x3, workspace), outs
+
+
+def quantize_dual(x: torch.Tensor, row_rounding: int = RNE, col_rounding: int = RNE, sr_seed: int = 0,
+                  row_stream: int = 0, col_stream: int = 0, outs=None, workspace: torch.Tensor | None = None):
+    """Both orientations of x from one read: (view along the last dimension,
+    transposed view along the rows), one tensor scale (nvfp4_quantize_dual)."""
+    args, _keep, outs = _dual_args(x, row_rounding, col_rounding, sr_seed, row_stream, col_stream, outs, workspace)
+    _check(lib().nvfp4_quantize_dual(*args), "nvfp4_quantize_dual")
+    return outs
+
+
+def bind_quantize_dual(x: torch.Tensor, outs, workspace: torch.Tensor, row_rounding: int = RNE,
+                       col_rounding: int = RNE, sr_seed: int = 0, row_stream: int = 0, col_stream: int = 0):
+    args, keep, outs = _dual_args(x, row_rounding, col_rounding, sr_seed, row_stream, col_stream, outs, workspace)
+    return BoundCall(lib().nvfp4_quantize_dual, args, keep, "nvfp4_quantize_dual", outs)
+
+
+def _attn_args(ds, q_seq: QTensor, k_seq: QTensor, dq, dk, alpha, sr_seed, ds_rounding, workspace):
+    bh, sq, sk = ds.shape
+    d = q_seq.rows
+    if not ds.is_contiguous() or ds.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("ds must be a contiguous [bh][sq][sk] bfloat16 or float32 tensor")
+    cfg = AttnCfgC(sr_seed, ds_rounding, 0)
+    qs, ks = q_seq.c_struct(), k_seq.c_struct()
+    args = (ds.data_ptr(), BF16 if ds.dtype == torch.bfloat16 else F32, ctypes.byref(qs), ctypes.byref(ks),
+            dq.data_ptr(), dk.data_ptr(), BF16 if dq.dtype == torch.bfloat16 else F32, bh, sq, sk, d,
+            ctypes.c_float(alpha), ctypes.byref(cfg), workspace.data_ptr(), workspace.numel(), _stream(ds.device))
+    return args, (cfg, qs, ks, ds, dq, dk, workspace)
+
+
+def attention_ds_grads(ds: torch.Tensor, q_seq: QTensor, k_seq: QTensor, alpha: float, sr_seed: int,
+                       ds_rounding: int = SR, out_dtype: torch.dtype = torch.bfloat16,
+                       workspace: torch.Tensor | None = None):
+    """(dQ, dK) = (alpha dS K, alpha dS^T Q) with dS quantized in both
+    orientations (nvfp4_attention_ds_grads); q_seq / k_seq are the
+    sequence-major views [bh][d][s] of Q and K."""
+    bh, sq, sk = ds.shape
+    d = q_seq.rows
+    dq = torch.empty(bh, sq, d, dtype=out_dtype, device=ds.device)
+    dk = torch.empty(bh, sk, d, dtype=out_dtype, device=ds.device)
+    if workspace is None:
+        workspace = new_workspace(nvfp4_attention_ds_workspace_size(bh, sq, sk), ds.device)
+    args, _keep = _attn_args(ds, q_seq, k_seq, dq, dk, alpha, sr_seed, ds_rounding, workspace)
+    _check(lib().nvfp4_attention_ds_grads(*args), "nvfp4_attention_ds_grads")
+    return dq, dk
+
+
+def bind_attention_ds_grads(ds, q_seq: QTensor, k_seq: QTensor, dq, dk, workspace: torch.Tensor, alpha: float,
+                            sr_seed: int, ds_rounding: int = SR) -> "BoundCall":
+    args, keep = _attn_args(ds, q_seq, k_seq, dq, dk, alpha, sr_seed, ds_rounding, workspace)
+    return BoundCall(lib().nvfp4_attention_ds_grads, args, keep, "nvfp4_attention_ds_grads", (dq, dk))
+
+
+def attention_ds_view(workspace: torch.Tensor, bh: int, sq: int, sk: int, which: int) -> QTensor:
+    """The quantized dS view nvfp4_attention_ds_grads left in `workspace`:
+    0 = along the keys [bh][sq][sk], 1 = along the queries [bh][sk][sq]
+    (the layout the header states: each view's codes, scales and tensor-scale
+    slot, 256-byte aligned, in that order)."""
+    n = bh * sq * sk
+
+    def up(v):
+        return (v + 255) // 256 * 256
+
+    off = 0
+    views = []
+    for i in range(2):
+        r, c = (sq, sk) if i == 0 else (sk, sq)
+        codes = workspace[off:off + n // 2].view(bh, r, c // 2)
+        off = up(off + n // 2)
+        scales = workspace[off:off + n // 16].view(bh, r, c // 16)
+        off = up(off + n // 16)
+        ts = workspace[off:off + 4].view(torch.float32)
+        off += 256
+        views.append(QTensor(codes, scales, ts, bh, r, c))
+    return views[which]
 
 
 class BoundCall:

@@ -200,6 +200,31 @@ nvfp4_status scratch_of_current_device(void **out) {
   return NVFP4_OK;
 }
 
+// Attention dS workspace: the two quantized views of dS (along the keys,
+// [bh][sq][sk], and along the queries, [bh][sk][sq]) with their tensor-scale
+// slots, then one quantize control block; every region 256-byte aligned.
+struct AttnLayout {
+  size_t codes[2], scales[2], st[2], ctrl;
+  size_t total;
+};
+
+AttnLayout attn_layout(int64_t bh, int64_t sq, int64_t sk) {
+  AttnLayout L{};
+  const size_t n = (size_t)bh * (size_t)sq * (size_t)sk;
+  size_t off = 0;
+  for (int i = 0; i < 2; ++i) {
+    L.codes[i] = off;
+    off = round_up(off + n / 2, 256);
+    L.scales[i] = off;
+    off = round_up(off + n / 16, 256);
+    L.st[i] = off;
+    off += 256;
+  }
+  L.ctrl = off;
+  L.total = off + sizeof(QuantCtrl);
+  return L;
+}
+
 }  // namespace
 
 NVFP4_EXPORT const char *nvfp4_status_string(int32_t status) {
@@ -248,6 +273,36 @@ NVFP4_EXPORT nvfp4_status nvfp4_quantize_noalloc(const void *x, int32_t x_dtype,
   const nvfp4::QuantProblem p = make_quant(x, x_dtype == NVFP4_BF16, batch, rows, cols, ld, batch_stride,
                                            axis == NVFP4_ALONG_ROWS, opts, out, ws);
   return nvfp4::launch_quantize(p, static_cast<hipStream_t>(stream));
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_quantize_dual(const void *x, int32_t x_dtype, int64_t batch, int64_t rows,
+                                              int64_t cols, int64_t ld, int64_t batch_stride,
+                                              const nvfp4_quant_opts *row_opts, const nvfp4_qtensor *row_out,
+                                              const nvfp4_quant_opts *col_opts, const nvfp4_qtensor *col_out,
+                                              void *workspace, size_t workspace_bytes, void *stream) {
+  // Each view is validated as its single-orientation call would be; both
+  // extents must then be multiples of 16, and neither view may ask for the
+  // transform (it would make the two views' maxima differ).
+  // The transposed view as for ALONG_ROWS (x aligned to its element size,
+  // rows % 16 == 0), then the view along the columns: its options, cols %
+  // 16 == 0 and its descriptor.
+  nvfp4_status st = validate_quantize(x, x_dtype, batch, rows, cols, ld, batch_stride, NVFP4_ALONG_ROWS, col_opts,
+                                      col_out, workspace, workspace_bytes);
+  if (st != NVFP4_OK) return st;
+  if (row_opts) {
+    if (row_opts->rounding != NVFP4_RNE && row_opts->rounding != NVFP4_SR) return NVFP4_EINVAL;
+    if (row_opts->rht != 0 && row_opts->rht != 1) return NVFP4_EINVAL;
+    if (row_opts->reserved != 0) return NVFP4_EINVAL;
+  }
+  if (cols % 16 != 0) return NVFP4_ESHAPE;
+  st = check_view(row_out, batch, rows, cols);
+  if (st != NVFP4_OK) return st;
+  if ((row_opts && row_opts->rht) || (col_opts && col_opts->rht)) return NVFP4_EUNSUPPORTED;
+  const nvfp4::QuantProblem pr = make_quant(x, x_dtype == NVFP4_BF16, batch, rows, cols, ld, batch_stride, false,
+                                            row_opts, row_out, workspace);
+  const nvfp4::QuantProblem pc = make_quant(x, x_dtype == NVFP4_BF16, batch, rows, cols, ld, batch_stride, true,
+                                            col_opts, col_out, workspace);
+  return nvfp4::launch_quantize_dual(pr, pc, static_cast<hipStream_t>(stream));
 }
 
 NVFP4_EXPORT size_t nvfp4_quantize_group_workspace_size(void) { return nvfp4::kGroupWorkspace; }
@@ -335,6 +390,49 @@ NVFP4_EXPORT nvfp4_status nvfp4_linear_view(void *workspace, size_t workspace_by
   out->rows = L.rows[which];
   out->cols = L.cols[which];
   return NVFP4_OK;
+}
+
+NVFP4_EXPORT size_t nvfp4_attention_ds_workspace_size(int64_t bh, int64_t sq, int64_t sk) {
+  if (bh <= 0 || sq <= 0 || sk <= 0 || bh > kMaxExtent || sq > kMaxExtent || sk > kMaxExtent) return 0;
+  return attn_layout(bh, sq, sk).total;
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_attention_ds_grads(const void *ds, int32_t ds_dtype, const nvfp4_qtensor *q_seq,
+                                                   const nvfp4_qtensor *k_seq, void *dq, void *dk, int32_t out_dtype,
+                                                   int64_t bh, int64_t sq, int64_t sk, int64_t d, float alpha,
+                                                   const nvfp4_attn_cfg *cfg, void *workspace,
+                                                   size_t workspace_bytes, void *stream) {
+  if (!ds || !q_seq || !k_seq || !dq || !dk || !cfg) return NVFP4_EINVAL;
+  if (ds_dtype != NVFP4_F32 && ds_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (cfg->ds_rounding != NVFP4_RNE && cfg->ds_rounding != NVFP4_SR) return NVFP4_EINVAL;
+  if (cfg->reserved != 0) return NVFP4_EINVAL;
+  if (bh <= 0 || sq <= 0 || sk <= 0 || d <= 0 || sq % 16 || sk % 16 || d % 16) return NVFP4_ESHAPE;
+  if (bh > 65535 || sq > kMaxExtent || sk > kMaxExtent || d > kMaxExtent) return NVFP4_ESHAPE;
+  nvfp4_status st = check_view(q_seq, bh, d, sq);
+  if (st != NVFP4_OK) return st;
+  st = check_view(k_seq, bh, d, sk);
+  if (st != NVFP4_OK) return st;
+  if (!aligned(ds, 16) || !aligned(dq, 16) || !aligned(dk, 16)) return NVFP4_EALIGN;
+  const AttnLayout L = attn_layout(bh, sq, sk);
+  if (!workspace || workspace_bytes < L.total) return NVFP4_EWORKSPACE;
+  if (!aligned(workspace, 256)) return NVFP4_EALIGN;
+  uint8_t *base = static_cast<uint8_t *>(workspace);
+  nvfp4_qtensor ds_row{base + L.codes[0], base + L.scales[0], reinterpret_cast<float *>(base + L.st[0]), bh, sq, sk};
+  nvfp4_qtensor ds_col{base + L.codes[1], base + L.scales[1], reinterpret_cast<float *>(base + L.st[1]), bh, sk, sq};
+  nvfp4_quant_opts row_o{cfg->ds_rounding, 0, cfg->sr_seed, 0, 4u, 0u};
+  nvfp4_quant_opts col_o{cfg->ds_rounding, 0, cfg->sr_seed, 0, 5u, 0u};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const nvfp4::QuantProblem pr = make_quant(ds, ds_dtype == NVFP4_BF16, bh, sq, sk, sk, sq * sk, false, &row_o,
+                                            &ds_row, base + L.ctrl);
+  const nvfp4::QuantProblem pc = make_quant(ds, ds_dtype == NVFP4_BF16, bh, sq, sk, sk, sq * sk, true, &col_o,
+                                            &ds_col, base + L.ctrl);
+  st = nvfp4::launch_quantize_dual(pr, pc, s);
+  if (st != NVFP4_OK) return st;
+  // dQ = alpha dS K: dS along the keys, K^T along the keys;  dK = alpha dS^T Q: dS^T and Q^T along the queries.
+  st = nvfp4::launch_gemm(make_gemm(&ds_row, k_seq, dq, out_dtype, d, sq * d, alpha), s);
+  if (st != NVFP4_OK) return st;
+  return nvfp4::launch_gemm(make_gemm(&ds_col, q_seq, dk, out_dtype, d, sk * d, alpha), s);
 }
 
 NVFP4_EXPORT nvfp4_status nvfp4_linear_fwd_bwd(const void *x, const void *w, const void *dy, void *y,

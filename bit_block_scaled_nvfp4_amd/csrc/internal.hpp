@@ -89,6 +89,10 @@ struct GemmProblem {
 
 nvfp4_status launch_quantize(const QuantProblem &p, hipStream_t stream);
 nvfp4_status launch_quantize_group(const QuantGroupProblem &p, hipStream_t stream);
+// Both orientations of one input in one encode pass: `row` describes the
+// input and the view along its columns, `col` the transposed view (its
+// input fields are ignored); no transform; both views get one tensor scale.
+nvfp4_status launch_quantize_dual(const QuantProblem &row, const QuantProblem &col, hipStream_t stream);
 nvfp4_status launch_gemm(const GemmProblem &p, hipStream_t stream);
 
 }  // namespace nvfp4

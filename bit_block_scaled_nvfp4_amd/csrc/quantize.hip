@@ -829,6 +829,106 @@ __global__ __launch_bounds__(kThreads) void col_encode_kernel(ColArgs a) {
   encode_finish(a.ctrl, a.tensor_scale, st);
 }
 
+// Both orientations from one read (encode pass of the dual quantize): the
+// tile and lane layout of col_encode_kernel, whose transposed view it writes
+// the same way; the same registers then give the view along the columns.  A
+// 16-column block of input row r is split over this lane (8 columns) and
+// its neighbour (lane ^ 1, the next column group): the block maximum takes
+// one lane-pair exchange, each lane encodes its 8 elements with the shared
+// block scale and stores them as 4 contiguous code bytes (the 16 lanes of a
+// row group write 64 contiguous bytes).  Without the transform both views
+// have the same tensor maximum, hence one tensor scale.
+struct DualArgs {
+  ColArgs c;                     // input, tiles, the transposed view and its stream
+  uint8_t *rcodes, *rscales;     // the view along the columns: [batch][R][C/2], [batch][R][C/16]
+  float *rtensor_scale;
+  uint64_t r_seed;
+  uint32_t r_stream;
+};
+
+template <bool kBF16, bool kColSR, bool kRowSR>
+__global__ __launch_bounds__(kThreads) void dual_encode_kernel(DualArgs d) {
+  const ColArgs &a = d.c;
+  __shared__ float recip[128];
+  __shared__ uint2 tile_codes[kColTileCG * 8][kColTileRB + 1];
+  __shared__ uint8_t tile_scales[kColTileCG * 8][kColTileRB + 4];
+  const float amax = __uint_as_float(load_amax(a.ctrl));
+  const float st = amax / 2688.0f;
+  const float d6 = 6.0f * st;
+  build_recip_table(recip, st);
+  __syncthreads();
+  const ColLane l = col_lane(a);
+  const int cgl = threadIdx.x % kColTileCG, rbl = threadIdx.x / kColTileCG;
+  ColTile<kBF16> t;
+  col_load<kBF16>(a, l.b, l.ld_rb, l.ld_cg, l.full, t);
+  // The transposed view, staged in LDS.
+  if (l.valid) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t c = 8 * l.cg + e;  // row of the transposed view
+      if (c >= a.C) break;
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = t.at(j, e);
+      const uint32_t S = block_scale_code(max_abs16(v), st, d6);
+      const int64_t vrow = l.b * a.C + c;
+      tile_codes[cgl * 8 + e][rbl] = encode16<kColSR>(v, recip[S], (uint64_t)(vrow * a.R + 16 * l.rb), a.sr_stream,
+                                                      a.sr_seed);
+      tile_scales[cgl * 8 + e][rbl] = (uint8_t)S;
+    }
+  }
+  // The view along the columns, stored directly.  Column groups come in
+  // pairs that are both inside or both outside the tensor (C % 16 == 0), so
+  // the pair exchange below never mixes a valid lane with an invalid one;
+  // every lane takes part in it.
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = t.at(j, i);
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, abs_bits(v[i]));
+    m = max(m, lane_xor1(m));
+    const uint32_t S = block_scale_code(m, st, d6);
+    const float r = recip[S];
+    if (l.valid) {
+      const int64_t row = l.b * a.R + 16 * l.rb + j;
+      const int64_t n0 = row * a.C + 8 * l.cg;  // logical index of this lane's first element
+      float q[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = v[i] * r;
+      uint32_t w;
+      if (kRowSR) {
+        const u32x4 rr = sr_block((uint64_t)n0 / 8, d.r_stream, d.r_seed);
+        w = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w |= e2m1_sr(q[i], sr_word(rr, i)) << (4 * i);
+      } else {
+        w = e2m1_rne8(q);
+      }
+      *reinterpret_cast<uint32_t *>(d.rcodes + row * (a.C / 2) + 4 * l.cg) = w;
+      if ((l.cg & 1) == 0) d.rscales[row * (a.C / 16) + l.cg / 2] = (uint8_t)S;
+    }
+  }
+  __syncthreads();
+  // Write out the transposed tile: 128 transposed rows x 16 row blocks.
+  const int64_t RB = a.R / 16;
+  const int64_t rb_n = min((int64_t)kColTileRB, RB - l.tr * kColTileRB);
+  for (int i = threadIdx.x; i < kColTileCG * 8 * kColTileRB; i += kThreads) {
+    const int tcol = i / kColTileRB, trb = i % kColTileRB;
+    const int64_t c = l.tc * kColTileCG * 8 + tcol;
+    if (c < a.C && trb < rb_n) {
+      const int64_t vrow = l.b * a.C + c;
+      const int64_t rb = l.tr * kColTileRB + trb;
+      st_stream(a.codes + vrow * (a.R / 2) + 8 * rb, tile_codes[tcol][trb]);
+      a.scales[vrow * RB + rb] = tile_scales[tcol][trb];
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *d.rtensor_scale = st;
+  encode_finish(a.ctrl, a.tensor_scale, st);
+}
+
 // Single-pass transposing quantize (BF16): at most one workgroup per CU, each
 // covering 16 kRB input rows x 128 columns, i.e. kRB x 16 units of 16 rows
 // x 8 columns, one unit per thread held in registers (64 dwords); kRB = 64
@@ -1184,6 +1284,72 @@ nvfp4_status launch_quantize_group(const QuantGroupProblem &p, hipStream_t s) {
     if (st != NVFP4_OK) return st;
   }
   return NVFP4_OK;
+}
+
+namespace {
+
+template <bool kBF16, bool kColSR, bool kRowSR>
+hipError_t run_dual(const RowArgs &ra, const DualArgs &d, bool contig, hipStream_t s) {
+  // amax over the input (orientation-free), then one encode pass for both views
+  const int g = grid_for((ra.nblocks + 63) / 64, (kThreads / 64) * kBatch, 256ull * 4);
+  if (contig) hipLaunchKernelGGL((row_amax_kernel<kBF16, false, true>), dim3(g), dim3(kThreads), 0, s, ra);
+  else hipLaunchKernelGGL((row_amax_kernel<kBF16, false, false>), dim3(g), dim3(kThreads), 0, s, ra);
+  const uint64_t tiles = (uint64_t)(d.c.batch * d.c.tiles_r * d.c.tiles_c);
+  if (tiles > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((dual_encode_kernel<kBF16, kColSR, kRowSR>), dim3((unsigned)tiles), dim3(kThreads), 0, s, d);
+  return hipGetLastError();
+}
+
+template <bool kBF16>
+hipError_t dispatch_dual(const RowArgs &ra, const DualArgs &d, bool col_sr, bool row_sr, bool contig, hipStream_t s) {
+  if (col_sr) return row_sr ? run_dual<kBF16, true, true>(ra, d, contig, s) : run_dual<kBF16, true, false>(ra, d, contig, s);
+  return row_sr ? run_dual<kBF16, false, true>(ra, d, contig, s) : run_dual<kBF16, false, false>(ra, d, contig, s);
+}
+
+}  // namespace
+
+nvfp4_status launch_quantize_dual(const QuantProblem &row, const QuantProblem &col, hipStream_t s) {
+  if (row.batch == 0 || row.rows == 0 || row.cols == 0) {
+    hipLaunchKernelGGL(store_zero_scale, dim3(1), dim3(1), 0, s, row.tensor_scale);
+    hipLaunchKernelGGL(store_zero_scale, dim3(1), dim3(1), 0, s, col.tensor_scale);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+  }
+  RowArgs ra{};
+  ra.x = row.x;
+  ra.nblocks = (uint64_t)(row.batch * row.rows * row.cols / 16);
+  ra.bpr = (uint64_t)(row.cols / 16);
+  ra.rows = row.rows;
+  ra.ld = row.ld;
+  ra.bstride = row.bstride;
+  ra.ctrl = row.ctrl;
+  const bool contig = (row.ld == row.cols) && (row.batch == 1 || row.bstride == row.rows * row.ld);
+  DualArgs d{};
+  ColArgs &a = d.c;
+  a.x = row.x;
+  a.batch = row.batch;
+  a.R = row.rows;
+  a.C = row.cols;
+  a.ld = row.ld;
+  a.bstride = row.bstride;
+  a.tiles_r = (row.rows / 16 + kColTileRB - 1) / kColTileRB;
+  a.tiles_c = (row.cols + 8 * kColTileCG - 1) / (8 * kColTileCG);
+  const int64_t esize = row.bf16 ? 2 : 4;
+  a.vec_ok = reinterpret_cast<uintptr_t>(row.x) % 16 == 0 && (row.ld * esize) % 16 == 0 &&
+             (row.batch == 1 || (row.bstride * esize) % 16 == 0);
+  a.codes = col.codes;
+  a.scales = col.scales;
+  a.tensor_scale = col.tensor_scale;
+  a.ctrl = row.ctrl;
+  a.sr_seed = col.sr_seed;
+  a.sr_stream = col.sr_stream;
+  d.rcodes = row.codes;
+  d.rscales = row.scales;
+  d.rtensor_scale = row.tensor_scale;
+  d.r_seed = row.sr_seed;
+  d.r_stream = row.sr_stream;
+  const hipError_t err = row.bf16 ? dispatch_dual<true>(ra, d, col.sr, row.sr, contig, s)
+                                  : dispatch_dual<false>(ra, d, col.sr, row.sr, contig, s);
+  return err == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 
 nvfp4_status launch_quantize(const QuantProblem &p, hipStream_t s) {

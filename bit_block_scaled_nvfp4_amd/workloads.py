@@ -21,8 +21,13 @@ trained weights are needed or used):
 * ``attn_scores``: attention scores QK^T ("Full-Stack FP4 ...", section 2.4):
   Q, K [4][32][4096][128], each (batch, head) slice scaled by a per-head RMS
   drawn log-uniformly in [0.5, 4].
+* ``attn_bwd``: the backward through dS of the same attention: Q, K as
+  above and dS [128][4096][4096], N(0, 1) times 1e-4 times a per-head factor
+  log-uniform in [0.25, 4].
 """
 from __future__ import annotations
+
+import os
 
 import numpy as np
 import torch
@@ -113,10 +118,42 @@ def attn_scores(seed: int = 4, b: int = 4, h: int = 32, s: int = 4096, d: int = 
     return out
 
 
+ATTN_BWD_SR_SEED = 0x5EED0006
+
+
+def attn_bwd(seed: int = 5, b: int = 4, h: int = 32, s: int = 4096, d: int = 128, heads: int | None = None):
+    """The attention backward through dS ("Full-Stack FP4 ...", section 2.4):
+    per (batch, head) slice i, drawn from its own stream default_rng([seed,
+    i]): Q and K N(0, 1) times a per-slice RMS log-uniform in [0.5, 4] (as in
+    attn_scores), and dS, the gradient of the scores, N(0, 1) times 1e-4 times
+    a per-slice factor log-uniform in [0.25, 4].  `heads` keeps the first
+    slices only (the same values as in the full draw)."""
+    bh = b * h if heads is None else heads
+    q = torch.empty((bh, s, d), dtype=torch.bfloat16)
+    k = torch.empty((bh, s, d), dtype=torch.bfloat16)
+    ds = torch.empty((bh, s, s), dtype=torch.bfloat16)
+    def draw(i):
+        rng = np.random.default_rng([seed, i])
+        for t in (q, k):
+            x = rng.standard_normal((s, d), dtype=np.float32)
+            x *= np.float32(np.exp(rng.uniform(np.log(0.5), np.log(4.0))))
+            t[i] = to_bf16(x)
+        scale = np.float32(1e-4 * np.exp(rng.uniform(np.log(0.25), np.log(4.0))))
+        ds[i] = to_bf16(rng.standard_normal((s, s), dtype=np.float32) * scale)
+
+    # slices are independent streams, so they can be drawn side by side
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
+        list(ex.map(draw, range(bh)))
+    return {"Q": q, "K": k, "dS": ds, "alpha": float(np.float32(1.0 / np.sqrt(float(d)))),
+            "sr_seed": ATTN_BWD_SR_SEED}
+
+
 WORKLOADS = {
     "tiny": tiny,
     "fprop_3b": fprop_3b,
     "mlp_up_12b": mlp_up_12b,
     "linear_train": linear_train,
     "attn_scores": attn_scores,
+    "attn_bwd": attn_bwd,
 }

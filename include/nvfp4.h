@@ -180,6 +180,25 @@ nvfp4_status nvfp4_quantize_noalloc(const void *x, int32_t x_dtype, int64_t batc
                                     int64_t cols, int64_t ld, int64_t batch_stride, int32_t axis,
                                     const nvfp4_quant_opts *opts, const nvfp4_qtensor *out, void *stream);
 
+/* Quantize one input in both orientations from one read: row_out as
+ * nvfp4_quantize with ALONG_COLS ([batch][rows][cols]) and col_out as with
+ * ALONG_ROWS ([batch][cols][rows]), each bit-identical to that call with its
+ * own options (rounding, sr_seed, sr_stream), and one tensor scale, the same
+ * in both views (without the transform both have the same maximum).  This is
+ * how one tensor serves two GEMMs that contract over different dimensions:
+ * [P3] section 2.4 quantizes Q, K and V once and reuses the quantized views
+ * in the forward and the backward pass (QK^T contracts over the head
+ * dimension, dS K and dS^T Q over the sequence).  rows % 16 == 0 and
+ * cols % 16 == 0; x aligned to its element size (16-byte aligned rows take
+ * the vector-load path); opts->rht must be 0 (NVFP4_EUNSUPPORTED otherwise);
+ * opts may be NULL (RNE); workspace as for nvfp4_quantize.  Runs as two
+ * passes over the input (tensor maximum, then both encodes). */
+nvfp4_status nvfp4_quantize_dual(const void *x, int32_t x_dtype, int64_t batch, int64_t rows, int64_t cols,
+                                 int64_t ld, int64_t batch_stride, const nvfp4_quant_opts *row_opts,
+                                 const nvfp4_qtensor *row_out, const nvfp4_quant_opts *col_opts,
+                                 const nvfp4_qtensor *col_out, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
 /* One tensor of nvfp4_quantize_group: x as for nvfp4_quantize (ALONG_COLS). */
 typedef struct nvfp4_quant_job {
   const void *x;
@@ -284,6 +303,39 @@ nvfp4_status nvfp4_linear_fwd_bwd(const void *x, const void *w, const void *dy, 
  *   workspace has run on its stream. */
 nvfp4_status nvfp4_linear_view(void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
                                int64_t K, int32_t which, nvfp4_qtensor *out);
+
+/* Attention backward through dS in NVFP4: [P3] section 2.4 runs QK^T and
+ * dS in NVFP4 (keeping P V, P^T dO and dO V^T in BF16) and reuses the
+ * quantized views of Q, K and V between the forward and the backward pass.
+ * Given dS (the gradient of the scores, [bh][sq][sk], dtype ds_dtype,
+ * contiguous) and the sequence-major quantized views q_seq [bh][d][sq] and
+ * k_seq [bh][d][sk] (made once, e.g. by nvfp4_quantize_dual in the forward
+ * pass, whose other view serves QK^T), this computes
+ *   dQ[b] = alpha * dS[b] K[b]    ([bh][sq][d], row-major)
+ *   dK[b] = alpha * dS[b]^T Q[b]  ([bh][sk][d], row-major)
+ * in dtype out_dtype: dS is quantized in both orientations from one read
+ * (nvfp4_quantize_dual; along the keys with stream 4, along the queries with
+ * stream 5, rounding cfg->ds_rounding, seed cfg->sr_seed), then two batched
+ * GEMMs as nvfp4_gemm.  sq, sk, d multiples of 16, bh <= 65535; ds, dq, dk
+ * 16-byte aligned; workspace >= nvfp4_attention_ds_workspace_size(bh, sq,
+ * sk) bytes, 256-byte aligned, zeroed before first use.  After the call the
+ * workspace holds the two dS views, in order: along the keys [bh][sq][sk],
+ * then along the queries [bh][sk][sq], each as codes, scales and a 256-byte
+ * tensor-scale slot, every region starting on a 256-byte boundary; then one
+ * quantize control block. */
+typedef struct nvfp4_attn_cfg {
+  uint64_t sr_seed;
+  int32_t ds_rounding; /* NVFP4_SR (the gradient reading) or NVFP4_RNE */
+  int32_t reserved;    /* 0 */
+} nvfp4_attn_cfg;
+
+size_t nvfp4_attention_ds_workspace_size(int64_t bh, int64_t sq, int64_t sk);
+
+nvfp4_status nvfp4_attention_ds_grads(const void *ds, int32_t ds_dtype, const nvfp4_qtensor *q_seq,
+                                      const nvfp4_qtensor *k_seq, void *dq, void *dk, int32_t out_dtype,
+                                      int64_t bh, int64_t sq, int64_t sk, int64_t d, float alpha,
+                                      const nvfp4_attn_cfg *cfg, void *workspace, size_t workspace_bytes,
+                                      void *stream);
 
 #ifdef __cplusplus
 }

@@ -172,3 +172,50 @@ def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(nv, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         nv.lib()
+
+
+def test_quantize_dual_argument_errors():
+    f = nv.nvfp4_quantize_dual
+    o = nv.QuantOptsC(0, 0, 0, 0, 0, 0)
+
+    def call(x=FAKE, dt=nv.BF16, b=1, r=32, c=64, ld=64, bs=32 * 64, ro=o, rq=None, co=o, cq=None, ws=FAKE, wsb=4096):
+        rq = rq if rq is not None else _q(b, r, c)
+        cq = cq if cq is not None else _q(b, c, r)
+        return f(x, dt, b, r, c, ld, bs, ro, rq, co, cq, ws, wsb, None)
+
+    assert call(dt=5) == nv.EINVAL
+    assert call(x=0) == nv.EINVAL
+    assert call(r=24, rq=_q(1, 24, 64), cq=_q(1, 64, 24)) == nv.ESHAPE     # rows % 16
+    assert call(c=40, ld=40, rq=_q(1, 32, 40), cq=_q(1, 40, 32)) == nv.ESHAPE  # cols % 16
+    assert call(rq=_q(1, 32, 48)) == nv.EINVAL                              # row view shape
+    assert call(cq=_q(1, 48, 32)) == nv.EINVAL                              # transposed view shape
+    assert call(ro=nv.QuantOptsC(0, 1, 0, 0, 0, 0)) == nv.EUNSUPPORTED     # no transform in the dual quantize
+    assert call(ro=nv.QuantOptsC(3, 0, 0, 0, 0, 0)) == nv.EINVAL
+    assert call(x=FAKE + 1) == nv.EALIGN                                    # BF16 needs 2-byte alignment
+    assert call(ws=0) == nv.EWORKSPACE
+
+
+def test_attention_ds_argument_errors_and_workspace_size():
+    bh, sq, sk, d = 2, 64, 32, 16
+    need = nv.nvfp4_attention_ds_workspace_size(bh, sq, sk)
+    n = bh * sq * sk
+    assert need >= 2 * (n // 2 + n // 16) + 4096
+    assert nv.nvfp4_attention_ds_workspace_size(0, sq, sk) == 0
+    cfg = nv.AttnCfgC(1, nv.SR, 0)
+    qs, ks = _q(bh, d, sq), _q(bh, d, sk)
+    f = nv.nvfp4_attention_ds_grads
+
+    def call(ds=FAKE, dt=nv.BF16, q=qs, k=ks, dq=FAKE, dk=FAKE, ot=nv.BF16, b=bh, s1=sq, s2=sk, dd=d, c=cfg,
+             ws=FAKE, wsb=need):
+        return f(ds, dt, q, k, dq, dk, ot, b, s1, s2, dd, 0.125, c, ws, wsb, None)
+
+    assert call(ds=0) == nv.EINVAL
+    assert call(c=None) == nv.EINVAL
+    assert call(c=nv.AttnCfgC(1, 7, 0)) == nv.EINVAL
+    assert call(c=nv.AttnCfgC(1, nv.SR, 1)) == nv.EINVAL
+    assert call(ot=4) == nv.EINVAL
+    assert call(dd=24, q=_q(bh, 24, sq), k=_q(bh, 24, sk)) == nv.ESHAPE
+    assert call(q=_q(bh, d, sk)) == nv.EINVAL                          # Q view over the wrong length
+    assert call(dq=FAKE + 8) == nv.EALIGN
+    assert call(wsb=need - 1) == nv.EWORKSPACE
+    assert call(ws=FAKE + 64) == nv.EALIGN
