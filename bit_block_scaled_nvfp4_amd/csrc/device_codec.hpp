@@ -65,26 +65,40 @@ __device__ __forceinline__ uint32_t e2m1_rne8(const float *q) {
   return w;
 }
 
-// Stochastic rounding onto the same grid with a 16-bit uniform word u: the
-// magnitude rounds up iff u < 2^16 * (|q| - lo) / step, lo the grid point
-// at or below |q| (saturated at 6).  Written without a branch on the range,
-// so that the lanes of a wavefront do not take both paths in turn: with
-// e' = max(exponent(|q|), 0), t = |q| * 2^(1 - e') is exact and lies in
-// [0, 2) for |q| < 1 (step 0.5, t = 2|q|) and in [2, 4) for |q| >= 1 (step
-// 2^(e' - 1)); the grid point below is code 2e' + floor(t) and
-// (|q| - lo) / step = t - floor(t), also exact.  For |q| >= 1 the test
-// equals comparing u << 6 with the low 22 mantissa bits of |q|.  At 6 the
-// fraction is 0, so no special case.  t - floor(t) is one v_fract_f32
-// (exact for t in [0, 4), where it never reaches its clamp below 1) and
-// floor(t) the truncating convert.
-__device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t u16) {
-  const uint32_t sign = (__float_as_uint(q) >> 28) & 8u;
-  const float a = fminf(fabsf(q), 6.0f);
-  const uint32_t ebits = __float_as_uint(a) >> 23;          // biased exponent (sign bit is 0)
-  const uint32_t e = (ebits > 127u ? ebits : 127u) - 127u;  // 0, 1 or 2
-  const float t = __builtin_ldexpf(a, 1 - (int)e);          // a * 2^(1 - e), in [0, 4), exact
-  const uint32_t up = ((float)u16 < __builtin_amdgcn_fractf(t) * 65536.0f) ? 1u : 0u;
-  return sign | (2u * e + (uint32_t)t + up);
+// Stochastic rounding onto the same grid: with f the rounding fraction of
+// |q| (clamped to 6) between its grid neighbours and F = floor(f * 2^22),
+// the magnitude rounds up iff 64 u < F for the element's 16-bit word u.
+// gfx950's stochastic-rounding converter adds the top 22 bits of a random
+// operand to the 22 fraction bits it keeps below the E2M1 point and rounds
+// up on the carry: with ~(u << 16) as that operand it rounds up iff
+// F + 2^22 - 1 - 64 u >= 2^22, which is the rule above.  Its two lanes share
+// one random operand (the high lane sees it shifted left by one), so each
+// conversion carries one element, the other lane converting +0 (code 0):
+// even elements in the low lane with ~(u << 16); odd elements in the high
+// lane with ((~w) >> 1) | 0x7FFF, whose left shift by one has ~u in its top
+// 16 bits and ones below (w the Philox word, u its high half).  Sign,
+// saturation and signed zeros come out as the rule has them.
+// tests/test_hw_converters.py checks every FP32 value at the words around
+// its rounding threshold against the oracle (both lanes); the rule is
+// monotone in u, so that covers every word.  Element j of the 8 uses 16-bit
+// half (j & 1) of word j / 2 of r; element j lands in nibble j.
+typedef float float2_v __attribute__((ext_vector_type(2)));
+// Byte 0 of the result: the code of q_even in the low nibble and of q_odd in
+// the high one (words u = w & 0xFFFF and w >> 16).  This build does not tie
+// the converter's destination to its first operand, so only the byte it is
+// told to write (byte 0 here) is defined; the caller gathers the bytes.
+__device__ __forceinline__ uint32_t e2m1_sr_pair(float q_even, float q_odd, uint32_t w) {
+  const uint32_t nw = ~w;
+  const float2_v lo = {q_even, 0.0f}, hi = {0.0f, q_odd};
+  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, lo, (nw << 16) | 0xFFFFu, 1.0f, 0) |
+         __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, hi, (nw >> 1) | 0x7FFFu, 1.0f, 0);
+}
+__device__ __forceinline__ uint32_t e2m1_sr8(const float *q, uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  const uint32_t x0 = e2m1_sr_pair(q[0], q[1], w0), x1 = e2m1_sr_pair(q[2], q[3], w1);
+  const uint32_t x2 = e2m1_sr_pair(q[4], q[5], w2), x3 = e2m1_sr_pair(q[6], q[7], w3);
+  const uint32_t a = __builtin_amdgcn_perm(x1, x0, 0x0C0C0400u);  // [x0.b0, x1.b0, 0, 0]
+  const uint32_t b = __builtin_amdgcn_perm(x3, x2, 0x0C0C0400u);  // [x2.b0, x3.b0, 0, 0]
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);                // [a.b0, a.b1, b.b0, b.b1]
 }
 
 // ---------------------------------------------------------------------------
@@ -172,10 +186,6 @@ __device__ __forceinline__ u32x4 sr_block(uint64_t g, uint32_t stream, uint64_t 
                        (uint32_t)(seed >> 32));
 }
 
-__device__ __forceinline__ uint32_t sr_word(const u32x4 &r, int j) {
-  const uint32_t w = (j >> 1) == 0 ? r.x : (j >> 1) == 1 ? r.y : (j >> 1) == 2 ? r.z : r.w;
-  return (j & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
 
 // ---------------------------------------------------------------------------
 // Lane-pair exchange

@@ -30,8 +30,8 @@
 //
 // Encode of a block: S = E4M3(fl(max|v| / fl(6 s_t))), q = fl(v * r_S) with
 // r_S = fl(1 / fl(E4M3(S) * s_t)) from a 127-entry LDS table built once per
-// workgroup, then E2M1 (hardware converter for RNE, integer compare against
-// a Philox word for stochastic rounding).
+// workgroup, then E2M1 (the hardware converters: round to nearest even, or
+// stochastic rounding driven by the element's Philox word).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -147,12 +147,7 @@ __device__ __forceinline__ uint2 encode16(const float (&v)[16], float r, uint64_
   if (kSR) {
     const u32x4 r0 = sr_block(n0 / 8, stream, seed);
     const u32x4 r1 = sr_block(n0 / 8 + 1, stream, seed);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lo |= e2m1_sr(q[j], sr_word(r0, j)) << (4 * j);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) hi |= e2m1_sr(q[8 + j], sr_word(r1, j)) << (4 * j);
-    return make_uint2(lo, hi);
+    return make_uint2(e2m1_sr8(q, r0.x, r0.y, r0.z, r0.w), e2m1_sr8(q + 8, r1.x, r1.y, r1.z, r1.w));
   }
   return make_uint2(e2m1_rne8(q), e2m1_rne8(q + 8));
 }
@@ -901,9 +896,7 @@ __global__ __launch_bounds__(kThreads) void dual_encode_kernel(DualArgs d) {
       uint32_t w;
       if (kRowSR) {
         const u32x4 rr = sr_block((uint64_t)n0 / 8, d.r_stream, d.r_seed);
-        w = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w |= e2m1_sr(q[i], sr_word(rr, i)) << (4 * i);
+        w = e2m1_sr8(q, rr.x, rr.y, rr.z, rr.w);
       } else {
         w = e2m1_rne8(q);
       }

@@ -79,8 +79,11 @@ int oracle_e2m1_encode_rne(float q) {
 
 /* Q8b: stochastic rounding onto the E2M1 grid.  u is a uniform 16-bit word.
  * With lo the largest grid value <= a and delta the spacing above it, the
- * magnitude rounds up with probability ceil(f * 2^16) / 2^16 where
- * f = (a - lo) / delta, i.e. iff u < f * 2^16.  Saturates at 6. */
+ * rounding fraction f = (a - lo) / delta (exact) is carried to 22 bits below
+ * the E2M1 point, F = floor(f * 2^22), and the magnitude rounds up iff
+ * 64 u < F, i.e. iff u / 2^16 < F / 2^22: with probability ceil(F / 64) /
+ * 2^16.  (For a >= 1 F is exactly the 22 mantissa bits below the E2M1 one,
+ * so there the rule is u / 2^16 < f.)  Saturates at 6. */
 int oracle_e2m1_encode_sr(float q, uint32_t u) {
   static const float grid[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
   float a = fminf(fabsf(q), 6.0f);
@@ -93,8 +96,9 @@ int oracle_e2m1_encode_sr(float q, uint32_t u) {
     for (int i = 0; i < 7; ++i)
       if (grid[i] <= a) lo_idx = i;
     float delta = grid[lo_idx + 1] - grid[lo_idx];
-    float f = (a - grid[lo_idx]) / delta; /* exact: Sterbenz, power-of-two divisor */
-    int up = ((float)(u & 0xFFFFu) < f * 65536.0f) ? 1 : 0;
+    float f = (a - grid[lo_idx]) / delta;           /* exact: Sterbenz, power-of-two divisor */
+    uint32_t F = (uint32_t)floorf(f * 4194304.0f);  /* exact scaling by 2^22, then the integer part */
+    int up = (64u * (u & 0xFFFFu) < F) ? 1 : 0;
     mag = lo_idx + up;
   }
   return (sign << 3) | mag;
@@ -152,6 +156,12 @@ void oracle_e2m1_encode_rne_array(const float *q, int64_t n, uint8_t *out) {
 void oracle_e4m3_encode_rne_sat_array(const float *y, int64_t n, uint8_t *out) {
   for (int64_t i = 0; i < n; ++i)
     out[i] = (uint8_t)oracle_e4m3_encode_rne_sat(y[i]);
+}
+
+/* Stochastic rounding of value q[i] under word u[i], for i < n. */
+void oracle_e2m1_encode_sr_pairs(const float *q, const uint32_t *u, int64_t n, uint8_t *out) {
+  for (int64_t i = 0; i < n; ++i)
+    out[i] = (uint8_t)oracle_e2m1_encode_sr(q[i], u[i]);
 }
 
 /* Stochastic rounding of each of nq values under every 16-bit word:

@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_e2m1_encode_rne_array.argtypes = [vp, i64, vp]
         L.oracle_e4m3_encode_rne_sat_array.argtypes = [vp, i64, vp]
         L.oracle_e2m1_encode_sr_all_words.argtypes = [vp, i64, vp]
+        L.oracle_e2m1_encode_sr_pairs.argtypes = [vp, vp, i64, vp]
         L.oracle_philox4x32_10.argtypes = [vp, vp, vp]
         L.oracle_sr_word.argtypes = [u64, u32, u64]
         L.oracle_sr_word.restype = u32
@@ -112,6 +113,16 @@ def e4m3_encode_array(y: np.ndarray) -> np.ndarray:
     y = np.ascontiguousarray(y, dtype=np.float32)
     out = np.empty(y.shape, dtype=np.uint8)
     lib().oracle_e4m3_encode_rne_sat_array(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def e2m1_encode_sr_pairs(q: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """Code of q[i] under the 16-bit word u[i]."""
+    q = np.ascontiguousarray(q, dtype=np.float32).reshape(-1)
+    u = np.ascontiguousarray(u, dtype=np.uint32).reshape(-1)
+    assert q.size == u.size
+    out = np.empty(q.size, dtype=np.uint8)
+    lib().oracle_e2m1_encode_sr_pairs(_ptr(q), _ptr(u), q.size, _ptr(out))
     return out
 
 

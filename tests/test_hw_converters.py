@@ -8,9 +8,11 @@ oracle or a library routine on the host:
   against the oracle's encoder (Q8a), nibble order included;
 * the E4M3 block-scale encode: every non-negative FP32 pattern up to +inf,
   against the oracle's encoder (Q5);
-* stochastic rounding: 4096 values (grid points, midpoints, saturation,
-  signed zeros, subnormals, random) under all 65536 words, against the
-  oracle (Q8b);
+* stochastic rounding through v_cvt_scalef32_sr_pk_fp4_f32, both of its
+  lanes: every FP32 value at the two words around its rounding threshold
+  (the rule is monotone in the word, so this covers every word), and 4096
+  values (grid points, midpoints, saturation, signed zeros, subnormals,
+  random) under all 65536 words, against the oracle (Q8b);
 * the GEMM operand decode (v_cvt_scalef32_pk_f16_fp4 at scale 2^8 times the
   E4M3 byte shifted into FP16), run through nvfp4_gemm_ex itself on every
   kernel and tile: every code against every scale byte the quantizer
@@ -44,7 +46,7 @@ def probe():
     L = ctypes.CDLL(PROBE)
     u32, i64, vp = ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p
     for name, args in [("hwprobe_e2m1_rne8", [u32, i64, vp, vp]), ("hwprobe_e4m3", [u32, i64, vp, vp]),
-                       ("hwprobe_e2m1_sr", [vp, i64, vp, vp]),
+                       ("hwprobe_e2m1_sr", [vp, i64, vp, vp, vp]), ("hwprobe_sr_threshold", [u32, i64, vp, vp, vp]),
                        ("hwprobe_bf16", [u32, i64, vp, vp])]:
         getattr(L, name).argtypes = args
         getattr(L, name).restype = ctypes.c_int
@@ -130,11 +132,59 @@ def test_stochastic_rounding_every_word():
     q = _sr_values()
     dq = torch.from_numpy(q).to("cuda:0")
     dev = torch.empty(q.size * 65536, dtype=torch.uint8, device="cuda:0")
-    assert L.hwprobe_e2m1_sr(dq.data_ptr(), q.size, dev.data_ptr(), _stream()) == 0
+    bad = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+    assert L.hwprobe_e2m1_sr(dq.data_ptr(), q.size, dev.data_ptr(), bad.data_ptr(), _stream()) == 0
     got = dev.cpu().numpy().reshape(q.size, 65536)
+    assert int(bad.item()) == 0, "the four bytes of one conversion disagree"
     want = _parallel(O.e2m1_encode_sr_all_words, q)
-    bad = np.argwhere(got != want)
-    assert bad.size == 0, f"{len(bad)} SR codes differ, first q={q[bad[0][0]]!r} u={bad[0][1]}"
+    for lane, g in (("low", got & 0xF), ("high", got >> 4)):
+        bad_i = np.argwhere(g != want)
+        assert bad_i.size == 0, f"{lane} lane: {len(bad_i)} SR codes differ, first q={q[bad_i[0][0]]!r} u={bad_i[0][1]}"
+
+
+def _sr_thresholds(f: np.ndarray) -> np.ndarray:
+    """U per value: the words u < U round up under the oracle's rule."""
+    a = np.minimum(np.abs(f), np.float32(6.0))
+    eb = (a.view(np.uint32) >> np.uint32(23)).astype(np.int32)
+    e = np.maximum(eb, 127) - 127
+    t = np.ldexp(a, (1 - e).astype(np.int32)).astype(np.float32)
+    F = np.floor((t - np.floor(t)) * np.float32(4194304.0)).astype(np.uint32)
+    return (F + np.uint32(63)) // np.uint32(64)
+
+
+def _oracle_pairs(f: np.ndarray, u: np.ndarray) -> np.ndarray:
+    parts = np.array_split(np.arange(f.size), _threads())
+    with ThreadPoolExecutor(len(parts)) as ex:
+        return np.concatenate(list(ex.map(lambda p: O.e2m1_encode_sr_pairs(f[p], u[p]), parts)))
+
+
+def test_stochastic_rounding_every_fp32_value_at_its_threshold():
+    L = probe()
+    dev = torch.empty(CHUNK, dtype=torch.int16, device="cuda:0")
+    nbad = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+    for c in range((1 << 32) // CHUNK):
+        first = c * CHUNK
+        assert L.hwprobe_sr_threshold(first, CHUNK, dev.data_ptr(), nbad.data_ptr(), _stream()) == 0
+        got = dev.cpu().numpy().view(np.uint16)
+        pats = _patterns(first, CHUNK)
+        ok = _not_nan(pats)
+        f = pats.view(np.float32)[ok]
+        g = got[ok]
+        U = _sr_thresholds(f)
+        u_lo = np.where(U == 0, 0, U - 1).astype(np.uint32)
+        u_hi = np.minimum(U, 65535).astype(np.uint32)
+        w_lo, w_hi = _oracle_pairs(f, u_lo), _oracle_pairs(f, u_hi)
+        # U is the oracle's own threshold: the codes on its two sides differ wherever it is inside 1..65535
+        inner = (U > 0) & (U < 65536)
+        assert np.all(w_lo[inner] != w_hi[inner])
+        assert np.all(w_lo[U == 0] == w_hi[U == 0])
+        for k, want in ((0, w_lo), (1, w_hi)):
+            byte = (g >> np.uint16(8 * k)) & np.uint16(0xFF)
+            for lane, code in (("low", byte & 0xF), ("high", byte >> 4)):
+                bad = np.nonzero(code != want)[0]
+                assert bad.size == 0, f"{lane} lane, word {'U-1' if k == 0 else 'U'}: {bad.size} codes differ, " \
+                    f"first value {f[bad[0]]!r}"
+    assert int(nbad.item()) == 0, "the four bytes of one conversion disagree"
 
 
 def _decode_operands(K: int):

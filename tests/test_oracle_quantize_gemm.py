@@ -44,8 +44,9 @@ def _sr_exact(a: float, u: int) -> int:
         return 7
     lo = max(i for i in range(8) if GRID[i] <= a)
     fa, flo, fhi = Fraction(a), Fraction(GRID[lo]), Fraction(GRID[lo + 1])
-    # round up iff u / 2^16 < (a - lo) / (hi - lo)
-    return lo + (1 if u * (fhi - flo) < (fa - flo) * 65536 else 0)
+    # the fraction (a - lo) / (hi - lo) carried to 22 bits: round up iff u / 2^16 < floor(f 2^22) / 2^22
+    F = ((fa - flo) / (fhi - flo) * 2 ** 22) // 1
+    return lo + (1 if 64 * u < F else 0)
 
 
 def brute_quantize(v: np.ndarray, rounding=O.RNE, sr_seed=0, sr_stream=0):
@@ -193,8 +194,10 @@ def test_zero_tensor():
 
 def test_sr_exact_expectation_all_words():
     """Averaging the decoded SR result over all 65536 words gives exactly
-    lo + delta * ceil(f * 2^16) / 2^16."""
-    for a in [0.1, 0.3, 0.74, 1.2, 1.9999, 2.3, 3.7, 4.5, 5.99, 6.0, 7.3]:
+    lo + delta * ceil(F / 64) / 2^16 with F = floor(f * 2^22), which is
+    lo + delta * ceil(f * 2^16) / 2^16 wherever f has at most 22 bits (all
+    a >= 1; tiny a: f * 2^22 < 1 never rounds up)."""
+    for a in [0.1, 0.3, 0.74, 1.2, 1.9999, 2.3, 3.7, 4.5, 5.99, 6.0, 7.3, 1e-7, 3e-7, 0.5 + 2 ** -24]:
         a32 = float(np.float32(a))
         total = sum(Fraction(O.e2m1_decode(O.e2m1_encode_sr(a32, u))) for u in range(65536))
         am = min(Fraction(a32), Fraction(6))
@@ -204,7 +207,10 @@ def test_sr_exact_expectation_all_words():
             lo = max(g for g in GRID if g <= am)
             hi = GRID[GRID.index(lo) + 1]
             f = (am - Fraction(lo)) / (Fraction(hi) - Fraction(lo))
-            want = Fraction(lo) + (Fraction(hi) - Fraction(lo)) * Fraction(-(-f * 65536 // 1), 65536)
+            F = (f * 2 ** 22) // 1
+            want = Fraction(lo) + (Fraction(hi) - Fraction(lo)) * Fraction(-(-F // 64), 65536)
+            if a32 >= 1.0:
+                assert want == Fraction(lo) + (Fraction(hi) - Fraction(lo)) * Fraction(-(-f * 65536 // 1), 65536)
         assert total / 65536 == want, a
 
 
