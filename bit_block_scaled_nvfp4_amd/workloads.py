@@ -24,6 +24,8 @@ trained weights are needed or used):
 * ``attn_bwd``: the backward through dS of the same attention: Q, K as
   above and dS [128][4096][4096], N(0, 1) times 1e-4 times a per-head factor
   log-uniform in [0.25, 4].
+* ``adamw_state``: FP32 AdamW moments m, v of a 20480x5120 weight, heavy
+  tailed with a per-row gradient scale.
 """
 from __future__ import annotations
 
@@ -149,6 +151,35 @@ def attn_bwd(seed: int = 5, b: int = 4, h: int = 32, s: int = 4096, d: int = 128
             "sr_seed": ATTN_BWD_SR_SEED}
 
 
+ADAMW_RHT_SEED = 0x4AD40007
+ADAMW_SR_SEED = 0x5EED0007
+
+
+def adamw_state(seed: int = 7, rows: int = 20480, cols: int = 5120):
+    """AdamW moments of one weight matrix (the 12B MLP up-projection's shape),
+    for the NVFP4 state codec ("Full-Stack FP4 ...", section 2.2): per row a
+    gradient scale g_r log-uniform in [1e-5, 1e-2]; m = g_r * Student-t(3)
+    (heavy tailed), v = (g_r * Student-t(3))^2 + (1e-3 g_r)^2 (a second,
+    independent draw, so v >= 0 and never exactly zero).  Row r comes from
+    default_rng([seed, r // 1024]) in chunks of 1024 rows."""
+    m = np.empty((rows, cols), np.float32)
+    v = np.empty((rows, cols), np.float32)
+
+    def draw(c):
+        r0, r1 = 1024 * c, min(rows, 1024 * (c + 1))
+        rng = np.random.default_rng([seed, c])
+        g = np.exp(rng.uniform(np.log(1e-5), np.log(1e-2), size=(r1 - r0, 1)))
+        m[r0:r1] = (rng.standard_t(3.0, size=(r1 - r0, cols)) * g).astype(np.float32)
+        t = rng.standard_t(3.0, size=(r1 - r0, cols)) * g
+        v[r0:r1] = (t * t + (1e-3 * g) ** 2).astype(np.float32)
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
+        list(ex.map(draw, range((rows + 1023) // 1024)))
+    return {"m": torch.from_numpy(m), "v": torch.from_numpy(v), "rht_seed": ADAMW_RHT_SEED,
+            "sr_seed": ADAMW_SR_SEED}
+
+
 WORKLOADS = {
     "tiny": tiny,
     "fprop_3b": fprop_3b,
@@ -156,4 +187,5 @@ WORKLOADS = {
     "linear_train": linear_train,
     "attn_scores": attn_scores,
     "attn_bwd": attn_bwd,
+    "adamw_state": adamw_state,
 }

@@ -430,3 +430,127 @@ int oracle_gemm_ref(const uint8_t *a_codes, const uint8_t *a_scales, float a_st,
   free(arow);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* S1..S4: the AdamW moments held in NVFP4 ("Full-Stack FP4 ...", section    */
+/* 2.2, Q-AdamW).  The page sends the first moment through the Hadamard     */
+/* transform and stochastic rounding, and the second through a square root, */
+/* a BF16 mean per tile taken out, the transform and NVFP4; reconstruction  */
+/* undoes each step and squares.  Readings: the tile is the 16-element      */
+/* NVFP4 block; the second moment rounds to nearest even; "adaptive 4/6     */
+/* bit" is read as plain NVFP4.                                             */
+/* ------------------------------------------------------------------------ */
+
+/* RNE of a finite binary32 to BF16 bits (the upper half of the binary32 whose
+ * value is nearest, ties to an even BF16 mantissa). */
+static uint16_t bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  uint32_t lower = u & 0xFFFFu, upper = u >> 16;
+  if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+    upper += 1u;
+  return (uint16_t)upper;
+}
+
+/* S1: one block of the second moment: s_j = sqrt(v_j) (IEEE, correctly
+ * rounded), mu = BF16_RNE(fl(s_0 + ... + s_15) / 16) with the sum taken from
+ * left to right, and the residuals r_j = fl(s_j - mu), returned in v.
+ * Returns mu's BF16 bits. */
+uint16_t oracle_sqrt_demean16(float v[16]) {
+  float s[16];
+  for (int j = 0; j < 16; ++j)
+    s[j] = sqrtf(v[j]);
+  float sum = s[0];
+  for (int j = 1; j < 16; ++j)
+    sum = sum + s[j];
+  uint16_t mb = bf16_rne(sum / 16.0f);
+  float mu = bf16_to_float(mb);
+  for (int j = 0; j < 16; ++j)
+    v[j] = s[j] - mu;
+  return mb;
+}
+
+/* S2: encode m and v ([rows][cols] FP32, row stride ld, cols % 16 == 0).
+ * m: the transform with rht_seed, then stochastic rounding with
+ * (sr_seed, sr_stream), through oracle_quantize.  v: S1 on every block, then
+ * the residuals through oracle_quantize with the transform and RNE.  Views
+ * are [rows][cols] along cols; means are [rows][cols/16].  Returns 0, -1 on
+ * a bad argument, -2 when out of memory. */
+int oracle_qadamw_encode(const float *m, const float *v, int64_t rows, int64_t cols, int64_t ld,
+                         uint64_t rht_seed, uint64_t sr_seed, uint32_t sr_stream,
+                         uint8_t *m_codes, uint8_t *m_scales, float *m_st,
+                         uint8_t *v_codes, uint8_t *v_scales, float *v_st, uint16_t *v_means) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0 || ld < cols)
+    return -1;
+  int rc = oracle_quantize(m, ORACLE_F32, 1, rows, cols, ld, rows * ld, ORACLE_ALONG_COLS,
+                           ORACLE_SR, sr_seed, sr_stream, 1, rht_seed, m_codes, m_scales, m_st);
+  if (rc != 0)
+    return rc;
+  float *res = (float *)malloc(sizeof(float) * (size_t)(rows * cols > 0 ? rows * cols : 1));
+  if (!res)
+    return -2;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t g = 0; g < cols / 16; ++g) {
+      float b[16];
+      for (int j = 0; j < 16; ++j)
+        b[j] = v[r * ld + 16 * g + j];
+      v_means[r * (cols / 16) + g] = oracle_sqrt_demean16(b);
+      for (int j = 0; j < 16; ++j)
+        res[r * cols + 16 * g + j] = b[j];
+    }
+  rc = oracle_quantize(res, ORACLE_F32, 1, rows, cols, cols, rows * cols, ORACLE_ALONG_COLS,
+                       ORACLE_RNE, 0, 0, 1, rht_seed, v_codes, v_scales, v_st);
+  free(res);
+  return rc;
+}
+
+/* S3: the inverse transform of one dequantized block, the transform being
+ * y = (1/4) H diag(s) x with H the 16-point Sylvester matrix (H H = 16 I):
+ * x_j = s_j * (1/4) * sum_k H[j][k] * y_k, with y_k = E2M1 * E4M3 * s_t.
+ * Every product and partial sum is exact in double (the y_k share the
+ * factor E4M3 * s_t, and the sums of E2M1 values are small multiples of
+ * 1/2), so the one rounding is the final conversion to FP32.  A sum that
+ * is zero is +0 (the sum starts from +0), so a zero result takes the sign
+ * of s_j.  H[j][k] = (-1)^popcount(j & k). */
+static void inverse_transform_block(const uint8_t *codes, uint8_t scale, float st, const float s[16],
+                                    float out[16]) {
+  double y[16];
+  for (int k = 0; k < 16; ++k) {
+    int code = (k % 2 == 0) ? (codes[k / 2] & 0xF) : (codes[k / 2] >> 4);
+    y[k] = oracle_e2m1_decode(code) * oracle_e4m3_decode(scale) * (double)st;
+  }
+  for (int j = 0; j < 16; ++j) {
+    double acc = 0.0;
+    for (int k = 0; k < 16; ++k)
+      acc += (__builtin_popcount((unsigned)(j & k)) & 1) ? -y[k] : y[k];
+    out[j] = (float)((double)s[j] * 0.25 * acc);
+  }
+}
+
+/* S4: reconstruct m and v ([rows][cols], row stride ld) from the encoded
+ * state: m_j = x_j; v_j = fl(fl(x_j + mu)^2) with mu the block's BF16
+ * mean widened to FP32. */
+int oracle_qadamw_decode(const uint8_t *m_codes, const uint8_t *m_scales, float m_st,
+                         const uint8_t *v_codes, const uint8_t *v_scales, float v_st,
+                         const uint16_t *v_means, int64_t rows, int64_t cols, int64_t ld,
+                         uint64_t rht_seed, float *m, float *v) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0 || ld < cols)
+    return -1;
+  float signs[16];
+  oracle_rht_signs(rht_seed, signs);
+  int64_t nb = cols / 16;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t g = 0; g < nb; ++g) {
+      float x[16];
+      inverse_transform_block(m_codes + r * (cols / 2) + 8 * g, m_scales[r * nb + g], m_st, signs, x);
+      for (int j = 0; j < 16; ++j)
+        m[r * ld + 16 * g + j] = x[j];
+      inverse_transform_block(v_codes + r * (cols / 2) + 8 * g, v_scales[r * nb + g], v_st, signs, x);
+      float mu = bf16_to_float(v_means[r * nb + g]);
+      for (int j = 0; j < 16; ++j) {
+        float sj = x[j] + mu;
+        v[r * ld + 16 * g + j] = sj * sj;
+      }
+    }
+  return 0;
+}

@@ -71,6 +71,13 @@ def lib() -> ctypes.CDLL:
         L.oracle_gemm_ref.argtypes = [vp, vp, ctypes.c_float, vp, vp, ctypes.c_float, i64, i64,
                                       i64, i64, ctypes.c_double, vp, i64, vp, vp]
         L.oracle_gemm_ref.restype = ctypes.c_int
+        L.oracle_sqrt_demean16.argtypes = [vp]
+        L.oracle_sqrt_demean16.restype = ctypes.c_uint16
+        L.oracle_qadamw_encode.argtypes = [vp, vp, i64, i64, i64, u64, u64, u32, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_qadamw_encode.restype = ctypes.c_int
+        L.oracle_qadamw_decode.argtypes = [vp, vp, ctypes.c_float, vp, vp, ctypes.c_float, vp, i64, i64, i64,
+                                           u64, vp, vp]
+        L.oracle_qadamw_decode.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -280,3 +287,58 @@ def gemm_accept(y: np.ndarray, y_ref: np.ndarray, sabs: np.ndarray, bf16: bool) 
     cancel_ok = np.abs(yv - y_ref) <= FP32_TOL * sabs + 0.5 * ulp_y
     return {"n": int(y.size), "ok": int(ulp_ok.sum()), "cancel_only": int((~ulp_ok & cancel_ok).sum()),
             "fail": int((~(ulp_ok | cancel_ok)).sum())}
+
+
+# --- S1..S4: AdamW moments in NVFP4 ---------------------------------------
+
+@dataclass
+class QAdamWState:
+    """m and v views [1][rows][cols] and the BF16 block means [rows][cols/16]."""
+    m: QTensor
+    v: QTensor
+    v_means: np.ndarray
+
+
+def sqrt_demean16(v: np.ndarray):
+    """S1 on one block: (residuals, BF16 bits of the mean)."""
+    b = np.ascontiguousarray(v, dtype=np.float32).copy()
+    assert b.shape == (16,)
+    mb = lib().oracle_sqrt_demean16(_ptr(b))
+    return b, int(mb)
+
+
+def qadamw_encode(m: np.ndarray, v: np.ndarray, rht_seed: int, sr_seed: int, sr_stream: int = 0) -> QAdamWState:
+    m = np.ascontiguousarray(m, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    assert m.shape == v.shape and m.ndim == 2
+    rows, cols = m.shape
+
+    def view():
+        return QTensor(np.zeros((1, rows, cols // 2), np.uint8), np.zeros((1, rows, cols // 16), np.uint8),
+                       np.float32(0), 1, rows, cols)
+    qm, qv = view(), view()
+    means = np.zeros((rows, cols // 16), np.uint16)
+    sts = np.zeros(2, np.float32)
+    rc = lib().oracle_qadamw_encode(_ptr(m), _ptr(v), rows, cols, cols, rht_seed, sr_seed, sr_stream,
+                                    _ptr(qm.codes), _ptr(qm.scales), ctypes.c_void_p(sts.ctypes.data),
+                                    _ptr(qv.codes), _ptr(qv.scales), ctypes.c_void_p(sts.ctypes.data + 4),
+                                    _ptr(means))
+    if rc != 0:
+        raise ValueError(f"oracle_qadamw_encode failed (rc={rc})")
+    qm.tensor_scale, qv.tensor_scale = np.float32(sts[0]), np.float32(sts[1])
+    return QAdamWState(qm, qv, means)
+
+
+def qadamw_decode(st: QAdamWState, rht_seed: int):
+    """(m, v) FP32 [rows][cols] reconstructed from the state."""
+    rows, cols = st.m.rows, st.m.cols
+    m = np.zeros((rows, cols), np.float32)
+    v = np.zeros((rows, cols), np.float32)
+    means = np.ascontiguousarray(st.v_means, dtype=np.uint16)
+    rc = lib().oracle_qadamw_decode(_ptr(np.ascontiguousarray(st.m.codes)), _ptr(np.ascontiguousarray(st.m.scales)),
+                                    float(st.m.tensor_scale), _ptr(np.ascontiguousarray(st.v.codes)),
+                                    _ptr(np.ascontiguousarray(st.v.scales)), float(st.v.tensor_scale),
+                                    _ptr(means), rows, cols, cols, rht_seed, _ptr(m), _ptr(v))
+    if rc != 0:
+        raise ValueError(f"oracle_qadamw_decode failed (rc={rc})")
+    return m, v
