@@ -57,6 +57,10 @@ class AttnCfgC(ctypes.Structure):
     _fields_ = [("sr_seed", ctypes.c_uint64), ("ds_rounding", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class QAdamWStateC(ctypes.Structure):
+    _fields_ = [("m", QTensorC), ("v", QTensorC), ("v_means", ctypes.c_void_p)]
+
+
 class LinearCfgC(ctypes.Structure):
     _fields_ = [("sr_seed", ctypes.c_uint64), ("rht_seed", ctypes.c_uint64),
                 ("wgrad_sr_x", ctypes.c_int32), ("dw_dtype", ctypes.c_int32)]
@@ -114,6 +118,12 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_linear_fwd_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64,
                                            ctypes.POINTER(LinearCfgC), vp, sz, vp]
         L.nvfp4_linear_fwd_bwd.restype = i32
+        L.nvfp4_qadamw_workspace_size.restype = sz
+        L.nvfp4_qadamw_encode.argtypes = [vp, vp, i64, i64, i64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32,
+                                          ctypes.POINTER(QAdamWStateC), vp, sz, vp]
+        L.nvfp4_qadamw_encode.restype = i32
+        L.nvfp4_qadamw_decode.argtypes = [ctypes.POINTER(QAdamWStateC), ctypes.c_uint64, vp, vp, i64, vp]
+        L.nvfp4_qadamw_decode.restype = i32
         _lib = L
     return _lib
 
@@ -137,6 +147,10 @@ def nvfp4_quantize_workspace_size() -> int:
 
 def nvfp4_quantize_group_workspace_size() -> int:
     return lib().nvfp4_quantize_group_workspace_size()
+
+
+def nvfp4_qadamw_workspace_size() -> int:
+    return int(lib().nvfp4_qadamw_workspace_size())
 
 
 def nvfp4_linear_workspace_size(M: int, N: int, K: int) -> int:
@@ -392,6 +406,89 @@ def attention_ds_view(workspace: torch.Tensor, bh: int, sq: int, sk: int, which:
         off += 256
         views.append(QTensor(codes, scales, ts, bh, r, c))
     return views[which]
+
+
+@dataclass
+class QAdamWState:
+    """AdamW moments in NVFP4: m (transformed, stochastic rounding), v (the
+    transformed residual of sqrt(v) after its 16-element block means, RNE)
+    and the BF16 block means [rows][cols/16] (uint16 bits)."""
+    m: QTensor
+    v: QTensor
+    v_means: torch.Tensor
+
+    @staticmethod
+    def empty(rows: int, cols: int, device) -> "QAdamWState":
+        n = rows * cols // 16
+        return QAdamWState(QTensor.empty(1, rows, cols, device), QTensor.empty(1, rows, cols, device),
+                           torch.empty(max(n, 1), dtype=torch.int16, device=device)[:n].view(rows, cols // 16))
+
+    def c_struct(self) -> QAdamWStateC:
+        return QAdamWStateC(self.m.c_struct(), self.v.c_struct(), self.v_means.data_ptr())
+
+
+def _moment(t: torch.Tensor, what: str) -> torch.Tensor:
+    if t.dim() != 2 or t.dtype != torch.float32:
+        raise ValueError(f"{what} must be a 2-D float32 tensor")
+    if t.size(1) > 1 and t.stride(1) != 1:
+        raise ValueError(f"the last dimension of {what} must be contiguous")
+    return t
+
+
+def _qadamw_encode_args(m, v, rht_seed, sr_seed, sr_stream, state, workspace):
+    m, v = _moment(m, "m"), _moment(v, "v")
+    if m.shape != v.shape or (m.size(0) > 1 and m.stride(0) != v.stride(0)):
+        raise ValueError("m and v must have one shape and one row stride")
+    rows, cols = m.shape
+    if state is None:
+        state = QAdamWState.empty(rows, cols, m.device)
+    if workspace is None:
+        workspace = new_workspace(nvfp4_qadamw_workspace_size(), m.device)
+    st = state.c_struct()
+    args = (m.data_ptr(), v.data_ptr(), rows, cols, m.stride(0) if rows > 1 else cols, rht_seed, sr_seed, sr_stream,
+            ctypes.byref(st), workspace.data_ptr(), workspace.numel(), _stream(m.device))
+    return args, (st, m, v, workspace), state
+
+
+def qadamw_encode(m: torch.Tensor, v: torch.Tensor, rht_seed: int, sr_seed: int, sr_stream: int = 0,
+                  state: QAdamWState | None = None, workspace: torch.Tensor | None = None) -> QAdamWState:
+    """Encode FP32 moments m, v ([rows][cols], v >= 0) into NVFP4 state."""
+    args, _keep, state = _qadamw_encode_args(m, v, rht_seed, sr_seed, sr_stream, state, workspace)
+    _check(lib().nvfp4_qadamw_encode(*args), "nvfp4_qadamw_encode")
+    return state
+
+
+def _qadamw_decode_args(state: QAdamWState, rht_seed: int, m_out, v_out):
+    rows, cols = state.m.rows, state.m.cols
+    dev = state.m.codes.device
+    m_out = torch.empty(rows, cols, dtype=torch.float32, device=dev) if m_out is None else _moment(m_out, "m")
+    v_out = torch.empty(rows, cols, dtype=torch.float32, device=dev) if v_out is None else _moment(v_out, "v")
+    if tuple(m_out.shape) != (rows, cols) or tuple(v_out.shape) != (rows, cols) or (
+            rows > 1 and m_out.stride(0) != v_out.stride(0)):
+        raise ValueError("outputs must be [rows][cols] with one row stride")
+    st = state.c_struct()
+    args = (ctypes.byref(st), rht_seed, m_out.data_ptr(), v_out.data_ptr(), m_out.stride(0) if rows > 1 else cols,
+            _stream(dev))
+    return args, (st, m_out, v_out), (m_out, v_out)
+
+
+def qadamw_decode(state: QAdamWState, rht_seed: int, m_out: torch.Tensor | None = None,
+                  v_out: torch.Tensor | None = None):
+    """Reconstruct the FP32 moments (m, v) from NVFP4 state."""
+    args, _keep, outs = _qadamw_decode_args(state, rht_seed, m_out, v_out)
+    _check(lib().nvfp4_qadamw_decode(*args), "nvfp4_qadamw_decode")
+    return outs
+
+
+def bind_qadamw_encode(m, v, state: QAdamWState, workspace: torch.Tensor, rht_seed: int, sr_seed: int,
+                       sr_stream: int = 0) -> "BoundCall":
+    args, keep, state = _qadamw_encode_args(m, v, rht_seed, sr_seed, sr_stream, state, workspace)
+    return BoundCall(lib().nvfp4_qadamw_encode, args, keep, "nvfp4_qadamw_encode", state)
+
+
+def bind_qadamw_decode(state: QAdamWState, rht_seed: int, m_out, v_out) -> "BoundCall":
+    args, keep, outs = _qadamw_decode_args(state, rht_seed, m_out, v_out)
+    return BoundCall(lib().nvfp4_qadamw_decode, args, keep, "nvfp4_qadamw_decode", outs)
 
 
 class BoundCall:

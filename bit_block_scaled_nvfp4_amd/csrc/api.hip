@@ -305,6 +305,67 @@ NVFP4_EXPORT nvfp4_status nvfp4_quantize_dual(const void *x, int32_t x_dtype, in
   return nvfp4::launch_quantize_dual(pr, pc, static_cast<hipStream_t>(stream));
 }
 
+NVFP4_EXPORT size_t nvfp4_qadamw_workspace_size(void) { return 2 * sizeof(QuantCtrl); }
+
+namespace {
+nvfp4_status validate_state(const nvfp4_qadamw_state *st, int64_t rows, int64_t cols) {
+  if (!st) return NVFP4_EINVAL;
+  nvfp4_status r = check_view(&st->m, 1, rows, cols);
+  if (r != NVFP4_OK) return r;
+  r = check_view(&st->v, 1, rows, cols);
+  if (r != NVFP4_OK) return r;
+  if (rows * cols > 0 && !st->v_means) return NVFP4_EINVAL;
+  if (!aligned(st->v_means, 2)) return NVFP4_EALIGN;
+  return NVFP4_OK;
+}
+}  // namespace
+
+NVFP4_EXPORT nvfp4_status nvfp4_qadamw_encode(const float *m, const float *v, int64_t rows, int64_t cols, int64_t ld,
+                                              uint64_t rht_seed, uint64_t sr_seed, uint32_t sr_stream,
+                                              const nvfp4_qadamw_state *state, void *workspace,
+                                              size_t workspace_bytes, void *stream) {
+  if (rows < 0 || cols < 0 || rows > kMaxExtent || cols > kMaxExtent || cols % 16) return NVFP4_ESHAPE;
+  if (rows * cols > 0 && (!m || !v)) return NVFP4_EINVAL;
+  if (rows * cols > 0 && (ld < cols || !aligned(m, 16) || !aligned(v, 16) || (ld * 4) % 16)) {
+    return ld < cols ? NVFP4_ESHAPE : NVFP4_EALIGN;
+  }
+  nvfp4_status r = validate_state(state, rows, cols);
+  if (r != NVFP4_OK) return r;
+  if (!workspace || workspace_bytes < 2 * sizeof(QuantCtrl)) return NVFP4_EWORKSPACE;
+  if (!aligned(workspace, 256)) return NVFP4_EALIGN;
+  QuantCtrl *ctrl = static_cast<QuantCtrl *>(workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // First moment: the transform, then stochastic rounding.
+  const nvfp4_quant_opts mo{NVFP4_SR, 1, sr_seed, rht_seed, sr_stream, 0u};
+  r = nvfp4::launch_quantize(make_quant(m, false, 1, rows, cols, ld, rows * ld, false, &mo, &state->m, ctrl), s);
+  if (r != NVFP4_OK) return r;
+  // Second moment: square root, block means, residual, the transform, RNE.
+  const nvfp4_quant_opts vo{NVFP4_RNE, 1, 0, rht_seed, 0u, 0u};
+  return nvfp4::launch_state_encode_second(make_quant(v, false, 1, rows, cols, ld, rows * ld, false, &vo, &state->v,
+                                                      ctrl + 1),
+                                           state->v_means, s);
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_qadamw_decode(const nvfp4_qadamw_state *state, uint64_t rht_seed, float *m, float *v,
+                                              int64_t ld, void *stream) {
+  if (!state) return NVFP4_EINVAL;
+  const int64_t rows = state->m.rows, cols = state->m.cols;
+  if (rows < 0 || cols < 0 || cols % 16 || rows > kMaxExtent || cols > kMaxExtent) return NVFP4_ESHAPE;
+  nvfp4_status r = validate_state(state, rows, cols);
+  if (r != NVFP4_OK) return r;
+  if (rows * cols > 0) {
+    if (!m || !v) return NVFP4_EINVAL;
+    if (ld < cols) return NVFP4_ESHAPE;
+    if (!aligned(m, 16) || !aligned(v, 16) || (ld * 4) % 16) return NVFP4_EALIGN;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  r = nvfp4::launch_state_decode(state->m.codes, state->m.scales, state->m.tensor_scale, nullptr, m, rows, cols, ld,
+                                 rht_seed, s);
+  if (r != NVFP4_OK) return r;
+  return nvfp4::launch_state_decode(state->v.codes, state->v.scales, state->v.tensor_scale, state->v_means, v, rows,
+                                    cols, ld, rht_seed, s);
+}
+
 NVFP4_EXPORT size_t nvfp4_quantize_group_workspace_size(void) { return nvfp4::kGroupWorkspace; }
 
 NVFP4_EXPORT nvfp4_status nvfp4_quantize_group(const nvfp4_quant_job *jobs, int32_t njobs, int32_t x_dtype,

@@ -93,6 +93,13 @@ nvfp4_status launch_quantize_group(const QuantGroupProblem &p, hipStream_t strea
 // input and the view along its columns, `col` the transposed view (its
 // input fields are ignored); no transform; both views get one tensor scale.
 nvfp4_status launch_quantize_dual(const QuantProblem &row, const QuantProblem &col, hipStream_t stream);
+// Quantized optimizer state: the second moment's encode (square root, BF16
+// block means into `means`, residual, transform, RNE; FP32 input, two passes)
+// and the reconstruction of either state (`means` null: the first moment).
+nvfp4_status launch_state_encode_second(const QuantProblem &p, uint16_t *means, hipStream_t stream);
+nvfp4_status launch_state_decode(const uint8_t *codes, const uint8_t *scales, const float *tensor_scale,
+                                 const uint16_t *means, float *out, int64_t rows, int64_t cols, int64_t ld,
+                                 uint64_t rht_seed, hipStream_t stream);
 nvfp4_status launch_gemm(const GemmProblem &p, hipStream_t stream);
 
 }  // namespace nvfp4

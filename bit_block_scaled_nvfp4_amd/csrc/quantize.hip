@@ -284,7 +284,27 @@ struct RowArgs {
   QuantCtrl *ctrl;
   uint64_t sr_seed, rht_seed;
   uint32_t sr_stream;
+  uint16_t *means;    // second-moment pre-step only: BF16 block means, one per block
 };
+
+// Second-moment pre-step of the quantized-state optimizer ("Full-Stack FP4
+// ...", section 2.2: square root, tile mean, then the Hadamard transform) on
+// one 16-element block of FP32 values: s_j = sqrt(v_j) (correctly rounded),
+// the block mean mu = BF16_RNE(fl(sum_j s_j) / 16) with the sum taken left to
+// right, and the residuals r_j = fl(s_j - mu) in place.  Returns mu's BF16
+// bits.
+__device__ __forceinline__ uint32_t sqrt_demean16(float (&v)[16]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = __builtin_sqrtf(v[j]);
+  float sum = v[0];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) sum = sum + v[j];
+  const uint32_t mb = pack_bf16x2_rne(sum * 0.0625f, 0.0f) & 0xFFFFu;  // the division by 16 is exact
+  const float mu = __uint_as_float(mb << 16);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = v[j] - mu;
+  return mb;
+}
 
 // Single pass: up to kMaxJobs contiguous tensors in one launch, each with
 // its own tensor scale.  Global segment g belongs to the job whose
@@ -581,7 +601,7 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
     for (int j = 0; j < njobs; ++j) *a.job[j].tensor_scale = published_scale(ctrl, s_st[j]);
 }
 
-template <bool kBF16, bool kRHT, bool kContig>
+template <bool kBF16, bool kRHT, bool kContig, bool kPre = false>
 __global__ __launch_bounds__(kThreads) void row_amax_kernel(RowArgs a) {
   const uint32_t mask = kRHT ? rht_sign_mask(a.rht_seed) : 0u;
   const int lane = threadIdx.x & 63;
@@ -596,11 +616,12 @@ __global__ __launch_bounds__(kThreads) void row_amax_kernel(RowArgs a) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       uint32_t bm;
-      if constexpr (kBF16 && !kRHT) {
+      if constexpr (kBF16 && !kRHT && !kPre) {
         bm = raw[i].max_abs_bf16();
       } else {
         float v[16];
         raw[i].values(v);
+        if constexpr (kPre) (void)sqrt_demean16(v);
         if (kRHT) {
           rht16_unscaled(v, mask);
           bm = quarter_max_bits(max_abs16(v));
@@ -614,7 +635,7 @@ __global__ __launch_bounds__(kThreads) void row_amax_kernel(RowArgs a) {
   block_amax_commit(m, a.ctrl);
 }
 
-template <bool kBF16, bool kRHT, bool kSR, bool kContig>
+template <bool kBF16, bool kRHT, bool kSR, bool kContig, bool kPre = false>
 __global__ __launch_bounds__(kThreads) void row_encode_kernel(RowArgs a) {
   __shared__ float recip[128];
   const uint32_t mask = kRHT ? rht_sign_mask(a.rht_seed) : 0u;
@@ -636,6 +657,7 @@ __global__ __launch_bounds__(kThreads) void row_encode_kernel(RowArgs a) {
       if (blk[i] < a.nblocks) {
         float v[16];
         raw[i].values(v);
+        if constexpr (kPre) a.means[blk[i]] = (uint16_t)sqrt_demean16(v);
         if (kRHT) rht16(v, mask);
         row_store_block<kSR>(a, blk[i], v, block_scale_code(max_abs16(v), st, d6), recip);
       }
@@ -1277,6 +1299,123 @@ nvfp4_status launch_quantize_group(const QuantGroupProblem &p, hipStream_t s) {
     if (st != NVFP4_OK) return st;
   }
   return NVFP4_OK;
+}
+
+namespace {
+
+// Reconstruction of a quantized optimizer state, one 16-element block per
+// lane (blocks in row-major order over [rows][cols / 16]): x_j =
+// fl(E2M1 * E4M3 * s_t) (the first product is exact), the inverse transform
+// (1/4) D H (butterflies with span 1, 2, 4, 8, then the exact product by 1/4,
+// then the signs), and for the second moment s_j = fl(x_j + mu), v_j =
+// fl(s_j * s_j).  Output rows have stride ld (floats).
+struct StateDecodeArgs {
+  const uint8_t *codes, *scales;
+  const float *tensor_scale;
+  const uint16_t *means;  // second moment only
+  float *out;
+  uint64_t nblocks, bpr;
+  int64_t ld;
+  uint64_t rht_seed;
+};
+
+template <bool kSecond>
+__global__ __launch_bounds__(kThreads) void state_decode_kernel(StateDecodeArgs a) {
+  const uint32_t mask = rht_sign_mask(a.rht_seed);
+  const float st = *a.tensor_scale;
+  for (uint64_t blk = (uint64_t)blockIdx.x * kThreads + threadIdx.x; blk < a.nblocks;
+       blk += (uint64_t)gridDim.x * kThreads) {
+    const uint2 c = *reinterpret_cast<const uint2 *>(a.codes + 8 * blk);
+    const float sc = e4m3_value(a.scales[blk]);
+    // E2M1 values of the block (scale 1), then H on them: every partial sum
+    // is a multiple of 1/2 no larger than 96 in magnitude, so exact.
+    float v[16];
+    const float2_v p[8] = {
+        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 0), __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 1),
+        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 2), __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 3),
+        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 0), __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 1),
+        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 2), __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 3)};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[2 * k] = p[k][0];
+      v[2 * k + 1] = p[k][1];
+    }
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i & h) continue;
+        const float x = v[i], y = v[i + h];
+        v[i] = x + y;
+        v[i + h] = x - y;
+      }
+    }
+    // (1/4) E4M3 is exact, and so is its product with a sum above (at most
+    // 12 significant bits); the tensor scale rounds once; then the signs.
+    // A zero sum is taken as +0 (the sums of -0 codes would give -0), so a
+    // zero result carries the sign of the diagonal alone.
+    const float q4 = sc * 0.25f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float z = v[j] + 0.0f;
+      v[j] = __uint_as_float(__float_as_uint((z * q4) * st) ^ (((mask >> j) & 1u) << 31));
+    }
+    if constexpr (kSecond) {
+      const float mu = __uint_as_float((uint32_t)a.means[blk] << 16);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float sj = v[j] + mu;
+        v[j] = sj * sj;
+      }
+    }
+    const uint64_t row = blk / a.bpr, cb = blk - row * a.bpr;
+    float4 *o = reinterpret_cast<float4 *>(a.out + row * a.ld + 16 * cb);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  }
+}
+
+}  // namespace
+
+nvfp4_status launch_state_encode_second(const QuantProblem &p, uint16_t *means, hipStream_t s) {
+  if (p.rows == 0 || p.cols == 0) {
+    hipLaunchKernelGGL(store_zero_scale, dim3(1), dim3(1), 0, s, p.tensor_scale);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+  }
+  RowArgs a{};
+  a.x = p.x;
+  a.nblocks = (uint64_t)(p.rows * p.cols / 16);
+  a.bpr = (uint64_t)(p.cols / 16);
+  a.rows = p.rows;
+  a.ld = p.ld;
+  a.bstride = p.rows * p.ld;
+  a.codes = p.codes;
+  a.scales = p.scales;
+  a.tensor_scale = p.tensor_scale;
+  a.ctrl = p.ctrl;
+  a.rht_seed = p.rht_seed;
+  a.means = means;
+  const int g = grid_for((a.nblocks + 63) / 64, (kThreads / 64) * kBatch, 256ull * 4);
+  if (p.ld == p.cols) {
+    hipLaunchKernelGGL((row_amax_kernel<false, true, true, true>), dim3(g), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((row_encode_kernel<false, true, false, true, true>), dim3(g), dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((row_amax_kernel<false, true, false, true>), dim3(g), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((row_encode_kernel<false, true, false, false, true>), dim3(g), dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
+
+nvfp4_status launch_state_decode(const uint8_t *codes, const uint8_t *scales, const float *tensor_scale,
+                                 const uint16_t *means, float *out, int64_t rows, int64_t cols, int64_t ld,
+                                 uint64_t rht_seed, hipStream_t s) {
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  StateDecodeArgs a{codes, scales, tensor_scale, means, out, (uint64_t)(rows * cols / 16), (uint64_t)(cols / 16), ld,
+                    rht_seed};
+  const int g = grid_for(a.nblocks, kThreads, 256ull * 16);
+  if (means) hipLaunchKernelGGL((state_decode_kernel<true>), dim3(g), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((state_decode_kernel<false>), dim3(g), dim3(kThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 
 namespace {

@@ -337,6 +337,40 @@ nvfp4_status nvfp4_attention_ds_grads(const void *ds, int32_t ds_dtype, const nv
                                       const nvfp4_attn_cfg *cfg, void *workspace, size_t workspace_bytes,
                                       void *stream);
 
+/* Optimizer state of AdamW stored in NVFP4 ([P3] section 2.2, Q-AdamW): the
+ * first moment m is passed through the 16-point random Hadamard transform
+ * and quantized with stochastic rounding; the second moment v (v >= 0) goes
+ * through a square root, a block mean taken out and kept in BF16 (the "tile"
+ * is the 16-element NVFP4 block: mu = BF16_RNE(fl(sum_j sqrt(v_j)) / 16),
+ * summed left to right), and the transform of the residual sqrt(v_j) - mu,
+ * quantized with round-to-nearest-even.  Reconstruction inverts each step in
+ * FP32: x = fl(E2M1 * E4M3 * s_t), the inverse transform (1/4) D H, then for
+ * the second moment fl(fl(x + mu)^2).  Both views are [1][rows][cols] along
+ * cols; one tensor scale each; the same rht_seed for encode and decode. */
+typedef struct nvfp4_qadamw_state {
+  nvfp4_qtensor m;    /* first moment, transformed, stochastic rounding */
+  nvfp4_qtensor v;    /* residual of sqrt(second moment) after its block means, transformed, RNE */
+  uint16_t *v_means;  /* device, rows*cols/16 BF16 block means of sqrt(v), 2-byte aligned */
+} nvfp4_qadamw_state;
+
+/* Bytes of workspace nvfp4_qadamw_encode needs (two quantize control blocks). */
+size_t nvfp4_qadamw_workspace_size(void);
+
+/* Encode FP32 moments m, v ([rows][cols], row stride ld floats, 16-byte
+ * aligned rows, cols % 16 == 0) into `state` (device arrays owned by the
+ * caller).  Stochastic rounding of m uses sr_seed and stream sr_stream as in
+ * nvfp4_quant_opts.  Workspace as for nvfp4_quantize (8 KiB, zeroed before
+ * first use, reusable). */
+nvfp4_status nvfp4_qadamw_encode(const float *m, const float *v, int64_t rows, int64_t cols, int64_t ld,
+                                 uint64_t rht_seed, uint64_t sr_seed, uint32_t sr_stream,
+                                 const nvfp4_qadamw_state *state, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* Reconstruct FP32 moments m, v ([rows][cols] with row stride ld, 16-byte
+ * aligned rows) from `state`. */
+nvfp4_status nvfp4_qadamw_decode(const nvfp4_qadamw_state *state, uint64_t rht_seed, float *m, float *v, int64_t ld,
+                                 void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -219,3 +219,42 @@ def test_attention_ds_argument_errors_and_workspace_size():
     assert call(dq=FAKE + 8) == nv.EALIGN
     assert call(wsb=need - 1) == nv.EWORKSPACE
     assert call(ws=FAKE + 64) == nv.EALIGN
+
+
+def test_qadamw_argument_errors_and_workspace_size():
+    assert nv.nvfp4_qadamw_workspace_size() == 8192
+    rows, cols = 8, 64
+
+    def state(r=rows, c=cols, means=FAKE, mq=None, vq=None):
+        return nv.QAdamWStateC(mq or _q(1, r, c), vq or _q(1, r, c), means)
+
+    L = nv.lib()
+
+    def enc(m=FAKE, v=FAKE, r=rows, c=cols, ld=cols, st=None, ws=FAKE, wsb=8192):
+        s = state() if st is None else st
+        return L.nvfp4_qadamw_encode(m, v, r, c, ld, 1, 2, 0, ctypes.byref(s), ws, wsb, None)
+
+    assert enc(m=0) == nv.EINVAL
+    assert enc(c=40, ld=40, st=state(c=40)) == nv.ESHAPE
+    assert enc(ld=cols - 4) == nv.ESHAPE
+    assert enc(ld=cols + 2) == nv.EALIGN              # rows of 16-byte multiples
+    assert enc(v=FAKE + 4) == nv.EALIGN
+    assert enc(st=state(means=0)) == nv.EINVAL
+    assert enc(st=state(means=FAKE + 1)) == nv.EALIGN
+    assert enc(st=state(vq=_q(1, rows, 2 * cols))) == nv.EINVAL
+    assert enc(st=state(mq=_q(2, rows, cols))) == nv.EINVAL
+    assert enc(wsb=8191) == nv.EWORKSPACE
+    assert enc(ws=FAKE + 128) == nv.EALIGN
+    assert L.nvfp4_qadamw_encode(FAKE, FAKE, rows, cols, cols, 1, 2, 0, None, FAKE, 8192, None) == nv.EINVAL
+
+    def dec(st=None, m=FAKE, v=FAKE, ld=cols):
+        s = state() if st is None else st
+        return L.nvfp4_qadamw_decode(ctypes.byref(s), 1, m, v, ld, None)
+
+    assert dec(m=0) == nv.EINVAL
+    assert dec(ld=cols - 16) == nv.ESHAPE
+    assert dec(ld=cols + 1) == nv.EALIGN
+    assert dec(v=FAKE + 8) == nv.EALIGN
+    assert dec(st=state(c=24)) == nv.ESHAPE
+    assert dec(st=state(vq=_q(1, rows + 1, cols))) == nv.EINVAL
+    assert L.nvfp4_qadamw_decode(None, 1, FAKE, FAKE, cols, None) == nv.EINVAL
