@@ -554,3 +554,71 @@ int oracle_qadamw_decode(const uint8_t *m_codes, const uint8_t *m_scales, float 
     }
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* R1..R3: the pieces of Newton-Schulz in NVFP4 ("Full-Stack FP4 ...",       */
+/* section 2.3, Q-Root) that are not a quantize or a GEMM.  Readings: the   */
+/* p99 clip is the nearest-rank order statistic of |x| (the ceil(q N)-th    */
+/* smallest), the tensor is clamped to [-p, p] before it is quantized, and  */
+/* the iteration starts from G / (||G||_F + 1e-7).                          */
+/* ------------------------------------------------------------------------ */
+
+/* |x| as its bit pattern: for x >= 0 the patterns order like the values, and
+ * NaN patterns sort above +inf. */
+static uint32_t abs_key(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  return u & 0x7FFFFFFFu;
+}
+
+static int cmp_u32(const void *a, const void *b) {
+  uint32_t x = *(const uint32_t *)a, y = *(const uint32_t *)b;
+  return (x > y) - (x < y);
+}
+
+/* R1: the ceil(q n)-th smallest |x| (1-based, clamped to [1, n]) over x[0..n).
+ * Returns 0, or -1 on a bad argument, -2 when out of memory. */
+int oracle_abs_quantile(const float *x, int64_t n, double q, float *out) {
+  if (n <= 0 || !(q > 0.0 && q <= 1.0))
+    return -1;
+  uint32_t *k = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)n);
+  if (!k)
+    return -2;
+  for (int64_t i = 0; i < n; ++i)
+    k[i] = abs_key(x[i]);
+  qsort(k, (size_t)n, sizeof(uint32_t), cmp_u32);
+  double r = ceil(q * (double)n);
+  if (r < 1.0)
+    r = 1.0;
+  if (r > (double)n)
+    r = (double)n;
+  uint32_t v = k[(int64_t)r - 1];
+  free(k);
+  memcpy(out, &v, 4);
+  return 0;
+}
+
+/* R2: out = x clamped to [-p, p] (NaN stays NaN). */
+void oracle_clip(const float *x, int64_t n, float p, float *out) {
+  for (int64_t i = 0; i < n; ++i) {
+    float v = x[i];
+    out[i] = (v > p) ? p : ((v < -p) ? -p : v);
+  }
+}
+
+/* R3: the normalization factor fl32(1 / (||g||_F + 1e-7)), the sum of
+ * squares taken in double, and x = fl(g * factor) ([rows][cols], g with row
+ * stride ld, x contiguous). */
+float oracle_frobenius_normalize(const void *g, int dtype, int64_t rows, int64_t cols, int64_t ld, float *x) {
+  double s = 0.0;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      float v = load_logical(g, dtype, ORACLE_ALONG_COLS, ld, 0, 0, r, c);
+      s += (double)v * (double)v;
+    }
+  float inv = (float)(1.0 / (sqrt(s) + 1e-7));
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c)
+      x[r * cols + c] = load_logical(g, dtype, ORACLE_ALONG_COLS, ld, 0, 0, r, c) * inv;
+  return inv;
+}

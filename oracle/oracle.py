@@ -78,6 +78,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_qadamw_decode.argtypes = [vp, vp, ctypes.c_float, vp, vp, ctypes.c_float, vp, i64, i64, i64,
                                            u64, vp, vp]
         L.oracle_qadamw_decode.restype = ctypes.c_int
+        L.oracle_abs_quantile.argtypes = [vp, i64, ctypes.c_double, vp]
+        L.oracle_abs_quantile.restype = ctypes.c_int
+        L.oracle_clip.argtypes = [vp, i64, ctypes.c_float, vp]
+        L.oracle_frobenius_normalize.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp]
+        L.oracle_frobenius_normalize.restype = ctypes.c_float
         _lib = L
     return _lib
 
@@ -342,3 +347,79 @@ def qadamw_decode(st: QAdamWState, rht_seed: int):
     if rc != 0:
         raise ValueError(f"oracle_qadamw_decode failed (rc={rc})")
     return m, v
+
+
+# --- R1..R3 and the Newton-Schulz step in NVFP4 ----------------------------
+
+def abs_quantile(x: np.ndarray, q: float) -> np.float32:
+    """R1: the ceil(q N)-th smallest |x|."""
+    a = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    out = np.zeros(1, np.float32)
+    rc = lib().oracle_abs_quantile(_ptr(a), a.size, float(q), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_abs_quantile failed (rc={rc})")
+    return out[0]
+
+
+def clip(x: np.ndarray, p) -> np.ndarray:
+    """R2: x clamped to [-p, p]."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty_like(a)
+    lib().oracle_clip(_ptr(a), a.size, float(np.float32(p)), _ptr(out))
+    return out
+
+
+def frobenius_normalize(g: np.ndarray, dtype: int):
+    """R3: (x = fl(g * f), f = fl32(1 / (||g||_F + 1e-7)))."""
+    a = np.ascontiguousarray(g)
+    rows, cols = a.shape
+    x = np.empty((rows, cols), np.float32)
+    f = lib().oracle_frobenius_normalize(_ptr(a), dtype, rows, cols, cols, _ptr(x))
+    return x, np.float32(f)
+
+
+def gemm_axpby_ref(a: QTensor, b: QTensor, alpha: float, c_in: np.ndarray, beta: float, rows=None):
+    """y_ref = alpha sA sB A^ B^^T + beta C (float64) and its bound
+    sum |alpha sA sB a b| + |beta C| for the selected rows (batch 0)."""
+    y, sabs = gemm_ref(a, b, alpha, 0, rows)
+    c = np.asarray(c_in, dtype=np.float64)
+    if rows is not None:
+        c = c[np.asarray(rows)]
+    bc = float(np.float32(beta)) * c
+    return y + bc, sabs + np.abs(bc)
+
+
+def ns_quantize(t: np.ndarray, q: float | None, axis: int = ALONG_COLS):
+    """The NVFP4 view of a Newton-Schulz operand: clipped at its q order
+    statistic of |t| (q None: no clipping), RNE, no transform."""
+    t = np.ascontiguousarray(t, dtype=np.float32)
+    p = None
+    if q is not None:
+        p = abs_quantile(t, q)
+        t = clip(t, p)
+    return quantize(t, F32, axis=axis), p
+
+
+def ns_chain(g: np.ndarray, dtype: int, coeffs, q: float | None, mask: int, quant: bool = True):
+    """The whole iteration on the host: X_0 = R3(g); per step (a, b, c):
+    A = X^ X^^T, B = c A^ A^^T + b A, X <- B^ X^T^ + a X, with the NVFP4
+    views (clipped where `mask` says) when `quant`, or the FP64 values
+    themselves otherwise; A, B and X are rounded to FP32 between steps as the
+    products store them.  Returns X as float32."""
+    x, _ = frobenius_normalize(g, dtype)
+    for a_, b_, c_ in coeffs:
+        a_, b_, c_ = float(np.float32(a_)), float(np.float32(b_)), float(np.float32(c_))
+        if quant:
+            qx, _ = ns_quantize(x, q if mask & 1 else None)
+            qxt, _ = ns_quantize(x.T, q if mask & 1 else None)
+            A = gemm_ref(qx, qx)[0].astype(np.float32)
+            qa, _ = ns_quantize(A, q if mask & 2 else None)
+            B = (c_ * gemm_ref(qa, qa)[0] + b_ * A.astype(np.float64)).astype(np.float32)
+            qb, _ = ns_quantize(B, q if mask & 4 else None)
+            x = (gemm_ref(qb, qxt)[0] + a_ * x.astype(np.float64)).astype(np.float32)
+        else:
+            xd = x.astype(np.float64)
+            A = (xd @ xd.T).astype(np.float32).astype(np.float64)
+            B = (c_ * (A @ A.T) + b_ * A).astype(np.float32).astype(np.float64)
+            x = (B @ xd + a_ * xd).astype(np.float32)
+    return x
