@@ -16,6 +16,7 @@ import ctypes
 import os
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +60,15 @@ class AttnCfgC(ctypes.Structure):
 
 class QAdamWStateC(ctypes.Structure):
     _fields_ = [("m", QTensorC), ("v", QTensorC), ("v_means", ctypes.c_void_p)]
+
+
+class NsCfgC(ctypes.Structure):
+    _fields_ = [("clip_quantile", ctypes.c_double), ("clip_mask", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+class NsStateC(ctypes.Structure):
+    _fields_ = [("x_prev", ctypes.c_void_p), ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                ("clip", ctypes.c_void_p * 3), ("inv_norm", ctypes.c_void_p), ("view", QTensorC * 4)]
 
 
 class LinearCfgC(ctypes.Structure):
@@ -124,6 +134,16 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_qadamw_encode.restype = i32
         L.nvfp4_qadamw_decode.argtypes = [ctypes.POINTER(QAdamWStateC), ctypes.c_uint64, vp, vp, i64, vp]
         L.nvfp4_qadamw_decode.restype = i32
+        L.nvfp4_gemm_axpby.argtypes = [ctypes.POINTER(QTensorC), ctypes.POINTER(QTensorC), vp, i32, i64, i64,
+                                       ctypes.c_float, vp, i64, i64, ctypes.c_float, vp]
+        L.nvfp4_gemm_axpby.restype = i32
+        L.nvfp4_ns_workspace_size.argtypes = [i64, i64]
+        L.nvfp4_ns_workspace_size.restype = sz
+        L.nvfp4_ns_orthogonalize.argtypes = [vp, i32, i64, i64, i64, vp, i32, ctypes.POINTER(NsCfgC), vp, i64,
+                                             vp, sz, vp]
+        L.nvfp4_ns_orthogonalize.restype = i32
+        L.nvfp4_ns_internals.argtypes = [vp, sz, i64, i64, ctypes.POINTER(NsStateC)]
+        L.nvfp4_ns_internals.restype = i32
         _lib = L
     return _lib
 
@@ -151,6 +171,10 @@ def nvfp4_quantize_group_workspace_size() -> int:
 
 def nvfp4_qadamw_workspace_size() -> int:
     return int(lib().nvfp4_qadamw_workspace_size())
+
+
+def nvfp4_ns_workspace_size(m: int, n: int) -> int:
+    return int(lib().nvfp4_ns_workspace_size(m, n))
 
 
 def nvfp4_linear_workspace_size(M: int, N: int, K: int) -> int:
@@ -661,3 +685,88 @@ def bind_linear_fwd_bwd(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, y: t
     """linear_fwd_bwd() bound to fixed inputs, outputs, workspace and the current stream."""
     args, keep = _linear_args(x, w, dy, y, dx, dw, sr_seed, rht_seed, wgrad_sr_x, workspace)
     return BoundCall(lib().nvfp4_linear_fwd_bwd, args, keep, "nvfp4_linear_fwd_bwd", (y, dx, dw))
+
+
+# --- GEMM with an FP32 addend, Newton-Schulz in NVFP4 ---------------------
+
+def gemm_axpby(a: QTensor, b: QTensor, c_in: torch.Tensor, beta: float, alpha: float = 1.0,
+               out_dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    """out = alpha sA sB A^ B^^T + beta c_in (c_in FP32 [batch][M][N] or [M][N],
+    last dimension contiguous); `out` may be c_in itself (FP32)."""
+    M, N = a.rows, b.rows
+    if c_in.dtype != torch.float32 or c_in.stride(-1) != 1:
+        raise ValueError("c_in must be float32 with a contiguous last dimension")
+    c3 = c_in.view(1, M, N) if c_in.dim() == 2 else c_in
+    if tuple(c3.shape) != (a.batch, M, N):
+        raise ValueError("c_in must be [batch][M][N]")
+    if out is None:
+        out = torch.empty((a.batch, M, N), dtype=out_dtype, device=a.codes.device)
+    o3 = out.view(1, M, N) if out.dim() == 2 else out
+    if o3.stride(-1) != 1:
+        raise ValueError("out must have a contiguous last dimension")
+    qa, qb = a.c_struct(), b.c_struct()
+    _check(lib().nvfp4_gemm_axpby(ctypes.byref(qa), ctypes.byref(qb), o3.data_ptr(),
+                                  BF16 if o3.dtype == torch.bfloat16 else F32, o3.stride(1),
+                                  o3.stride(0), alpha, c3.data_ptr(), c3.stride(1), c3.stride(0), beta,
+                                  _stream(o3.device)), "nvfp4_gemm_axpby")
+    return out
+
+
+NS_VIEWS = ("X", "X^T", "A", "B")
+
+
+def _ns_args(g, coeffs, clip_quantile, clip_mask, out, workspace):
+    if g.dim() != 2 or g.dtype not in (torch.float32, torch.bfloat16) or (g.size(1) > 1 and g.stride(1) != 1):
+        raise ValueError("g must be a 2-D float32 or bfloat16 tensor with contiguous rows")
+    m, n = g.shape
+    co = np.ascontiguousarray(np.asarray(coeffs, dtype=np.float32).reshape(-1, 3))
+    if out is None:
+        out = torch.empty(m, n, dtype=torch.float32, device=g.device)
+    if workspace is None:
+        workspace = new_workspace(nvfp4_ns_workspace_size(m, n), g.device)
+    cfg = NsCfgC(clip_quantile, clip_mask, 0)
+    args = (g.data_ptr(), BF16 if g.dtype == torch.bfloat16 else F32, m, n, g.stride(0) if m > 1 else n,
+            co.ctypes.data, co.shape[0], ctypes.byref(cfg), out.data_ptr(), out.stride(0) if m > 1 else n,
+            workspace.data_ptr(), workspace.numel(), _stream(g.device))
+    return args, (co, cfg, g, out, workspace), out
+
+
+def ns_orthogonalize(g: torch.Tensor, coeffs, clip_quantile: float = 0.99, clip_mask: int = 1,
+                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Newton-Schulz orthogonalization of g [m][n] with every product in NVFP4;
+    coeffs is a sequence of (a, b, c) per step."""
+    args, _keep, out = _ns_args(g, coeffs, clip_quantile, clip_mask, out, workspace)
+    _check(lib().nvfp4_ns_orthogonalize(*args), "nvfp4_ns_orthogonalize")
+    return out
+
+
+def bind_ns_orthogonalize(g, coeffs, out, workspace, clip_quantile: float = 0.99, clip_mask: int = 1) -> BoundCall:
+    args, keep, out = _ns_args(g, coeffs, clip_quantile, clip_mask, out, workspace)
+    return BoundCall(lib().nvfp4_ns_orthogonalize, args, keep, "nvfp4_ns_orthogonalize", out)
+
+
+def ns_internals(workspace: torch.Tensor, m: int, n: int) -> dict:
+    """The last step's intermediates in a Newton-Schulz workspace, as tensors
+    aliasing it: x_prev [m][n], a, b [m][m] (FP32), clip [3] values (float32
+    scalars), inv_norm, and the views X, X^T, A, B (QTensor)."""
+    st = NsStateC()
+    _check(lib().nvfp4_ns_internals(workspace.data_ptr(), workspace.numel(), m, n, ctypes.byref(st)),
+           "nvfp4_ns_internals")
+    base = workspace.data_ptr()
+
+    def sub(ptr, nbytes):
+        off = ptr - base
+        return workspace[off:off + nbytes]
+
+    views = {}
+    for i, name in enumerate(NS_VIEWS):
+        q = st.view[i]
+        views[name] = QTensor(sub(q.codes, q.rows * q.cols // 2).view(1, q.rows, q.cols // 2),
+                              sub(q.scales, q.rows * q.cols // 16).view(1, q.rows, q.cols // 16),
+                              sub(q.tensor_scale, 4).view(torch.float32), 1, q.rows, q.cols)
+    return {"x_prev": sub(st.x_prev, 4 * m * n).view(torch.float32).view(m, n),
+            "a": sub(st.a, 4 * m * m).view(torch.float32).view(m, m),
+            "b": sub(st.b, 4 * m * m).view(torch.float32).view(m, m),
+            "clip": [sub(st.clip[i], 4).view(torch.float32) for i in range(3)],
+            "inv_norm": sub(st.inv_norm, 4).view(torch.float32),
+            "views": views}

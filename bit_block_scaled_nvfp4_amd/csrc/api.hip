@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdint>
 
 #include "../../include/nvfp4.h"
@@ -413,6 +414,30 @@ NVFP4_EXPORT nvfp4_status nvfp4_gemm_ex(const nvfp4_qtensor *a, const nvfp4_qten
                             static_cast<hipStream_t>(stream));
 }
 
+NVFP4_EXPORT nvfp4_status nvfp4_gemm_axpby(const nvfp4_qtensor *a, const nvfp4_qtensor *b, void *c, int32_t c_dtype,
+                                           int64_t ldc, int64_t batch_stride_c, float alpha, const float *c_in,
+                                           int64_t ldc_in, int64_t batch_stride_c_in, float beta, void *stream) {
+  nvfp4_status st = validate_gemm(a, b, c, c_dtype, ldc, batch_stride_c);
+  if (st != NVFP4_OK) return st;
+  const int64_t M = a->rows, N = b->rows;
+  if (a->batch * M * N > 0) {
+    if (!c_in) return NVFP4_EINVAL;
+    if (ldc_in < N) return NVFP4_ESHAPE;
+    if (a->batch > 1 && batch_stride_c_in < M * ldc_in) return NVFP4_ESHAPE;
+    if (!aligned(c_in, 4)) return NVFP4_EALIGN;
+    // In place is allowed only as the very same array.
+    if (static_cast<const void *>(c_in) == c && (c_dtype != NVFP4_F32 || ldc_in != ldc ||
+                                                 (a->batch > 1 && batch_stride_c_in != batch_stride_c)))
+      return NVFP4_EINVAL;
+  }
+  nvfp4::GemmProblem p = make_gemm(a, b, c, c_dtype, ldc, batch_stride_c, alpha);
+  p.cin = c_in;
+  p.ldcin = ldc_in;
+  p.bstride_cin = batch_stride_c_in;
+  p.beta = beta;
+  return nvfp4::launch_gemm(p, static_cast<hipStream_t>(stream));
+}
+
 NVFP4_EXPORT nvfp4_status nvfp4_quantize_workspace_check(const void *workspace, size_t workspace_bytes,
                                                          void *stream) {
   if (!workspace || workspace_bytes < sizeof(QuantCtrl)) return NVFP4_EWORKSPACE;
@@ -553,6 +578,197 @@ NVFP4_EXPORT nvfp4_status nvfp4_linear_fwd_bwd(const void *x, const void *w, con
     const nvfp4_status st =
         nvfp4::launch_gemm(make_gemm(&v[gs[gi].a], &v[gs[gi].b], gs[gi].c, gs[gi].dtype, gs[gi].ldc, 0, 1.0f), s);
     if (st != NVFP4_OK) return st;
+  }
+  return NVFP4_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Newton-Schulz orthogonalization with every matrix product in NVFP4
+// ("Full-Stack FP4 ...", section 2.3, Q-Root).
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// Workspace: three quantize control blocks, three select states (X, A, B)
+// and their shared histogram, the normalization partials, the second iterate
+// buffer, A and B in FP32, and the four quantized views; 256-byte regions.
+struct NsLayout {
+  size_t ctrl[3], sel[3], hist, partial, inv, xbuf, a, b;
+  size_t codes[4], scales[4], st[4];
+  int64_t rows[4], cols[4];
+  size_t total;
+};
+
+NsLayout ns_layout(int64_t m, int64_t n) {
+  NsLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  for (int i = 0; i < 3; ++i) L.ctrl[i] = take(sizeof(QuantCtrl));
+  for (int i = 0; i < 3; ++i) L.sel[i] = take(sizeof(nvfp4::SelectState));
+  L.hist = take(2048 * sizeof(uint32_t));
+  L.partial = take(1024 * sizeof(double));
+  L.inv = take(sizeof(float));
+  L.xbuf = take((size_t)m * (size_t)n * 4);
+  L.a = take((size_t)m * (size_t)m * 4);
+  L.b = take((size_t)m * (size_t)m * 4);
+  const int64_t shapes[4][2] = {{m, n}, {n, m}, {m, m}, {m, m}};
+  for (int i = 0; i < 4; ++i) {
+    L.rows[i] = shapes[i][0];
+    L.cols[i] = shapes[i][1];
+    const size_t e = (size_t)shapes[i][0] * (size_t)shapes[i][1];
+    L.codes[i] = take(e / 2);
+    L.scales[i] = take(e / 16);
+    L.st[i] = take(sizeof(float));
+  }
+  L.total = off;
+  return L;
+}
+
+nvfp4_qtensor ns_view(uint8_t *base, const NsLayout &L, int i) {
+  nvfp4_qtensor q{};
+  q.codes = base + L.codes[i];
+  q.scales = base + L.scales[i];
+  q.tensor_scale = reinterpret_cast<float *>(base + L.st[i]);
+  q.batch = 1;
+  q.rows = L.rows[i];
+  q.cols = L.cols[i];
+  return q;
+}
+
+bool ns_shape_ok(int64_t m, int64_t n) {
+  return m > 0 && n > 0 && m % 16 == 0 && n % 16 == 0 && m <= (int64_t(1) << 20) && n <= (int64_t(1) << 20) &&
+         (double)m * (double)n < 4.0e9;
+}
+
+// 0-based rank of the q-quantile of N values: the ceil(q N)-th smallest.
+uint64_t quantile_rank(double q, uint64_t n) {
+  double k = std::ceil(q * (double)n);
+  if (k < 1.0) k = 1.0;
+  if (k > (double)n) k = (double)n;
+  return (uint64_t)k - 1;
+}
+
+}  // namespace
+
+NVFP4_EXPORT size_t nvfp4_ns_workspace_size(int64_t m, int64_t n) {
+  if (!ns_shape_ok(m, n)) return 0;
+  return ns_layout(m, n).total;
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_ns_internals(void *workspace, size_t workspace_bytes, int64_t m, int64_t n,
+                                             nvfp4_ns_state *out) {
+  if (!workspace || !out) return NVFP4_EINVAL;
+  if (!ns_shape_ok(m, n)) return NVFP4_ESHAPE;
+  const NsLayout L = ns_layout(m, n);
+  if (workspace_bytes < L.total) return NVFP4_EWORKSPACE;
+  uint8_t *base = static_cast<uint8_t *>(workspace);
+  out->x_prev = reinterpret_cast<float *>(base + L.xbuf);
+  out->a = reinterpret_cast<float *>(base + L.a);
+  out->b = reinterpret_cast<float *>(base + L.b);
+  for (int i = 0; i < 3; ++i)
+    out->clip[i] = &reinterpret_cast<nvfp4::SelectState *>(base + L.sel[i])->value;
+  out->inv_norm = reinterpret_cast<float *>(base + L.inv);
+  for (int i = 0; i < 4; ++i) out->view[i] = ns_view(base, L, i);
+  return NVFP4_OK;
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_ns_orthogonalize(const void *g, int32_t g_dtype, int64_t m, int64_t n, int64_t ldg,
+                                                 const float *coeffs, int32_t steps, const nvfp4_ns_cfg *cfg,
+                                                 float *x, int64_t ldx, void *workspace, size_t workspace_bytes,
+                                                 void *stream) {
+  if (!g || !x || !cfg || (steps > 0 && !coeffs)) return NVFP4_EINVAL;
+  if (g_dtype != NVFP4_F32 && g_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (steps < 0 || steps > 64) return NVFP4_EINVAL;
+  if (cfg->clip_mask > 7u || cfg->reserved != 0) return NVFP4_EINVAL;
+  if (cfg->clip_mask && !(cfg->clip_quantile > 0.0 && cfg->clip_quantile <= 1.0)) return NVFP4_EINVAL;
+  if (!ns_shape_ok(m, n)) return NVFP4_ESHAPE;
+  if (ldg < n || ldx < n) return NVFP4_ESHAPE;
+  const size_t gsz = g_dtype == NVFP4_F32 ? 4 : 2;
+  if (!aligned(g, 4 * gsz) || ldg % 4 || !aligned(x, 16) || ldx % 4) return NVFP4_EALIGN;
+  const NsLayout L = ns_layout(m, n);
+  if (!workspace || workspace_bytes < L.total) return NVFP4_EWORKSPACE;
+  if (!aligned(workspace, 256)) return NVFP4_EALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t *base = static_cast<uint8_t *>(workspace);
+  float *xbuf = reinterpret_cast<float *>(base + L.xbuf);
+  float *A = reinterpret_cast<float *>(base + L.a);
+  float *B = reinterpret_cast<float *>(base + L.b);
+  auto sel = [&](int i) { return reinterpret_cast<nvfp4::SelectState *>(base + L.sel[i]); };
+  uint32_t *hist = reinterpret_cast<uint32_t *>(base + L.hist);
+  const nvfp4_qtensor vX = ns_view(base, L, 0), vXT = ns_view(base, L, 1), vA = ns_view(base, L, 2),
+                      vB = ns_view(base, L, 3);
+  // The iterates alternate so that the last one lands in x.
+  float *P[2];
+  int64_t ldp[2];
+  P[steps % 2] = x;
+  ldp[steps % 2] = ldx;
+  P[(steps + 1) % 2] = xbuf;
+  ldp[(steps + 1) % 2] = n;
+  nvfp4_status r = nvfp4::launch_frobenius_normalize(g, g_dtype == NVFP4_BF16, m, n, ldg,
+                                                     reinterpret_cast<double *>(base + L.partial),
+                                                     reinterpret_cast<float *>(base + L.inv), P[0], ldp[0], s);
+  if (r != NVFP4_OK) return r;
+  const nvfp4_quant_opts rne{NVFP4_RNE, 0, 0, 0, 0u, 0u};
+  for (int k = 0; k < steps; ++k) {
+    float *Xc = P[k % 2], *Xn = P[(k + 1) % 2];
+    const int64_t ldc_ = ldp[k % 2], ldn = ldp[(k + 1) % 2];
+    const float ca = coeffs[3 * k], cb = coeffs[3 * k + 1], cc = coeffs[3 * k + 2];
+    // X: clip value, then both orientations from one read.
+    const float *clip_x = nullptr;
+    if (cfg->clip_mask & 1u) {
+      r = nvfp4::launch_abs_select(Xc, m, n, ldc_, quantile_rank(cfg->clip_quantile, (uint64_t)(m * n)), sel(0),
+                                   hist, s);
+      if (r != NVFP4_OK) return r;
+      clip_x = &sel(0)->value;
+    }
+    nvfp4::QuantProblem qx = make_quant(Xc, false, 1, m, n, ldc_, m * ldc_, false, &rne, &vX, base + L.ctrl[0]);
+    qx.clip = clip_x;
+    nvfp4::QuantProblem qxt = make_quant(Xc, false, 1, m, n, ldc_, m * ldc_, true, &rne, &vXT, base + L.ctrl[0]);
+    r = nvfp4::launch_quantize_dual(qx, qxt, s);
+    if (r != NVFP4_OK) return r;
+    // A = X X^T
+    r = nvfp4::launch_gemm(make_gemm(&vX, &vX, A, NVFP4_F32, m, m * m, 1.0f), s);
+    if (r != NVFP4_OK) return r;
+    const float *clip_a = nullptr;
+    if (cfg->clip_mask & 2u) {
+      r = nvfp4::launch_abs_select(A, m, m, m, quantile_rank(cfg->clip_quantile, (uint64_t)(m * m)), sel(1), hist, s);
+      if (r != NVFP4_OK) return r;
+      clip_a = &sel(1)->value;
+    }
+    nvfp4::QuantProblem qa = make_quant(A, false, 1, m, m, m, m * m, false, &rne, &vA, base + L.ctrl[1]);
+    qa.clip = clip_a;
+    r = nvfp4::launch_quantize(qa, s);
+    if (r != NVFP4_OK) return r;
+    // B = c A A^T + b A  (A is symmetric)
+    nvfp4::GemmProblem pb = make_gemm(&vA, &vA, B, NVFP4_F32, m, m * m, cc);
+    pb.cin = A;
+    pb.ldcin = m;
+    pb.bstride_cin = m * m;
+    pb.beta = cb;
+    r = nvfp4::launch_gemm(pb, s);
+    if (r != NVFP4_OK) return r;
+    const float *clip_b = nullptr;
+    if (cfg->clip_mask & 4u) {
+      r = nvfp4::launch_abs_select(B, m, m, m, quantile_rank(cfg->clip_quantile, (uint64_t)(m * m)), sel(2), hist, s);
+      if (r != NVFP4_OK) return r;
+      clip_b = &sel(2)->value;
+    }
+    nvfp4::QuantProblem qb = make_quant(B, false, 1, m, m, m, m * m, false, &rne, &vB, base + L.ctrl[2]);
+    qb.clip = clip_b;
+    r = nvfp4::launch_quantize(qb, s);
+    if (r != NVFP4_OK) return r;
+    // X' = B X + a X
+    nvfp4::GemmProblem px = make_gemm(&vB, &vXT, Xn, NVFP4_F32, ldn, m * ldn, 1.0f);
+    px.cin = Xc;
+    px.ldcin = ldc_;
+    px.bstride_cin = m * ldc_;
+    px.beta = ca;
+    r = nvfp4::launch_gemm(px, s);
+    if (r != NVFP4_OK) return r;
   }
   return NVFP4_OK;
 }

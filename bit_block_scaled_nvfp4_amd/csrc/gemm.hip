@@ -89,6 +89,9 @@ struct GemmArgs {
   void *c;
   int64_t ldc, bstride_c;
   float alpha;
+  const float *cin;  // optional FP32 addend [batch][M][N] (row stride ldcin), times beta
+  int64_t ldcin, bstride_cin;
+  float beta;
 };
 
 // LDS stage: codes [rows][64 B] and scales [rows][8 B] per operand.
@@ -436,6 +439,48 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[kFragM][kFragN]
   const int64_t row0 = wrow0 + 4 * h;
   const int64_t col0 = wcol0 + r32;
   const bool full = wrow0 + 128 <= g.M && wcol0 + 32 * kFragN <= g.N;
+  if (g.cin) {
+    // y = fl(fl(acc * s) + fl(beta * c)): each element is read and written
+    // by the same lane, so c may be the output itself.  The addends of one
+    // accumulator row pair of one fragment row are loaded before any is used
+    // (addresses clamped into the tensor, so the loads need no predicate and
+    // issue back to back).
+    const float *ci_ptr = g.cin + batch * g.bstride_cin;
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      const int64_t rv = row0 + 8 * (v >> 2) + (v & 3);
+#pragma unroll
+      for (int i = 0; i < kFragM; ++i) {
+        const int64_t r = rv + 32 * i;
+        const int64_t r0 = min(r, g.M - 1), r1 = min(r + 1, g.M - 1);
+        float cv[kFragN][2];
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j) {
+          const int64_t col = min(col0 + 32 * j, g.N - 1);
+          cv[j][0] = ci_ptr[r0 * g.ldcin + col];
+          cv[j][1] = ci_ptr[r1 * g.ldcin + col];
+        }
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j) {
+          const int64_t col = col0 + 32 * j;
+          const bool col_ok = full || col < g.N;
+          const bool ok0 = col_ok && (full || r < g.M), ok1 = col_ok && (full || r + 1 < g.M);
+          const float y0 = acc[i][j][v] * sc + g.beta * cv[j][0];
+          const float y1 = acc[i][j][v + 1] * sc + g.beta * cv[j][1];
+          OutT *pr = cb_ptr + r * g.ldc + col;
+          if constexpr (kBF16Out) {
+            const uint32_t b2 = pack_bf16x2_rne(y0, y1);
+            if (ok0) pr[0] = (uint16_t)b2;
+            if (ok1) pr[g.ldc] = (uint16_t)(b2 >> 16);
+          } else {
+            if (ok0) pr[0] = y0;
+            if (ok1) pr[g.ldc] = y1;
+          }
+        }
+      }
+    }
+    return;
+  }
   // One accumulator row pair at a time, so no table of row offsets stays
   // live beside the accumulators.
 #pragma unroll
@@ -982,6 +1027,10 @@ nvfp4_status launch_gemm(const GemmProblem &p, hipStream_t s) {
   g.ldc = p.ldc;
   g.bstride_c = p.bstride_c;
   g.alpha = p.alpha;
+  g.cin = p.cin;
+  g.ldcin = p.ldcin;
+  g.bstride_cin = p.bstride_cin;
+  g.beta = p.beta;
   // The 8-wavefront kernel's loads use 32-bit offsets within an operand and
   // 24-bit row and row-size factors.
   const bool fast = p.K % BK == 0;

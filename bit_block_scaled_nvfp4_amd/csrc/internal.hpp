@@ -59,6 +59,7 @@ struct QuantProblem {
   uint8_t *codes, *scales;
   float *tensor_scale;
   QuantCtrl *ctrl;
+  const float *clip;  // FP32 rows or dual views only: x <- clamp(x, -*clip, *clip) first (two passes)
 };
 
 // Several tensors quantized along their contiguous dimension with the same
@@ -85,7 +86,26 @@ struct GemmProblem {
   int64_t ldc, bstride_c;
   float alpha;
   int tile_m, tile_n;  // 0, 0: automatic choice; otherwise a requested workgroup tile
+  const float *cin;    // optional FP32 addend: y = fl(acc * s) + fl(beta * cin)
+  int64_t ldcin, bstride_cin;
+  float beta;
 };
+
+// Exact order statistic of |x| (radix select): state->value = the element of
+// rank `rank` (0-based, ascending by the bit pattern of |x|) of x [rows][cols]
+// (row stride ld; cols and ld multiples of 4, x 16-byte aligned).  `hist`
+// holds 2048 counters, zero on entry and on return.
+struct SelectState {
+  uint32_t prefix;
+  float value;
+  uint64_t rank;
+};
+nvfp4_status launch_abs_select(const float *x, int64_t rows, int64_t cols, int64_t ld, uint64_t rank,
+                               SelectState *state, uint32_t *hist, hipStream_t stream);
+// x = g / (||g||_F + 1e-7), with the norm from FP64 sums over 1024 fixed
+// partials (partial: 1024 doubles) and *inv = fl32(1 / (||g|| + 1e-7)).
+nvfp4_status launch_frobenius_normalize(const void *g, bool bf16, int64_t rows, int64_t cols, int64_t ld,
+                                        double *partial, float *inv, float *x, int64_t xld, hipStream_t stream);
 
 nvfp4_status launch_quantize(const QuantProblem &p, hipStream_t stream);
 nvfp4_status launch_quantize_group(const QuantGroupProblem &p, hipStream_t stream);

@@ -285,7 +285,11 @@ struct RowArgs {
   uint64_t sr_seed, rht_seed;
   uint32_t sr_stream;
   uint16_t *means;    // second-moment pre-step only: BF16 block means, one per block
+  const float *clip;  // FP32 only: values are first clamped to [-*clip, *clip]
 };
+
+// x clamped to [-c, c]; NaN stays NaN.
+__device__ __forceinline__ float clamp_abs(float x, float c) { return x > c ? c : (x < -c ? -c : x); }
 
 // Second-moment pre-step of the quantized-state optimizer ("Full-Stack FP4
 // ...", section 2.2: square root, tile mean, then the Hadamard transform) on
@@ -604,6 +608,7 @@ __global__ __launch_bounds__(kFusedThreads, kFusedThreads / 256) void row_fused_
 template <bool kBF16, bool kRHT, bool kContig, bool kPre = false>
 __global__ __launch_bounds__(kThreads) void row_amax_kernel(RowArgs a) {
   const uint32_t mask = kRHT ? rht_sign_mask(a.rht_seed) : 0u;
+  const float clip = (!kBF16 && a.clip) ? *a.clip : 0.0f;
   const int lane = threadIdx.x & 63;
   const uint64_t nseg = (a.nblocks + 63) / 64;
   const uint64_t nwaves = (uint64_t)gridDim.x * (kThreads / 64);
@@ -622,6 +627,10 @@ __global__ __launch_bounds__(kThreads) void row_amax_kernel(RowArgs a) {
         float v[16];
         raw[i].values(v);
         if constexpr (kPre) (void)sqrt_demean16(v);
+        if (!kBF16 && a.clip) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[j] = clamp_abs(v[j], clip);
+        }
         if (kRHT) {
           rht16_unscaled(v, mask);
           bm = quarter_max_bits(max_abs16(v));
@@ -642,6 +651,7 @@ __global__ __launch_bounds__(kThreads) void row_encode_kernel(RowArgs a) {
   const float amax = __uint_as_float(load_amax(a.ctrl));
   const float st = amax / 2688.0f;
   const float d6 = 6.0f * st;
+  const float clip = (!kBF16 && a.clip) ? *a.clip : 0.0f;
   build_recip_table(recip, st);
   __syncthreads();
   const int lane = threadIdx.x & 63;
@@ -658,6 +668,10 @@ __global__ __launch_bounds__(kThreads) void row_encode_kernel(RowArgs a) {
         float v[16];
         raw[i].values(v);
         if constexpr (kPre) a.means[blk[i]] = (uint16_t)sqrt_demean16(v);
+        if (!kBF16 && a.clip) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[j] = clamp_abs(v[j], clip);
+        }
         if (kRHT) rht16(v, mask);
         row_store_block<kSR>(a, blk[i], v, block_scale_code(max_abs16(v), st, d6), recip);
       }
@@ -689,6 +703,7 @@ struct ColArgs {
   QuantCtrl *ctrl;
   uint64_t sr_seed, rht_seed;
   uint32_t sr_stream;
+  const float *clip;                 // dual encode of FP32 only: clamp to [-*clip, *clip] first
 };
 
 // 16 rows x 8 columns of raw input held as BF16 pairs (4 dwords per row) or
@@ -878,6 +893,15 @@ __global__ __launch_bounds__(kThreads) void dual_encode_kernel(DualArgs d) {
   const int cgl = threadIdx.x % kColTileCG, rbl = threadIdx.x / kColTileCG;
   ColTile<kBF16> t;
   col_load<kBF16>(a, l.b, l.ld_rb, l.ld_cg, l.full, t);
+  if constexpr (!kBF16) {
+    if (a.clip) {
+      const float c = *a.clip;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t.w[j][e] = __float_as_uint(clamp_abs(__uint_as_float(t.w[j][e]), c));
+    }
+  }
   // The transposed view, staged in LDS.
   if (l.valid) {
 #pragma unroll
@@ -1177,7 +1201,7 @@ hipError_t run_row_two_pass(const RowArgs &a, hipStream_t s) {
 
 template <bool kBF16, bool kRHT, bool kSR>
 hipError_t run_row(const RowArgs &a, bool contig, hipStream_t s) {
-  if (contig) {
+  if (contig && !a.clip) {
     hipError_t err = hipSuccess;
     if (try_row_fused<kBF16, kRHT, kSR>(fused_single(a), s, err)) return hipSuccess;
     if (err != hipSuccess) return err;  // a launch that was refused is reported, not retried
@@ -1446,8 +1470,10 @@ nvfp4_status launch_quantize_dual(const QuantProblem &row, const QuantProblem &c
     hipLaunchKernelGGL(store_zero_scale, dim3(1), dim3(1), 0, s, col.tensor_scale);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
   }
+  if (row.clip && row.bf16) return NVFP4_EUNSUPPORTED;
   RowArgs ra{};
   ra.x = row.x;
+  ra.clip = row.clip;
   ra.nblocks = (uint64_t)(row.batch * row.rows * row.cols / 16);
   ra.bpr = (uint64_t)(row.cols / 16);
   ra.rows = row.rows;
@@ -1474,6 +1500,7 @@ nvfp4_status launch_quantize_dual(const QuantProblem &row, const QuantProblem &c
   a.ctrl = row.ctrl;
   a.sr_seed = col.sr_seed;
   a.sr_stream = col.sr_stream;
+  a.clip = row.clip;
   d.rcodes = row.codes;
   d.rscales = row.scales;
   d.rtensor_scale = row.tensor_scale;
@@ -1491,9 +1518,11 @@ nvfp4_status launch_quantize(const QuantProblem &p, hipStream_t s) {
     hipLaunchKernelGGL(store_zero_scale, dim3(1), dim3(1), 0, s, p.tensor_scale);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
   }
+  if (p.clip && (p.bf16 || p.along_rows)) return NVFP4_EUNSUPPORTED;
   hipError_t err;
   if (!p.along_rows) {
     RowArgs a{};
+    a.clip = p.clip;
     a.x = p.x;
     a.nblocks = (uint64_t)(p.batch * p.rows * p.cols / 16);
     a.bpr = (uint64_t)(p.cols / 16);

@@ -26,6 +26,7 @@ trained weights are needed or used):
   log-uniform in [0.25, 4].
 * ``adamw_state``: FP32 AdamW moments m, v of a 20480x5120 weight, heavy
   tailed with a per-row gradient scale.
+* ``ns_3b``: a 3072x8192 BF16 weight gradient for Newton-Schulz in NVFP4.
 """
 from __future__ import annotations
 
@@ -180,6 +181,23 @@ def adamw_state(seed: int = 7, rows: int = 20480, cols: int = 5120):
             "sr_seed": ADAMW_SR_SEED}
 
 
+NS_COEFFS = [(1.875, -1.25, 0.375)] * 5
+
+
+def ns_3b(seed: int = 8, m: int = 3072, n: int = 8192):
+    """A weight gradient for Newton-Schulz orthogonalization in NVFP4
+    ("Full-Stack FP4 ...", section 2.3): the [3072][8192] MLP weight of the
+    3B model, G = 1e-3 N(0, 1) times a per-row scale log-uniform in [0.5, 2],
+    with 0.1% of entries times 20 as outliers, in BF16; five steps of the
+    textbook quintic (a, b, c) = (15/8, -10/8, 3/8), clipping X at p99."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((m, n), dtype=np.float32) * np.float32(1e-3)
+    g *= np.exp(rng.uniform(np.log(0.5), np.log(2.0), size=(m, 1))).astype(np.float32)
+    idx = rng.choice(m * n, int(round(0.001 * m * n)), replace=False)
+    g.reshape(-1)[idx] *= np.float32(20.0)
+    return {"G": to_bf16(g), "coeffs": NS_COEFFS, "clip_quantile": 0.99, "clip_mask": 1}
+
+
 WORKLOADS = {
     "tiny": tiny,
     "fprop_3b": fprop_3b,
@@ -188,4 +206,5 @@ WORKLOADS = {
     "attn_scores": attn_scores,
     "attn_bwd": attn_bwd,
     "adamw_state": adamw_state,
+    "ns_3b": ns_3b,
 }

@@ -263,6 +263,19 @@ nvfp4_status nvfp4_gemm_ex(const nvfp4_qtensor *a, const nvfp4_qtensor *b, void 
                            int64_t ldc, int64_t batch_stride_c, float alpha, int32_t tile_m,
                            int32_t tile_n, void *stream);
 
+/* nvfp4_gemm plus a scaled FP32 addend, the form of every Newton-Schulz
+ * product of [P3] section 2.3 (X <- a X + (b A + c A A^T) X, run in NVFP4):
+ *   C[b][i][j] = fl(fl(acc * fl(fl(sA*sB)*alpha)) + fl(beta * C_in[b][i][j]))
+ * then stored as c_dtype (BF16: rounded to nearest even).
+ *   c_in  device FP32 [batch][M][N], row stride ldc_in >= N, batch stride
+ *         batch_stride_c_in >= M*ldc_in, 4-byte aligned.  It may be the output
+ *         itself only as the very same FP32 array (same pointer, ldc and
+ *         batch stride); any other overlap is undefined.
+ * Otherwise as nvfp4_gemm. */
+nvfp4_status nvfp4_gemm_axpby(const nvfp4_qtensor *a, const nvfp4_qtensor *b, void *c, int32_t c_dtype,
+                              int64_t ldc, int64_t batch_stride_c, float alpha, const float *c_in,
+                              int64_t ldc_in, int64_t batch_stride_c_in, float beta, void *stream);
+
 /* Linear-layer training step in NVFP4: the quantized linear projections of
  * [P3] sections 1 and 2.1 (forward and backward GEMMs in NVFP4), stochastic
  * rounding and Hadamard mixing of [P3] section 2.2 on the gradient-side
@@ -370,6 +383,61 @@ nvfp4_status nvfp4_qadamw_encode(const float *m, const float *v, int64_t rows, i
  * aligned rows) from `state`. */
 nvfp4_status nvfp4_qadamw_decode(const nvfp4_qadamw_state *state, uint64_t rht_seed, float *m, float *v, int64_t ld,
                                  void *stream);
+
+/* Newton-Schulz orthogonalization with every matrix product in NVFP4, the
+ * Q-Root recipe of [P3] section 2.3 (the products run directly in NVFP4,
+ * stabilised by per-step coefficients a, b, c and clipping of p99 outliers):
+ *   X_0 = G / (||G||_F + 1e-7)   (norm in FP64, factor rounded to FP32)
+ *   for k = 0 .. steps-1, with (a, b, c) = coeffs[3k .. 3k+2]:
+ *     X^  = NVFP4 of clip(X_k) along its rows, X^T^ = NVFP4 of clip(X_k)^T
+ *     A   = X^ X^^T                          (FP32 [m][m])
+ *     B   = c * A^ A^^T + b * A             (A^ = NVFP4 of clip(A); A is symmetric)
+ *     X_{k+1} = B^ X^ + a * X_k             (B^ = NVFP4 of clip(B))
+ * every GEMM through the block-scaled kernel with the FP32 addend epilogue
+ * of nvfp4_gemm_axpby, every quantization RNE without the transform.
+ * clip(T) clamps T to [-p, p] with p the clip_quantile order statistic of
+ * |T| (the ceil(q * numel)-th smallest, exact), for the tensors selected by
+ * clip_mask (bit 0: X, bit 1: A, bit 2: B); the FP32 terms a X_k and b A use
+ * the unclipped tensors.  The page gives neither the coefficients nor the
+ * tensors clipped: both are the caller's.
+ *   g     device [m][n], dtype g_dtype, row stride ldg (multiple of 4),
+ *         16-byte aligned (8 for BF16);  m, n multiples of 16, m*n < 4e9.
+ *   coeffs  host, 3*steps floats; steps in [0, 64] (0: X = X_0).
+ *   x     device FP32 [m][n] output, row stride ldx (multiple of 4), 16-byte
+ *         aligned; it must not overlap g or the workspace.
+ * The caller passes the orientation it wants orthogonalized (A is m x m:
+ * m <= n is the cheap one).  Workspace: nvfp4_ns_workspace_size(m, n)
+ * bytes, 256-byte aligned, zeroed before first use, reusable; after a call
+ * it holds the last step's intermediates (nvfp4_ns_internals). */
+typedef struct nvfp4_ns_cfg {
+  double clip_quantile;  /* in (0, 1]; 0.99 is the page's p99 */
+  uint32_t clip_mask;    /* bit 0: X, bit 1: A, bit 2: B; 0: no clipping */
+  uint32_t reserved;     /* must be 0 */
+} nvfp4_ns_cfg;
+
+size_t nvfp4_ns_workspace_size(int64_t m, int64_t n);
+
+nvfp4_status nvfp4_ns_orthogonalize(const void *g, int32_t g_dtype, int64_t m, int64_t n, int64_t ldg,
+                                    const float *coeffs, int32_t steps, const nvfp4_ns_cfg *cfg, float *x,
+                                    int64_t ldx, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Where the last step's intermediates live in a Newton-Schulz workspace
+ * (host computation only): x_prev = X_{steps-1} ([m][n], row stride n; valid
+ * when steps >= 1), a = A and b = B ([m][m] FP32), clip[i] = the clip value
+ * of X, A, B (device floats; valid when that bit was set), inv_norm = the
+ * normalization factor, and the quantized views 0: X^ [m][n], 1: X^T^
+ * [n][m], 2: A^ [m][m], 3: B^ [m][m]. */
+typedef struct nvfp4_ns_state {
+  float *x_prev;
+  float *a;
+  float *b;
+  const float *clip[3];
+  const float *inv_norm;
+  nvfp4_qtensor view[4];
+} nvfp4_ns_state;
+
+nvfp4_status nvfp4_ns_internals(void *workspace, size_t workspace_bytes, int64_t m, int64_t n,
+                                nvfp4_ns_state *out);
 
 #ifdef __cplusplus
 }

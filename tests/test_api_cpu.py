@@ -258,3 +258,56 @@ def test_qadamw_argument_errors_and_workspace_size():
     assert dec(st=state(c=24)) == nv.ESHAPE
     assert dec(st=state(vq=_q(1, rows + 1, cols))) == nv.EINVAL
     assert L.nvfp4_qadamw_decode(None, 1, FAKE, FAKE, cols, None) == nv.EINVAL
+
+
+def test_gemm_axpby_argument_errors():
+    a, b = _q(1, 32, 64), _q(1, 48, 64)
+    L = nv.lib()
+
+    def call(cin=FAKE, ldcin=48, bs=32 * 48, c=FAKE + 0x100000, ldc=48, dt=nv.F32):
+        return L.nvfp4_gemm_axpby(ctypes.byref(a), ctypes.byref(b), c, dt, ldc, 32 * ldc, 1.0, cin, ldcin, bs,
+                                  0.5, None)
+
+    assert call(cin=0) == nv.EINVAL
+    assert call(ldcin=47) == nv.ESHAPE
+    assert call(cin=FAKE + 2) == nv.EALIGN
+    assert call(c=FAKE, ldc=64) == nv.EINVAL            # in place needs the same row stride
+    assert call(c=FAKE, dt=nv.BF16) == nv.EINVAL        # and an FP32 output
+    assert call(dt=5) == nv.EINVAL
+
+
+def test_ns_argument_errors_and_layout():
+    m, n = 32, 48
+    need = nv.nvfp4_ns_workspace_size(m, n)
+    assert need > 4 * (m * n + 2 * m * m) + 3 * 4096
+    assert nv.nvfp4_ns_workspace_size(24, 48) == 0 and nv.nvfp4_ns_workspace_size(0, 16) == 0
+    L = nv.lib()
+    co = (ctypes.c_float * 6)(1.5, -0.5, 0.0, 1.5, -0.5, 0.0)
+    cfg = nv.NsCfgC(0.99, 1, 0)
+
+    def call(g=FAKE, dt=nv.BF16, mm=m, nn=n, ldg=n, coeffs=co, steps=2, c=cfg, x=FAKE + 0x100000, ldx=n,
+             ws=FAKE + 0x200000, wsb=need):
+        return L.nvfp4_ns_orthogonalize(g, dt, mm, nn, ldg, coeffs, steps, ctypes.byref(c) if c else None, x, ldx,
+                                        ws, wsb, None)
+
+    assert call(g=0) == nv.EINVAL
+    assert call(c=None) == nv.EINVAL
+    assert call(coeffs=None) == nv.EINVAL
+    assert call(steps=-1) == nv.EINVAL
+    assert call(c=nv.NsCfgC(0.0, 1, 0)) == nv.EINVAL
+    assert call(c=nv.NsCfgC(1.5, 1, 0)) == nv.EINVAL
+    assert call(c=nv.NsCfgC(0.99, 8, 0)) == nv.EINVAL
+    assert call(c=nv.NsCfgC(0.99, 1, 1)) == nv.EINVAL
+    assert call(mm=24) == nv.ESHAPE
+    assert call(ldg=n - 4) == nv.ESHAPE
+    assert call(ldg=n + 2) == nv.EALIGN
+    assert call(x=FAKE + 8) == nv.EALIGN
+    assert call(wsb=need - 1) == nv.EWORKSPACE
+    assert call(ws=FAKE + 0x200080) == nv.EALIGN
+    st = nv.NsStateC()
+    assert L.nvfp4_ns_internals(FAKE, need, m, n, ctypes.byref(st)) == nv.OK
+    assert st.view[0].rows == m and st.view[0].cols == n and st.view[1].rows == n and st.view[1].cols == m
+    assert st.view[2].rows == st.view[2].cols == m
+    regions = [st.x_prev, st.a, st.b, st.inv_norm] + list(st.clip) + [v.codes for v in st.view]
+    assert all(FAKE <= r < FAKE + need for r in regions) and len(set(regions)) == len(regions)
+    assert L.nvfp4_ns_internals(FAKE, need - 1, m, n, ctypes.byref(st)) == nv.EWORKSPACE
