@@ -27,6 +27,7 @@ trained weights are needed or used):
 * ``adamw_state``: FP32 AdamW moments m, v of a 20480x5120 weight, heavy
   tailed with a per-row gradient scale.
 * ``ns_3b``: a 3072x8192 BF16 weight gradient for Newton-Schulz in NVFP4.
+* ``lora_3b``: the fprop_3b layer split as W_res + beta L2 L1, rank 64.
 """
 from __future__ import annotations
 
@@ -198,6 +199,20 @@ def ns_3b(seed: int = 8, m: int = 3072, n: int = 8192):
     return {"G": to_bf16(g), "coeffs": NS_COEFFS, "clip_quantile": 0.99, "clip_mask": 1}
 
 
+def lora_3b(seed: int = 10, m: int = 8192, k: int = 3072, n: int = 3072, r: int = 64):
+    """The fprop_3b layer as W = W_res + beta L2 L1 ("Full-Stack FP4 ...",
+    section 2.1): X as in fprop_3b (1% of columns x20), W_res std 0.02, L1
+    [r][K] N(0, 1/K), L2 [N][r] N(0, 0.05^2), beta 0.5, rank 64, all BF16."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((m, k), dtype=np.float32)
+    idx = rng.choice(k, int(round(0.01 * k)), replace=False)
+    x[:, idx] *= np.float32(20.0)
+    w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    l1 = rng.standard_normal((r, k), dtype=np.float32) * np.float32(1.0 / np.sqrt(k))
+    l2 = rng.standard_normal((n, r), dtype=np.float32) * np.float32(0.05)
+    return {"X": to_bf16(x), "W_res": to_bf16(w), "L1": to_bf16(l1), "L2": to_bf16(l2), "beta": 0.5}
+
+
 WORKLOADS = {
     "tiny": tiny,
     "fprop_3b": fprop_3b,
@@ -207,4 +222,5 @@ WORKLOADS = {
     "attn_bwd": attn_bwd,
     "adamw_state": adamw_state,
     "ns_3b": ns_3b,
+    "lora_3b": lora_3b,
 }

@@ -423,3 +423,29 @@ def ns_chain(g: np.ndarray, dtype: int, coeffs, q: float | None, mask: int, quan
             B = (c_ * (A @ A.T) + b_ * A).astype(np.float32).astype(np.float64)
             x = (B @ xd + a_ * xd).astype(np.float32)
     return x
+
+
+# --- L1, L2: the LoRA-style forward (residual NVFP4, subspace BF16) -------
+
+def bf16_values(bits: np.ndarray) -> np.ndarray:
+    """BF16 bit patterns (uint16) -> float64 values (exact)."""
+    with np.errstate(invalid="ignore"):  # NaN patterns stay NaN
+        return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def lora_down_ref(x_bits: np.ndarray, l1_bits: np.ndarray, rows=None):
+    """L1: T = X L1^T in float64 (before its BF16 rounding) and sum |X| |L1|^T
+    for the selected rows; X [M][K], L1 [r][K] as BF16 bit patterns."""
+    x = bf16_values(x_bits if rows is None else np.asarray(x_bits)[np.asarray(rows)])
+    l1 = bf16_values(l1_bits)
+    return x @ l1.T, np.abs(x) @ np.abs(l1).T
+
+
+def lora_forward_ref(qx: QTensor, qw: QTensor, t_bits: np.ndarray, l2_bits: np.ndarray, beta: float, rows=None):
+    """L2: y = sX sW X^ W^^T + beta T L2^T in float64 for the selected rows,
+    with T the BF16 T (bit patterns [M][r]) and its bound."""
+    y, s = gemm_ref(qx, qw, 1.0, 0, rows)
+    t = bf16_values(t_bits if rows is None else np.asarray(t_bits)[np.asarray(rows)])
+    l2 = bf16_values(l2_bits)
+    b = float(np.float32(beta))
+    return y + b * (t @ l2.T), s + abs(b) * (np.abs(t) @ np.abs(l2).T)
