@@ -144,6 +144,14 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_ns_orthogonalize.restype = i32
         L.nvfp4_ns_internals.argtypes = [vp, sz, i64, i64, ctypes.POINTER(NsStateC)]
         L.nvfp4_ns_internals.restype = i32
+        L.nvfp4_lora_workspace_size.argtypes = [i64, i64, i64]
+        L.nvfp4_lora_workspace_size.restype = sz
+        L.nvfp4_lora_forward.argtypes = [vp, ctypes.POINTER(QTensorC), vp, vp, i64, i64, i64, i64, ctypes.c_float,
+                                         vp, i32, i64, vp, sz, vp]
+        L.nvfp4_lora_forward.restype = i32
+        L.nvfp4_lora_internals.argtypes = [vp, sz, i64, i64, i64, ctypes.POINTER(QTensorC),
+                                           ctypes.POINTER(ctypes.c_void_p)]
+        L.nvfp4_lora_internals.restype = i32
         _lib = L
     return _lib
 
@@ -770,3 +778,60 @@ def ns_internals(workspace: torch.Tensor, m: int, n: int) -> dict:
             "clip": [sub(st.clip[i], 4).view(torch.float32) for i in range(3)],
             "inv_norm": sub(st.inv_norm, 4).view(torch.float32),
             "views": views}
+
+
+# --- LoRA-style forward: residual in NVFP4, subspace in BF16 ---------------
+
+def nvfp4_lora_workspace_size(M: int, K: int, r: int) -> int:
+    return int(lib().nvfp4_lora_workspace_size(M, K, r))
+
+
+def _lora_args(x, w_res: QTensor, l1, l2, beta, out_dtype, out, workspace):
+    for t, name in ((x, "x"), (l1, "l1"), (l2, "l2")):
+        if t.dim() != 2 or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 2-D bfloat16 tensor")
+    M, K = x.shape
+    r = l1.size(0)
+    N = w_res.rows
+    if l1.size(1) != K or tuple(l2.shape) != (N, r) or w_res.cols != K:
+        raise ValueError("shapes: x [M][K], w_res [N][K], l1 [r][K], l2 [N][r]")
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=x.device)
+    if workspace is None:
+        workspace = new_workspace(nvfp4_lora_workspace_size(M, K, r), x.device)
+    qw = w_res.c_struct()
+    args = (x.data_ptr(), ctypes.byref(qw), l1.data_ptr(), l2.data_ptr(), M, N, K, r, beta, out.data_ptr(),
+            BF16 if out.dtype == torch.bfloat16 else F32, out.stride(0) if M > 1 else N, workspace.data_ptr(),
+            workspace.numel(), _stream(x.device))
+    return args, (qw, x, l1, l2, out, workspace), out
+
+
+def lora_forward(x: torch.Tensor, w_res: QTensor, l1: torch.Tensor, l2: torch.Tensor, beta: float,
+                 out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X W_res^T (NVFP4) + beta (X L1^T) L2^T (BF16) for x [M][K] BF16."""
+    args, _keep, out = _lora_args(x, w_res, l1, l2, beta, out_dtype, out, workspace)
+    _check(lib().nvfp4_lora_forward(*args), "nvfp4_lora_forward")
+    return out
+
+
+def bind_lora_forward(x, w_res: QTensor, l1, l2, beta: float, out: torch.Tensor, workspace: torch.Tensor) -> BoundCall:
+    args, keep, out = _lora_args(x, w_res, l1, l2, beta, out.dtype, out, workspace)
+    return BoundCall(lib().nvfp4_lora_forward, args, keep, "nvfp4_lora_forward", out)
+
+
+def lora_internals(workspace: torch.Tensor, M: int, K: int, r: int):
+    """(X view, T [M][r] bfloat16) held by a LoRA workspace, aliasing it."""
+    q = QTensorC()
+    t = ctypes.c_void_p()
+    _check(lib().nvfp4_lora_internals(workspace.data_ptr(), workspace.numel(), M, K, r, ctypes.byref(q),
+                                      ctypes.byref(t)), "nvfp4_lora_internals")
+    base = workspace.data_ptr()
+
+    def sub(ptr, nbytes):
+        off = ptr - base
+        return workspace[off:off + nbytes]
+
+    xv = QTensor(sub(q.codes, M * K // 2).view(1, M, K // 2), sub(q.scales, M * K // 16).view(1, M, K // 16),
+                 sub(q.tensor_scale, 4).view(torch.float32), 1, M, K)
+    return xv, sub(t.value, 2 * M * r).view(torch.bfloat16).view(M, r)

@@ -772,3 +772,93 @@ NVFP4_EXPORT nvfp4_status nvfp4_ns_orthogonalize(const void *g, int32_t g_dtype,
   }
   return NVFP4_OK;
 }
+
+// ---------------------------------------------------------------------------
+// LoRA-style forward with the residual weight in NVFP4 and the low-rank
+// subspace in BF16 ("Full-Stack FP4 ...", section 2.1).
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct LoraLayout {
+  size_t ctrl, codes, scales, st, t, total;
+};
+
+LoraLayout lora_layout(int64_t M, int64_t K, int64_t r) {
+  LoraLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  L.ctrl = take(sizeof(QuantCtrl));
+  L.codes = take((size_t)M * (size_t)K / 2);
+  L.scales = take((size_t)M * (size_t)K / 16);
+  L.st = take(sizeof(float));
+  L.t = take((size_t)M * (size_t)r * 2);
+  L.total = off;
+  return L;
+}
+
+bool lora_shape_ok(int64_t M, int64_t K, int64_t r) {
+  return M > 0 && K > 0 && K % 16 == 0 && r > 0 && r % 16 == 0 && r <= 128 && M <= kMaxExtent && K <= kMaxExtent;
+}
+
+}  // namespace
+
+NVFP4_EXPORT size_t nvfp4_lora_workspace_size(int64_t M, int64_t K, int64_t r) {
+  if (!lora_shape_ok(M, K, r)) return 0;
+  return lora_layout(M, K, r).total;
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_lora_internals(void *workspace, size_t workspace_bytes, int64_t M, int64_t K,
+                                               int64_t r, nvfp4_qtensor *x_view, uint16_t **t) {
+  if (!workspace || !x_view || !t) return NVFP4_EINVAL;
+  if (!lora_shape_ok(M, K, r)) return NVFP4_ESHAPE;
+  const LoraLayout L = lora_layout(M, K, r);
+  if (workspace_bytes < L.total) return NVFP4_EWORKSPACE;
+  uint8_t *base = static_cast<uint8_t *>(workspace);
+  x_view->codes = base + L.codes;
+  x_view->scales = base + L.scales;
+  x_view->tensor_scale = reinterpret_cast<float *>(base + L.st);
+  x_view->batch = 1;
+  x_view->rows = M;
+  x_view->cols = K;
+  *t = reinterpret_cast<uint16_t *>(base + L.t);
+  return NVFP4_OK;
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_lora_forward(const void *x, const nvfp4_qtensor *w_res, const void *l1,
+                                             const void *l2, int64_t M, int64_t N, int64_t K, int64_t r, float beta,
+                                             void *y, int32_t y_dtype, int64_t ldy, void *workspace,
+                                             size_t workspace_bytes, void *stream) {
+  if (!x || !w_res || !l1 || !l2 || !y) return NVFP4_EINVAL;
+  if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (!(beta != 0.0f) || !std::isfinite(beta)) return NVFP4_EINVAL;
+  if (!lora_shape_ok(M, K, r) || N <= 0 || N > kMaxExtent) return NVFP4_ESHAPE;
+  nvfp4_status st = check_view(w_res, 1, N, K);
+  if (st != NVFP4_OK) return st;
+  if (ldy < N) return NVFP4_ESHAPE;
+  if (!aligned(x, 16) || !aligned(l1, 16) || !aligned(l2, 16) || !aligned(y, y_dtype == NVFP4_F32 ? 4 : 2))
+    return NVFP4_EALIGN;
+  const LoraLayout L = lora_layout(M, K, r);
+  if (!workspace || workspace_bytes < L.total) return NVFP4_EWORKSPACE;
+  if (!aligned(workspace, 256)) return NVFP4_EALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  nvfp4_qtensor xv{};
+  uint16_t *t = nullptr;
+  nvfp4_lora_internals(workspace, workspace_bytes, M, K, r, &xv, &t);
+  uint8_t *base = static_cast<uint8_t *>(workspace);
+  const nvfp4_quant_opts rne{NVFP4_RNE, 0, 0, 0, 0u, 0u};
+  st = nvfp4::launch_quantize(make_quant(x, true, 1, M, K, K, M * K, false, &rne, &xv, base + L.ctrl), s);
+  if (st != NVFP4_OK) return st;
+  st = nvfp4::launch_lora_down(static_cast<const uint16_t *>(x), M, K, K, static_cast<const uint16_t *>(l1), r, t, s);
+  if (st != NVFP4_OK) return st;
+  nvfp4::GemmProblem p = make_gemm(&xv, w_res, y, y_dtype, ldy, M * ldy, 1.0f);
+  p.lr_t = t;
+  p.lr_l2 = static_cast<const uint16_t *>(l2);
+  p.lr_r = r;
+  p.lr_beta = beta;
+  return nvfp4::launch_gemm(p, s);
+}

@@ -92,6 +92,11 @@ struct GemmArgs {
   const float *cin;  // optional FP32 addend [batch][M][N] (row stride ldcin), times beta
   int64_t ldcin, bstride_cin;
   float beta;
+  // optional low-rank term lr_beta * T L2^T in BF16 (batch 1): T [M][lr_r],
+  // L2 [N][lr_r], row-major, lr_r a multiple of 16
+  const uint16_t *lr_t, *lr_l2;
+  int64_t lr_r;
+  float lr_beta;
 };
 
 // LDS stage: codes [rows][64 B] and scales [rows][8 B] per operand.
@@ -428,13 +433,65 @@ __device__ __forceinline__ void pipelined_kstep_lite(Stage<kBN> &cur, const Stag
   mfma_and_decode<0>(r, sc, av, bv, acc);
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// The low-rank term of a LoRA-style layer ("Full-Stack FP4 ...", section
+// 2.1: W = W_res + beta L2 L1, the subspace kept in BF16), folded into the
+// accumulators before the main loop so that it costs no registers beside
+// them: acc <- fl(q * (T L2^T)) with q = fl(beta / s), s = fl(fl(sA sB)
+// alpha), and the epilogue multiplies by s, giving s acc_main + beta T L2^T
+// to FP32 rounding.  With s = 0 (a zero operand, so acc_main = 0) the
+// factors are q = 1 and beta.  T L2^T runs over K = lr_r on the BF16 MFMA,
+// operands loaded straight from global memory (T and L2 are small and stay
+// in L2): lane l takes row l % 32 of a fragment and the 8 elements at
+// 8 (l / 32) of each 16-wide step, in A and B alike.  Rows and columns past
+// the tensor read clamped addresses; those results are never stored.
+// (q, epilogue factor) of the low-rank fold.
+__device__ __forceinline__ float2 lowrank_factors(const GemmArgs &g) {
+  const float s = (*g.a_st * *g.b_st) * g.alpha;
+  return s != 0.0f ? make_float2(g.lr_beta / s, s) : make_float2(1.0f, g.lr_beta);
+}
+
+// T L2^T of one 32 x 32 fragment, four 16-wide steps per round (their loads
+// issue together).
+__device__ __forceinline__ floatx16 lowrank_fragment(const GemmArgs &g, int64_t row0, int64_t col0) {
+  const int lane = threadIdx.x & 63;
+  const int r32 = lane & 31, k8 = 8 * (lane >> 5);
+  const uint16_t *tp = g.lr_t + min(row0 + r32, g.M - 1) * g.lr_r + k8;
+  const uint16_t *lp = g.lr_l2 + min(col0 + r32, g.N - 1) * g.lr_r + k8;
+  floatx16 t{};
+  for (int64_t k0 = 0; k0 < g.lr_r; k0 += 64) {
+    bf16x8_t a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t k = min(k0 + 16 * u, g.lr_r - 16);  // past r: a repeated step, not used
+      a[u] = *reinterpret_cast<const bf16x8_t *>(tp + k);
+      b[u] = *reinterpret_cast<const bf16x8_t *>(lp + k);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (k0 + 16 * u < g.lr_r) t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[u], t, 0, 0, 0);
+  }
+  return t;
+}
+
+template <int kFragN>
+__device__ __forceinline__ void lowrank_init(floatx16 (&acc)[kFragM][kFragN], const GemmArgs &g, int64_t wrow0,
+                                             int64_t wcol0) {
+  const float q = lowrank_factors(g).x;
+#pragma unroll
+  for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+    for (int j = 0; j < kFragN; ++j) acc[i][j] = lowrank_fragment(g, wrow0 + 32 * i, wcol0 + 32 * j) * q;
+}
+
 template <int kFragN, bool kBF16Out>
 __device__ __forceinline__ void store_tile(const floatx16 (&acc)[kFragM][kFragN], const GemmArgs &g, int64_t batch,
                                            int64_t wrow0, int64_t wcol0) {
   using OutT = typename std::conditional<kBF16Out, uint16_t, float>::type;
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5, r32 = lane & 31;
-  const float sc = (*g.a_st * *g.b_st) * g.alpha;
+  const float sc = g.lr_t ? lowrank_factors(g).y : (*g.a_st * *g.b_st) * g.alpha;
   OutT *cb_ptr = static_cast<OutT *>(g.c) + batch * g.bstride_c;
   const int64_t row0 = wrow0 + 4 * h;
   const int64_t col0 = wcol0 + r32;
@@ -547,6 +604,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
     for (int j = 0; j < kFragN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  // (the 256 x 256 tile has no registers to spare for it: never chosen with
+  // the low-rank term)
+  if constexpr (kFragN < 4) {
+    if (g.lr_t) lowrank_init<kFragN>(acc, g, m0 + wm * 128, n0 + wn * (32 * kFragN));
+  }
 
   const int ksteps = (int)((g.K + BK - 1) / BK);
   if constexpr (kFast && kFragN <= 3) {
@@ -882,7 +944,7 @@ __device__ __forceinline__ void w8_step(const W8Stage<128 * kWM, 96 * kWN> *__re
   w8_compute<128 * kWM, 96 * kWN>(*cur, c.arow, c.brow, c.h, c.qa, c.qb, acc);
 }
 
-template <int kWM, int kWN, bool kBF16Out>
+template <int kWM, int kWN, bool kBF16Out, bool kLowRank>
 __global__ __launch_bounds__(kW8Threads) void gemm_nvfp4_w8_kernel(GemmArgs g) {
   using L = W8Loader<kWM, kWN>;
   constexpr int kBM = L::kBM, kBN = L::kBN;
@@ -923,6 +985,8 @@ __global__ __launch_bounds__(kW8Threads) void gemm_nvfp4_w8_kernel(GemmArgs g) {
     for (int j = 0; j < 3; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  // a separate instantiation: the kernel runs at its register limit
+  if constexpr (kLowRank) lowrank_init<3>(acc, g, m0 + wm * 128, n0 + wn * 96);
 
   const L ld{ac, as, bc, bs, g.M, g.N, m0, n0, (uint32_t)(g.K / 2), (uint32_t)(g.K / 16)};
   const int ksteps = (int)(g.K / BK);
@@ -961,10 +1025,14 @@ hipError_t launch_tiles(const GemmArgs &g, int64_t batch, bool fast, bool bf16, 
 template <int kWM, int kWN>
 hipError_t launch_w8(const GemmArgs &g, int64_t batch, bool bf16, hipStream_t s) {
   const dim3 grid((unsigned)(g.tiles_m * g.tiles_n), (unsigned)batch);
-  if (bf16)
-    hipLaunchKernelGGL((gemm_nvfp4_w8_kernel<kWM, kWN, true>), grid, dim3(kW8Threads), 0, s, g);
-  else
-    hipLaunchKernelGGL((gemm_nvfp4_w8_kernel<kWM, kWN, false>), grid, dim3(kW8Threads), 0, s, g);
+  if (g.lr_t) {
+    if (bf16) hipLaunchKernelGGL((gemm_nvfp4_w8_kernel<kWM, kWN, true, true>), grid, dim3(kW8Threads), 0, s, g);
+    else hipLaunchKernelGGL((gemm_nvfp4_w8_kernel<kWM, kWN, false, true>), grid, dim3(kW8Threads), 0, s, g);
+  } else if (bf16) {
+    hipLaunchKernelGGL((gemm_nvfp4_w8_kernel<kWM, kWN, true, false>), grid, dim3(kW8Threads), 0, s, g);
+  } else {
+    hipLaunchKernelGGL((gemm_nvfp4_w8_kernel<kWM, kWN, false, false>), grid, dim3(kW8Threads), 0, s, g);
+  }
   return hipGetLastError();
 }
 
@@ -979,7 +1047,7 @@ struct TilePick {
   int bm, bn;
 };
 
-TilePick pick_tiles(int64_t M, int64_t N, int64_t batch, bool fast, int force_bm, int force_bn) {
+TilePick pick_tiles(int64_t M, int64_t N, int64_t batch, bool fast, int force_bm, int force_bn, bool lowrank) {
   struct Cand {
     int kind, bm, bn;
     double cost;
@@ -991,6 +1059,7 @@ TilePick pick_tiles(int64_t M, int64_t N, int64_t batch, bool fast, int force_bm
   TilePick pick{4, 256, 256};
   for (const Cand &c : cands) {
     if (c.need_fast && !fast) continue;
+    if (lowrank && c.kind == 4) continue;
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * batch;
     const double t = (double)((tiles + 255) / 256) * c.bm * c.bn * c.cost;
     if (t < best - 1e-9) {
@@ -1003,7 +1072,8 @@ TilePick pick_tiles(int64_t M, int64_t N, int64_t batch, bool fast, int force_bm
   if (force_bm != 0 || force_bn != 0) {
     pick = TilePick{-1, 0, 0};
     for (const Cand &c : cands)
-      if (c.bm == force_bm && c.bn == force_bn && (fast || !c.need_fast)) pick = TilePick{c.kind, c.bm, c.bn};
+      if (c.bm == force_bm && c.bn == force_bn && (fast || !c.need_fast) && !(lowrank && c.kind == 4))
+        pick = TilePick{c.kind, c.bm, c.bn};
   }
   return pick;
 }
@@ -1031,12 +1101,16 @@ nvfp4_status launch_gemm(const GemmProblem &p, hipStream_t s) {
   g.ldcin = p.ldcin;
   g.bstride_cin = p.bstride_cin;
   g.beta = p.beta;
+  g.lr_t = p.lr_t;
+  g.lr_l2 = p.lr_l2;
+  g.lr_r = p.lr_r;
+  g.lr_beta = p.lr_beta;
   // The 8-wavefront kernel's loads use 32-bit offsets within an operand and
   // 24-bit row and row-size factors.
   const bool fast = p.K % BK == 0;
   const bool small = p.M * (p.K / 2) < ((int64_t)1 << 31) && p.N * (p.K / 2) < ((int64_t)1 << 31) &&
                      p.M < (1 << 24) && p.N < (1 << 24) && p.K / 2 < (1 << 24);
-  const TilePick tp = pick_tiles(p.M, p.N, p.batch, fast && small, p.tile_m, p.tile_n);
+  const TilePick tp = pick_tiles(p.M, p.N, p.batch, fast && small, p.tile_m, p.tile_n, p.lr_t != nullptr);
   if (tp.kind < 0) return NVFP4_EUNSUPPORTED;
   const int64_t tm = (p.M + tp.bm - 1) / tp.bm, tn = (p.N + tp.bn - 1) / tp.bn;
   if (tm * tn > 0x7FFFFFFF) return NVFP4_EUNSUPPORTED;

@@ -89,6 +89,9 @@ struct GemmProblem {
   const float *cin;    // optional FP32 addend: y = fl(acc * s) + fl(beta * cin)
   int64_t ldcin, bstride_cin;
   float beta;
+  const uint16_t *lr_t, *lr_l2;  // optional low-rank BF16 term lr_beta * T L2^T (batch 1)
+  int64_t lr_r;
+  float lr_beta;
 };
 
 // Exact order statistic of |x| (radix select): state->value = the element of
@@ -106,6 +109,11 @@ nvfp4_status launch_abs_select(const float *x, int64_t rows, int64_t cols, int64
 // partials (partial: 1024 doubles) and *inv = fl32(1 / (||g|| + 1e-7)).
 nvfp4_status launch_frobenius_normalize(const void *g, bool bf16, int64_t rows, int64_t cols, int64_t ld,
                                         double *partial, float *inv, float *x, int64_t xld, hipStream_t stream);
+
+// T = BF16_RNE(X L1^T): X [M][K] BF16 (row stride ldx, 16-byte aligned
+// rows), L1 [r][K], T [M][r]; K % 16 == 0, r % 16 == 0, r <= 128.
+nvfp4_status launch_lora_down(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const uint16_t *l1, int64_t r,
+                              uint16_t *t, hipStream_t stream);
 
 nvfp4_status launch_quantize(const QuantProblem &p, hipStream_t stream);
 nvfp4_status launch_quantize_group(const QuantGroupProblem &p, hipStream_t stream);

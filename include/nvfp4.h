@@ -439,6 +439,36 @@ typedef struct nvfp4_ns_state {
 nvfp4_status nvfp4_ns_internals(void *workspace, size_t workspace_bytes, int64_t m, int64_t n,
                                 nvfp4_ns_state *out);
 
+/* Forward of a linear layer parametrized as W = W_res + beta L2 L1 ([P3]
+ * section 2.1, LoRA-SVD: the dominant residual W_res in NVFP4, the compact
+ * subspace L2 L1 kept in BF16):
+ *   T = BF16_RNE(X L1^T)                 (FP32 accumulation)
+ *   Y = s * X^ W_res^^T + beta * T L2^T   (FP32 accumulation, then y_dtype)
+ * with X^ the NVFP4 view of X (RNE, no transform; stays in the workspace),
+ * s = fl(fl(sX sW) * 1).  The low-rank product is folded into the NVFP4
+ * GEMM's FP32 accumulators before its main loop, pre-divided by s (q =
+ * fl(beta / s); q = 1 and factor beta when s = 0), so Y agrees with the
+ * exact s * sum + beta * T L2^T to the FP32 accumulation tolerance; results
+ * are unspecified if fl(beta / s) overflows.
+ *   x      device BF16 [M][K], contiguous, 16-byte aligned.
+ *   w_res  host struct, the NVFP4 view [1][N][K] of W_res.
+ *   l1     device BF16 [r][K], l2 device BF16 [N][r], contiguous, 16-byte
+ *          aligned; r a multiple of 16, 16 <= r <= 128.
+ *   beta   finite and nonzero.
+ *   y      device [M][N], dtype y_dtype, row stride ldy.
+ * K a multiple of 16.  Workspace: nvfp4_lora_workspace_size(M, K, r) bytes,
+ * 256-byte aligned, zeroed before first use; it keeps X^ and T. */
+size_t nvfp4_lora_workspace_size(int64_t M, int64_t K, int64_t r);
+
+nvfp4_status nvfp4_lora_forward(const void *x, const nvfp4_qtensor *w_res, const void *l1, const void *l2,
+                                int64_t M, int64_t N, int64_t K, int64_t r, float beta, void *y, int32_t y_dtype,
+                                int64_t ldy, void *workspace, size_t workspace_bytes, void *stream);
+
+/* The view X^ ([1][M][K]) and T (device BF16 [M][r]) a LoRA workspace holds
+ * (host computation only). */
+nvfp4_status nvfp4_lora_internals(void *workspace, size_t workspace_bytes, int64_t M, int64_t K, int64_t r,
+                                  nvfp4_qtensor *x_view, uint16_t **t);
+
 #ifdef __cplusplus
 }
 #endif

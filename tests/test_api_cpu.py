@@ -311,3 +311,33 @@ def test_ns_argument_errors_and_layout():
     regions = [st.x_prev, st.a, st.b, st.inv_norm] + list(st.clip) + [v.codes for v in st.view]
     assert all(FAKE <= r < FAKE + need for r in regions) and len(set(regions)) == len(regions)
     assert L.nvfp4_ns_internals(FAKE, need - 1, m, n, ctypes.byref(st)) == nv.EWORKSPACE
+
+
+def test_lora_argument_errors_and_layout():
+    M, N, K, r = 64, 48, 128, 32
+    need = nv.nvfp4_lora_workspace_size(M, K, r)
+    assert need >= M * K // 2 + M * K // 16 + 2 * M * r + 4096
+    assert nv.nvfp4_lora_workspace_size(M, K, 24) == 0 and nv.nvfp4_lora_workspace_size(M, K, 144) == 0
+    assert nv.nvfp4_lora_workspace_size(M, 40, r) == 0
+    L = nv.lib()
+    w = _q(1, N, K)
+
+    def call(x=FAKE, wq=w, l1=FAKE, l2=FAKE, mm=M, nn=N, kk=K, rr=r, beta=0.5, y=FAKE, dt=nv.BF16, ldy=N,
+             ws=FAKE + 0x100000, wsb=need):
+        return L.nvfp4_lora_forward(x, ctypes.byref(wq), l1, l2, mm, nn, kk, rr, beta, y, dt, ldy, ws, wsb, None)
+
+    assert call(x=0) == nv.EINVAL
+    assert call(beta=0.0) == nv.EINVAL
+    assert call(beta=float("inf")) == nv.EINVAL
+    assert call(dt=3) == nv.EINVAL
+    assert call(rr=24) == nv.ESHAPE
+    assert call(kk=40, wq=_q(1, N, 40)) == nv.ESHAPE
+    assert call(wq=_q(1, N + 1, K)) == nv.EINVAL
+    assert call(ldy=N - 1) == nv.ESHAPE
+    assert call(l1=FAKE + 8) == nv.EALIGN
+    assert call(wsb=need - 1) == nv.EWORKSPACE
+    assert call(ws=FAKE + 0x100010) == nv.EALIGN
+    q = nv.QTensorC()
+    t = ctypes.c_void_p()
+    assert L.nvfp4_lora_internals(FAKE, need, M, K, r, ctypes.byref(q), ctypes.byref(t)) == nv.OK
+    assert q.rows == M and q.cols == K and FAKE < t.value < FAKE + need
