@@ -21,7 +21,8 @@ Order of work:
      checks this run's outputs against the oracle.
 
 Prints one JSON line.  `value` is the whole-step NVFP4 GEMM throughput
-(2*M*N*K per step time, TFLOP/s).  `roofline` describes the dominant kernel
+(2*M*N*K per step time, TFLOP/s; for the HBM-bound AdamW state codec, the
+step's algorithmic GB/s).  `roofline` describes the dominant kernel
 (the GEMM, or the attention-scores write) from its back-to-back duration:
 achieved = algorithmic flops (or bytes) per launch / duration, against the
 dense FP16 MFMA peak (or HBM), with `traffic` the HBM bytes per launch from
@@ -65,7 +66,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="fprop_3b",
-                   choices=["fprop_3b", "mlp_up_12b", "linear_train", "attn_scores"])
+                   choices=["fprop_3b", "mlp_up_12b", "linear_train", "attn_scores", "attn_bwd", "adamw_state",
+                            "ns_3b", "lora_3b"])
     p.add_argument("--reps", type=int, default=100, help="back-to-back launches per call in the per-call timing")
     p.add_argument("--settle-ms", type=float, default=300.0,
                    help="wall time of untimed steps before the per-call timing (lets the shader clock settle)")
@@ -213,7 +215,8 @@ def main():
     copy_gbps = copy_bandwidth()
     t = W.WORKLOADS[args.workload]()
     setup = {"fprop_3b": setup_linear_gemm, "mlp_up_12b": setup_linear_gemm,
-             "linear_train": setup_linear_train, "attn_scores": setup_attn}[args.workload]
+             "linear_train": setup_linear_train, "attn_scores": setup_attn, "attn_bwd": setup_attn_bwd,
+             "adamw_state": setup_adamw, "ns_3b": setup_ns, "lora_3b": setup_lora}[args.workload]
     S = setup(t, dev)
     steps, nbuf = S["steps"], S["nbuf"]
 
@@ -271,10 +274,14 @@ def main():
     roofline["kernel"] = dom
     roofline["duration_us"] = dom_us
 
+    if "step_bytes" in S:  # an HBM-bound step: its rate in GB/s
+        value, unit = round(S["step_bytes"] / (ms_per_step * 1e-3) / 1e9, 1), "GB/s"
+    else:
+        value, unit = round(S["step_flops"] / (ms_per_step * 1e-3) / 1e12, 2), "TFLOP/s"
     out = {
-        "metric": METRIC,
-        "value": round(S["step_flops"] / (ms_per_step * 1e-3) / 1e12, 2),
-        "unit": "TFLOP/s",
+        "metric": S.get("metric", METRIC),
+        "value": value,
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -282,7 +289,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16",
+        "dtype": S.get("dtype", "fp16"),
         "data": "synthetic",
         "config": dict(S["config"], workload=args.workload, rotating_buffers=nbuf),
         "roofline": roofline,
@@ -438,6 +445,95 @@ def setup_attn(t, dev) -> dict:
             "dominant": "gemm", "bound": "hbm",
             "config": {"batch": B, "heads": H, "seq": S_, "head_dim": D, "x_dtype": "bf16", "y_dtype": "fp32",
                        "rounding": "rne", "alpha": t["alpha"]}}
+
+
+def setup_attn_bwd(t, dev) -> dict:
+    """Attention backward through dS in NVFP4: the forward's dual views of Q
+    and K (one read each), then nvfp4_attention_ds_grads (dS quantized in
+    both orientations from one read, dQ = alpha dS K, dK = alpha dS^T Q)."""
+    q_cpu, k_cpu, ds_cpu = t["Q"], t["K"], t["dS"]
+    bh, sq, d = q_cpu.shape
+    sk = k_cpu.shape[1]
+    q, k, ds = q_cpu.to(dev), k_cpu.to(dev), ds_cpu.to(dev)
+    q_hd, q_seq = nv.QTensor.empty(bh, sq, d, dev), nv.QTensor.empty(bh, d, sq, dev)
+    k_hd, k_seq = nv.QTensor.empty(bh, sk, d, dev), nv.QTensor.empty(bh, d, sk, dev)
+    wq = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
+    wk = nv.new_workspace(nv.nvfp4_quantize_workspace_size(), dev)
+    wds = nv.new_workspace(nv.nvfp4_attention_ds_workspace_size(bh, sq, sk), dev)
+    dq = torch.empty(bh, sq, d, dtype=torch.bfloat16, device=dev)
+    dk = torch.empty(bh, sk, d, dtype=torch.bfloat16, device=dev)
+    cq = nv.bind_quantize_dual(q, (q_hd, q_seq), wq)
+    ck = nv.bind_quantize_dual(k, (k_hd, k_seq), wk)
+    cg = nv.bind_attention_ds_grads(ds, q_seq, k_seq, dq, dk, wds, t["alpha"], t["sr_seed"])
+    flops = 2 * 2.0 * bh * sq * sk * d
+    ds_bytes = 2.0 * bh * sq * sk + 2 * bh * sq * sk * (0.5 + 1 / 16) + 2 * bh * (sq + sk) * d * (0.5 + 1 / 16)
+    return {"steps": [(cq, ck, cg)], "calls": {"quantize_dual_q": [cq], "quantize_dual_k": [ck],
+                                               "attention_ds_grads": [cg]}, "nbuf": 1,
+            "flops": {"attention_ds_grads": flops}, "step_flops": flops,
+            "bytes": {"quantize_dual_q": (2 + 2 * (0.5 + 1 / 16)) * q.numel(),
+                      "quantize_dual_k": (2 + 2 * (0.5 + 1 / 16)) * k.numel(), "attention_ds_grads": ds_bytes},
+            "dominant": "attention_ds_grads", "bound": "hbm",
+            "metric": "attention dS backward (dS dual quantize + dQ, dK GEMMs) TFLOP/s at 128x4096x4096x128",
+            "config": {"batch_heads": bh, "seq_q": sq, "seq_k": sk, "head_dim": d, "ds_rounding": "sr",
+                       "out_dtype": "bf16"}}
+
+
+def setup_adamw(t, dev) -> dict:
+    """AdamW state codec: encode FP32 m, v into NVFP4 state, then decode."""
+    m_cpu, v_cpu = t["m"], t["v"]
+    R, C = m_cpu.shape
+    nbuf = rotation(8 * m_cpu.numel())
+    ms = [m_cpu.to(dev) for _ in range(nbuf)]
+    vs = [v_cpu.to(dev) for _ in range(nbuf)]
+    sts = [nv.QAdamWState.empty(R, C, dev) for _ in range(nbuf)]
+    ws = nv.new_workspace(nv.nvfp4_qadamw_workspace_size(), dev)
+    om, ov = torch.empty(R, C, device=dev), torch.empty(R, C, device=dev)
+    enc = [nv.bind_qadamw_encode(ms[j], vs[j], sts[j], ws, t["rht_seed"], t["sr_seed"]) for j in range(nbuf)]
+    dec = [nv.bind_qadamw_decode(sts[j], t["rht_seed"], om, ov) for j in range(nbuf)]
+    n = R * C
+    b = n * (8 + 2 * (0.5 + 1 / 16) + 2 / 16)  # FP32 m, v <-> two NVFP4 views and the BF16 means
+    return {"steps": list(zip(enc, dec)), "calls": {"qadamw_encode": enc, "qadamw_decode": dec}, "nbuf": nbuf,
+            "flops": {}, "step_flops": 0.0, "bytes": {"qadamw_encode": b, "qadamw_decode": b}, "step_bytes": 2 * b,
+            "dominant": "qadamw_encode", "bound": "hbm", "dtype": "f32",
+            "metric": "AdamW state codec GB/s (encode + decode) at 20480x5120",
+            "config": {"rows": R, "cols": C, "m": "rht+sr", "v": "sqrt, bf16 block mean, rht, rne"}}
+
+
+def setup_ns(t, dev) -> dict:
+    """Newton-Schulz orthogonalization with every product in NVFP4."""
+    g_cpu = t["G"]
+    m, n = g_cpu.shape
+    co = t["coeffs"]
+    g = g_cpu.to(dev)
+    ws = nv.new_workspace(nv.nvfp4_ns_workspace_size(m, n), dev)
+    x = torch.empty(m, n, device=dev)
+    c = nv.bind_ns_orthogonalize(g, co, x, ws, t["clip_quantile"], t["clip_mask"])
+    flops = len(co) * 2.0 * (m * m * n + m * m * m + m * n * m)
+    return {"steps": [(c,)], "calls": {"ns_orthogonalize": [c]}, "nbuf": 1, "flops": {"ns_orthogonalize": flops},
+            "step_flops": flops, "bytes": {}, "dominant": "ns_orthogonalize", "bound": "mfma",
+            "metric": "Newton-Schulz in NVFP4 TFLOP/s (5 steps) at 3072x8192",
+            "config": {"m": m, "n": n, "steps": len(co), "coeffs": list(co[0]), "clip_quantile": t["clip_quantile"],
+                       "clip_mask": t["clip_mask"]}}
+
+
+def setup_lora(t, dev) -> dict:
+    """LoRA-style forward: quantize X, T = BF16(X L1^T), Y = X^ W_res^^T +
+    beta T L2^T with the low-rank term folded into the NVFP4 GEMM."""
+    x_cpu, w_cpu, l1_cpu, l2_cpu = t["X"], t["W_res"], t["L1"], t["L2"]
+    M, K = x_cpu.shape
+    N, r = w_cpu.shape[0], l1_cpu.shape[0]
+    nbuf = rotation(x_cpu.numel() * 2)
+    xs = [x_cpu.to(dev) for _ in range(nbuf)]
+    wv = nv.quantize(w_cpu.to(dev))
+    l1, l2 = l1_cpu.to(dev), l2_cpu.to(dev)
+    ws = nv.new_workspace(nv.nvfp4_lora_workspace_size(M, K, r), dev)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    calls = [nv.bind_lora_forward(xs[j], wv, l1, l2, t["beta"], y, ws) for j in range(nbuf)]
+    flops = 2.0 * M * N * K + 2.0 * M * K * r + 2.0 * M * N * r
+    return {"steps": [(c,) for c in calls], "calls": {"lora_forward": calls}, "nbuf": nbuf,
+            "flops": {"lora_forward": flops}, "step_flops": flops, "bytes": {}, "dominant": "lora_forward",
+            "bound": "mfma", "metric": "LoRA-style forward TFLOP/s (NVFP4 residual + BF16 rank-64) at 8192x3072x3072",
+            "config": {"M": M, "N": N, "K": K, "rank": r, "beta": t["beta"], "y_dtype": "bf16"}}
 
 
 if __name__ == "__main__":
