@@ -590,7 +590,7 @@ NVFP4_EXPORT nvfp4_status nvfp4_linear_fwd_bwd(const void *x, const void *w, con
 namespace {
 
 // Workspace: three quantize control blocks, three select states (X, A, B)
-// and their shared histogram, the normalization partials, the second iterate
+// and their shared 4096-counter histogram, the normalization partials, the second iterate
 // buffer, A and B in FP32, and the four quantized views; 256-byte regions.
 struct NsLayout {
   size_t ctrl[3], sel[3], hist, partial, inv, xbuf, a, b;
@@ -609,7 +609,7 @@ NsLayout ns_layout(int64_t m, int64_t n) {
   };
   for (int i = 0; i < 3; ++i) L.ctrl[i] = take(sizeof(QuantCtrl));
   for (int i = 0; i < 3; ++i) L.sel[i] = take(sizeof(nvfp4::SelectState));
-  L.hist = take(2048 * sizeof(uint32_t));
+  L.hist = take(4096 * sizeof(uint32_t));
   L.partial = take(1024 * sizeof(double));
   L.inv = take(sizeof(float));
   L.xbuf = take((size_t)m * (size_t)n * 4);

@@ -441,48 +441,62 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 // them: acc <- fl(q * (T L2^T)) with q = fl(beta / s), s = fl(fl(sA sB)
 // alpha), and the epilogue multiplies by s, giving s acc_main + beta T L2^T
 // to FP32 rounding.  With s = 0 (a zero operand, so acc_main = 0) the
-// factors are q = 1 and beta.  T L2^T runs over K = lr_r on the BF16 MFMA,
-// operands loaded straight from global memory (T and L2 are small and stay
-// in L2): lane l takes row l % 32 of a fragment and the 8 elements at
-// 8 (l / 32) of each 16-wide step, in A and B alike.  Rows and columns past
-// the tensor read clamped addresses; those results are never stored.
+// factors are q = 1 and beta.  T L2^T runs over K = lr_r on the BF16 MFMA:
+// lane l takes row l % 32 of a fragment and the 8 elements at 8 (l / 32) of
+// each 16-wide step, in A and B alike.  Rows and columns past the tensor
+// read clamped addresses; those results are never stored.
 // (q, epilogue factor) of the low-rank fold.
 __device__ __forceinline__ float2 lowrank_factors(const GemmArgs &g) {
   const float s = (*g.a_st * *g.b_st) * g.alpha;
   return s != 0.0f ? make_float2(g.lr_beta / s, s) : make_float2(1.0f, g.lr_beta);
 }
 
-// T L2^T of one 32 x 32 fragment, four 16-wide steps per round (their loads
-// issue together).
-__device__ __forceinline__ floatx16 lowrank_fragment(const GemmArgs &g, int64_t row0, int64_t col0) {
+// The fold through LDS: per chunk of 32 along r, the workgroup copies its
+// rows of T ([m0, m0 + kTM)) and of L2 ([n0, n0 + kTN)) into two LDS
+// buffers (the pipeline stages, still unused), one 16-byte load per piece,
+// so the chunk costs one memory latency; then each wavefront runs its
+// fragments' MFMAs on operands read from LDS.  Staged rows are 80 bytes
+// apart (32 BF16 and 16 bytes of padding against bank conflicts).
+template <int kFragN, int kTM, int kTN, int kNT>
+__device__ __forceinline__ void lowrank_init(floatx16 (&acc)[kFragM][kFragN], const GemmArgs &g, int64_t m0,
+                                             int64_t n0, int wrow, int wcol, uint8_t *lt, uint8_t *ll) {
+  constexpr int kPitch = 80;
   const int lane = threadIdx.x & 63;
   const int r32 = lane & 31, k8 = 8 * (lane >> 5);
-  const uint16_t *tp = g.lr_t + min(row0 + r32, g.M - 1) * g.lr_r + k8;
-  const uint16_t *lp = g.lr_l2 + min(col0 + r32, g.N - 1) * g.lr_r + k8;
-  floatx16 t{};
-  for (int64_t k0 = 0; k0 < g.lr_r; k0 += 64) {
-    bf16x8_t a[4], b[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t k = min(k0 + 16 * u, g.lr_r - 16);  // past r: a repeated step, not used
-      a[u] = *reinterpret_cast<const bf16x8_t *>(tp + k);
-      b[u] = *reinterpret_cast<const bf16x8_t *>(lp + k);
+  for (int64_t k0 = 0; k0 < g.lr_r; k0 += 32) {
+    for (int p = threadIdx.x; p < (kTM + kTN) * 4; p += kNT) {
+      const bool is_t = p < kTM * 4;
+      const int q = is_t ? p : p - kTM * 4;
+      const int row = q >> 2, piece = q & 3;
+      const int64_t kk = min(k0 + 8 * piece, g.lr_r - 8);  // past r: a repeated piece, never used
+      const uint4 v = is_t ? *reinterpret_cast<const uint4 *>(g.lr_t + min(m0 + row, g.M - 1) * g.lr_r + kk)
+                           : *reinterpret_cast<const uint4 *>(g.lr_l2 + min(n0 + row, g.N - 1) * g.lr_r + kk);
+      *reinterpret_cast<uint4 *>((is_t ? lt : ll) + row * kPitch + 16 * piece) = v;
     }
+    __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (k0 + 16 * u < g.lr_r) t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[u], t, 0, 0, 0);
+    for (int u = 0; u < 2; ++u) {
+      if (k0 + 16 * u < g.lr_r) {
+        bf16x8_t b[kFragN];
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j)
+          b[j] = *reinterpret_cast<const bf16x8_t *>(ll + (wcol + 32 * j + r32) * kPitch + 2 * (16 * u + k8));
+#pragma unroll
+        for (int i = 0; i < kFragM; ++i) {
+          const bf16x8_t a =
+              *reinterpret_cast<const bf16x8_t *>(lt + (wrow + 32 * i + r32) * kPitch + 2 * (16 * u + k8));
+#pragma unroll
+          for (int j = 0; j < kFragN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
   }
-  return t;
-}
-
-template <int kFragN>
-__device__ __forceinline__ void lowrank_init(floatx16 (&acc)[kFragM][kFragN], const GemmArgs &g, int64_t wrow0,
-                                             int64_t wcol0) {
   const float q = lowrank_factors(g).x;
 #pragma unroll
   for (int i = 0; i < kFragM; ++i)
 #pragma unroll
-    for (int j = 0; j < kFragN; ++j) acc[i][j] = lowrank_fragment(g, wrow0 + 32 * i, wcol0 + 32 * j) * q;
+    for (int j = 0; j < kFragN; ++j) acc[i][j] = acc[i][j] * q;
 }
 
 template <int kFragN, bool kBF16Out>
@@ -607,7 +621,10 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
   // (the 256 x 256 tile has no registers to spare for it: never chosen with
   // the low-rank term)
   if constexpr (kFragN < 4) {
-    if (g.lr_t) lowrank_init<kFragN>(acc, g, m0 + wm * 128, n0 + wn * (32 * kFragN));
+    static_assert(BM * 80 <= sizeof(Stage<kBN>) && kBN * 80 <= sizeof(Stage<kBN>), "low-rank staging fits a stage");
+    if (g.lr_t)
+      lowrank_init<kFragN, BM, kBN, kThreads>(acc, g, m0, n0, wm * 128, wn * (32 * kFragN),
+                                              reinterpret_cast<uint8_t *>(&st0), reinterpret_cast<uint8_t *>(&st1));
   }
 
   const int ksteps = (int)((g.K + BK - 1) / BK);
@@ -986,7 +1003,12 @@ __global__ __launch_bounds__(kW8Threads) void gemm_nvfp4_w8_kernel(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   // a separate instantiation: the kernel runs at its register limit
-  if constexpr (kLowRank) lowrank_init<3>(acc, g, m0 + wm * 128, n0 + wn * 96);
+  if constexpr (kLowRank) {
+    static_assert(kBM * 80 <= sizeof(W8Stage<kBM, kBN>) && kBN * 80 <= sizeof(W8Stage<kBM, kBN>),
+                  "low-rank staging fits a stage");
+    lowrank_init<3, kBM, kBN, kW8Threads>(acc, g, m0, n0, wm * 128, wn * 96, reinterpret_cast<uint8_t *>(&st0),
+                                          reinterpret_cast<uint8_t *>(&st1));
+  }
 
   const L ld{ac, as, bc, bs, g.M, g.N, m0, n0, (uint32_t)(g.K / 2), (uint32_t)(g.K / 16)};
   const int ksteps = (int)(g.K / BK);

@@ -97,7 +97,7 @@ struct GemmProblem {
 // Exact order statistic of |x| (radix select): state->value = the element of
 // rank `rank` (0-based, ascending by the bit pattern of |x|) of x [rows][cols]
 // (row stride ld; cols and ld multiples of 4, x 16-byte aligned).  `hist`
-// holds 2048 counters, zero on entry and on return.
+// holds 4096 counters, zero on entry and on return.
 struct SelectState {
   uint32_t prefix;
   float value;

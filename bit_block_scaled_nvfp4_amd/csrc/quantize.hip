@@ -1343,59 +1343,80 @@ struct StateDecodeArgs {
   uint64_t rht_seed;
 };
 
+// One thread per 16-element block, 256 consecutive blocks per workgroup
+// and round.  A thread's block is 64 contiguous output bytes, so storing it
+// directly would have every store instruction touch 64 partial lines; the
+// round's blocks are staged in LDS instead and written back as consecutive
+// 16-byte pieces by consecutive threads.
+constexpr int kDecodeBlocks = 256;
+
 template <bool kSecond>
-__global__ __launch_bounds__(kThreads) void state_decode_kernel(StateDecodeArgs a) {
+__global__ __launch_bounds__(kDecodeBlocks) void state_decode_kernel(StateDecodeArgs a) {
+  __shared__ float4 stage[kDecodeBlocks * 4];
   const uint32_t mask = rht_sign_mask(a.rht_seed);
   const float st = *a.tensor_scale;
-  for (uint64_t blk = (uint64_t)blockIdx.x * kThreads + threadIdx.x; blk < a.nblocks;
-       blk += (uint64_t)gridDim.x * kThreads) {
-    const uint2 c = *reinterpret_cast<const uint2 *>(a.codes + 8 * blk);
-    const float sc = e4m3_value(a.scales[blk]);
-    // E2M1 values of the block (scale 1), then H on them: every partial sum
-    // is a multiple of 1/2 no larger than 96 in magnitude, so exact.
-    float v[16];
-    const float2_v p[8] = {
-        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 0), __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 1),
-        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 2), __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 3),
-        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 0), __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 1),
-        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 2), __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 3)};
+  for (uint64_t base = (uint64_t)blockIdx.x * kDecodeBlocks; base < a.nblocks;
+       base += (uint64_t)gridDim.x * kDecodeBlocks) {
+    const uint64_t blk = base + threadIdx.x;
+    if (blk < a.nblocks) {
+      const uint2 c = *reinterpret_cast<const uint2 *>(a.codes + 8 * blk);
+      const float sc = e4m3_value(a.scales[blk]);
+      // E2M1 values of the block (scale 1), then H on them: every partial
+      // sum is a multiple of 1/2 no larger than 96 in magnitude, so exact.
+      float v[16];
+      const float2_v p[8] = {
+          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 0), __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 1),
+          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 2), __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 3),
+          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 0), __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 1),
+          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 2), __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 3)};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      v[2 * k] = p[k][0];
-      v[2 * k + 1] = p[k][1];
-    }
-#pragma unroll
-    for (int h = 1; h < 16; h <<= 1) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i & h) continue;
-        const float x = v[i], y = v[i + h];
-        v[i] = x + y;
-        v[i + h] = x - y;
+      for (int k = 0; k < 8; ++k) {
+        v[2 * k] = p[k][0];
+        v[2 * k + 1] = p[k][1];
       }
-    }
-    // (1/4) E4M3 is exact, and so is its product with a sum above (at most
-    // 12 significant bits); the tensor scale rounds once; then the signs.
-    // A zero sum is taken as +0 (the sums of -0 codes would give -0), so a
-    // zero result carries the sign of the diagonal alone.
-    const float q4 = sc * 0.25f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float z = v[j] + 0.0f;
-      v[j] = __uint_as_float(__float_as_uint((z * q4) * st) ^ (((mask >> j) & 1u) << 31));
-    }
-    if constexpr (kSecond) {
-      const float mu = __uint_as_float((uint32_t)a.means[blk] << 16);
+      for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (i & h) continue;
+          const float x = v[i], y = v[i + h];
+          v[i] = x + y;
+          v[i + h] = x - y;
+        }
+      }
+      // (1/4) E4M3 is exact, and so is its product with a sum above (at
+      // most 12 significant bits); the tensor scale rounds once; then the
+      // signs.  A zero sum is taken as +0 (the sums of -0 codes would give
+      // -0), so a zero result carries the sign of the diagonal alone.
+      const float q4 = sc * 0.25f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float sj = v[j] + mu;
-        v[j] = sj * sj;
+        const float z = v[j] + 0.0f;
+        v[j] = __uint_as_float(__float_as_uint((z * q4) * st) ^ (((mask >> j) & 1u) << 31));
+      }
+      if constexpr (kSecond) {
+        const float mu = __uint_as_float((uint32_t)a.means[blk] << 16);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float sj = v[j] + mu;
+          v[j] = sj * sj;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        stage[4 * threadIdx.x + q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = threadIdx.x + kDecodeBlocks * i;  // 16-byte piece of the round
+      const uint64_t b = base + slot / 4;
+      if (b < a.nblocks) {
+        const uint64_t row = b / a.bpr, cb = b - row * a.bpr;
+        *reinterpret_cast<float4 *>(a.out + row * a.ld + 16 * cb + 4 * (slot & 3)) = stage[slot];
       }
     }
-    const uint64_t row = blk / a.bpr, cb = blk - row * a.bpr;
-    float4 *o = reinterpret_cast<float4 *>(a.out + row * a.ld + 16 * cb);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    __syncthreads();
   }
 }
 
@@ -1436,9 +1457,9 @@ nvfp4_status launch_state_decode(const uint8_t *codes, const uint8_t *scales, co
   if (rows == 0 || cols == 0) return NVFP4_OK;
   StateDecodeArgs a{codes, scales, tensor_scale, means, out, (uint64_t)(rows * cols / 16), (uint64_t)(cols / 16), ld,
                     rht_seed};
-  const int g = grid_for(a.nblocks, kThreads, 256ull * 16);
-  if (means) hipLaunchKernelGGL((state_decode_kernel<true>), dim3(g), dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((state_decode_kernel<false>), dim3(g), dim3(kThreads), 0, s, a);
+  const int g = grid_for(a.nblocks, kDecodeBlocks, 256ull * 16);
+  if (means) hipLaunchKernelGGL((state_decode_kernel<true>), dim3(g), dim3(kDecodeBlocks), 0, s, a);
+  else hipLaunchKernelGGL((state_decode_kernel<false>), dim3(g), dim3(kDecodeBlocks), 0, s, a);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 

@@ -6,13 +6,15 @@
 //
 // Radix select.  For x >= 0 the IEEE bit patterns order like the values
 // (NaN patterns above +inf), so the k-th smallest |x| is found digit by
-// digit on u = bits(x) & 0x7FFFFFFF: bits 30..20 (11), 19..9 (11), 8..0 (9).
+// digit on u = bits(x) & 0x7FFFFFFF: bits 30..19 (12), 18..8 (11), 7..0 (8).
 // Pass p histograms digit p of the elements whose higher digits equal the
-// prefix found so far (2048 LDS bins per workgroup, one global atomic add per
+// prefix found so far (LDS bins per workgroup, one global atomic add per
 // nonzero bin), then one workgroup scans the histogram, narrows the prefix
 // and the rank left inside it, and clears the histogram for the next pass or
 // call.  Counts are exact integers, so the result does not depend on the
-// order of the atomics.
+// order of the atomics.  The first digit is the widest: every element
+// counts in that pass, and real data crowd into a few exponents, whose bins
+// the LDS atomics then serialize on.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -23,23 +25,25 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kSelThreads = 256;
-constexpr int kBins = 2048;
+constexpr int kBins = 4096;  // the widest digit's bins (the histogram's size)
+
+// Digit widths and positions: pass 0 bits 30..19, pass 1 bits 18..8, pass 2
+// bits 7..0.
+constexpr int kDigitBits[3] = {12, 11, 8};
+constexpr int kDigitShift[3] = {19, 8, 0};
 
 __device__ __forceinline__ uint32_t abs_u(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
 
 template <int kPass>
 __device__ __forceinline__ uint32_t digit(uint32_t u) {
-  if constexpr (kPass == 0) return u >> 20;
-  else if constexpr (kPass == 1) return (u >> 9) & 0x7FFu;
-  else return u & 0x1FFu;
+  return (u >> kDigitShift[kPass]) & ((1u << kDigitBits[kPass]) - 1u);
 }
 
 // The higher digits of u, compared with the prefix of pass kPass.
 template <int kPass>
 __device__ __forceinline__ bool in_prefix(uint32_t u, uint32_t prefix) {
   if constexpr (kPass == 0) return true;
-  else if constexpr (kPass == 1) return (u >> 20) == prefix;
-  else return (u >> 9) == prefix;
+  else return (u >> kDigitShift[kPass - 1]) == prefix;
 }
 
 struct SelArgs {
@@ -51,8 +55,9 @@ struct SelArgs {
 
 template <int kPass>
 __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelArgs a) {
-  __shared__ uint32_t bins[kBins];
-  for (int i = threadIdx.x; i < kBins; i += kSelThreads) bins[i] = 0u;
+  constexpr int kN = 1 << kDigitBits[kPass];
+  __shared__ uint32_t bins[kN];
+  for (int i = threadIdx.x; i < kN; i += kSelThreads) bins[i] = 0u;
   __syncthreads();
   const uint32_t prefix = kPass == 0 ? 0u : a.state->prefix;
   const uint64_t vpr = (uint64_t)(a.cols / 4);  // float4 per row
@@ -67,7 +72,7 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelArgs a) {
       if (in_prefix<kPass>(u[i], prefix)) atomicAdd(&bins[digit<kPass>(u[i])], 1u);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < kBins; i += kSelThreads)
+  for (int i = threadIdx.x; i < kN; i += kSelThreads)
     if (bins[i]) atomicAdd(&a.hist[i], bins[i]);
 }
 
@@ -76,7 +81,7 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelArgs a) {
 // last pass the prefix is the whole pattern: store the value.
 template <int kPass>
 __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(SelectState *st, uint32_t *hist, uint64_t rank0) {
-  constexpr int kPer = kBins / kSelThreads;  // 8 bins per thread
+  constexpr int kPer = (1 << kDigitBits[kPass]) / kSelThreads;  // bins per thread
   __shared__ uint64_t part[kSelThreads];
   const uint64_t rank = kPass == 0 ? rank0 : st->rank;
   uint32_t c[kPer];
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(SelectState *s
       if (b < 0) below += c[i];
     }
     const uint32_t d = (uint32_t)(threadIdx.x * kPer + b);
-    const uint32_t prefix = kPass == 0 ? d : ((kPass == 1 ? (st->prefix << 11) : (st->prefix << 9)) | d);
+    const uint32_t prefix = kPass == 0 ? d : ((st->prefix << kDigitBits[kPass]) | d);
     st->prefix = prefix;
     st->rank = rank - below;
     if (kPass == 2) st->value = __uint_as_float(prefix);
