@@ -16,14 +16,16 @@ Order of work:
      launch stream; the mean is the kernel duration plus the launch gap), and
      isolated (one launch between events after a device synchronisation);
   2. W untimed warm-up steps, then exactly K timed steps bracketed by device
-     synchronisation, timed by the host clock;
+     synchronisation, timed by the host clock; then K more steps, untimed,
+     with an event pair around every call, for each call's duration inside
+     the step (`us_in_step`);
   3. the CPU oracle on the same step (the `cpu_baseline` leg), which also
      checks this run's outputs against the oracle.
 
 Prints one JSON line.  `value` is the whole-step NVFP4 GEMM throughput
 (2*M*N*K per step time, TFLOP/s; for the HBM-bound AdamW state codec, the
 step's algorithmic GB/s).  `roofline` describes the dominant kernel
-(the GEMM, or the attention-scores write) from its back-to-back duration:
+(the GEMM, or the attention-scores write) from its duration inside the step:
 achieved = algorithmic flops (or bytes) per launch / duration, against the
 dense FP16 MFMA peak (or HBM), with `traffic` the HBM bytes per launch from
 the committed rocprofv3 counter summary (null once the library sources have
@@ -200,6 +202,30 @@ def time_isolated(calls, reps: int) -> float:
     return float(np.median(ts))
 
 
+def time_in_step(steps, names, nsteps: int, start: int) -> dict:
+    """Mean microseconds of each call as it runs inside the step: `nsteps`
+    steps in the timed region's order, an event pair recorded around every
+    call on the launch stream (the events only add idle time between
+    calls, never inside one)."""
+    nbuf = len(steps)
+    pairs = []
+    for i in range(nsteps):
+        row = []
+        for c, name in zip(steps[(start + i) % nbuf], names):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            c()
+            e1.record()
+            row.append((name, e0, e1))
+        pairs.append(row)
+    torch.cuda.synchronize()
+    acc = {}
+    for row in pairs:
+        for name, e0, e1 in row:
+            acc.setdefault(name, []).append(e0.elapsed_time(e1) * 1e3)
+    return {k: float(np.mean(v)) for k, v in acc.items()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -261,8 +287,18 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
 
+    # 2b. the same steps once more (untimed), each call between two events:
+    #     the duration of every call inside the step, the dominant one's
+    #     roofline figure (a profiler's per-kernel mean over a run is this)
+    names = []
+    for c in steps[0]:
+        names.append(next(n for n, cs in S["calls"].items() if cs[0] is c))
+    in_step = time_in_step(steps, names, args.steps, args.warmup + args.steps)
+    for n, us in in_step.items():
+        kernels[n]["us_in_step"] = round(us, 2)
+
     dom = S["dominant"]
-    dom_us = kernels[dom]["us"]
+    dom_us = in_step.get(dom, kernels[dom]["us"])
     if S["bound"] == "mfma":
         achieved = S["flops"][dom] / (dom_us * 1e-6) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
@@ -347,6 +383,8 @@ def setup_linear_gemm(t, dev) -> dict:
             "bytes": {"quantize_xw": QUANT_BYTES_PER_ELEM * (M * K + N * K),
                       "quantize_x": QUANT_BYTES_PER_ELEM * M * K, "quantize_w": QUANT_BYTES_PER_ELEM * N * K},
             "dominant": "gemm", "bound": "mfma", "baseline": baseline,
+            "metric": METRIC if (M, N, K) == (8192, 3072, 3072) else
+            f"NVFP4 GEMM TFLOP/s + %MFMA peak; quantize GB/s + %HBM at {M}x{N}x{K}",
             "config": {"M": M, "N": N, "K": K, "x_dtype": "bf16", "y_dtype": "bf16", "rounding": "rne"}}
 
 
@@ -416,6 +454,7 @@ def setup_linear_train(t, dev) -> dict:
     return {"steps": [(c,) for c in calls], "calls": {"linear_fwd_bwd": calls}, "nbuf": nbuf,
             "flops": {"linear_fwd_bwd": flops}, "step_flops": flops, "bytes": {},
             "dominant": "linear_fwd_bwd", "bound": "mfma",
+            "metric": f"NVFP4 linear training step (Fprop + Dgrad + Wgrad) TFLOP/s at M={M} N={N} K={K}",
             "config": {"M": M, "N": N, "K": K, "x_dtype": "bf16", "y_dtype": "bf16",
                        "rounding": "rne fprop, sr dgrad, rht+sr wgrad"}}
 
@@ -443,6 +482,7 @@ def setup_attn(t, dev) -> dict:
             "bytes": {"quantize_q": QUANT_BYTES_PER_ELEM * q_cpu.numel(),
                       "quantize_k": QUANT_BYTES_PER_ELEM * k_cpu.numel(), "gemm": gemm_bytes},
             "dominant": "gemm", "bound": "hbm",
+            "metric": f"NVFP4 attention scores QK^T TFLOP/s + %HBM of the FP32 scores at {B}x{H}x{S_}x{S_}x{D}",
             "config": {"batch": B, "heads": H, "seq": S_, "head_dim": D, "x_dtype": "bf16", "y_dtype": "fp32",
                        "rounding": "rne", "alpha": t["alpha"]}}
 

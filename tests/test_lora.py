@@ -46,8 +46,9 @@ def _check(x, w_view, l1, l2, beta, y, ws, r, rows=None, what=""):
     return st, sy
 
 
-@pytest.mark.parametrize("M,N,K,r", [(16, 16, 16, 16), (48, 80, 32, 32), (160, 272, 96, 48), (512, 384, 1024, 64),
-                                     (300, 200, 256, 128), (33, 64, 128, 96)])
+@pytest.mark.parametrize("M,N,K,r", [(1, 1, 16, 16), (16, 16, 16, 16), (48, 80, 32, 32), (160, 272, 96, 48),
+                                     (512, 384, 1024, 64), (300, 200, 256, 128), (33, 64, 128, 96),
+                                     (1000, 520, 4096, 16)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_lora_forward_matches_oracle(M, N, K, r, out_dtype):
     x = _bf16((M, K), M + K, 2.0)
