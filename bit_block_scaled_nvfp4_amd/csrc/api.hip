@@ -590,10 +590,11 @@ NVFP4_EXPORT nvfp4_status nvfp4_linear_fwd_bwd(const void *x, const void *w, con
 namespace {
 
 // Workspace: three quantize control blocks, three select states (X, A, B)
-// and their shared 4096-counter histogram, the normalization partials, the second iterate
+// and their shared 4096-counter histogram and compact buffer, the normalization partials, the second iterate
 // buffer, A and B in FP32, and the four quantized views; 256-byte regions.
 struct NsLayout {
-  size_t ctrl[3], sel[3], hist, partial, inv, xbuf, a, b;
+  size_t ctrl[3], sel[3], hist, compact, partial, inv, xbuf, a, b;
+  uint64_t cap;  // keys the select's compact buffer holds
   size_t codes[4], scales[4], st[4];
   int64_t rows[4], cols[4];
   size_t total;
@@ -610,6 +611,10 @@ NsLayout ns_layout(int64_t m, int64_t n) {
   for (int i = 0; i < 3; ++i) L.ctrl[i] = take(sizeof(QuantCtrl));
   for (int i = 0; i < 3; ++i) L.sel[i] = take(sizeof(nvfp4::SelectState));
   L.hist = take(4096 * sizeof(uint32_t));
+  // the select's bracket copy: a sixteenth of the larger operand (the
+  // bracket holds about 1.6% of it; more falls back to the full passes)
+  L.cap = ((uint64_t)m * (uint64_t)(n > m ? n : m)) / 16 + 1024;
+  L.compact = take(L.cap * sizeof(uint32_t));
   L.partial = take(1024 * sizeof(double));
   L.inv = take(sizeof(float));
   L.xbuf = take((size_t)m * (size_t)n * 4);
@@ -699,6 +704,7 @@ NVFP4_EXPORT nvfp4_status nvfp4_ns_orthogonalize(const void *g, int32_t g_dtype,
   float *B = reinterpret_cast<float *>(base + L.b);
   auto sel = [&](int i) { return reinterpret_cast<nvfp4::SelectState *>(base + L.sel[i]); };
   uint32_t *hist = reinterpret_cast<uint32_t *>(base + L.hist);
+  uint32_t *compact = reinterpret_cast<uint32_t *>(base + L.compact);
   const nvfp4_qtensor vX = ns_view(base, L, 0), vXT = ns_view(base, L, 1), vA = ns_view(base, L, 2),
                       vB = ns_view(base, L, 3);
   // The iterates alternate so that the last one lands in x.
@@ -721,7 +727,7 @@ NVFP4_EXPORT nvfp4_status nvfp4_ns_orthogonalize(const void *g, int32_t g_dtype,
     const float *clip_x = nullptr;
     if (cfg->clip_mask & 1u) {
       r = nvfp4::launch_abs_select(Xc, m, n, ldc_, quantile_rank(cfg->clip_quantile, (uint64_t)(m * n)), sel(0),
-                                   hist, s);
+                                   hist, compact, L.cap, s);
       if (r != NVFP4_OK) return r;
       clip_x = &sel(0)->value;
     }
@@ -735,7 +741,7 @@ NVFP4_EXPORT nvfp4_status nvfp4_ns_orthogonalize(const void *g, int32_t g_dtype,
     if (r != NVFP4_OK) return r;
     const float *clip_a = nullptr;
     if (cfg->clip_mask & 2u) {
-      r = nvfp4::launch_abs_select(A, m, m, m, quantile_rank(cfg->clip_quantile, (uint64_t)(m * m)), sel(1), hist, s);
+      r = nvfp4::launch_abs_select(A, m, m, m, quantile_rank(cfg->clip_quantile, (uint64_t)(m * m)), sel(1), hist, compact, L.cap, s);
       if (r != NVFP4_OK) return r;
       clip_a = &sel(1)->value;
     }
@@ -753,7 +759,7 @@ NVFP4_EXPORT nvfp4_status nvfp4_ns_orthogonalize(const void *g, int32_t g_dtype,
     if (r != NVFP4_OK) return r;
     const float *clip_b = nullptr;
     if (cfg->clip_mask & 4u) {
-      r = nvfp4::launch_abs_select(B, m, m, m, quantile_rank(cfg->clip_quantile, (uint64_t)(m * m)), sel(2), hist, s);
+      r = nvfp4::launch_abs_select(B, m, m, m, quantile_rank(cfg->clip_quantile, (uint64_t)(m * m)), sel(2), hist, compact, L.cap, s);
       if (r != NVFP4_OK) return r;
       clip_b = &sel(2)->value;
     }

@@ -102,9 +102,19 @@ struct SelectState {
   uint32_t prefix;
   float value;
   uint64_t rank;
+  // the sampled bracket (see root.hip)
+  uint32_t lo, hi;         // keys bracketing the rank, from a sorted sample
+  uint32_t mode;           // 1: the bracket pass ran (its copy is used if it holds the rank); 0: it did not
+  uint32_t overflow;       // the bracket held more keys than the compact buffer
+  unsigned long long below;  // keys < lo
+  uint32_t count;          // keys in [lo, hi], copied to the compact buffer
+  uint32_t pad;
+  uint64_t rank0;          // the target rank among all the keys
 };
+// `compact` holds `cap` keys (the bracket's copy).
 nvfp4_status launch_abs_select(const float *x, int64_t rows, int64_t cols, int64_t ld, uint64_t rank,
-                               SelectState *state, uint32_t *hist, hipStream_t stream);
+                               SelectState *state, uint32_t *hist, uint32_t *compact, uint64_t cap,
+                               hipStream_t stream);
 // x = g / (||g||_F + 1e-7), with the norm from FP64 sums over 1024 fixed
 // partials (partial: 1024 doubles) and *inv = fl32(1 / (||g|| + 1e-7)).
 nvfp4_status launch_frobenius_normalize(const void *g, bool bf16, int64_t rows, int64_t cols, int64_t ld,

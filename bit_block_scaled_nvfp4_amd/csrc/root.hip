@@ -15,6 +15,17 @@
 // order of the atomics.  The first digit is the widest: every element
 // counts in that pass, and real data crowd into a few exponents, whose bins
 // the LDS atomics then serialize on.
+//
+// Sampled bracket.  Before the digit passes, one workgroup sorts 1024 keys
+// sampled at evenly spaced positions and takes the keys 24 sample ranks
+// either side of the target's sample rank as a bracket [lo, hi]; one pass
+// over the tensor counts the keys below lo and copies the keys inside the
+// bracket to a compact buffer (about 5% of them), staged per workgroup in
+// LDS so that each workgroup reserves its space with one atomic.  If the target rank falls inside the bracket, the digit passes
+// run over the compact copy for the rank relative to it; otherwise (a
+// bracket that missed, or more keys than the buffer holds) they run over
+// the tensor as before.  Either way the result is the exact order
+// statistic; the sample only decides how much the digit passes read.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -51,7 +62,148 @@ struct SelArgs {
   int64_t rows, cols, ld;   // [rows][cols], row stride ld; cols % 4 == 0, ld % 4 == 0
   SelectState *state;
   uint32_t *hist;           // kBins counters, zero on entry
+  uint32_t *compact;        // the bracket's keys
+  uint64_t cap;             // capacity of `compact`
 };
+
+constexpr int kSampleThreads = 512;
+constexpr int kSamples = 1024;   // sorted in LDS by one workgroup
+constexpr int kMargin = 24;      // sample ranks either side of the target's (7.5 standard deviations at p99)
+
+// Element (flat index i of [rows][cols]) as its key.
+__device__ __forceinline__ uint32_t key_at(const SelArgs &a, uint64_t i) {
+  const uint64_t r = i / (uint64_t)a.cols, c = i - r * (uint64_t)a.cols;
+  return abs_u(a.x[r * a.ld + c]);
+}
+
+__global__ __launch_bounds__(kSampleThreads) void select_sample_kernel(SelArgs a, uint64_t rank) {
+  __shared__ uint32_t k[kSamples];
+  SelectState *st = a.state;
+  const uint64_t n = (uint64_t)a.rows * (uint64_t)a.cols;
+  for (int i = threadIdx.x; i < kSamples; i += kSampleThreads) k[i] = key_at(a, (uint64_t)i * n / kSamples);
+  __syncthreads();
+  // bitonic sort, ascending: at each stage every thread takes whole
+  // compare-exchange pairs (i, i + stride)
+  for (int size = 2; size <= kSamples; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int p = threadIdx.x; p < kSamples / 2; p += kSampleThreads) {
+        const int i = ((p & ~(stride - 1)) << 1) | (p & (stride - 1)), j = i + stride;  // stride: a power of 2
+        const uint32_t x = k[i], y = k[j];
+        const bool up = (i & size) == 0;
+        if ((x > y) == up) {
+          k[i] = y;
+          k[j] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (threadIdx.x == 0) {
+    const int64_t ks = (int64_t)(rank * kSamples / n);
+    st->lo = ks - kMargin <= 0 ? 0u : k[ks - kMargin];
+    st->hi = ks + kMargin >= kSamples - 1 ? 0xFFFFFFFFu : k[ks + kMargin];
+    st->below = 0ull;
+    st->count = 0u;
+    st->overflow = 0u;
+    st->rank0 = rank;
+    st->mode = 1u;
+  }
+}
+
+// One pass over the tensor: keys below the bracket counted, keys inside it
+// copied out.  One workgroup per CU (few global atomics on the two shared
+// counters, whose same-address updates serialize), four 16-byte loads per
+// thread in flight per round.  A workgroup stages its bracket keys in LDS
+// (an LDS atomic per key; they are about 2% of the keys) and at the end
+// reserves their place in the compact buffer with one global atomic; keys
+// beyond the staging space go straight out, one global atomic each.
+constexpr int kBracketThreads = 1024;
+constexpr int kBracketUnroll = 4;
+constexpr int kBracketKeys = 8192;
+
+__global__ __launch_bounds__(kBracketThreads) void select_bracket_kernel(SelArgs a) {
+  __shared__ uint32_t lbuf[kBracketKeys];
+  __shared__ uint32_t lcount, gbase;
+  __shared__ unsigned long long red[kBracketThreads / 64];
+  SelectState *st = a.state;
+  if (threadIdx.x == 0) lcount = 0u;
+  __syncthreads();
+  const uint32_t lo = st->lo, hi = st->hi;
+  const uint64_t vpr = (uint64_t)(a.cols / 4);
+  const uint64_t nvec = (uint64_t)a.rows * vpr;
+  const uint64_t stride = (uint64_t)gridDim.x * kBracketThreads;
+  uint32_t below = 0;
+  for (uint64_t v0 = (uint64_t)blockIdx.x * kBracketThreads + threadIdx.x; v0 < nvec;
+       v0 += kBracketUnroll * stride) {
+    float4 q[kBracketUnroll];
+#pragma unroll
+    for (int t = 0; t < kBracketUnroll; ++t) {
+      // past the end: a clamped (in-bounds) load, masked below
+      const uint64_t v = min(v0 + t * stride, nvec - 1);
+      const uint64_t r = v / vpr, c4 = v - r * vpr;
+      q[t] = *reinterpret_cast<const float4 *>(a.x + r * a.ld + 4 * c4);
+    }
+#pragma unroll
+    for (int t = 0; t < kBracketUnroll; ++t) {
+      if (v0 + t * stride >= nvec) break;
+      const uint32_t u[4] = {abs_u(q[t].x), abs_u(q[t].y), abs_u(q[t].z), abs_u(q[t].w)};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        below += u[i] < lo ? 1u : 0u;
+        if (u[i] >= lo && u[i] <= hi) {
+          const uint32_t slot = atomicAdd(&lcount, 1u);
+          if (slot < kBracketKeys) {
+            lbuf[slot] = u[i];
+          } else {
+            const uint32_t pos = atomicAdd(&st->count, 1u);
+            if (pos < a.cap) a.compact[pos] = u[i];
+            else st->overflow = 1u;
+          }
+        }
+      }
+    }
+  }
+  // the workgroup's count below the bracket: one atomic
+  unsigned long long b = below;
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) b += __shfl_xor(b, d, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = b;
+  __syncthreads();
+  const uint32_t nl = min(lcount, (uint32_t)kBracketKeys);
+  if (threadIdx.x == 0) {
+    unsigned long long t = 0;
+    for (int w = 0; w < kBracketThreads / 64; ++w) t += red[w];
+    atomicAdd(&st->below, t);
+    gbase = nl ? atomicAdd(&st->count, nl) : 0u;
+  }
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < nl; i += kBracketThreads) {
+    const uint64_t pos = (uint64_t)gbase + i;
+    if (pos < a.cap) a.compact[pos] = lbuf[i];
+    else st->overflow = 1u;
+  }
+}
+
+// The digit passes run over the bracket's compact copy if it was taken, did
+// not overflow and holds the target rank; else over the tensor.  Every
+// reader decides from the counters the bracket pass left, so no workgroup
+// has to publish the decision.
+__device__ __forceinline__ bool compact_hit(const SelectState *st) {
+  const uint64_t k = st->rank0, b = st->below;
+  return st->mode == 1u && !st->overflow && k >= b && k - b < st->count;
+}
+
+// The rank the first digit pass looks for: inside the compact copy, the
+// keys below the bracket are already counted.
+__device__ __forceinline__ uint64_t first_rank(const SelectState *st) {
+  return compact_hit(st) ? st->rank0 - st->below : st->rank0;
+}
+
+// Small tensors skip the bracket: the digit passes run over the tensor.
+__global__ void select_full_kernel(SelectState *st, uint64_t rank) {
+  st->mode = 0u;
+  st->rank0 = rank;
+}
 
 template <int kPass>
 __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelArgs a) {
@@ -60,30 +212,39 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelArgs a) {
   for (int i = threadIdx.x; i < kN; i += kSelThreads) bins[i] = 0u;
   __syncthreads();
   const uint32_t prefix = kPass == 0 ? 0u : a.state->prefix;
-  const uint64_t vpr = (uint64_t)(a.cols / 4);  // float4 per row
-  const uint64_t nvec = (uint64_t)a.rows * vpr;
-  for (uint64_t v = (uint64_t)blockIdx.x * kSelThreads + threadIdx.x; v < nvec;
-       v += (uint64_t)gridDim.x * kSelThreads) {
-    const uint64_t r = v / vpr, c4 = v - r * vpr;
-    const float4 q = *reinterpret_cast<const float4 *>(a.x + r * a.ld + 4 * c4);
-    const uint32_t u[4] = {abs_u(q.x), abs_u(q.y), abs_u(q.z), abs_u(q.w)};
+  if (compact_hit(a.state)) {
+    // the bracket's compact copy: keys already
+    const uint32_t n = a.state->count;
+    for (uint32_t i = blockIdx.x * kSelThreads + threadIdx.x; i < n; i += gridDim.x * kSelThreads) {
+      const uint32_t u = a.compact[i];
+      if (in_prefix<kPass>(u, prefix)) atomicAdd(&bins[digit<kPass>(u)], 1u);
+    }
+  } else {
+    const uint64_t vpr = (uint64_t)(a.cols / 4);  // float4 per row
+    const uint64_t nvec = (uint64_t)a.rows * vpr;
+    for (uint64_t v = (uint64_t)blockIdx.x * kSelThreads + threadIdx.x; v < nvec;
+         v += (uint64_t)gridDim.x * kSelThreads) {
+      const uint64_t r = v / vpr, c4 = v - r * vpr;
+      const float4 q = *reinterpret_cast<const float4 *>(a.x + r * a.ld + 4 * c4);
+      const uint32_t u[4] = {abs_u(q.x), abs_u(q.y), abs_u(q.z), abs_u(q.w)};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (in_prefix<kPass>(u[i], prefix)) atomicAdd(&bins[digit<kPass>(u[i])], 1u);
+      for (int i = 0; i < 4; ++i)
+        if (in_prefix<kPass>(u[i], prefix)) atomicAdd(&bins[digit<kPass>(u[i])], 1u);
+    }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < kN; i += kSelThreads)
     if (bins[i]) atomicAdd(&a.hist[i], bins[i]);
 }
 
-// One workgroup: find the bin holding rank `rank` (0-based, ascending) among
+// One workgroup: find the bin holding the rank (0-based, ascending) among
 // this pass's elements, narrow the prefix, and clear the histogram.  On the
 // last pass the prefix is the whole pattern: store the value.
 template <int kPass>
-__global__ __launch_bounds__(kSelThreads) void select_scan_kernel(SelectState *st, uint32_t *hist, uint64_t rank0) {
-  constexpr int kPer = (1 << kDigitBits[kPass]) / kSelThreads;  // bins per thread
+__global__ __launch_bounds__(kSelThreads) void select_scan_kernel(SelectState *st, uint32_t *hist) {
   __shared__ uint64_t part[kSelThreads];
-  const uint64_t rank = kPass == 0 ? rank0 : st->rank;
+  constexpr int kPer = (1 << kDigitBits[kPass]) / kSelThreads;  // bins per thread
+  const uint64_t rank = kPass == 0 ? first_rank(st) : st->rank;
   uint32_t c[kPer];
   uint64_t sum = 0;
 #pragma unroll
@@ -199,16 +360,29 @@ int stride_grid(uint64_t nvec, uint64_t cap) {
 }  // namespace
 
 nvfp4_status launch_abs_select(const float *x, int64_t rows, int64_t cols, int64_t ld, uint64_t rank,
-                               SelectState *state, uint32_t *hist, hipStream_t s) {
+                               SelectState *state, uint32_t *hist, uint32_t *compact, uint64_t cap,
+                               hipStream_t s) {
   if (rows <= 0 || cols <= 0) return NVFP4_EINVAL;
-  SelArgs a{x, rows, cols, ld, state, hist};
-  const int g = stride_grid((uint64_t)rows * (uint64_t)(cols / 4), 2048);
-  hipLaunchKernelGGL(select_hist_kernel<0>, dim3(g), dim3(kSelThreads), 0, s, a);
-  hipLaunchKernelGGL(select_scan_kernel<0>, dim3(1), dim3(kSelThreads), 0, s, state, hist, rank);
-  hipLaunchKernelGGL(select_hist_kernel<1>, dim3(g), dim3(kSelThreads), 0, s, a);
-  hipLaunchKernelGGL(select_scan_kernel<1>, dim3(1), dim3(kSelThreads), 0, s, state, hist, rank);
-  hipLaunchKernelGGL(select_hist_kernel<2>, dim3(g), dim3(kSelThreads), 0, s, a);
-  hipLaunchKernelGGL(select_scan_kernel<2>, dim3(1), dim3(kSelThreads), 0, s, state, hist, rank);
+  SelArgs a{x, rows, cols, ld, state, hist, compact, cap};
+  const uint64_t n = (uint64_t)rows * (uint64_t)cols;
+  const int g = stride_grid(n / 4, 2048);
+  // With the bracket the digit passes read a few percent of the keys: fewer
+  // workgroups (each clears and flushes a whole histogram); if the bracket
+  // misses they cover the tensor with the same grid, only slower.
+  int gh = g;
+  if (n >= 32ull * kSamples && compact && cap > 0) {
+    hipLaunchKernelGGL(select_sample_kernel, dim3(1), dim3(kSampleThreads), 0, s, a, rank);
+    hipLaunchKernelGGL(select_bracket_kernel, dim3(256), dim3(kBracketThreads), 0, s, a);
+    gh = g < 256 ? g : 256;
+  } else {
+    hipLaunchKernelGGL(select_full_kernel, dim3(1), dim3(1), 0, s, state, rank);
+  }
+  hipLaunchKernelGGL(select_hist_kernel<0>, dim3(gh), dim3(kSelThreads), 0, s, a);
+  hipLaunchKernelGGL(select_scan_kernel<0>, dim3(1), dim3(kSelThreads), 0, s, state, hist);
+  hipLaunchKernelGGL(select_hist_kernel<1>, dim3(gh), dim3(kSelThreads), 0, s, a);
+  hipLaunchKernelGGL(select_scan_kernel<1>, dim3(1), dim3(kSelThreads), 0, s, state, hist);
+  hipLaunchKernelGGL(select_hist_kernel<2>, dim3(gh), dim3(kSelThreads), 0, s, a);
+  hipLaunchKernelGGL(select_scan_kernel<2>, dim3(1), dim3(kSelThreads), 0, s, state, hist);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 

@@ -98,7 +98,7 @@ def check_last_step(g, m, n, coeffs, q, mask, ws, x_out, rows=None, what=""):
     return X
 
 
-@pytest.mark.parametrize("m,n", [(16, 16), (32, 48), (48, 160), (128, 384), (272, 400)])
+@pytest.mark.parametrize("m,n", [(16, 16), (32, 48), (48, 160), (128, 384), (272, 400), (384, 512)])
 @pytest.mark.parametrize("mask", [0, 1, 7])
 def test_ns_steps_match_oracle(m, n, mask):
     g = torch.from_numpy(_f32((m, n), m * n + mask, 1e-2)).to(torch.bfloat16)
@@ -143,3 +143,41 @@ def test_ns_full_size():
     sv = np.linalg.svd(X[:512].astype(np.float64), compute_uv=False)
     print(f"\nparity ns_3b: step 5 checked on {rows.size} rows; singular values of 512 rows in "
           f"[{sv.min():.3f}, {sv.max():.3f}]", flush=True)
+
+
+def _ns_clip_value(g: torch.Tensor, q: float):
+    m, n = g.shape
+    ws = nv.new_workspace(nv.nvfp4_ns_workspace_size(m, n), DEV)
+    nv.ns_orthogonalize(g.to(DEV), [(1.5, -0.5, 0.0)], q, 1, workspace=ws)
+    torch.cuda.synchronize()
+    st = nv.ns_internals(ws, m, n)
+    return st["clip"][0].item(), st["x_prev"].cpu().numpy()
+
+
+@pytest.mark.parametrize("q", [1e-7, 0.5, 0.99, 0.9999, 1.0])
+def test_clip_value_through_the_sampled_bracket(q):
+    """384 x 512 (above the size where the select samples a bracket first):
+    the clip value equals the oracle's order statistic for quantiles at both
+    ends (brackets open below or above) and in between."""
+    rng = np.random.default_rng(int(q * 1e6))
+    g = torch.from_numpy((rng.standard_t(3, size=(384, 512)) * 1e-2).astype(np.float32))
+    got, x0 = _ns_clip_value(g, q)
+    assert got == O.abs_quantile(x0, q), q
+
+
+def test_clip_value_when_the_bracket_misses_or_overflows():
+    m, n = 384, 512
+    N = m * n
+    # every sampled position holds 0, every other element is large: the
+    # sample's bracket holds only zeros and misses the rank
+    rng = np.random.default_rng(12)
+    g = (rng.uniform(1.0, 2.0, size=N)).astype(np.float32)
+    g[(np.arange(8192, dtype=np.int64) * N) // 8192] = 0.0
+    g = torch.from_numpy(g.reshape(m, n))
+    got, x0 = _ns_clip_value(g, 0.99)
+    assert got == O.abs_quantile(x0, 0.99)
+    # nearly constant: the bracket holds more keys than the compact buffer
+    g = np.full((m, n), 0.25, np.float32)
+    g[0, :7] = [1, 2, 3, 4, 5, 6, 7]
+    got, x0 = _ns_clip_value(torch.from_numpy(g), 0.99)
+    assert got == O.abs_quantile(x0, 0.99)
