@@ -63,7 +63,7 @@ class QAdamWStateC(ctypes.Structure):
 
 
 class NsCfgC(ctypes.Structure):
-    _fields_ = [("clip_quantile", ctypes.c_double), ("clip_mask", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+    _fields_ = [("clip_quantile", ctypes.c_double), ("clip_mask", ctypes.c_uint32), ("product", ctypes.c_uint32)]
 
 
 class NsStateC(ctypes.Structure):
@@ -723,7 +723,7 @@ def gemm_axpby(a: QTensor, b: QTensor, c_in: torch.Tensor, beta: float, alpha: f
 NS_VIEWS = ("X", "X^T", "A", "B")
 
 
-def _ns_args(g, coeffs, clip_quantile, clip_mask, out, workspace):
+def _ns_args(g, coeffs, clip_quantile, clip_mask, out, workspace, product=0):
     if g.dim() != 2 or g.dtype not in (torch.float32, torch.bfloat16) or (g.size(1) > 1 and g.stride(1) != 1):
         raise ValueError("g must be a 2-D float32 or bfloat16 tensor with contiguous rows")
     m, n = g.shape
@@ -732,7 +732,7 @@ def _ns_args(g, coeffs, clip_quantile, clip_mask, out, workspace):
         out = torch.empty(m, n, dtype=torch.float32, device=g.device)
     if workspace is None:
         workspace = new_workspace(nvfp4_ns_workspace_size(m, n), g.device)
-    cfg = NsCfgC(clip_quantile, clip_mask, 0)
+    cfg = NsCfgC(clip_quantile, clip_mask, product)
     args = (g.data_ptr(), BF16 if g.dtype == torch.bfloat16 else F32, m, n, g.stride(0) if m > 1 else n,
             co.ctypes.data, co.shape[0], ctypes.byref(cfg), out.data_ptr(), out.stride(0) if m > 1 else n,
             workspace.data_ptr(), workspace.numel(), _stream(g.device))
@@ -740,10 +740,12 @@ def _ns_args(g, coeffs, clip_quantile, clip_mask, out, workspace):
 
 
 def ns_orthogonalize(g: torch.Tensor, coeffs, clip_quantile: float = 0.99, clip_mask: int = 1,
-                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                     product: int = 0) -> torch.Tensor:
     """Newton-Schulz orthogonalization of g [m][n] with every product in NVFP4;
-    coeffs is a sequence of (a, b, c) per step."""
-    args, _keep, out = _ns_args(g, coeffs, clip_quantile, clip_mask, out, workspace)
+    coeffs is a sequence of (a, b, c) per step.  product: how B^ X^ is
+    launched (0 automatic, 1 as [m][n], 2 as its transpose)."""
+    args, _keep, out = _ns_args(g, coeffs, clip_quantile, clip_mask, out, workspace, product)
     _check(lib().nvfp4_ns_orthogonalize(*args), "nvfp4_ns_orthogonalize")
     return out
 

@@ -688,7 +688,7 @@ NVFP4_EXPORT nvfp4_status nvfp4_ns_orthogonalize(const void *g, int32_t g_dtype,
   if (!g || !x || !cfg || (steps > 0 && !coeffs)) return NVFP4_EINVAL;
   if (g_dtype != NVFP4_F32 && g_dtype != NVFP4_BF16) return NVFP4_EINVAL;
   if (steps < 0 || steps > 64) return NVFP4_EINVAL;
-  if (cfg->clip_mask > 7u || cfg->reserved != 0) return NVFP4_EINVAL;
+  if (cfg->clip_mask > 7u || cfg->product > 2u) return NVFP4_EINVAL;
   if (cfg->clip_mask && !(cfg->clip_quantile > 0.0 && cfg->clip_quantile <= 1.0)) return NVFP4_EINVAL;
   if (!ns_shape_ok(m, n)) return NVFP4_ESHAPE;
   if (ldg < n || ldx < n) return NVFP4_ESHAPE;
@@ -719,6 +719,8 @@ NVFP4_EXPORT nvfp4_status nvfp4_ns_orthogonalize(const void *g, int32_t g_dtype,
                                                      reinterpret_cast<float *>(base + L.inv), P[0], ldp[0], s);
   if (r != NVFP4_OK) return r;
   const nvfp4_quant_opts rne{NVFP4_RNE, 0, 0, 0, 0u, 0u};
+  const bool transposed = cfg->product == 2u || (cfg->product == 0u && nvfp4::gemm_tile_cost(n, m, m, 1) <
+                                                                            nvfp4::gemm_tile_cost(m, n, m, 1));
   for (int k = 0; k < steps; ++k) {
     float *Xc = P[k % 2], *Xn = P[(k + 1) % 2];
     const int64_t ldc_ = ldp[k % 2], ldn = ldp[(k + 1) % 2];
@@ -767,8 +769,13 @@ NVFP4_EXPORT nvfp4_status nvfp4_ns_orthogonalize(const void *g, int32_t g_dtype,
     qb.clip = clip_b;
     r = nvfp4::launch_quantize(qb, s);
     if (r != NVFP4_OK) return r;
-    // X' = B X + a X
+    // X' = B X + a X, or its transpose X^T B^T + a X^T stored transposed
+    // (the same products and sums, so the same values).
     nvfp4::GemmProblem px = make_gemm(&vB, &vXT, Xn, NVFP4_F32, ldn, m * ldn, 1.0f);
+    if (transposed) {
+      px = make_gemm(&vXT, &vB, Xn, NVFP4_F32, ldn, m * ldn, 1.0f);
+      px.c_transposed = true;
+    }
     px.cin = Xc;
     px.ldcin = ldc_;
     px.bstride_cin = m * ldc_;

@@ -97,6 +97,9 @@ struct GemmArgs {
   const uint16_t *lr_t, *lr_l2;
   int64_t lr_r;
   float lr_beta;
+  bool ct;      // C stored transposed: tile element (r, c) at c * ldc + r (FP32)
+  bool staged;  // FP32 output with an addend or transposed, C and cin 16-byte aligned
+                // with strides multiples of 4: full tiles go through the LDS patch
 };
 
 // LDS stage: codes [rows][64 B] and scales [rows][8 B] per operand.
@@ -499,9 +502,14 @@ __device__ __forceinline__ void lowrank_init(floatx16 (&acc)[kFragM][kFragN], co
     for (int j = 0; j < kFragN; ++j) acc[i][j] = acc[i][j] * q;
 }
 
+// Transposed epilogue staging: one 32 x 32 fragment per wave at a time, rows
+// of 36 floats (16-byte aligned float4 columns, rows spread over the banks).
+constexpr int kTPitch = 36;
+constexpr int kTPatchBytes = 32 * kTPitch * 4;
+
 template <int kFragN, bool kBF16Out>
 __device__ __forceinline__ void store_tile(const floatx16 (&acc)[kFragM][kFragN], const GemmArgs &g, int64_t batch,
-                                           int64_t wrow0, int64_t wcol0) {
+                                           int64_t wrow0, int64_t wcol0, float *tpatch) {
   using OutT = typename std::conditional<kBF16Out, uint16_t, float>::type;
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5, r32 = lane & 31;
@@ -510,6 +518,86 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[kFragM][kFragN]
   const int64_t row0 = wrow0 + 4 * h;
   const int64_t col0 = wcol0 + r32;
   const bool full = wrow0 + 128 <= g.M && wcol0 + 32 * kFragN <= g.N;
+  if constexpr (!kBF16Out) {
+    if (g.staged && full) {
+      // Through this wave's LDS patch, one 32 x 32 fragment at a time: the
+      // fragment goes in (as its transpose when C is stored transposed) and
+      // is read back by output rows, so the addend loads and the stores are
+      // 16 bytes per lane, 128-byte row segments (8 rows of 32 floats per
+      // instruction).  A fragment's addends are all loaded before its
+      // exchange, so their latency overlaps it; each lane reads exactly the
+      // addends of the elements it stores, so c may be the output itself.
+      // Only this wave uses the patch and its LDS accesses run in order; the
+      // fences keep the compiler from moving them across each other.
+      // y = fl(fl(acc * s) + fl(beta * c)) as below.
+      const float *ci_ptr = g.cin ? g.cin + batch * g.bstride_cin : nullptr;
+      const int prow = lane >> 3, pcol = 4 * (lane & 7);
+#pragma unroll
+      for (int i = 0; i < kFragM; ++i) {
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j) {
+          // the lane's first output element of this fragment
+          const int64_t orow = g.ct ? wcol0 + 32 * j + prow : wrow0 + 32 * i + prow;
+          const int64_t ocol = g.ct ? wrow0 + 32 * i + pcol : wcol0 + 32 * j + pcol;
+          float4 cv[4];
+          if (ci_ptr) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) cv[p] = *reinterpret_cast<const float4 *>(ci_ptr + (orow + 8 * p) * g.ldcin + ocol);
+          }
+          if (g.ct) {
+            // accumulator rows 8q + 4h + t (t = 0..3) of column r32 -> patch row r32
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<float4 *>(tpatch + r32 * kTPitch + 8 * q + 4 * h) =
+                  make_float4(acc[i][j][4 * q] * sc, acc[i][j][4 * q + 1] * sc, acc[i][j][4 * q + 2] * sc,
+                              acc[i][j][4 * q + 3] * sc);
+          } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) tpatch[(8 * (v >> 2) + 4 * h + (v & 3)) * kTPitch + r32] = acc[i][j][v] * sc;
+          }
+          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            float4 y = *reinterpret_cast<const float4 *>(tpatch + (prow + 8 * p) * kTPitch + pcol);
+            if (ci_ptr) {
+              y.x += g.beta * cv[p].x;
+              y.y += g.beta * cv[p].y;
+              y.z += g.beta * cv[p].z;
+              y.w += g.beta * cv[p].w;
+            }
+            *reinterpret_cast<float4 *>(cb_ptr + (orow + 8 * p) * g.ldc + ocol) = y;
+          }
+          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        }
+      }
+      return;
+    }
+    if (g.ct) {
+      // Transposed store of a partial tile, element by element (element
+      // (r, c) at c * ldc + r); y = fl(fl(acc * s) + fl(beta * c)) as below.
+      const float *ci_ptr = g.cin ? g.cin + batch * g.bstride_cin : nullptr;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int i = 0; i < kFragM; ++i) {
+          const int64_t r = row0 + 8 * q + 32 * i;
+#pragma unroll
+          for (int j = 0; j < kFragN; ++j) {
+            const int64_t col = col0 + 32 * j;
+            if (col >= g.N) continue;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              if (r + t >= g.M) continue;
+              float y = acc[i][j][4 * q + t] * sc;
+              if (ci_ptr) y += g.beta * ci_ptr[col * g.ldcin + r + t];
+              cb_ptr[col * g.ldc + r + t] = y;
+            }
+          }
+        }
+      }
+      return;
+    }
+  }
   if (g.cin) {
     // y = fl(fl(acc * s) + fl(beta * c)): each element is read and written
     // by the same lane, so c may be the output itself.  The addends of one
@@ -734,7 +822,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
     }
   }
 
-  store_tile<kFragN, kBF16Out>(acc, g, batch, m0 + wm * 128, n0 + wn * (32 * kFragN));
+  // The stages are free (the loop ends with a barrier): the staged epilogue
+  // (an addend, or C transposed) uses them.
+  static_assert(4 * kTPatchBytes <= sizeof(Stage<kBN>), "transpose patches fit a stage");
+  store_tile<kFragN, kBF16Out>(acc, g, batch, m0 + wm * 128, n0 + wn * (32 * kFragN),
+                               reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(&st0) + wave * kTPatchBytes));
 }
 
 // ---------------------------------------------------------------------------
@@ -1023,7 +1115,12 @@ __global__ __launch_bounds__(kW8Threads) void gemm_nvfp4_w8_kernel(GemmArgs g) {
     if (kt + 2 < ksteps) w8_step<kWM, kWN>(&st2, &st1, ld, c, kt + 2, ksteps, acc);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the refills issued past the last step
-  store_tile<3, kBF16Out>(acc, g, batch, m0 + wm * 128, n0 + wn * 96);
+  // The staged epilogue (an addend, or C transposed) uses st0 once every
+  // wave is done with the stages.
+  static_assert(8 * kTPatchBytes <= sizeof(W8Stage<kBM, kBN>), "transpose patches fit a stage");
+  if (g.staged) __syncthreads();
+  store_tile<3, kBF16Out>(acc, g, batch, m0 + wm * 128, n0 + wn * 96,
+                          reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(&st0) + wave * kTPatchBytes));
 }
 
 template <int kFragN>
@@ -1067,7 +1164,15 @@ hipError_t launch_w8(const GemmArgs &g, int64_t batch, bool bf16, hipStream_t s)
 struct TilePick {
   int kind;  // 4-wavefront kFragN (4, 3, 2), or 8-wavefront: 10 (512 x 192), 11 (256 x 384)
   int bm, bn;
+  double cost;  // rounds of 256 tiles x tile area x the kernel's relative cost per element
 };
+
+// The 8-wavefront kernels need K % BK == 0; their loads use 32-bit offsets
+// within an operand and 24-bit row and row-size factors.
+bool w8_applies(int64_t M, int64_t N, int64_t K) {
+  return K % BK == 0 && M * (K / 2) < ((int64_t)1 << 31) && N * (K / 2) < ((int64_t)1 << 31) && M < (1 << 24) &&
+         N < (1 << 24) && K / 2 < (1 << 24);
+}
 
 TilePick pick_tiles(int64_t M, int64_t N, int64_t batch, bool fast, int force_bm, int force_bn, bool lowrank) {
   struct Cand {
@@ -1078,7 +1183,7 @@ TilePick pick_tiles(int64_t M, int64_t N, int64_t batch, bool fast, int force_bm
   const Cand cands[5] = {{10, 512, 192, 0.96, true}, {11, 256, 384, 0.96, true},
                          {4, 256, 256, 1.0, false},  {3, 256, 192, 1.02, false}, {2, 256, 128, 1.12, false}};
   double best = 1e300;
-  TilePick pick{4, 256, 256};
+  TilePick pick{4, 256, 256, 0.0};
   for (const Cand &c : cands) {
     if (c.need_fast && !fast) continue;
     if (lowrank && c.kind == 4) continue;
@@ -1086,21 +1191,25 @@ TilePick pick_tiles(int64_t M, int64_t N, int64_t batch, bool fast, int force_bm
     const double t = (double)((tiles + 255) / 256) * c.bm * c.bn * c.cost;
     if (t < best - 1e-9) {
       best = t;
-      pick = TilePick{c.kind, c.bm, c.bn};
+      pick = TilePick{c.kind, c.bm, c.bn, t};
     }
   }
   // A requested tile (tuning and tests) replaces the choice where its
   // kernel applies; otherwise the request is refused.
   if (force_bm != 0 || force_bn != 0) {
-    pick = TilePick{-1, 0, 0};
+    pick = TilePick{-1, 0, 0, 0.0};
     for (const Cand &c : cands)
       if (c.bm == force_bm && c.bn == force_bn && (fast || !c.need_fast) && !(lowrank && c.kind == 4))
-        pick = TilePick{c.kind, c.bm, c.bn};
+        pick = TilePick{c.kind, c.bm, c.bn, 0.0};
   }
   return pick;
 }
 
 }  // namespace
+
+double gemm_tile_cost(int64_t M, int64_t N, int64_t K, int64_t batch) {
+  return pick_tiles(M, N, batch, w8_applies(M, N, K), 0, 0, false).cost;
+}
 
 nvfp4_status launch_gemm(const GemmProblem &p, hipStream_t s) {
   if (p.batch == 0 || p.M == 0 || p.N == 0) return NVFP4_OK;
@@ -1127,12 +1236,20 @@ nvfp4_status launch_gemm(const GemmProblem &p, hipStream_t s) {
   g.lr_l2 = p.lr_l2;
   g.lr_r = p.lr_r;
   g.lr_beta = p.lr_beta;
-  // The 8-wavefront kernel's loads use 32-bit offsets within an operand and
-  // 24-bit row and row-size factors.
+  g.ct = p.c_transposed;
+  auto a16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  const bool c_vec = !p.c_bf16 && p.ldc % 4 == 0 && p.bstride_c % 4 == 0 && a16(p.c);
+  const bool cin_vec = !p.cin || (p.ldcin % 4 == 0 && p.bstride_cin % 4 == 0 && a16(p.cin));
+  if (g.ct) {
+    if (p.c_bf16 || p.lr_t) return NVFP4_EUNSUPPORTED;
+    if (!c_vec || !cin_vec) return NVFP4_EALIGN;
+  }
+  g.staged = c_vec && cin_vec && (g.ct || p.cin);
   const bool fast = p.K % BK == 0;
+  // operands small enough for 32-bit load offsets (the 8-wavefront kernels, the 4-wavefront offset variant)
   const bool small = p.M * (p.K / 2) < ((int64_t)1 << 31) && p.N * (p.K / 2) < ((int64_t)1 << 31) &&
                      p.M < (1 << 24) && p.N < (1 << 24) && p.K / 2 < (1 << 24);
-  const TilePick tp = pick_tiles(p.M, p.N, p.batch, fast && small, p.tile_m, p.tile_n, p.lr_t != nullptr);
+  const TilePick tp = pick_tiles(p.M, p.N, p.batch, w8_applies(p.M, p.N, p.K), p.tile_m, p.tile_n, p.lr_t != nullptr);
   if (tp.kind < 0) return NVFP4_EUNSUPPORTED;
   const int64_t tm = (p.M + tp.bm - 1) / tp.bm, tn = (p.N + tp.bn - 1) / tp.bn;
   if (tm * tn > 0x7FFFFFFF) return NVFP4_EUNSUPPORTED;

@@ -92,7 +92,16 @@ struct GemmProblem {
   const uint16_t *lr_t, *lr_l2;  // optional low-rank BF16 term lr_beta * T L2^T (batch 1)
   int64_t lr_r;
   float lr_beta;
+  // Store the product transposed: element (m, n) at n * ldc + m, the addend
+  // read the same way (FP32 output, ldc / ldcin / batch strides multiples of
+  // 4 and C / cin 16-byte aligned; no low-rank term).
+  bool c_transposed;
 };
+
+// Relative time of the automatic tile choice for an M x N product (units of
+// tile area; lower is faster): lets a caller that may compute either C or
+// C^T pick the orientation that fills the GPU better.
+double gemm_tile_cost(int64_t M, int64_t N, int64_t K, int64_t batch);
 
 // Exact order statistic of |x| (radix select): state->value = the element of
 // rank `rank` (0-based, ascending by the bit pattern of |x|) of x [rows][cols]

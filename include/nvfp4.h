@@ -412,7 +412,12 @@ nvfp4_status nvfp4_qadamw_decode(const nvfp4_qadamw_state *state, uint64_t rht_s
 typedef struct nvfp4_ns_cfg {
   double clip_quantile;  /* in (0, 1]; 0.99 is the page's p99 */
   uint32_t clip_mask;    /* bit 0: X, bit 1: A, bit 2: B; 0: no clipping */
-  uint32_t reserved;     /* must be 0 */
+  uint32_t product;      /* how B^ X^ is launched: 0 automatic, 1 as the [m][n]
+                            product, 2 as its transpose X^T^ B^^T ([n][m], the
+                            workgroup tiles of the [n][m] shape may fill the GPU
+                            better) stored transposed.  The same products and
+                            sums either way; 0 picks the one with fewer rounds
+                            of workgroup tiles. */
 } nvfp4_ns_cfg;
 
 size_t nvfp4_ns_workspace_size(int64_t m, int64_t n);

@@ -297,7 +297,7 @@ def test_ns_argument_errors_and_layout():
     assert call(c=nv.NsCfgC(0.0, 1, 0)) == nv.EINVAL
     assert call(c=nv.NsCfgC(1.5, 1, 0)) == nv.EINVAL
     assert call(c=nv.NsCfgC(0.99, 8, 0)) == nv.EINVAL
-    assert call(c=nv.NsCfgC(0.99, 1, 1)) == nv.EINVAL
+    assert call(c=nv.NsCfgC(0.99, 1, 3)) == nv.EINVAL
     assert call(mm=24) == nv.ESHAPE
     assert call(ldg=n - 4) == nv.ESHAPE
     assert call(ldg=n + 2) == nv.EALIGN

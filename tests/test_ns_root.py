@@ -44,8 +44,13 @@ def test_gemm_axpby_matches_oracle(m, n, k, beta):
     cd = c.to(DEV).clone()
     nv.gemm_axpby(qa, qb, cd, beta, alpha=0.75, out=cd)
     yb = nv.gemm_axpby(qa, qb, c.to(DEV), beta, alpha=0.75, out_dtype=torch.bfloat16)
+    # an addend row stride that is not a multiple of 4 (no 16-byte row segments)
+    cw = torch.zeros(m, n + 1, device=DEV)
+    cw[:, :n] = c.to(DEV)
+    yw = nv.gemm_axpby(qa, qb, cw[:, :n], beta, alpha=0.75)
     torch.cuda.synchronize()
     assert torch.equal(cd.cpu(), y[0].cpu())
+    assert torch.equal(yw.cpu(), y.cpu())
     check_gemm(yb[0].float().cpu().numpy(), y_ref, sabs, True, "axpby bf16")
 
 
@@ -100,15 +105,19 @@ def check_last_step(g, m, n, coeffs, q, mask, ws, x_out, rows=None, what=""):
 
 @pytest.mark.parametrize("m,n", [(16, 16), (32, 48), (48, 160), (128, 384), (272, 400), (384, 512)])
 @pytest.mark.parametrize("mask", [0, 1, 7])
-def test_ns_steps_match_oracle(m, n, mask):
+@pytest.mark.parametrize("product", [1, 2])
+def test_ns_steps_match_oracle(m, n, mask, product):
+    """Both launches of B^ X^ (as [m][n], and as its transpose stored
+    transposed, through partial workgroup tiles at these sizes)."""
     g = torch.from_numpy(_f32((m, n), m * n + mask, 1e-2)).to(torch.bfloat16)
     coeffs = [(3.4445, -4.775, 2.0315), (1.875, -1.25, 0.375), (1.5, -0.5, 0.0)]
     ws = nv.new_workspace(nv.nvfp4_ns_workspace_size(m, n), DEV)
     gd = g.to(DEV)
     for k in range(1, 4):
-        x = nv.ns_orthogonalize(gd, coeffs[:k], 0.99, mask, workspace=ws)
+        x = nv.ns_orthogonalize(gd, coeffs[:k], 0.99, mask, workspace=ws, product=product)
         torch.cuda.synchronize()
-        check_last_step(g, m, n, coeffs[:k], 0.99, mask, ws, x, what=f"{m}x{n} mask {mask} step {k}")
+        check_last_step(g, m, n, coeffs[:k], 0.99, mask, ws, x,
+                        what=f"{m}x{n} mask {mask} product {product} step {k}")
 
 
 def test_ns_fp32_input_strided_output_and_zero_steps():
@@ -122,10 +131,11 @@ def test_ns_fp32_input_strided_output_and_zero_steps():
     fg = np.float32(nv.ns_internals(ws, m, n)["inv_norm"].item())
     np.testing.assert_array_equal(x0.cpu().numpy(), g.numpy() * fg)
     assert np.abs(x0.cpu().numpy() - want).max() <= 1e-6 * np.abs(want).max()
-    x = nv.ns_orthogonalize(g.to(DEV), [(1.5, -0.5, 0.0)], 0.5, 7, out=out[:, :n], workspace=ws)
-    torch.cuda.synchronize()
-    check_last_step(g, m, n, [(1.5, -0.5, 0.0)], 0.5, 7, ws, x, what="fp32 strided")
-    assert (out[:, n:] == 9.0).all()
+    for product in (1, 2):
+        x = nv.ns_orthogonalize(g.to(DEV), [(1.5, -0.5, 0.0)], 0.5, 7, out=out[:, :n], workspace=ws, product=product)
+        torch.cuda.synchronize()
+        check_last_step(g, m, n, [(1.5, -0.5, 0.0)], 0.5, 7, ws, x, what=f"fp32 strided, product {product}")
+        assert (out[:, n:] == 9.0).all()
 
 
 def test_ns_full_size():
@@ -141,8 +151,13 @@ def test_ns_full_size():
     rows = np.sort(np.random.default_rng(9).choice(m, 1024, replace=False))
     X = check_last_step(g, m, n, co, q, mask, ws, x, rows=rows, what="ns_3b step 5")
     sv = np.linalg.svd(X[:512].astype(np.float64), compute_uv=False)
+    # The other launch of B^ X^ (automatic is the transposed one here): the
+    # same products and sums, the same bits.
+    x1 = nv.ns_orthogonalize(g.to(DEV), co, q, mask, product=1)
+    torch.cuda.synchronize()
+    assert torch.equal(x1.view(torch.int32), x.view(torch.int32))
     print(f"\nparity ns_3b: step 5 checked on {rows.size} rows; singular values of 512 rows in "
-          f"[{sv.min():.3f}, {sv.max():.3f}]", flush=True)
+          f"[{sv.min():.3f}, {sv.max():.3f}]; both launches of B^ X^ bit-identical", flush=True)
 
 
 def _ns_clip_value(g: torch.Tensor, q: float):
