@@ -7,6 +7,7 @@
 // the Hadamard mixing of section 2.2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -591,9 +592,10 @@ namespace {
 
 // Workspace: three quantize control blocks, three select states (X, A, B)
 // and their shared 4096-counter histogram and compact buffer, the normalization partials, the second iterate
-// buffer, A and B in FP32, and the four quantized views; 256-byte regions.
+// buffer, A and B in FP32, the partial tiles of the symmetric products, and
+// the four quantized views; 256-byte regions.
 struct NsLayout {
-  size_t ctrl[3], sel[3], hist, compact, partial, inv, xbuf, a, b;
+  size_t ctrl[3], sel[3], hist, compact, partial, inv, xbuf, a, b, sym, sym_bytes;
   uint64_t cap;  // keys the select's compact buffer holds
   size_t codes[4], scales[4], st[4];
   int64_t rows[4], cols[4];
@@ -612,7 +614,7 @@ NsLayout ns_layout(int64_t m, int64_t n) {
   for (int i = 0; i < 3; ++i) L.sel[i] = take(sizeof(nvfp4::SelectState));
   L.hist = take(4096 * sizeof(uint32_t));
   // the select's bracket copy: a sixteenth of the larger operand (the
-  // bracket holds about 1.6% of it; more falls back to the full passes)
+  // bracket holds about 5% of it; more falls back to the full passes)
   L.cap = ((uint64_t)m * (uint64_t)(n > m ? n : m)) / 16 + 1024;
   L.compact = take(L.cap * sizeof(uint32_t));
   L.partial = take(1024 * sizeof(double));
@@ -620,6 +622,8 @@ NsLayout ns_layout(int64_t m, int64_t n) {
   L.xbuf = take((size_t)m * (size_t)n * 4);
   L.a = take((size_t)m * (size_t)m * 4);
   L.b = take((size_t)m * (size_t)m * 4);
+  L.sym_bytes = std::max(nvfp4::gemm_symmetric_partial_bytes(m, n), nvfp4::gemm_symmetric_partial_bytes(m, m));
+  L.sym = take(L.sym_bytes);
   const int64_t shapes[4][2] = {{m, n}, {n, m}, {m, m}, {m, m}};
   for (int i = 0; i < 4; ++i) {
     L.rows[i] = shapes[i][0];
@@ -738,8 +742,11 @@ NVFP4_EXPORT nvfp4_status nvfp4_ns_orthogonalize(const void *g, int32_t g_dtype,
     nvfp4::QuantProblem qxt = make_quant(Xc, false, 1, m, n, ldc_, m * ldc_, true, &rne, &vXT, base + L.ctrl[0]);
     r = nvfp4::launch_quantize_dual(qx, qxt, s);
     if (r != NVFP4_OK) return r;
-    // A = X X^T
-    r = nvfp4::launch_gemm(make_gemm(&vX, &vX, A, NVFP4_F32, m, m * m, 1.0f), s);
+    // A = X X^T (symmetric: the upper triangle split along K, where it applies)
+    float *part = reinterpret_cast<float *>(base + L.sym);
+    const nvfp4::GemmProblem pa = make_gemm(&vX, &vX, A, NVFP4_F32, m, m * m, 1.0f);
+    r = nvfp4::launch_gemm_symmetric(pa, part, L.sym_bytes, s);
+    if (r == NVFP4_EUNSUPPORTED) r = nvfp4::launch_gemm(pa, s);
     if (r != NVFP4_OK) return r;
     const float *clip_a = nullptr;
     if (cfg->clip_mask & 2u) {
@@ -757,7 +764,8 @@ NVFP4_EXPORT nvfp4_status nvfp4_ns_orthogonalize(const void *g, int32_t g_dtype,
     pb.ldcin = m;
     pb.bstride_cin = m * m;
     pb.beta = cb;
-    r = nvfp4::launch_gemm(pb, s);
+    r = nvfp4::launch_gemm_symmetric(pb, part, L.sym_bytes, s);
+    if (r == NVFP4_EUNSUPPORTED) r = nvfp4::launch_gemm(pb, s);
     if (r != NVFP4_OK) return r;
     const float *clip_b = nullptr;
     if (cfg->clip_mask & 4u) {

@@ -49,6 +49,7 @@
 // kGroupM tile rows, to keep A and B panels in that XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -97,6 +98,10 @@ struct GemmArgs {
   const uint16_t *lr_t, *lr_l2;
   int64_t lr_r;
   float lr_beta;
+  // symmetric split-K (A^ A^^T): tiles per side, splits, K steps per split,
+  // and the partial tiles [pair * splits + split][BM][BM]
+  int sym_t, sym_splits, sym_steps;
+  float *sym_part;
   bool ct;      // C stored transposed: tile element (r, c) at c * ldc + r (FP32)
   bool staged;  // FP32 output with an addend or transposed, C and cin 16-byte aligned
                 // with strides multiples of 4: full tiles go through the LDS patch
@@ -507,13 +512,14 @@ __device__ __forceinline__ void lowrank_init(floatx16 (&acc)[kFragM][kFragN], co
 constexpr int kTPitch = 36;
 constexpr int kTPatchBytes = 32 * kTPitch * 4;
 
-template <int kFragN, bool kBF16Out>
+// kRaw: store the accumulators unscaled (split-K partial tiles).
+template <int kFragN, bool kBF16Out, bool kRaw = false>
 __device__ __forceinline__ void store_tile(const floatx16 (&acc)[kFragM][kFragN], const GemmArgs &g, int64_t batch,
                                            int64_t wrow0, int64_t wcol0, float *tpatch) {
   using OutT = typename std::conditional<kBF16Out, uint16_t, float>::type;
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5, r32 = lane & 31;
-  const float sc = g.lr_t ? lowrank_factors(g).y : (*g.a_st * *g.b_st) * g.alpha;
+  const float sc = kRaw ? 1.0f : (g.lr_t ? lowrank_factors(g).y : (*g.a_st * *g.b_st) * g.alpha);
   OutT *cb_ptr = static_cast<OutT *>(g.c) + batch * g.bstride_c;
   const int64_t row0 = wrow0 + 4 * h;
   const int64_t col0 = wcol0 + r32;
@@ -668,25 +674,45 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[kFragM][kFragN]
   }
 }
 
-template <int kFragN, bool kFast, bool kBF16Out, bool kOff32>
+// kSym: one (tile pair, K range) item of a symmetric product split along K
+// (the upper-triangle tile (I, J), I <= J, over K steps [split * sym_steps,
+// ...)), stored unscaled as a partial tile; sym_reduce_kernel finishes it.
+template <int kFragN, bool kFast, bool kBF16Out, bool kOff32, bool kSym = false>
 __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
   constexpr int kBN = 64 * kFragN;
+  static_assert(!kSym || (kFragN == 4 && kFast && !kBF16Out), "split-K items are square FP32 tiles");
   // Two stages as separate objects: the compiler can then tell a read of one
   // from a global->LDS load in flight into the other and does not wait for it.
   __shared__ Stage<kBN> st0, st1;
 
-  // XCD-aware tile order: consecutive workgroups go to different XCDs, so
-  // give XCD x the x-th contiguous slice of the grouped tile order.
-  const int ntiles = g.tiles_m * g.tiles_n;
-  const int bid = blockIdx.x;
-  const int per_xcd = ntiles / 8;
-  const int t = (ntiles % 8 == 0) ? (bid % 8) * per_xcd + bid / 8 : bid;
-  const int group = t / (kGroupM * g.tiles_n);
-  const int first_m = group * kGroupM;
-  const int gm = min(g.tiles_m - first_m, kGroupM);
-  const int in_group = t - group * kGroupM * g.tiles_n;
-  const int tm = first_m + in_group % gm;
-  const int tn = in_group / gm;
+  int tm, tn;
+  int64_t kbeg = 0;  // first K element of this item
+  int ksteps = (int)((g.K + BK - 1) / BK);
+  if constexpr (kSym) {
+    const int pair = (int)blockIdx.x / g.sym_splits, split = (int)blockIdx.x - pair * g.sym_splits;
+    int row = 0, rem = pair;  // row-major upper triangle: row I holds T - I pairs
+    while (rem >= g.sym_t - row) {
+      rem -= g.sym_t - row;
+      ++row;
+    }
+    tm = row;
+    tn = row + rem;
+    kbeg = (int64_t)split * g.sym_steps * BK;
+    ksteps = min(g.sym_steps, ksteps - split * g.sym_steps);
+  } else {
+    // XCD-aware tile order: consecutive workgroups go to different XCDs, so
+    // give XCD x the x-th contiguous slice of the grouped tile order.
+    const int ntiles = g.tiles_m * g.tiles_n;
+    const int bid = blockIdx.x;
+    const int per_xcd = ntiles / 8;
+    const int t = (ntiles % 8 == 0) ? (bid % 8) * per_xcd + bid / 8 : bid;
+    const int group = t / (kGroupM * g.tiles_n);
+    const int first_m = group * kGroupM;
+    const int gm = min(g.tiles_m - first_m, kGroupM);
+    const int in_group = t - group * kGroupM * g.tiles_n;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+  }
 
   const int64_t batch = blockIdx.y;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * kBN;
@@ -694,10 +720,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, r32 = lane & 31;
 
-  const uint8_t *ac = g.a_codes + batch * g.M * (g.K / 2);
-  const uint8_t *as = g.a_scales + batch * g.M * (g.K / 16);
-  const uint8_t *bc = g.b_codes + batch * g.N * (g.K / 2);
-  const uint8_t *bs = g.b_scales + batch * g.N * (g.K / 16);
+  // (K stays the row stride; a split item starts kbeg elements in)
+  const uint8_t *ac = g.a_codes + batch * g.M * (g.K / 2) + kbeg / 2;
+  const uint8_t *as = g.a_scales + batch * g.M * (g.K / 16) + kbeg / 16;
+  const uint8_t *bc = g.b_codes + batch * g.N * (g.K / 2) + kbeg / 2;
+  const uint8_t *bs = g.b_scales + batch * g.N * (g.K / 16) + kbeg / 16;
 
   floatx16 acc[kFragM][kFragN];
 #pragma unroll
@@ -715,7 +742,6 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
                                               reinterpret_cast<uint8_t *>(&st0), reinterpret_cast<uint8_t *>(&st1));
   }
 
-  const int ksteps = (int)((g.K + BK - 1) / BK);
   if constexpr (kFast && kFragN <= 3) {
     const TileSrc src{ac, as, bc, bs, g.M, g.N, g.K, m0, n0};
     const LaneCoord c{wm, wn, h, r32};
@@ -822,11 +848,28 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
     }
   }
 
-  // The stages are free (the loop ends with a barrier): the staged epilogue
-  // (an addend, or C transposed) uses them.
+  // The stages are free for the staged epilogue (an addend, C transposed, or
+  // a partial tile): every wave has passed the main loop's last barrier, no
+  // global->LDS load is in flight, and what a wave still reads from the
+  // stages after that barrier is never used.
   static_assert(4 * kTPatchBytes <= sizeof(Stage<kBN>), "transpose patches fit a stage");
-  store_tile<kFragN, kBF16Out>(acc, g, batch, m0 + wm * 128, n0 + wn * (32 * kFragN),
-                               reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(&st0) + wave * kTPatchBytes));
+  float *patch = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(&st0) + wave * kTPatchBytes);
+  if constexpr (kSym) {
+    // the partial tile, unscaled, [BM][BM] row-major
+    GemmArgs gp = g;
+    gp.c = g.sym_part + (int64_t)blockIdx.x * (BM * kBN);
+    gp.M = BM;
+    gp.N = kBN;
+    gp.ldc = kBN;
+    gp.bstride_c = 0;
+    gp.cin = nullptr;
+    gp.lr_t = nullptr;
+    gp.ct = false;
+    gp.staged = true;
+    store_tile<kFragN, false, true>(acc, gp, 0, wm * 128, wn * (32 * kFragN), patch);
+  } else {
+    store_tile<kFragN, kBF16Out>(acc, g, batch, m0 + wm * 128, n0 + wn * (32 * kFragN), patch);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1205,7 +1248,150 @@ TilePick pick_tiles(int64_t M, int64_t N, int64_t batch, bool fast, int force_bm
   return pick;
 }
 
+// Finish a symmetric split-K product: for tile pair (I, J) and a 64 x 64
+// sub-block of it, add the partial tiles in split order, y = fl(fl(sum * s) +
+// fl(beta * c)) at (r, c), and when I != J the same sums at the mirrored
+// position (c, r) with that position's addend (the sums go through LDS to be
+// read back by the mirror's rows).
+struct SymArgs {
+  const float *part;
+  int T, S;
+  int64_t m;
+  const float *a_st, *b_st;
+  float alpha;
+  const float *cin;  // optional [m][m], row stride ldcin
+  int64_t ldcin;
+  float beta;
+  float *c;  // [m][m], row stride ldc
+  int64_t ldc;
+};
+
+__global__ __launch_bounds__(256) void sym_reduce_kernel(SymArgs a) {
+  __shared__ float tr[64][65];
+  const int pair = (int)blockIdx.x >> 4, sub = (int)blockIdx.x & 15;
+  int I = 0, rem = pair;
+  while (rem >= a.T - I) {
+    rem -= a.T - I;
+    ++I;
+  }
+  const int J = I + rem;
+  const int sr = sub >> 2, sc4 = sub & 3;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const float s = (*a.a_st * *a.b_st) * a.alpha;
+  const int64_t R0 = (int64_t)I * BM + 64 * sr, C0 = (int64_t)J * BM + 64 * sc4;
+  const float *p0 = a.part + (int64_t)pair * a.S * (BM * BM) + (64 * sr) * BM + 64 * sc4 + 4 * tx;
+  float4 y[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = ty + 16 * q;
+    const float *p = p0 + row * BM;
+    float4 t = *reinterpret_cast<const float4 *>(p);
+    for (int k = 1; k < a.S; ++k) {
+      const float4 u = *reinterpret_cast<const float4 *>(p + (int64_t)k * (BM * BM));
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
+    }
+    y[q] = make_float4(t.x * s, t.y * s, t.z * s, t.w * s);
+    const int64_t r = R0 + row, c = C0 + 4 * tx;  // m % 16 == 0: c < m covers c + 3
+    if (r < a.m && c < a.m) {
+      float4 o = y[q];
+      if (a.cin) {
+        const float4 x = *reinterpret_cast<const float4 *>(a.cin + r * a.ldcin + c);
+        o.x += a.beta * x.x;
+        o.y += a.beta * x.y;
+        o.z += a.beta * x.z;
+        o.w += a.beta * x.w;
+      }
+      *reinterpret_cast<float4 *>(a.c + r * a.ldc + c) = o;
+    }
+  }
+  if (I == J) return;  // a diagonal tile holds both orders itself (block-uniform)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = ty + 16 * q;
+    tr[row][4 * tx] = y[q].x;
+    tr[row][4 * tx + 1] = y[q].y;
+    tr[row][4 * tx + 2] = y[q].z;
+    tr[row][4 * tx + 3] = y[q].w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int mr = ty + 16 * q;  // the mirror's row: column mr of the sub-block
+    const int64_t r = C0 + mr, c = R0 + 4 * tx;
+    if (r < a.m && c < a.m) {
+      float4 o = make_float4(tr[4 * tx][mr], tr[4 * tx + 1][mr], tr[4 * tx + 2][mr], tr[4 * tx + 3][mr]);
+      if (a.cin) {
+        const float4 x = *reinterpret_cast<const float4 *>(a.cin + r * a.ldcin + c);
+        o.x += a.beta * x.x;
+        o.y += a.beta * x.y;
+        o.z += a.beta * x.z;
+        o.w += a.beta * x.w;
+      }
+      *reinterpret_cast<float4 *>(a.c + r * a.ldc + c) = o;
+    }
+  }
+}
+
+// Tiles per side, tile pairs, splits and K steps per split of a symmetric
+// split-K product, or splits < 2 where it does not apply.
+struct SymPlan {
+  int T, P, S, steps;
+};
+
+SymPlan sym_plan(int64_t m, int64_t K) {
+  SymPlan p{0, 0, 0, 0};
+  if (m <= 0 || K <= 0 || K % BK || m % 16 || !w8_applies(m, m, K)) return p;
+  const int64_t T = (m + BM - 1) / BM, P = T * (T + 1) / 2, ks = K / BK;
+  if (P > 128) return p;
+  int64_t S = std::min<int64_t>(256 / P, ks);
+  if (S < 2) return p;
+  const int64_t steps = (ks + S - 1) / S;
+  S = (ks + steps - 1) / steps;  // no empty split
+  if (S < 2) return p;
+  p = SymPlan{(int)T, (int)P, (int)S, (int)steps};
+  return p;
+}
+
 }  // namespace
+
+size_t gemm_symmetric_partial_bytes(int64_t m, int64_t K) {
+  const SymPlan p = sym_plan(m, K);
+  return p.S < 2 ? 0 : (size_t)p.P * p.S * BM * BM * sizeof(float);
+}
+
+nvfp4_status launch_gemm_symmetric(const GemmProblem &p, float *part, size_t part_bytes, hipStream_t s) {
+  auto a16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  if (p.batch != 1 || p.M != p.N || p.a_codes != p.b_codes || p.a_scales != p.b_scales || p.a_st != p.b_st ||
+      p.c_bf16 || p.c_transposed || p.lr_t || p.ldc % 4 || !a16(p.c) ||
+      (p.cin && (p.ldcin % 4 || !a16(p.cin))) || p.tile_m || p.tile_n)
+    return NVFP4_EUNSUPPORTED;
+  const SymPlan sp = sym_plan(p.M, p.K);
+  if (sp.S < 2) return NVFP4_EUNSUPPORTED;
+  if (!part || part_bytes < (size_t)sp.P * sp.S * BM * BM * sizeof(float) || !a16(part)) return NVFP4_EWORKSPACE;
+  GemmArgs g{};
+  g.a_codes = p.a_codes;
+  g.a_scales = p.a_scales;
+  g.a_st = p.a_st;
+  g.b_codes = p.b_codes;
+  g.b_scales = p.b_scales;
+  g.b_st = p.b_st;
+  g.M = p.M;
+  g.N = p.N;
+  g.K = p.K;
+  g.alpha = p.alpha;
+  g.sym_t = sp.T;
+  g.sym_splits = sp.S;
+  g.sym_steps = sp.steps;
+  g.sym_part = part;
+  hipLaunchKernelGGL((gemm_nvfp4_kernel<4, true, false, true, true>), dim3((unsigned)(sp.P * sp.S)), dim3(kThreads),
+                     0, s, g);
+  SymArgs r{part, sp.T, sp.S, p.M, p.a_st, p.b_st, p.alpha, p.cin, p.ldcin, p.beta, static_cast<float *>(p.c), p.ldc};
+  hipLaunchKernelGGL(sym_reduce_kernel, dim3((unsigned)(sp.P * 16)), dim3(256), 0, s, r);
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
 
 double gemm_tile_cost(int64_t M, int64_t N, int64_t K, int64_t batch) {
   return pick_tiles(M, N, batch, w8_applies(M, N, K), 0, 0, false).cost;

@@ -103,6 +103,16 @@ struct GemmProblem {
 // C^T pick the orientation that fills the GPU better.
 double gemm_tile_cost(int64_t M, int64_t N, int64_t K, int64_t batch);
 
+// A symmetric product C = alpha s s A^ A^^T (+ beta cin), A^ [m][K] as both
+// operands (the same codes, scales and tensor scale), FP32 C [m][m]: only the
+// upper-triangle 256 x 256 tiles are computed, each split along K so that the
+// items fill the GPU in one round, and a reduction adds the partial tiles in
+// split order and writes both halves.  NVFP4_EUNSUPPORTED where the shape or
+// the arguments do not allow it (the caller then runs launch_gemm);
+// `part` holds gemm_symmetric_partial_bytes(m, K) bytes (0: not applicable).
+size_t gemm_symmetric_partial_bytes(int64_t m, int64_t K);
+nvfp4_status launch_gemm_symmetric(const GemmProblem &p, float *part, size_t part_bytes, hipStream_t stream);
+
 // Exact order statistic of |x| (radix select): state->value = the element of
 // rank `rank` (0-based, ascending by the bit pattern of |x|) of x [rows][cols]
 // (row stride ld; cols and ld multiples of 4, x 16-byte aligned).  `hist`

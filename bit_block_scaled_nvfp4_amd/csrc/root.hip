@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kSampleThreads) void select_sample_kernel(SelArgs a
 // copied out.  One workgroup per CU (few global atomics on the two shared
 // counters, whose same-address updates serialize), four 16-byte loads per
 // thread in flight per round.  A workgroup stages its bracket keys in LDS
-// (an LDS atomic per key; they are about 2% of the keys) and at the end
+// (an LDS atomic per key; they are about 5% of the keys) and at the end
 // reserves their place in the compact buffer with one global atomic; keys
 // beyond the staging space go straight out, one global atomic each.
 constexpr int kBracketThreads = 1024;
