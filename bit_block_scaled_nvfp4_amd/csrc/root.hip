@@ -45,6 +45,16 @@ constexpr int kDigitShift[3] = {19, 8, 0};
 
 __device__ __forceinline__ uint32_t abs_u(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
 
+// Element offset of float4 number v of a tensor with vpr float4 per row and
+// row stride ld: 4 v where the rows are contiguous, else through the row
+// index (a 64-bit division, which would otherwise cost more than the rest of
+// these memory-bound loops).
+__device__ __forceinline__ uint64_t vec_off(uint64_t v, uint64_t vpr, int64_t ld) {
+  if ((uint64_t)ld == 4 * vpr) return 4 * v;
+  const uint64_t r = v / vpr;
+  return r * (uint64_t)ld + 4 * (v - r * vpr);
+}
+
 template <int kPass>
 __device__ __forceinline__ uint32_t digit(uint32_t u) {
   return (u >> kDigitShift[kPass]) & ((1u << kDigitBits[kPass]) - 1u);
@@ -140,8 +150,7 @@ __global__ __launch_bounds__(kBracketThreads) void select_bracket_kernel(SelArgs
     for (int t = 0; t < kBracketUnroll; ++t) {
       // past the end: a clamped (in-bounds) load, masked below
       const uint64_t v = min(v0 + t * stride, nvec - 1);
-      const uint64_t r = v / vpr, c4 = v - r * vpr;
-      q[t] = *reinterpret_cast<const float4 *>(a.x + r * a.ld + 4 * c4);
+      q[t] = *reinterpret_cast<const float4 *>(a.x + vec_off(v, vpr, a.ld));
     }
 #pragma unroll
     for (int t = 0; t < kBracketUnroll; ++t) {
@@ -224,8 +233,7 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelArgs a) {
     const uint64_t nvec = (uint64_t)a.rows * vpr;
     for (uint64_t v = (uint64_t)blockIdx.x * kSelThreads + threadIdx.x; v < nvec;
          v += (uint64_t)gridDim.x * kSelThreads) {
-      const uint64_t r = v / vpr, c4 = v - r * vpr;
-      const float4 q = *reinterpret_cast<const float4 *>(a.x + r * a.ld + 4 * c4);
+      const float4 q = *reinterpret_cast<const float4 *>(a.x + vec_off(v, vpr, a.ld));
       const uint32_t u[4] = {abs_u(q.x), abs_u(q.y), abs_u(q.z), abs_u(q.w)};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -298,13 +306,14 @@ struct NormArgs {
   int64_t xld;
 };
 
-__device__ __forceinline__ float4 load4(const NormArgs &a, uint64_t r, uint64_t c4) {
+// Four elements of g at element offset off.
+__device__ __forceinline__ float4 load4(const NormArgs &a, uint64_t off) {
   if (a.bf16) {
-    const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(a.g) + r * a.ld + 4 * c4);
+    const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(a.g) + off);
     return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
                        __uint_as_float(w.y & 0xFFFF0000u));
   }
-  return *reinterpret_cast<const float4 *>(static_cast<const float *>(a.g) + r * a.ld + 4 * c4);
+  return *reinterpret_cast<const float4 *>(static_cast<const float *>(a.g) + off);
 }
 
 __global__ __launch_bounds__(kSelThreads) void norm_partial_kernel(NormArgs a) {
@@ -314,8 +323,7 @@ __global__ __launch_bounds__(kSelThreads) void norm_partial_kernel(NormArgs a) {
   double s = 0.0;
   for (uint64_t v = (uint64_t)blockIdx.x * kSelThreads + threadIdx.x; v < nvec;
        v += (uint64_t)gridDim.x * kSelThreads) {
-    const uint64_t r = v / vpr, c4 = v - r * vpr;
-    const float4 q = load4(a, r, c4);
+    const float4 q = load4(a, vec_off(v, vpr, a.ld));
     s += (double)q.x * q.x + (double)q.y * q.y + (double)q.z * q.z + (double)q.w * q.w;
   }
   red[threadIdx.x] = s;
@@ -346,9 +354,8 @@ __global__ __launch_bounds__(kSelThreads) void norm_scale_kernel(NormArgs a) {
   const uint64_t nvec = (uint64_t)a.rows * vpr;
   for (uint64_t v = (uint64_t)blockIdx.x * kSelThreads + threadIdx.x; v < nvec;
        v += (uint64_t)gridDim.x * kSelThreads) {
-    const uint64_t r = v / vpr, c4 = v - r * vpr;
-    const float4 q = load4(a, r, c4);
-    *reinterpret_cast<float4 *>(a.x + r * a.xld + 4 * c4) = make_float4(q.x * inv, q.y * inv, q.z * inv, q.w * inv);
+    const float4 q = load4(a, vec_off(v, vpr, a.ld));
+    *reinterpret_cast<float4 *>(a.x + vec_off(v, vpr, a.xld)) = make_float4(q.x * inv, q.y * inv, q.z * inv, q.w * inv);
   }
 }
 
