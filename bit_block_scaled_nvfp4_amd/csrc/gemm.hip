@@ -46,7 +46,8 @@
 //
 // Workgroups are mapped to tiles so that each XCD (blockIdx mod 8 under the
 // round-robin dispatch) works on a contiguous range of tiles, in groups of
-// kGroupM tile rows, to keep A and B panels in that XCD's L2.
+// tile rows (8 for square tiles, 4 where the A tile is the larger), to keep
+// A and B panels in that XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -67,7 +68,7 @@ constexpr int BM = 256, BK = 128;
 constexpr int kThreads = 256;
 constexpr int kRowBytes = BK / 2;  // 64 code bytes per row per K step
 constexpr int kFragM = 4;          // 32-row A fragments per wavefront
-constexpr int kGroupM = 8;         // tile rows per L2 group
+constexpr int kGroupM = 8;         // tile rows per L2 group (square tiles)
 // VALU instructions the scheduler places after each MFMA of a pipelined
 // sub-step (the decode of the next sub-step); 4 and 5 measured best.
 constexpr int kInterleave = 5;
@@ -701,15 +702,19 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_kernel(GemmArgs g) {
     ksteps = min(g.sym_steps, ksteps - split * g.sym_steps);
   } else {
     // XCD-aware tile order: consecutive workgroups go to different XCDs, so
-    // give XCD x the x-th contiguous slice of the grouped tile order.
+    // give XCD x the x-th contiguous slice of the grouped tile order.  Groups
+    // of kGroup tile rows: 8 for the square tile, 4 where the A tile is the
+    // larger (an XCD's 32 concurrent tiles then span 4 x 8 of them, the
+    // least operand data per XCD).
+    constexpr int kGroup = kFragN == 4 ? kGroupM : 4;
     const int ntiles = g.tiles_m * g.tiles_n;
     const int bid = blockIdx.x;
     const int per_xcd = ntiles / 8;
     const int t = (ntiles % 8 == 0) ? (bid % 8) * per_xcd + bid / 8 : bid;
-    const int group = t / (kGroupM * g.tiles_n);
-    const int first_m = group * kGroupM;
-    const int gm = min(g.tiles_m - first_m, kGroupM);
-    const int in_group = t - group * kGroupM * g.tiles_n;
+    const int group = t / (kGroup * g.tiles_n);
+    const int first_m = group * kGroup;
+    const int gm = min(g.tiles_m - first_m, kGroup);
+    const int in_group = t - group * kGroup * g.tiles_n;
     tm = first_m + in_group % gm;
     tn = in_group / gm;
   }
@@ -1104,14 +1109,19 @@ __global__ __launch_bounds__(kW8Threads) void gemm_nvfp4_w8_kernel(GemmArgs g) {
   // from the global->LDS loads in flight into the others.
   __shared__ W8Stage<kBM, kBN> st0, st1, st2;
 
+  // XCD-aware grouped order as in the 4-wavefront kernel; with the tall
+  // 512 x 192 tile (A tiles 2.7 times the B tiles), groups of 4 tile rows
+  // give an XCD's 32 concurrent tiles a 4 x 8 block, the least operand data
+  // per XCD: 51 MB fetched at 8192 x 3072 x 3072 against 70 MB with 8 x 4.
+  constexpr int kGroup = kBM > kBN ? 4 : kGroupM;
   const int ntiles = g.tiles_m * g.tiles_n;
   const int bid = blockIdx.x;
   const int per_xcd = ntiles / 8;
   const int t = (ntiles % 8 == 0) ? (bid % 8) * per_xcd + bid / 8 : bid;
-  const int group = t / (kGroupM * g.tiles_n);
-  const int first_m = group * kGroupM;
-  const int gm = min(g.tiles_m - first_m, kGroupM);
-  const int in_group = t - group * kGroupM * g.tiles_n;
+  const int group = t / (kGroup * g.tiles_n);
+  const int first_m = group * kGroup;
+  const int gm = min(g.tiles_m - first_m, kGroup);
+  const int in_group = t - group * kGroup * g.tiles_n;
   const int tm = first_m + in_group % gm;
   const int tn = in_group / gm;
 
