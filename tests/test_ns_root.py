@@ -54,6 +54,32 @@ def test_gemm_axpby_matches_oracle(m, n, k, beta):
     check_gemm(yb[0].float().cpu().numpy(), y_ref, sabs, True, "axpby bf16")
 
 
+@pytest.mark.parametrize("m,n,k", [(1024, 1024, 256), (3072, 3072, 256), (8192, 3072, 128)])
+def test_gemm_axpby_every_kernel(m, n, k):
+    """The addend epilogue staged through LDS in each kernel the automatic
+    choice takes at these shapes (256x256, 256x192, and the 8-wavefront
+    512x192): 256 seeded rows against the oracle, in place, and with an
+    addend row stride that is not a multiple of 4 (the element-wise epilogue,
+    the same bits)."""
+    rng = np.random.default_rng(m + n + k)
+    a = torch.from_numpy((rng.standard_normal((m, k)) * 2.0).astype(np.float32))
+    b = torch.from_numpy(rng.standard_normal((n, k)).astype(np.float32))
+    c = torch.from_numpy((rng.standard_normal((m, n)) * 3.0).astype(np.float32))
+    qa, qb = nv.quantize(a.to(DEV)), nv.quantize(b.to(DEV))
+    cd = c.to(DEV)
+    y = nv.gemm_axpby(qa, qb, cd, -1.25, alpha=0.75)
+    yi = cd.clone()
+    nv.gemm_axpby(qa, qb, yi, -1.25, alpha=0.75, out=yi)
+    cw = torch.zeros(m, n + 1, device=DEV)
+    cw[:, :n] = cd
+    yw = nv.gemm_axpby(qa, qb, cw[:, :n], -1.25, alpha=0.75)
+    torch.cuda.synchronize()
+    assert torch.equal(yi, y[0]) and torch.equal(yw, y)
+    rows = np.sort(rng.choice(m, 256, replace=False))
+    y_ref, sabs = O.gemm_axpby_ref(to_oracle_view(qa), to_oracle_view(qb), 0.75, c.numpy(), -1.25, rows=rows)
+    check_gemm(y[0].cpu().numpy()[rows], y_ref, sabs, False, f"axpby {m}x{n}x{k}")
+
+
 def _oracle_rows(qa, qb, alpha, rows):
     (y, s), = gemm_ref_tasks(qa, qb, alpha, [(0, rows)])
     return y, s
