@@ -186,6 +186,24 @@ def test_ns_full_size():
           f"[{sv.min():.3f}, {sv.max():.3f}]; both launches of B^ X^ bit-identical", flush=True)
 
 
+def test_ns_ragged_large_both_launches():
+    """3008x8192, one step: B^ X^ as the [8192][3008] transposed launch takes
+    the 8-wavefront 512x192 tiles with a ragged last tile column, and the
+    Gram products the symmetric split-K with a ragged last tile.  The step is
+    checked on 256 rows against the oracle, and the direct launch must give
+    the same bits."""
+    m, n = 3008, 8192
+    g = torch.from_numpy(_f32((m, n), 31, 1e-2)).to(torch.bfloat16)
+    co = [(1.875, -1.25, 0.375)]
+    ws = nv.new_workspace(nv.nvfp4_ns_workspace_size(m, n), DEV)
+    x = nv.ns_orthogonalize(g.to(DEV), co, 0.99, 1, workspace=ws, product=2)
+    x1 = nv.ns_orthogonalize(g.to(DEV), co, 0.99, 1, product=1)
+    torch.cuda.synchronize()
+    assert torch.equal(x1.view(torch.int32), x.view(torch.int32))
+    rows = np.sort(np.random.default_rng(3).choice(m, 256, replace=False))
+    check_last_step(g, m, n, co, 0.99, 1, ws, x, rows=rows, what="3008x8192 step 1")
+
+
 def _ns_clip_value(g: torch.Tensor, q: float):
     m, n = g.shape
     ws = nv.new_workspace(nv.nvfp4_ns_workspace_size(m, n), DEV)
