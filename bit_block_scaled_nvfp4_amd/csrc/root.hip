@@ -6,26 +6,29 @@
 //
 // Radix select.  For x >= 0 the IEEE bit patterns order like the values
 // (NaN patterns above +inf), so the k-th smallest |x| is found digit by
-// digit on u = bits(x) & 0x7FFFFFFF: bits 30..19 (12), 18..8 (11), 7..0 (8).
-// Pass p histograms digit p of the elements whose higher digits equal the
-// prefix found so far (LDS bins per workgroup, one global atomic add per
-// nonzero bin), then one workgroup scans the histogram, narrows the prefix
-// and the rank left inside it, and clears the histogram for the next pass or
-// call.  Counts are exact integers, so the result does not depend on the
-// order of the atomics.  The first digit is the widest: every element
-// counts in that pass, and real data crowd into a few exponents, whose bins
-// the LDS atomics then serialize on.
+// digit on the keys u = bits(x) & 0x7FFFFFFF, taken relative to a base
+// (d = u - base, of which the low W bits vary): digits of up to 12, 12 and 8
+// bits from the top of those W bits.  Pass p histograms digit p of the keys
+// whose higher digits equal the prefix found so far (LDS bins per workgroup,
+// one global atomic add per nonzero bin), then one workgroup scans the
+// histogram, narrows the prefix and the rank left inside it, and clears the
+// histogram for the next pass or call.  Counts are exact integers, so the
+// result does not depend on the order of the atomics.
 //
 // Sampled bracket.  Before the digit passes, one workgroup sorts 1024 keys
 // sampled at evenly spaced positions and takes the keys 24 sample ranks
 // either side of the target's sample rank as a bracket [lo, hi]; one pass
 // over the tensor counts the keys below lo and copies the keys inside the
 // bracket to a compact buffer (about 5% of them), staged per workgroup in
-// LDS so that each workgroup reserves its space with one atomic.  If the target rank falls inside the bracket, the digit passes
-// run over the compact copy for the rank relative to it; otherwise (a
-// bracket that missed, or more keys than the buffer holds) they run over
-// the tensor as before.  Either way the result is the exact order
-// statistic; the sample only decides how much the digit passes read.
+// LDS so that each workgroup reserves its space with one atomic.  If the
+// target rank falls inside the bracket, the digit passes run over the
+// compact copy for the rank relative to it, with base lo and W the width of
+// hi - lo: the first digit then spreads the bracket's keys over up to 4096
+// bins, where digits of u itself would crowd them into the few exponents
+// they share.  Otherwise (a bracket that missed, or more keys than the
+// buffer holds) they run over the tensor with base 0 and W = 31.  Either way
+// the result is the exact order statistic; the sample only decides how much
+// the digit passes read.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -38,11 +41,6 @@ namespace {
 constexpr int kSelThreads = 256;
 constexpr int kBins = 4096;  // the widest digit's bins (the histogram's size)
 
-// Digit widths and positions: pass 0 bits 30..19, pass 1 bits 18..8, pass 2
-// bits 7..0.
-constexpr int kDigitBits[3] = {12, 11, 8};
-constexpr int kDigitShift[3] = {19, 8, 0};
-
 __device__ __forceinline__ uint32_t abs_u(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
 
 // Element offset of float4 number v of a tensor with vpr float4 per row and
@@ -53,18 +51,6 @@ __device__ __forceinline__ uint64_t vec_off(uint64_t v, uint64_t vpr, int64_t ld
   if ((uint64_t)ld == 4 * vpr) return 4 * v;
   const uint64_t r = v / vpr;
   return r * (uint64_t)ld + 4 * (v - r * vpr);
-}
-
-template <int kPass>
-__device__ __forceinline__ uint32_t digit(uint32_t u) {
-  return (u >> kDigitShift[kPass]) & ((1u << kDigitBits[kPass]) - 1u);
-}
-
-// The higher digits of u, compared with the prefix of pass kPass.
-template <int kPass>
-__device__ __forceinline__ bool in_prefix(uint32_t u, uint32_t prefix) {
-  if constexpr (kPass == 0) return true;
-  else return (u >> kDigitShift[kPass - 1]) == prefix;
 }
 
 struct SelArgs {
@@ -208,6 +194,33 @@ __device__ __forceinline__ uint64_t first_rank(const SelectState *st) {
   return compact_hit(st) ? st->rank0 - st->below : st->rank0;
 }
 
+// The digits of a selection: keys d = u - base whose low W bits vary, and
+// per pass the digit's position and width (bits shift .. shift + width - 1
+// of d; the widths add up to W, the last digit's shift is 0).  Every reader
+// derives it from the bracket's counters, like compact_hit.
+struct DigitPlan {
+  uint32_t base;
+  int shift[3], width[3];
+};
+
+__device__ __forceinline__ DigitPlan digit_plan(const SelectState *st) {
+  DigitPlan p;
+  uint32_t span = 0x7FFFFFFFu;  // the whole tensor: every key
+  p.base = 0u;
+  if (compact_hit(st)) {
+    p.base = st->lo;
+    span = st->hi - st->lo;
+  }
+  const int w = span ? 32 - __clz((int)span) : 0;
+  p.shift[0] = max(w - 12, 0);
+  p.width[0] = w - p.shift[0];
+  p.shift[1] = max(p.shift[0] - 12, 0);
+  p.width[1] = p.shift[0] - p.shift[1];
+  p.shift[2] = 0;
+  p.width[2] = p.shift[1];  // <= 8: w <= 32
+  return p;
+}
+
 // Small tensors skip the bracket: the digit passes run over the tensor.
 __global__ void select_full_kernel(SelectState *st, uint64_t rank) {
   st->mode = 0u;
@@ -216,42 +229,70 @@ __global__ void select_full_kernel(SelectState *st, uint64_t rank) {
 
 template <int kPass>
 __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelArgs a) {
-  constexpr int kN = 1 << kDigitBits[kPass];
-  __shared__ uint32_t bins[kN];
-  for (int i = threadIdx.x; i < kN; i += kSelThreads) bins[i] = 0u;
+  __shared__ uint32_t bins[kBins];
+  for (int i = threadIdx.x; i < kBins; i += kSelThreads) bins[i] = 0u;
   __syncthreads();
+  const DigitPlan pl = digit_plan(a.state);
+  const int sh = pl.shift[kPass];
+  const uint32_t mask = (1u << pl.width[kPass]) - 1u;
+  // keys of this pass: the higher digits (d >> the previous digit's shift)
+  // equal the prefix found so far
+  const int psh = kPass == 0 ? 0 : pl.shift[kPass - 1];
   const uint32_t prefix = kPass == 0 ? 0u : a.state->prefix;
+  auto count = [&](uint32_t u) {
+    const uint32_t d = u - pl.base;
+    if (kPass == 0 || (d >> psh) == prefix) atomicAdd(&bins[(d >> sh) & mask], 1u);
+  };
   if (compact_hit(a.state)) {
-    // the bracket's compact copy: keys already
-    const uint32_t n = a.state->count;
-    for (uint32_t i = blockIdx.x * kSelThreads + threadIdx.x; i < n; i += gridDim.x * kSelThreads) {
-      const uint32_t u = a.compact[i];
-      if (in_prefix<kPass>(u, prefix)) atomicAdd(&bins[digit<kPass>(u)], 1u);
+    // The bracket's compact copy: keys already, all in [lo, hi].  Four keys
+    // per 16-byte load and two loads in flight per thread (one at a time,
+    // the loop waited out a load latency per key); then the last n % 4.
+    const uint32_t n = a.state->count, n4 = n / 4;
+    const uint4 *c4 = reinterpret_cast<const uint4 *>(a.compact);  // 256-byte aligned
+    const uint32_t stride = gridDim.x * kSelThreads;
+    for (uint32_t i = blockIdx.x * kSelThreads + threadIdx.x; i < n4; i += 2 * stride) {
+      const bool two = i + stride < n4;
+      const uint4 k0 = c4[i];
+      const uint4 k1 = c4[two ? i + stride : i];
+      count(k0.x);
+      count(k0.y);
+      count(k0.z);
+      count(k0.w);
+      if (two) {
+        count(k1.x);
+        count(k1.y);
+        count(k1.z);
+        count(k1.w);
+      }
     }
+    const uint32_t t = 4 * n4 + blockIdx.x * kSelThreads + threadIdx.x;
+    if (t < n) count(a.compact[t]);
   } else {
     const uint64_t vpr = (uint64_t)(a.cols / 4);  // float4 per row
     const uint64_t nvec = (uint64_t)a.rows * vpr;
     for (uint64_t v = (uint64_t)blockIdx.x * kSelThreads + threadIdx.x; v < nvec;
          v += (uint64_t)gridDim.x * kSelThreads) {
       const float4 q = *reinterpret_cast<const float4 *>(a.x + vec_off(v, vpr, a.ld));
-      const uint32_t u[4] = {abs_u(q.x), abs_u(q.y), abs_u(q.z), abs_u(q.w)};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (in_prefix<kPass>(u[i], prefix)) atomicAdd(&bins[digit<kPass>(u[i])], 1u);
+      count(abs_u(q.x));
+      count(abs_u(q.y));
+      count(abs_u(q.z));
+      count(abs_u(q.w));
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < kN; i += kSelThreads)
+  for (int i = threadIdx.x; i < kBins; i += kSelThreads)
     if (bins[i]) atomicAdd(&a.hist[i], bins[i]);
 }
 
 // One workgroup: find the bin holding the rank (0-based, ascending) among
-// this pass's elements, narrow the prefix, and clear the histogram.  On the
-// last pass the prefix is the whole pattern: store the value.
+// this pass's elements, narrow the prefix (d >> this digit's shift), and
+// clear the histogram.  On the last pass the prefix is d itself: store the
+// value base + d.
 template <int kPass>
 __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(SelectState *st, uint32_t *hist) {
   __shared__ uint64_t part[kSelThreads];
-  constexpr int kPer = (1 << kDigitBits[kPass]) / kSelThreads;  // bins per thread
+  constexpr int kPer = kBins / kSelThreads;  // bins per thread
+  const DigitPlan pl = digit_plan(st);
   const uint64_t rank = kPass == 0 ? first_rank(st) : st->rank;
   uint32_t c[kPer];
   uint64_t sum = 0;
@@ -280,11 +321,11 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(SelectState *s
       if (b < 0 && rank < below + c[i]) b = i;
       if (b < 0) below += c[i];
     }
-    const uint32_t d = (uint32_t)(threadIdx.x * kPer + b);
-    const uint32_t prefix = kPass == 0 ? d : ((st->prefix << kDigitBits[kPass]) | d);
+    const uint32_t dg = (uint32_t)(threadIdx.x * kPer + b);
+    const uint32_t prefix = kPass == 0 ? dg : ((st->prefix << pl.width[kPass]) | dg);
     st->prefix = prefix;
     st->rank = rank - below;
-    if (kPass == 2) st->value = __uint_as_float(prefix);
+    if (kPass == 2) st->value = __uint_as_float(pl.base + prefix);
   }
   __syncthreads();
 #pragma unroll

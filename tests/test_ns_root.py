@@ -240,3 +240,17 @@ def test_clip_value_when_the_bracket_misses_or_overflows():
     g[0, :7] = [1, 2, 3, 4, 5, 6, 7]
     got, x0 = _ns_clip_value(torch.from_numpy(g), 0.99)
     assert got == O.abs_quantile(x0, 0.99)
+
+
+def test_clip_value_when_the_bracket_is_one_key():
+    """Ties at the target: every 18th element is 1.0 (5.5%, within the compact
+    buffer), the rest uniform in (0, 2), so the median falls among the ties,
+    the sample brackets it with lo == hi, and the digit passes have no bits
+    left to split (the value is lo itself)."""
+    m, n = 384, 512
+    rng = np.random.default_rng(13)
+    g = rng.uniform(0.0, 2.0, size=m * n).astype(np.float32)
+    g[::18] = 1.0
+    got, x0 = _ns_clip_value(torch.from_numpy(g.reshape(m, n)), 0.5)
+    assert got == O.abs_quantile(x0, 0.5)
+    assert (np.abs(x0) == got).sum() >= m * n // 18
