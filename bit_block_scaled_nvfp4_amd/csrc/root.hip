@@ -68,6 +68,7 @@ constexpr int kMargin = 24;      // sample ranks either side of the target's (7.
 
 // Element (flat index i of [rows][cols]) as its key.
 __device__ __forceinline__ uint32_t key_at(const SelArgs &a, uint64_t i) {
+  if (a.ld == a.cols) return abs_u(a.x[i]);
   const uint64_t r = i / (uint64_t)a.cols, c = i - r * (uint64_t)a.cols;
   return abs_u(a.x[r * a.ld + c]);
 }
