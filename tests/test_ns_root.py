@@ -129,7 +129,8 @@ def check_last_step(g, m, n, coeffs, q, mask, ws, x_out, rows=None, what=""):
     return X
 
 
-@pytest.mark.parametrize("m,n", [(16, 16), (32, 48), (48, 160), (128, 384), (272, 400), (384, 512), (640, 1024)])
+@pytest.mark.parametrize("m,n", [(16, 16), (32, 48), (48, 160), (128, 384), (272, 400), (384, 512), (640, 1024),
+                                 (400, 272), (1024, 640)])
 @pytest.mark.parametrize("mask", [0, 1, 7])
 @pytest.mark.parametrize("product", [1, 2])
 def test_ns_steps_match_oracle(m, n, mask, product):
