@@ -9,17 +9,18 @@ inputs already resident in HBM.  Inputs rotate over enough copies to exceed
 twice the 256 MB Infinity Cache, so every step reads its operands from HBM.
 
 Order of work:
-  1. per-call timing, after --settle-ms of untimed steps (the shader clock
-     ramps over the first tens of milliseconds of load): each call of the
-     step launched alone, back to back
-     (`reps` launches over the rotating buffers between two HIP events on the
-     launch stream; the mean is the kernel duration plus the launch gap), and
-     isolated (one launch between events after a device synchronisation);
-  2. W untimed warm-up steps, then exactly K timed steps bracketed by device
-     synchronisation, timed by the host clock; then K more steps, untimed,
-     with an event pair around every call, for each call's duration inside
-     the step (`us_in_step`);
-  3. the CPU oracle on the same step (the `cpu_baseline` leg), which also
+  1. --settle-ms of untimed steps (the shader clock ramps over the first
+     tens of milliseconds of load);
+  2. right after them, W untimed warm-up steps, then exactly K timed steps
+     bracketed by device synchronisation, timed by the host clock;
+  3. K more steps, untimed, with an event pair around every call, for each
+     call's duration inside the step (`us_in_step`); then per-call timing:
+     each call of the step launched alone, back to back (`reps` launches
+     over the rotating buffers between two HIP events on the launch stream;
+     the mean is the kernel duration plus the launch gap), and isolated (one
+     launch between events after a device synchronisation), last because
+     the isolated launches let the shader clock drop;
+  4. the CPU oracle on the same step (the `cpu_baseline` leg), which also
      checks this run's outputs against the oracle.
 
 Prints one JSON line.  `value` is the whole-step NVFP4 GEMM throughput
@@ -246,8 +247,8 @@ def main():
     S = setup(t, dev)
     steps, nbuf = S["steps"], S["nbuf"]
 
-    # 1. per-call timing, after the step has run long enough for the shader
-    #    clock to settle (it ramps over the first ~10-20 ms of load)
+    # 1. untimed steps until the shader clock has settled (it ramps over the
+    #    first ~10-20 ms of load)
     settle_end = time.perf_counter() + args.settle_ms * 1e-3
     i = 0
     while time.perf_counter() < settle_end or i < 2 * nbuf:
@@ -257,6 +258,32 @@ def main():
         if i % nbuf == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    def step(i):
+        for c in steps[i % nbuf]:
+            c()
+
+    # 2. warm-up and the timed region right after, while the clock is up:
+    #    exactly K steps, nothing else on the stream
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+
+    # 3. the same steps once more (untimed), each call between two events:
+    #     the duration of every call inside the step, the dominant one's
+    #     roofline figure (a profiler's per-kernel mean over a run is this)
+    names = []
+    for c in steps[0]:
+        names.append(next(n for n, cs in S["calls"].items() if cs[0] is c))
+    in_step = time_in_step(steps, names, args.steps, args.warmup + args.steps)
+
+    # 3b. per-call timing, last (the isolated launches let the clock drop):
+    #     each call of the step back to back, and isolated
     kernels = {}
     for name, calls in S["calls"].items():
         b2b = time_back_to_back(calls, args.reps)
@@ -272,28 +299,6 @@ def main():
                 info["frac_copy"] = round(gbps / copy_gbps, 4)
         kernels[name] = info
 
-    def step(i):
-        for c in steps[i % nbuf]:
-            c()
-
-    # 2. warm-up and the timed region: exactly K steps, nothing else on the stream
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall / args.steps * 1e3
-
-    # 2b. the same steps once more (untimed), each call between two events:
-    #     the duration of every call inside the step, the dominant one's
-    #     roofline figure (a profiler's per-kernel mean over a run is this)
-    names = []
-    for c in steps[0]:
-        names.append(next(n for n, cs in S["calls"].items() if cs[0] is c))
-    in_step = time_in_step(steps, names, args.steps, args.warmup + args.steps)
     for n, us in in_step.items():
         kernels[n]["us_in_step"] = round(us, 2)
 
@@ -334,7 +339,7 @@ def main():
         "mfma_ceiling": ceiling,
         "cpu_baseline": None,
     }
-    # 3. the oracle on the same step, and this run's outputs against it
+    # 4. the oracle on the same step, and this run's outputs against it
     if not args.no_cpu_baseline and "baseline" in S:
         out["cpu_baseline"] = S["baseline"]()
     print(json.dumps(out), flush=True)
